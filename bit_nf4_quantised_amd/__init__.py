@@ -1,0 +1,220 @@
+"""NF4-quantised QLoRA linear layer on AMD Instinct MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libqlora_nf4.so`` (the C ABI in ``include/qlora_nf4.h``). Every function
+only checks tensor placement and marshals device pointers, sizes and the current HIP stream; all
+computation runs in the library's HIP kernels. PyTorch supplies device memory and streams.
+
+The library must have been built (``python -m bit_nf4_quantised_amd.build``); importing this
+package without it raises ImportError, and there is no CPU fallback.
+
+Operations ("QLoRA, explained", pofe.ai): blockwise absmax NF4 quantisation with two indices per
+byte, double quantisation of the scales to E4M3, two-level dequantisation to bf16, and the adapted
+linear's forward y = x W~^T + s x A^T B^T and backward (dX, dA, dB; no gradient for W).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first with "
+        "`python -m bit_nf4_quantised_amd.build` (hipcc, gfx950). There is no CPU fallback.")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_RANK, NF4_ERR_WORKSPACE, NF4_ERR_HIP = range(7)
+
+
+class CNF4Weight(ctypes.Structure):
+    """Mirror of ``nf4_weight`` in include/qlora_nf4.h."""
+    _fields_ = [("packed", ctypes.c_void_p), ("scale_q", ctypes.c_void_p),
+                ("scale_c2", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+_p, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_W = ctypes.POINTER(CNF4Weight)
+_SIGS = {
+    "nf4_quantize": (ctypes.c_int, [_p, _i64, _p, _p, _p]),
+    "nf4_double_quant": (ctypes.c_int, [_p, _i64, _p, _p, _p]),
+    "nf4_dequant": (ctypes.c_int, [_W, _p, _p]),
+    "qlora_linear_fwd": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz, _p]),
+    "qlora_linear_bwd": (ctypes.c_int, [_W, _p, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _p,
+                                        ctypes.c_int, _p, _sz, _p]),
+    "qlora_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "nf4_storage_bytes": (_i64, [_i64]),
+    "nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
+    "nf4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class NF4Error(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {lib.nf4_status_string(status).decode()} (status {status})")
+
+
+def _check(status: int, call: str) -> None:
+    if status != NF4_OK:
+        raise NF4Error(status, call)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dtype(t, *allowed):
+    if t is not None and t.dtype not in allowed:
+        raise TypeError(f"dtype {t.dtype} not in {allowed}")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+@dataclass
+class NF4Weight:
+    """A quantised, double-quantised N x K weight held in three device tensors."""
+    packed: torch.Tensor     # uint8 [N*K/2]
+    scale_q: torch.Tensor    # uint8 [N*K/64]
+    scale_c2: torch.Tensor   # float32 [ceil(N*K/16384)]
+    N: int
+    K: int
+
+    def c_struct(self) -> CNF4Weight:
+        return CNF4Weight(_ptr(self.packed), _ptr(self.scale_q), _ptr(self.scale_c2), self.N, self.K)
+
+
+# ------------------------------------------------------------------------- the five calls
+def nf4_quantize(w, packed, absmax, stream=None) -> None:
+    _dtype(w, torch.float32); _dtype(packed, torch.uint8); _dtype(absmax, torch.float32)
+    n = w.numel()
+    if packed.numel() * 2 != n or absmax.numel() * 64 != n:
+        raise ValueError("output sizes must be numel/2 and numel/64")
+    _check(lib.nf4_quantize(_ptr(w), n, _ptr(packed), _ptr(absmax), _stream(stream)), "nf4_quantize")
+
+
+def nf4_double_quant(absmax, scale_q, scale_c2, stream=None) -> None:
+    _dtype(absmax, torch.float32); _dtype(scale_q, torch.uint8); _dtype(scale_c2, torch.float32)
+    nb = absmax.numel()
+    if scale_q.numel() != nb or scale_c2.numel() != (nb + 255) // 256:
+        raise ValueError("output sizes must be nblocks and ceil(nblocks/256)")
+    _check(lib.nf4_double_quant(_ptr(absmax), nb, _ptr(scale_q), _ptr(scale_c2), _stream(stream)),
+           "nf4_double_quant")
+
+
+def nf4_dequant(weight: NF4Weight, out, stream=None) -> None:
+    _dtype(out, *_BF16)
+    if out.numel() != weight.N * weight.K:
+        raise ValueError("out must hold N*K values")
+    cw = weight.c_struct()
+    _check(lib.nf4_dequant(ctypes.byref(cw), _ptr(out), _stream(stream)), "nf4_dequant")
+
+
+def qlora_linear_fwd(weight: NF4Weight, x, A, B, scale: float, y, u_out=None, ws=None,
+                     stream=None) -> None:
+    for t in (x, A, B, y):
+        _dtype(t, *_BF16)
+    _dtype(u_out, torch.float32)
+    M = x.shape[0]
+    r = A.shape[0]
+    if x.shape != (M, weight.K) or A.shape != (r, weight.K) or B.shape != (weight.N, r) \
+            or y.shape != (M, weight.N) or (u_out is not None and u_out.numel() != M * r):
+        raise ValueError("shape mismatch")
+    if ws is None:
+        ws = workspace(M, weight.N, weight.K, r, x.device)
+    cw = weight.c_struct()
+    _check(lib.qlora_linear_fwd(ctypes.byref(cw), _ptr(x), M, _ptr(A), _ptr(B), r, scale, _ptr(y),
+                                _ptr(u_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)), "qlora_linear_fwd")
+
+
+def qlora_linear_bwd(weight: NF4Weight, x, dy, A, B, scale: float, u, dx, dA, dB,
+                     accumulate: bool = False, ws=None, stream=None) -> None:
+    for t in (x, dy, A, B, dx):
+        _dtype(t, *_BF16)
+    for t in (u, dA, dB):
+        _dtype(t, torch.float32)
+    M = x.shape[0]
+    r = A.shape[0]
+    if x.shape != (M, weight.K) or dy.shape != (M, weight.N) or A.shape != (r, weight.K) \
+            or B.shape != (weight.N, r) or u.numel() != M * r or dA.shape != (r, weight.K) \
+            or dB.shape != (weight.N, r) or (dx is not None and dx.shape != (M, weight.K)):
+        raise ValueError("shape mismatch")
+    if ws is None:
+        ws = workspace(M, weight.N, weight.K, r, x.device)
+    cw = weight.c_struct()
+    _check(lib.qlora_linear_bwd(ctypes.byref(cw), _ptr(x), _ptr(dy), M, _ptr(A), _ptr(B), r, scale,
+                                _ptr(u), _ptr(dx), _ptr(dA), _ptr(dB), int(bool(accumulate)),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qlora_linear_bwd")
+
+
+# ------------------------------------------------------------------------- helpers
+def qlora_workspace_bytes(M: int, N: int, K: int, r: int) -> int:
+    return int(lib.qlora_workspace_bytes(M, N, K, r))
+
+
+def nf4_storage_bytes(numel: int) -> int:
+    return int(lib.nf4_storage_bytes(numel))
+
+
+def nf4_codebook() -> list:
+    out = (ctypes.c_float * 16)()
+    lib.nf4_codebook(out)
+    return list(out)
+
+
+def workspace(M: int, N: int, K: int, r: int, device="cuda") -> torch.Tensor:
+    """A device workspace large enough for qlora_linear_fwd/bwd at these sizes."""
+    nbytes = max(qlora_workspace_bytes(M, N, K, r), 256)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def empty_weight(N: int, K: int, device="cuda") -> NF4Weight:
+    nb = N * K // 64
+    return NF4Weight(torch.empty(N * K // 2, dtype=torch.uint8, device=device),
+                     torch.empty(nb, dtype=torch.uint8, device=device),
+                     torch.empty((nb + 255) // 256, dtype=torch.float32, device=device), N, K)
+
+
+def quantize_weight(w: torch.Tensor, stream=None, absmax: torch.Tensor | None = None) -> NF4Weight:
+    """Quantise a float32 N x K device tensor: nf4_quantize followed by nf4_double_quant."""
+    N, K = w.shape
+    qw = empty_weight(N, K, w.device)
+    if absmax is None:
+        absmax = torch.empty(N * K // 64, dtype=torch.float32, device=w.device)
+    nf4_quantize(w, qw.packed, absmax, stream)
+    nf4_double_quant(absmax, qw.scale_q, qw.scale_c2, stream)
+    return qw
+
+
+__all__ = ["lib", "LIB_PATH", "EXPORTED", "NF4Error", "NF4Weight", "CNF4Weight", "nf4_quantize",
+           "nf4_double_quant", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_bwd",
+           "qlora_workspace_bytes", "nf4_storage_bytes", "nf4_codebook", "workspace",
+           "empty_weight", "quantize_weight"]

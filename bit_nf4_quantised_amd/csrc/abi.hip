@@ -1,0 +1,157 @@
+// C ABI of the NF4 QLoRA linear layer: host-side validation and kernel sequencing.
+// Declarations and the contract of every call are in include/qlora_nf4.h.
+#include "../../include/qlora_nf4.h"
+
+#include <string.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr uint32_t kCodeBits[16] = {NF4_CODE_BITS};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_weight(const nf4_weight* W) {
+  if (!W || !W->packed || !W->scale_q || !W->scale_c2) return NF4_ERR_NULL;
+  if (W->N < 16 || W->K < 64 || W->N % 16 || W->K % 64) return NF4_ERR_SHAPE;
+  if (W->N > (int64_t(1) << 31) || W->K > (int64_t(1) << 31)) return NF4_ERR_SHAPE;
+  if (!aligned16(W->packed) || !aligned16(W->scale_q) || !aligned16(W->scale_c2)) return NF4_ERR_ALIGN;
+  return NF4_OK;
+}
+
+int check_rank(int32_t r) { return (r >= 16 && r <= 128 && r % 16 == 0) ? NF4_OK : NF4_ERR_RANK; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Workspace layout (bytes, each region 256-aligned):
+//   forward : [u (M*r fp32)] [partials: skinny splits or adapter down-projection chunks]
+//   backward: [v (M*r fp32)] [partials of v]
+size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
+  size_t part = nf4::skinny_eligible(M) ? nf4::skinny_workspace_floats(M, N, K, r)
+                                        : (size_t)nf4::lora_down_chunks(M, K) * M * r;
+  return align_up((size_t)M * r * 4) + align_up(part * 4);
+}
+size_t bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
+  (void)K;
+  size_t part = (size_t)nf4::lora_down_chunks(M, N) * M * r;
+  return align_up((size_t)M * r * 4) + align_up(part * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nf4_status_string(int status) {
+  switch (status) {
+    case NF4_OK: return "ok";
+    case NF4_ERR_NULL: return "a required pointer is NULL";
+    case NF4_ERR_SHAPE: return "a size violates the contract";
+    case NF4_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case NF4_ERR_RANK: return "LoRA rank must be a multiple of 16 in 16..128";
+    case NF4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NF4_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+void nf4_codebook(float out[16]) { memcpy(out, kCodeBits, sizeof(kCodeBits)); }
+
+int64_t nf4_storage_bytes(int64_t numel) {
+  if (numel < 0 || numel % 64) return -1;
+  const int64_t nb = numel / 64;
+  return numel / 2 + nb + 4 * ((nb + 255) / 256);
+}
+
+int nf4_quantize(const float* w, int64_t numel, uint8_t* packed, float* absmax, hipStream_t stream) {
+  if (numel < 0 || numel % 64) return NF4_ERR_SHAPE;
+  if (numel == 0) return NF4_OK;
+  if (!w || !packed || !absmax) return NF4_ERR_NULL;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(absmax)) return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_quantize(w, numel, packed, absmax, stream));
+}
+
+int nf4_double_quant(const float* absmax, int64_t nblocks, uint8_t* scale_q, float* scale_c2,
+                     hipStream_t stream) {
+  if (nblocks < 0) return NF4_ERR_SHAPE;
+  if (nblocks == 0) return NF4_OK;
+  if (!absmax || !scale_q || !scale_c2) return NF4_ERR_NULL;
+  if (!aligned16(absmax) || !aligned16(scale_q) || !aligned16(scale_c2)) return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_double_quant(absmax, nblocks, scale_q, scale_c2, stream));
+}
+
+int nf4_dequant(const nf4_weight* W, uint16_t* out, hipStream_t stream) {
+  int st = check_weight(W);
+  if (st) return st;
+  if (!out) return NF4_ERR_NULL;
+  if (!aligned16(out)) return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_dequant(W->packed, W->scale_q, W->scale_c2, W->N * W->K, out, stream));
+}
+
+size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (M < 0 || N < 16 || K < 64 || N % 16 || K % 64 || check_rank(r)) return 0;
+  if (M == 0) return 0;
+  size_t a = fwd_ws(M, N, K, r), b = bwd_ws(M, N, K, r);
+  return a > b ? a : b;
+}
+
+int qlora_linear_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float scale, uint16_t* y, float* u_out, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  int st = check_weight(W);
+  if (st) return st;
+  if (M < 0) return NF4_ERR_SHAPE;
+  if ((st = check_rank(r))) return st;
+  if (M == 0) return NF4_OK;
+  if (!x || !A || !B || !y) return NF4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) ||
+      (u_out && !aligned16(u_out)) || (ws && !aligned16(ws)))
+    return NF4_ERR_ALIGN;
+  const int64_t N = W->N, K = W->K;
+  const size_t need = fwd_ws(M, N, K, r);
+  if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;
+  float* u = u_out ? u_out : static_cast<float*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
+  if (nf4::skinny_eligible(M)) {
+    return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, N, K, x, M, A, B, r,
+                                           scale, part, u, y, stream));
+  }
+  hipError_t e = nf4::launch_lora_down(x, M, K, A, false, r, part, u, stream);
+  if (e != hipSuccess) return NF4_ERR_HIP;
+  return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, N, K, x, M, u, B, r, scale,
+                                       y, stream));
+}
+
+int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int32_t r, float scale, const float* u,
+                     uint16_t* dx, float* dA, float* dB, int accumulate, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  int st = check_weight(W);
+  if (st) return st;
+  if (M < 0) return NF4_ERR_SHAPE;
+  if ((st = check_rank(r))) return st;
+  if (M == 0) return NF4_OK;
+  if (!x || !dy || !A || !B || !u || !dA || !dB) return NF4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(A) || !aligned16(B) || !aligned16(u) ||
+      (dx && !aligned16(dx)) || !aligned16(dA) || !aligned16(dB) || (ws && !aligned16(ws)))
+    return NF4_ERR_ALIGN;
+  const int64_t N = W->N, K = W->K;
+  const size_t need = bwd_ws(M, N, K, r);
+  if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;
+  float* v = static_cast<float*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
+  hipError_t e = nf4::launch_lora_down(dy, M, N, B, true, r, part, v, stream);
+  if (e != hipSuccess) return NF4_ERR_HIP;
+  if (dx) {
+    e = nf4::launch_dx_gemm(W->packed, W->scale_q, W->scale_c2, N, K, dy, M, v, A, r, scale, dx, stream);
+    if (e != hipSuccess) return NF4_ERR_HIP;
+  }
+  e = nf4::launch_lora_grad(v, x, M, K, r, scale, dA, false, accumulate, stream);
+  if (e != hipSuccess) return NF4_ERR_HIP;
+  return from_hip(nf4::launch_lora_grad(u, dy, M, N, r, scale, dB, true, accumulate, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,218 @@
+// NF4 quantisation, double quantisation and standalone dequantisation kernels (gfx950).
+//
+//   nf4_quantize_kernel      "QLoRA, explained", Blockwise absmax quantisation / NormalFloat 4:
+//                            per block of 64 the absmax and, per value, the nearest code index,
+//                            packed two per byte.
+//   nf4_double_quant_kernel  same page, Double quantisation: scales to E4M3 in groups of 256 with
+//                            one fp32 constant (the group maximum) per group.
+//   nf4_dequant_kernel       same page, The forward pass and gradients: two-level dequantisation
+//                            to bf16 (c1' = fl32(e4m3 * c2), w~ = bf16(fl32(q[idx] * c1'))).
+#include "common.h"
+#include "launch.h"
+
+namespace nf4 {
+
+// ------------------------------------------------------------------------------------------
+// Quantise. One wave handles 8 blocks per iteration: lane l covers 8 consecutive values of block
+// (l / 8). The nearest-code decision must be exact (as if w / c were computed without rounding):
+//   fast path: x = w * (1/c) is within 2^-22.9 of w / c. The 15 decision midpoints of the
+//     codebook, binned on a grid of width 1/16 over [-1, 1], fall one per bin at most and at least
+//     1.6e-3 from any bin edge, so the bin of x gives the count of midpoints below it up to the
+//     one midpoint inside the bin, which is compared directly. If x lies within 2^-20 of that
+//     midpoint, or the block scale is below 2^-100 (1/c could overflow), the value takes the
+//     slow path;
+//   slow path: count the midpoints m_i with w > c * m_i in fp64, where the product of a 24-bit
+//     scale and a <= 26-bit midpoint is exact.
+struct BinEntry {
+  float mid;       // the midpoint inside the bin, or +inf
+  uint32_t base;   // number of midpoints below the bin's lower edge
+};
+
+__device__ __forceinline__ double mid64(int i) {
+  return ((double)code_value(i) + (double)code_value(i + 1)) * 0.5;
+}
+
+__global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restrict__ w,
+                                                           int64_t nblocks,
+                                                           uint32_t* __restrict__ packed,
+                                                           float* __restrict__ absmax) {
+  __shared__ BinEntry tab[33];
+  if (threadIdx.x < 33) {
+    const double lo = threadIdx.x / 16.0 - 1.0, hi = (threadIdx.x + 1) / 16.0 - 1.0;
+    uint32_t base = 0;
+    float mid = __builtin_inff();
+    for (int i = 0; i < 15; ++i) {
+      double m = mid64(i);
+      if (m < lo) ++base;
+      else if (m < hi) mid = (float)m;
+    }
+    tab[threadIdx.x] = BinEntry{mid, base};
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const int64_t iters = (nblocks + 7) / 8;
+  for (int64_t it = wave; it < iters; it += nwaves) {
+    const int64_t blk = it * 8 + (lane >> 3);
+    const bool valid = blk < nblocks;
+    float v[8];
+    if (valid) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(w + blk * kBlock + (lane & 7) * 8);
+      f32x4 a = __builtin_nontemporal_load(src), b = __builtin_nontemporal_load(src + 1);
+      v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+      v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    amax = max8(amax);
+    const float inv = 1.0f / amax;
+    const bool tiny = amax < 0x1p-100f;
+    uint32_t word = 0, slow = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = v[e] * inv;
+      const uint32_t bin = min(__float2uint_rz(fmaf(x, 16.f, 16.f)), 32u);
+      const BinEntry be = tab[bin];
+      const uint32_t idx = be.base + (x > be.mid ? 1u : 0u);
+      if (fabsf(x - be.mid) <= 0x1p-20f || tiny) slow |= 1u << e;
+      word |= idx << (8 * (e >> 1) + ((e & 1) ? 0 : 4));
+    }
+    if (__builtin_expect(__any(slow != 0), 0)) {
+      if (slow) {
+        const double c = (double)amax;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (slow & (1u << e)) {
+            uint32_t idx = 0;
+            for (int i = 0; i < 15; ++i) idx += ((double)v[e] > c * mid64(i)) ? 1u : 0u;
+            const int sh = 8 * (e >> 1) + ((e & 1) ? 0 : 4);
+            word = (word & ~(0xFu << sh)) | (idx << sh);
+          }
+        }
+      }
+    }
+    if (amax == 0.f) word = 0x77777777u;  // all-zero block: every value takes the zero code
+    if (valid) {
+      __builtin_nontemporal_store(word, packed + blk * 8 + (lane & 7));
+      if ((lane & 7) == 0) absmax[blk] = amax;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Double quantisation. One wave per group of 256 scales, 4 per lane. c2 is the exact group
+// maximum; the code is the E4M3 value in [0, 1] nearest to the exact ratio c1 / c2 (ties to the
+// even code), found by binary search over the 56 midpoints with exact fp64 products.
+__device__ __forceinline__ double e4m3_mid(int j) {
+  return ((double)e4m3_decode(j) + (double)e4m3_decode(j + 1)) * 0.5;
+}
+
+__device__ __forceinline__ uint32_t e4m3_code_of_ratio(float c1, float c2) {
+  if (c2 == 0.f) return 0;
+  const double a = c1, b = c2;
+  int lo = 0, hi = 56;  // count of midpoints strictly below c1 / c2
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (a > b * e4m3_mid(mid)) lo = mid + 1;
+    else hi = mid;
+  }
+  if (lo < 56 && (lo & 1) && a == b * e4m3_mid(lo)) ++lo;
+  return (uint32_t)lo;
+}
+
+__global__ __launch_bounds__(256) void nf4_double_quant_kernel(const float* __restrict__ absmax,
+                                                               int64_t nblocks,
+                                                               uint8_t* __restrict__ scale_q,
+                                                               float* __restrict__ scale_c2) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+  if (g >= ngroups) return;
+  const int64_t first = g * kGroup + lane * 4;
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = (first + i < nblocks) ? absmax[first + i] : 0.f;
+  const float c2 = wave_max(fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])));
+  uint32_t code[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) code[i] = e4m3_code_of_ratio(c[i], c2);
+  if (first + 3 < nblocks) {
+    *reinterpret_cast<uint32_t*>(scale_q + first) =
+        code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+  } else {
+    for (int i = 0; i < 4; ++i)
+      if (first + i < nblocks) scale_q[first + i] = (uint8_t)code[i];
+  }
+  if (lane == 0) scale_c2[g] = c2;
+}
+
+// ------------------------------------------------------------------------------------------
+// Standalone dequantisation: lane handles 32 values (16 packed bytes, half a block) per
+// iteration and writes 64 bytes of bf16.
+__global__ __launch_bounds__(256) void nf4_dequant_kernel(const u32x4* __restrict__ packed,
+                                                          const uint8_t* __restrict__ scale_q,
+                                                          const float* __restrict__ scale_c2,
+                                                          int64_t nchunks, u32x4* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
+    const u32x4 p = __builtin_nontemporal_load(packed + c);
+    const BlockLut t = make_lut(block_scale(scale_q, scale_c2, c >> 1));
+    u32x4 o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t d[4];
+      dequant8(t, p[i], d);
+      o[i] = u32x4{d[0], d[1], d[2], d[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(o[i], out + c * 4 + i);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+static int grid_for(int64_t work_items, int per_block, int max_blocks) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > max_blocks) g = max_blocks;
+  return (int)g;
+}
+
+hipError_t launch_quantize(const float* w, int64_t numel, uint8_t* packed, float* absmax,
+                           hipStream_t stream) {
+  const int64_t nblocks = numel / kBlock;
+  if (nblocks == 0) return hipSuccess;
+  const int64_t iters = (nblocks + 7) / 8;         // one wave iteration per 8 blocks
+  const int grid = grid_for(iters, 4, 256 * 32);   // 4 waves per workgroup
+  hipLaunchKernelGGL(nf4_quantize_kernel, dim3(grid), dim3(256), 0, stream, w, nblocks,
+                     reinterpret_cast<uint32_t*>(packed), absmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_quant(const float* absmax, int64_t nblocks, uint8_t* scale_q,
+                               float* scale_c2, hipStream_t stream) {
+  if (nblocks == 0) return hipSuccess;
+  const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+  const int grid = (int)((ngroups + 3) / 4);
+  hipLaunchKernelGGL(nf4_double_quant_kernel, dim3(grid), dim3(256), 0, stream, absmax, nblocks,
+                     scale_q, scale_c2);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
+                          int64_t numel, uint16_t* out, hipStream_t stream) {
+  const int64_t nchunks = numel / 32;
+  if (nchunks == 0) return hipSuccess;
+  const int grid = grid_for(nchunks, 256, 256 * 16);
+  hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(packed), scale_q, scale_c2, nchunks,
+                     reinterpret_cast<u32x4*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace nf4

@@ -1,0 +1,189 @@
+// Skinny forward of the adapted linear for a few tokens (M <= 16): the dequant-GEMV regime.
+//
+// "QLoRA, explained", The forward pass and gradients / The algorithm, step by step:
+// y = x W~^T + s (x A^T) B^T. With M <= 16 the weight is read once and each dequantised value is
+// used M times, so the kernel is bound by HBM bandwidth on the packed weight (0.52 bytes per
+// value). Layout of the work:
+//   * rows of W (N of them) followed by the r rows of A form the "row" axis, cut into tiles of 64;
+//     the k axis is cut into S splits of whole 256-column sub-chunks;
+//   * a workgroup (4 waves) takes one row tile and one split; wave w takes sub-chunks w, w+4, ...;
+//     lane (row = lane % 16, grp = lane / 16) dequantises the 64-value block at column
+//     kb + 64 * grp of its row straight into MFMA operand registers (no LDS), and the same lane
+//     holds x[m = lane % 16][kb + 64 * grp ...] as the other operand, so v_mfma_f32_16x16x32_bf16
+//     contracts over a permuted but consistent k order;
+//   * the four waves are summed in LDS in wave order and the workgroup writes one fp32 partial;
+//   * skinny_epilogue_kernel sums the S partials in split order, forms u = x A^T from the A rows,
+//     adds s * u B^T in fp32 and rounds y to bf16.
+#include "common.h"
+#include "launch.h"
+
+namespace nf4 {
+
+constexpr int kSub = 256;   // k columns per sub-chunk (4 lane groups x one 64-value block)
+
+struct SkinnyArgs {
+  const uint8_t* packed;
+  const uint8_t* scale_q;
+  const float* scale_c2;
+  int64_t N, K;
+  const uint16_t* x;   // [M x K] bf16
+  int64_t M;
+  const uint16_t* A;   // [r x K] bf16
+  int r;
+  int splits, sub_per_split;
+  float* part;         // [splits][M][N + r]
+};
+
+__global__ __launch_bounds__(256) void skinny_fwd_kernel(const SkinnyArgs g) {
+  __shared__ float red[4][4][64][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 4;
+  const int64_t rows = g.N + g.r;
+  const int64_t row_tile0 = (int64_t)blockIdx.x * 64;
+  const int split = blockIdx.y;
+  const int64_t nsub = (g.K + kSub - 1) / kSub;
+  const int64_t sub_begin = (int64_t)split * g.sub_per_split;
+  const int64_t sub_end = min(nsub, sub_begin + g.sub_per_split);
+  const int64_t m = lane & 15;
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t sub = sub_begin + wave; sub < sub_end; sub += 4) {
+    const int64_t kk = sub * kSub + 64 * grp;
+    const bool kvalid = kk < g.K;
+    bf16x8 b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      b[j] = bf16x8{};
+      if (kvalid && m < g.M) b[j] = *reinterpret_cast<const bf16x8*>(g.x + m * g.K + kk + 8 * j);
+    }
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      const int64_t row = row_tile0 + tn * 16 + (lane & 15);
+      const int64_t tile_first = row_tile0 + tn * 16;
+      uint32_t a[8][4];
+      if (tile_first < g.N) {
+        // NF4 rows (N % 16 == 0, so a 16-row tile is all NF4 or all adapter rows)
+        if (kvalid) {
+          const int64_t e = row * g.K + kk;
+          const u32x4* src = reinterpret_cast<const u32x4*>(g.packed + e / 2);
+          const u32x4 p0 = __builtin_nontemporal_load(src), p1 = __builtin_nontemporal_load(src + 1);
+          const BlockLut t = make_lut(block_scale(g.scale_q, g.scale_c2, e / kBlock));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dequant8(t, p0[i], a[i]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dequant8(t, p1[i], a[4 + i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a[i][0] = a[i][1] = a[i][2] = a[i][3] = 0u;
+        }
+      } else if (tile_first < rows) {
+        const int64_t j = row - g.N;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          u32x4 v = u32x4{0u, 0u, 0u, 0u};
+          if (kvalid && j < g.r) v = *reinterpret_cast<const u32x4*>(g.A + j * g.K + kk + 8 * i);
+          a[i][0] = v[0]; a[i][1] = v[1]; a[i][2] = v[2]; a[i][3] = v[3];
+        }
+      } else {
+        continue;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u32x4 av = u32x4{a[i][0], a[i][1], a[i][2], a[i][3]};
+        acc[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), b[i],
+                                                          acc[tn], 0, 0, 0);
+      }
+    }
+  }
+  // acc[tn][i]: row = tile row tn*16 + 4*grp + i, column m = lane % 16
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][tn][lane][i] = acc[tn][i];
+  __syncthreads();
+  // 64 rows x 16 columns per workgroup; thread t takes (row = t / 4, m = 4 * (t % 4) .. +3)
+  const int rloc = tid >> 2, tn = rloc >> 4, rin = rloc & 15;
+  const int64_t row = row_tile0 + rloc;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int mm = 4 * (tid & 3) + q;
+    const int ln = (rin >> 2) * 16 + mm, ii = rin & 3;
+    const float v = ((red[0][tn][ln][ii] + red[1][tn][ln][ii]) + red[2][tn][ln][ii]) + red[3][tn][ln][ii];
+    if (mm < g.M && row < rows) g.part[((int64_t)split * g.M + mm) * rows + row] = v;
+  }
+}
+
+// y[m][n] = bf16(sum_s part[s][m][n] + scale * sum_j u[m][j] B[n][j]),  u[m][j] = sum_s part[s][m][N + j].
+// Each workgroup rebuilds u (M x r, at most 16 x 128) in LDS from the adapter-row partials, stages
+// its 256 columns of B, and sums the weight partials in split order.
+__global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __restrict__ part, int splits,
+                                                              int64_t M, int64_t N, int r,
+                                                              const uint16_t* __restrict__ B, float scale,
+                                                              float* __restrict__ u_out,
+                                                              uint16_t* __restrict__ y) {
+  __shared__ float us[16][128];
+  __shared__ uint16_t bs[128][256 + 2];
+  const int64_t rows = N + r;
+  const int64_t n0 = (int64_t)blockIdx.x * 256;
+  for (int idx = threadIdx.x; idx < M * r; idx += 256) {
+    const int mm = idx / r, j = idx % r;
+    float s = 0.f;
+    for (int sp = 0; sp < splits; ++sp) s += part[((int64_t)sp * M + mm) * rows + N + j];
+    us[mm][j] = s;
+    if (blockIdx.x == 0) u_out[(int64_t)mm * r + j] = s;
+  }
+  for (int idx = threadIdx.x; idx < 256 * r; idx += 256) {
+    const int nl = idx / r, j = idx % r;
+    bs[j][nl] = (n0 + nl < N) ? B[(n0 + nl) * r + j] : (uint16_t)0;
+  }
+  __syncthreads();
+  const int64_t n = n0 + threadIdx.x;
+  if (n >= N) return;
+  for (int mm = 0; mm < M; ++mm) {
+    float s = 0.f;
+    for (int sp = 0; sp < splits; ++sp) s += part[((int64_t)sp * M + mm) * rows + n];
+    float l = 0.f;
+    for (int j = 0; j < r; ++j) l = fmaf(us[mm][j], __uint_as_float((uint32_t)bs[j][threadIdx.x] << 16), l);
+    const float v = s + scale * l;
+    y[mm * N + n] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+  }
+}
+
+bool skinny_eligible(int64_t M) { return M >= 1 && M <= 16; }
+
+void skinny_plan(int64_t N, int64_t K, int r, int* splits, int* sub_per_split, int* row_tiles) {
+  *row_tiles = (int)((N + r + 63) / 64);
+  const int64_t nsub = (K + kSub - 1) / kSub;
+  int64_t want = (1024 + *row_tiles - 1) / *row_tiles;
+  int64_t cap = nsub / 4;        // keep at least 4 sub-chunks (one per wave) per split
+  if (cap < 1) cap = 1;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  *sub_per_split = (int)((nsub + want - 1) / want);
+  *splits = (int)((nsub + *sub_per_split - 1) / *sub_per_split);
+}
+
+size_t skinny_workspace_floats(int64_t M, int64_t N, int64_t K, int r) {
+  int s, spp, rt;
+  skinny_plan(N, K, r, &s, &spp, &rt);
+  return (size_t)s * (size_t)M * (size_t)(N + r);
+}
+
+hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
+                             int64_t N, int64_t K, const uint16_t* x, int64_t M, const uint16_t* A,
+                             const uint16_t* B, int r, float scale, float* part, float* u_out,
+                             uint16_t* y, hipStream_t stream) {
+  int splits, spp, row_tiles;
+  skinny_plan(N, K, r, &splits, &spp, &row_tiles);
+  SkinnyArgs g{packed, scale_q, scale_c2, N, K, x, M, A, r, splits, spp, part};
+  hipLaunchKernelGGL(skinny_fwd_kernel, dim3((unsigned)row_tiles, (unsigned)splits), dim3(256), 0,
+                     stream, g);
+  hipLaunchKernelGGL(skinny_epilogue_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
+                     part, splits, M, N, r, B, scale, u_out, y);
+  return hipGetLastError();
+}
+
+}  // namespace nf4

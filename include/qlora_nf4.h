@@ -1,0 +1,130 @@
+/* qlora_nf4.h - C ABI of the NF4-quantised QLoRA linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the method as stated on "QLoRA, explained" (pofe.ai):
+ *   nf4_quantize      sections "Blockwise absmax quantisation" and "NormalFloat 4 (NF4)": a weight is
+ *                     flattened row-major and cut into blocks of 64; each block stores its absmax and
+ *                     each value the index of the nearest of 16 NF4 codes; "Minimal implementation":
+ *                     two indices per byte.
+ *   nf4_double_quant  section "Double quantisation": the block scales are quantised to 8-bit floats
+ *                     in groups of 256 with one fp32 constant per group.
+ *   nf4_dequant       section "The forward pass and gradients": first the 8-bit scales are restored
+ *                     with the fp32 constants, then the indices with those scales, giving bf16.
+ *   qlora_linear_fwd  section "The algorithm, step by step": y = x W~^T + s x A^T B^T.
+ *   qlora_linear_bwd  section "The forward pass and gradients": dX = dY (W~ + s B A),
+ *                     dA = s B^T G, dB = s G A^T with G = dY^T X; W gets no gradient.
+ *
+ * Data formats (all little-endian, row-major):
+ *   W        N x K (out x in, like nn.Linear), K % 64 == 0, N % 16 == 0. Blocks of 64 run along K.
+ *   packed   uint8[N*K/2]: byte j holds the code index of element 2j in its high nibble and of
+ *            element 2j+1 in its low nibble. Codes are ascending; index 7 is the exact zero.
+ *   scale_q  uint8[N*K/64]: OCP E4M3 code of c1[b] / c2[b / 256], the nearest E4M3 value in [0, 1]
+ *            to the exact ratio, ties to the even code.
+ *   scale_c2 float[ceil(N*K/64/256)]: c2[g] = max of the 256 block absmax values of group g.
+ *   bf16     stored as uint16 bit patterns. Dequantised value: bf16_rne(fl32(q[idx] * c1')) with
+ *            c1' = fl32(e4m3(scale_q) * c2).
+ *   LoRA     A: bf16 r x K, B: bf16 N x r, scale s = lora_alpha / r; 16 <= r <= 128, r % 16 == 0.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers to caller-owned memory (except nf4_codebook's output, a host
+ *     array), each 16-byte aligned. The library never allocates or frees device memory, never
+ *     synchronises and keeps no mutable global state; calls are thread-safe.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the default stream).
+ *     The return value reports argument validation and launch status; faults inside kernels
+ *     surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before any HIP call; on error nothing is enqueued.
+ *   - Inputs must be finite; NaN and Inf are outside the contract and are not checked.
+ *   - Results are deterministic: every reduction runs in a fixed order without atomics.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NF4_OK = 0,
+  NF4_ERR_NULL = 1,       /* a required pointer is NULL */
+  NF4_ERR_SHAPE = 2,      /* a size violates the contract (see each call) */
+  NF4_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned */
+  NF4_ERR_RANK = 4,       /* r outside 16..128 or not a multiple of 16 */
+  NF4_ERR_WORKSPACE = 5,  /* ws is NULL or smaller than qlora_workspace_bytes() */
+  NF4_ERR_HIP = 6         /* the HIP runtime rejected a kernel launch */
+} nf4_status;
+
+/* A quantised, double-quantised weight W (N x K). All three arrays are device memory. */
+typedef struct {
+  const uint8_t *packed;    /* [N*K/2]                 */
+  const uint8_t *scale_q;   /* [N*K/64]                */
+  const float *scale_c2;    /* [ceil(N*K/64/256)]      */
+  int64_t N, K;
+} nf4_weight;
+
+/* Blockwise absmax NF4 quantisation of a float32 array (any shape, flattened row-major).
+ *   w       [numel] float32 input; numel % 64 == 0 (callers zero-pad), numel >= 0.
+ *   packed  [numel/2] output, two indices per byte (see Data formats).
+ *   absmax  [numel/64] output, exact float32 block maxima of |w| (first-level scales).
+ * Nearest code: the exact real quotient w / absmax decides, ties to the lower index; a block
+ * whose absmax is 0 stores index 7 everywhere.
+ * Errors: NF4_ERR_NULL (w, packed or absmax NULL while numel > 0), NF4_ERR_SHAPE, NF4_ERR_ALIGN. */
+int nf4_quantize(const float *w, int64_t numel, uint8_t *packed, float *absmax, hipStream_t stream);
+
+/* Double quantisation of block scales.
+ *   absmax    [nblocks] float32 input (from nf4_quantize).
+ *   scale_q   [nblocks] output E4M3 codes; scale_c2 [ceil(nblocks/256)] output group maxima
+ *             (the last group may hold fewer than 256 scales; a group of zeros stores code 0).
+ * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (nblocks < 0), NF4_ERR_ALIGN. */
+int nf4_double_quant(const float *absmax, int64_t nblocks, uint8_t *scale_q, float *scale_c2,
+                     hipStream_t stream);
+
+/* Two-level dequantisation of W to bf16.
+ *   out  [N*K] uint16 (bf16) output, row-major N x K; bit-exact with the formula in Data formats.
+ * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (N % 16, K % 64, N < 16, K < 64), NF4_ERR_ALIGN. */
+int nf4_dequant(const nf4_weight *W, uint16_t *out, hipStream_t stream);
+
+/* Forward of the adapted linear: y = x W~^T + s (x A^T) B^T, bf16 inputs, fp32 accumulation,
+ * W~ dequantised on the fly (never written to memory).
+ *   x      [M x K] bf16;  A [r x K] bf16;  B [N x r] bf16;  scale = s.
+ *   y      [M x N] bf16 output.
+ *   u_out  [M x r] float32 output u = x A^T (saved for qlora_linear_bwd), or NULL.
+ *   ws     device workspace of at least qlora_workspace_bytes(M, N, K, r) bytes.
+ * M == 0 is a no-op. Errors: NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_RANK,
+ * NF4_ERR_WORKSPACE, NF4_ERR_HIP. */
+int qlora_linear_fwd(const nf4_weight *W, const uint16_t *x, int64_t M, const uint16_t *A,
+                     const uint16_t *B, int32_t r, float scale, uint16_t *y, float *u_out, void *ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* Backward of the adapted linear given dY, with W~ dequantised again on the fly:
+ *   dx = dY W~ + s (dY B) A          [M x K] bf16 output, or NULL to skip it;
+ *   dA = s (dY B)^T x                [r x K] float32 output;
+ *   dB = s dY^T u                    [N x r] float32 output, u = x A^T from qlora_linear_fwd.
+ *   accumulate: 0 overwrites dA and dB, 1 adds into them. No gradient is produced for W.
+ * M == 0 is a no-op. Errors as qlora_linear_fwd. */
+int qlora_linear_bwd(const nf4_weight *W, const uint16_t *x, const uint16_t *dy, int64_t M,
+                     const uint16_t *A, const uint16_t *B, int32_t r, float scale, const float *u,
+                     uint16_t *dx, float *dA, float *dB, int accumulate, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Workspace bytes that qlora_linear_fwd and qlora_linear_bwd need for these sizes (the larger of
+ * the two). Returns 0 for invalid sizes. */
+size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/* Bytes of an NF4 + double-quantised weight with numel values: numel/2 + numel/64 + 4*ceil(numel/16384).
+ * Returns -1 if numel is negative or not a multiple of 64. */
+int64_t nf4_storage_bytes(int64_t numel);
+
+/* Host copy of the 16 float32 NF4 codes the kernels use (ascending, index 7 is 0). */
+void nf4_codebook(float out[16]);
+
+/* Static description of a status code. */
+const char *nf4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

@@ -55,3 +55,20 @@ def linear_bwd_f64(x, dy, w, a, b, scale: float):
     d_a = scale * (b.T @ g)
     d_x = dy @ (w + scale * (b @ a))
     return d_x, d_a, d_b
+
+
+def linear_bwd_sampled(x_bits, dy_bits, w_bits, a_bits, b_bits, scale: float, x_rows, a_cols, b_rows):
+    """``linear_bwd`` restricted to a sample of outputs, for sizes where G = dY^T X (N x K) is too
+    large to form: rows ``x_rows`` of dX, columns ``a_cols`` of dA and rows ``b_rows`` of dB.
+
+    Same formulas, restricted: dX[i] = dY[i] (W~ + s B A); dA[:, c] = s B^T G[:, c] with
+    G[:, c] = dY^T X[:, c]; dB[n] = s G[n] A^T with G[n] = dY[:, n]^T X.
+    """
+    x, dy, w, a, b = _f64(x_bits), _f64(dy_bits), _f64(w_bits), _f64(a_bits), _f64(b_bits)
+    x_rows, a_cols, b_rows = np.asarray(x_rows), np.asarray(a_cols), np.asarray(b_rows)
+    d_x = dy[x_rows] @ (w + scale * (b @ a))
+    g_cols = dy.T @ x[:, a_cols]
+    d_a = scale * (b.T @ g_cols)
+    g_rows = dy[:, b_rows].T @ x
+    d_b = scale * (g_rows @ a.T)
+    return d_x, d_a, d_b

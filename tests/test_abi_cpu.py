@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI: the library loads, exports every call the header declares, and
+rejects bad arguments with the documented status before touching the GPU. No kernel runs here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+q = pytest.importorskip("bit_nf4_quantised_amd")
+lib = q.lib
+
+FAKE = 0x100000          # an aligned, never-dereferenced address
+MISALIGNED = FAKE + 4
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "qlora_nf4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(q.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_codebook_constants_equal_oracle():
+    got = np.array(q.nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), oracle.codebook().view(np.uint32))
+
+
+def test_storage_bytes():
+    for numel in (0, 64, 64 * 300, 4096 * 4096, 8192 * 28672):
+        nb = numel // 64
+        want = numel // 2 + nb + 4 * ((nb + 255) // 256)
+        assert q.nf4_storage_bytes(numel) == want
+    assert q.nf4_storage_bytes(65) == -1 and q.nf4_storage_bytes(-64) == -1
+    # at scale, bits per parameter match the page's 4.127
+    n = 8192 * 28672
+    assert round(8 * q.nf4_storage_bytes(n) / n, 3) == round(oracle.storage_bits(64), 3)
+
+
+def test_workspace_bytes():
+    assert q.qlora_workspace_bytes(2048, 4096, 4096, 16) > 0
+    assert q.qlora_workspace_bytes(1, 8192, 28672, 16) > 0
+    assert q.qlora_workspace_bytes(16, 4096, 4096, 8) == 0          # bad rank
+    assert q.qlora_workspace_bytes(16, 4095, 4096, 16) == 0         # N % 16
+    assert q.qlora_workspace_bytes(16, 4096, 4000, 16) == 0         # K % 64
+
+
+def test_status_strings():
+    for s in range(7):
+        assert lib.nf4_status_string(s)
+    assert b"unknown" in lib.nf4_status_string(99)
+
+
+def test_quantize_validation():
+    assert lib.nf4_quantize(FAKE, 65, FAKE, FAKE, None) == q.NF4_ERR_SHAPE
+    assert lib.nf4_quantize(FAKE, -64, FAKE, FAKE, None) == q.NF4_ERR_SHAPE
+    assert lib.nf4_quantize(None, 64, FAKE, FAKE, None) == q.NF4_ERR_NULL
+    assert lib.nf4_quantize(MISALIGNED, 64, FAKE, FAKE, None) == q.NF4_ERR_ALIGN
+    assert lib.nf4_quantize(None, 0, None, None, None) == q.NF4_OK      # empty input: nothing to do
+
+
+def test_double_quant_validation():
+    assert lib.nf4_double_quant(FAKE, -1, FAKE, FAKE, None) == q.NF4_ERR_SHAPE
+    assert lib.nf4_double_quant(FAKE, 10, None, FAKE, None) == q.NF4_ERR_NULL
+    assert lib.nf4_double_quant(FAKE, 10, FAKE, MISALIGNED, None) == q.NF4_ERR_ALIGN
+    assert lib.nf4_double_quant(None, 0, None, None, None) == q.NF4_OK
+
+
+def _w(N=4096, K=4096, packed=FAKE):
+    return q.CNF4Weight(packed, FAKE, FAKE, N, K)
+
+
+def test_dequant_validation():
+    assert lib.nf4_dequant(None, FAKE, None) == q.NF4_ERR_NULL
+    assert lib.nf4_dequant(ctypes.byref(_w(packed=None)), FAKE, None) == q.NF4_ERR_NULL
+    assert lib.nf4_dequant(ctypes.byref(_w(N=4090)), FAKE, None) == q.NF4_ERR_SHAPE
+    assert lib.nf4_dequant(ctypes.byref(_w(K=4000)), FAKE, None) == q.NF4_ERR_SHAPE
+    assert lib.nf4_dequant(ctypes.byref(_w(N=0)), FAKE, None) == q.NF4_ERR_SHAPE
+    assert lib.nf4_dequant(ctypes.byref(_w(packed=MISALIGNED)), FAKE, None) == q.NF4_ERR_ALIGN
+    assert lib.nf4_dequant(ctypes.byref(_w()), None, None) == q.NF4_ERR_NULL
+
+
+def test_fwd_validation():
+    w = ctypes.byref(_w())
+    ws = q.qlora_workspace_bytes(64, 4096, 4096, 16)
+    f = lib.qlora_linear_fwd
+    assert f(w, FAKE, 64, FAKE, FAKE, 8, 2.0, FAKE, None, FAKE, ws, None) == q.NF4_ERR_RANK
+    assert f(w, FAKE, 64, FAKE, FAKE, 24, 2.0, FAKE, None, FAKE, ws, None) == q.NF4_ERR_RANK
+    assert f(w, FAKE, 64, FAKE, FAKE, 256, 2.0, FAKE, None, FAKE, ws, None) == q.NF4_ERR_RANK
+    assert f(w, FAKE, -1, FAKE, FAKE, 16, 2.0, FAKE, None, FAKE, ws, None) == q.NF4_ERR_SHAPE
+    assert f(w, None, 64, FAKE, FAKE, 16, 2.0, FAKE, None, FAKE, ws, None) == q.NF4_ERR_NULL
+    assert f(w, FAKE, 64, FAKE, FAKE, 16, 2.0, None, None, FAKE, ws, None) == q.NF4_ERR_NULL
+    assert f(w, FAKE, 64, MISALIGNED, FAKE, 16, 2.0, FAKE, None, FAKE, ws, None) == q.NF4_ERR_ALIGN
+    assert f(w, FAKE, 64, FAKE, FAKE, 16, 2.0, FAKE, None, None, ws, None) == q.NF4_ERR_WORKSPACE
+    assert f(w, FAKE, 64, FAKE, FAKE, 16, 2.0, FAKE, None, FAKE, 16, None) == q.NF4_ERR_WORKSPACE
+    assert f(w, FAKE, 0, FAKE, FAKE, 16, 2.0, FAKE, None, None, 0, None) == q.NF4_OK
+    assert f(None, FAKE, 64, FAKE, FAKE, 16, 2.0, FAKE, None, FAKE, ws, None) == q.NF4_ERR_NULL
+
+
+def test_bwd_validation():
+    w = ctypes.byref(_w())
+    ws = q.qlora_workspace_bytes(64, 4096, 4096, 16)
+    f = lib.qlora_linear_bwd
+    ok = [w, FAKE, FAKE, 64, FAKE, FAKE, 16, 2.0, FAKE, FAKE, FAKE, FAKE, 0, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(ok)
+        pos = {"x": 1, "dy": 2, "M": 3, "A": 4, "B": 5, "r": 6, "u": 8, "dx": 9, "dA": 10, "dB": 11,
+               "ws": 13, "ws_bytes": 14}
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return f(*a)
+
+    assert call(r=48 + 1) == q.NF4_ERR_RANK
+    assert call(M=-2) == q.NF4_ERR_SHAPE
+    assert call(u=None) == q.NF4_ERR_NULL
+    assert call(dA=None) == q.NF4_ERR_NULL
+    assert call(dy=MISALIGNED) == q.NF4_ERR_ALIGN
+    assert call(ws=None) == q.NF4_ERR_WORKSPACE
+    assert call(ws_bytes=ws // 4) == q.NF4_ERR_WORKSPACE
+    assert call(M=0) == q.NF4_OK

@@ -1,0 +1,124 @@
+"""GPU parity of the adapted linear's forward and backward against the oracle.
+
+Tolerance (bf16 inputs, fp32 accumulation): relative Frobenius error <= 5e-3 and elementwise
+|err| <= 1e-2 * max|ref|, for y, dX, dA and dB separately; u = x A^T is checked the same way.
+Exact special cases pin layout and transposition: with B = 0, one-hot rows of x give rows of y that
+equal columns of the dequantised weight bit for bit, and one-hot rows of dY give rows of dX equal
+to rows of it.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_helpers import (assert_close, f64_from_bits, gpu_fwd_bwd, gpu_quantize, log,
+                         oracle_weight)
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, M, N, K, r, kind="gauss", sigma=0.02):
+    w = wl.weight("single", 200 + seed, N, K, kind, sigma)
+    g = wl.rng_for("single", 200 + seed, "x")
+    x = wl.to_bf16_bits(g.standard_normal((M, K), dtype=np.float32))
+    a = wl.to_bf16_bits(g.standard_normal((r, K), dtype=np.float32) * np.float32(0.01))
+    b = wl.to_bf16_bits(g.standard_normal((N, r), dtype=np.float32) * np.float32(0.01))
+    dy = wl.to_bf16_bits(g.standard_normal((M, N), dtype=np.float32))
+    return w, x, a, b, dy
+
+
+def check_full(w, x, a, b, dy, s, name, accumulate=False, dA0=None, dB0=None):
+    N, K = w.shape
+    M = x.shape[0]
+    log(f"[linear] {name} M={M} N={N} K={K} r={a.shape[0]} s={s}")
+    qw = gpu_quantize(w)[0]
+    y, u, dx, dA, dB = gpu_fwd_bwd(qw, x, a, b, dy, s, accumulate=accumulate, dA0=dA0, dB0=dB0)
+    wt = oracle_weight(w)
+    yr, ur = oracle.linear_fwd(x, wt, a, b, s)
+    dxr, dar, dbr = oracle.linear_bwd(x, dy, wt, a, b, s)
+    if accumulate:
+        dar = dar + dA0
+        dbr = dbr + dB0
+    assert_close("y", f64_from_bits(y), yr)
+    assert_close("u", u, ur)
+    assert_close("dx", f64_from_bits(dx), dxr)
+    assert_close("dA", dA, dar)
+    assert_close("dB", dB, dbr)
+    return y, u, dx, dA, dB
+
+
+def test_single_linear_workload():
+    wlk = wl.WORKLOADS["single"]
+    w, x, a, b, dy = wl.linear_inputs(wlk, 0, wlk.linears[0])
+    check_full(w, x, a, b, dy, wlk.scale, "single")
+
+
+@pytest.mark.parametrize("M,N,K,r,s", [
+    (300, 400, 960, 16, 2.0),      # ragged in every tile dimension
+    (300, 400, 960, 64, 0.25),
+    (77, 1040, 1088, 128, 0.5),    # one partial row tile, rank 128
+    (40, 256, 512, 32, 1.0),       # 17..64 tokens: small-M tile
+    (513, 128, 128, 16, 2.0),      # three row tiles, the last with one row
+    (1, 400, 960, 16, 2.0),        # skinny forward
+    (4, 400, 960, 64, 0.25),
+    (16, 416, 1024, 16, 2.0),
+    (16, 64, 64, 16, 2.0),         # one block per row
+])
+def test_ragged_shapes(M, N, K, r, s):
+    check_full(*_inputs(M * 7 + r, M, N, K, r), s, "ragged")
+
+
+def test_accumulate_mode():
+    M, N, K, r = 96, 256, 512, 16
+    w, x, a, b, dy = _inputs(9, M, N, K, r)
+    rng = np.random.default_rng(9)
+    dA0 = rng.standard_normal((r, K)).astype(np.float32)
+    dB0 = rng.standard_normal((N, r)).astype(np.float32)
+    check_full(w, x, a, b, dy, 2.0, "accumulate", accumulate=True, dA0=dA0, dB0=dB0)
+
+
+@pytest.mark.parametrize("M", [8, 200])
+def test_one_hot_rows_are_exact(M):
+    """B = 0 and one-hot rows: y rows are columns of W~ and dX rows are rows of W~, bit for bit."""
+    N, K, r = 256, 512, 16
+    w, x, a, b, dy = _inputs(13, M, N, K, r)
+    b = np.zeros_like(b)
+    x = np.zeros_like(x)
+    cols = (np.arange(M) * 37) % K
+    x[np.arange(M), cols] = 0x3F80                      # bf16 1.0
+    dy = np.zeros_like(dy)
+    rows = (np.arange(M) * 11) % N
+    dy[np.arange(M), rows] = 0x3F80
+    log(f"[linear] one-hot M={M}")
+    qw = gpu_quantize(w)[0]
+    y, u, dx, dA, dB = gpu_fwd_bwd(qw, x, a, b, dy, 2.0)
+    wt = oracle_weight(w)
+    assert np.array_equal(y, wt[:, cols].T), "y rows must equal columns of W~"
+    assert np.array_equal(dx, wt[rows, :]), "dX rows must equal rows of W~"
+
+
+def test_zero_weight_gives_adapter_term():
+    M, N, K, r = 64, 256, 512, 16
+    w, x, a, b, dy = _inputs(14, M, N, K, r)
+    check_full(np.zeros_like(w), x, a, b, dy, 2.0, "zero weight")
+
+
+def test_zero_input():
+    M, N, K, r = 64, 256, 512, 16
+    w, x, a, b, dy = _inputs(15, M, N, K, r)
+    x = np.zeros_like(x)
+    log("[linear] zero x")
+    qw = gpu_quantize(w)[0]
+    y, u, dx, dA, dB = gpu_fwd_bwd(qw, x, a, b, dy, 2.0)
+    assert not f64_from_bits(y).any() and not u.any() and not dA.any() and not dB.any()
+
+
+def test_fwd_bwd_deterministic():
+    M, N, K, r = 300, 400, 960, 16
+    w, x, a, b, dy = _inputs(16, M, N, K, r)
+    log("[linear] determinism")
+    qw = gpu_quantize(w)[0]
+    r1 = gpu_fwd_bwd(qw, x, a, b, dy, 2.0)
+    r2 = gpu_fwd_bwd(qw, x, a, b, dy, 2.0)
+    for p, q_ in zip(r1, r2):
+        assert np.array_equal(p, q_)

@@ -121,3 +121,13 @@ def test_special_cases():
     assert not y.any() and not u.any()
     _, da, db = oracle.linear_bwd(z, _bits(rng, (m, n), 1.0), w, a, b, 2.0)
     assert not da.any() and not db.any()
+
+
+def test_sampled_backward_equals_full():
+    x, w, a, b, dy = _small(6, m=9, n=12, k=16, r=4)
+    full = oracle.linear_bwd(x, dy, w, a, b, 0.5)
+    rows, cols, brows = [0, 5, 8], [1, 2, 15], [3, 11]
+    dx, da, db = oracle.linear_bwd_sampled(x, dy, w, a, b, 0.5, rows, cols, brows)
+    assert np.allclose(dx, full[0][rows], rtol=1e-13, atol=1e-13)
+    assert np.allclose(da, full[1][:, cols], rtol=1e-13, atol=1e-13)
+    assert np.allclose(db, full[2][brows], rtol=1e-13, atol=1e-13)
