@@ -1,0 +1,307 @@
+"""Benchmark of the NF4 QLoRA linear layer on one MI355X.
+
+A step is one forward + backward (dX, dA, dB) through all seven NF4 linears of a Llama-3.1-8B
+layer (q/o 4096x4096, k/v 1024x4096, gate/up 14336x4096, down 4096x14336) at 2048 tokens, LoRA
+rank 16, alpha 32: the training hot path, in which each weight is dequantised twice per step
+inside the fused GEMMs. `value` is the algorithmic fwd+bwd TFLOP/s of the whole step, with inputs
+already resident in HBM.
+
+The same run also measures, each in its own timed loop:
+  * the fused forward GEMM kernel alone (one launch per call through the forward-recompute entry),
+    for the roofline against the bf16 dense MFMA peak;
+  * quantise, double quantise and dequantise over 136 matrices of 4096 x 14336 (7.99e9 weights)
+    drawn from a pool of 8 distinct matrices, and the skinny forward of an 8192 x 28672 weight at
+    1, 4 and 16 tokens with 4 rotating weight copies, in HBM GB/s against 8 TB/s;
+  * the CPU oracle on a bounded sample of the same workload (cpu_baseline).
+
+Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+METRIC = "QLoRA NF4 linear fwd+bwd TFLOP/s (% bf16 MFMA peak); NF4 dequant HBM GB/s"
+
+
+def flops_fwd_bwd(n: int, k: int, m: int, r: int) -> int:
+    """Forward 2MNK + 2Mr(K+N); backward dX 2MNK + 2Mr(N+K), dA 2rMK, dB 2NMr."""
+    return (2 * m * n * k + 2 * m * r * (k + n)) + (2 * m * n * k + 2 * m * r * (n + k)
+                                                    + 2 * r * m * k + 2 * n * m * r)
+
+
+def nf4_bytes(numel: int) -> int:
+    nb = numel // 64
+    return numel // 2 + nb + 4 * ((nb + 255) // 256)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_nf4_quantised_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str):
+    """HBM bytes per launch of a kernel, from the committed rocprofv3 counter summary, if it was
+    taken from the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    ent = t.get("kernels", {}).get(kernel_key)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def timed(fn, iters, torch):
+    """Average milliseconds per call of fn() with HIP events on the current stream."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for i in range(iters):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "llama65b", "llama70b"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paths", action="store_true", help="skip the bandwidth-path loops")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (the data-"
+                                   "parallel sharding across GPUs is described, not built)"}))
+        sys.exit(2)
+
+    import torch
+    import bit_nf4_quantised_amd as q
+
+    dev = torch.device("cuda:0")
+    wk = wl.WORKLOADS[args.workload]
+    M, r, s = wk.m, wk.r, wk.scale
+
+    # ---------------------------------------------------------------- step inputs, resident in HBM
+    log(f"[bench] preparing {args.workload}: {len(wk.linears)} linears, M={M}, r={r}")
+    lin_state = []
+    ws_bytes = 0
+    flops = 0
+    for li, lin in enumerate(wk.linears):
+        w, x, a, b, dy = wl.linear_inputs(wk, li, lin)
+        wt = torch.from_numpy(w).to(dev)
+        qw = q.quantize_weight(wt)
+        del wt
+        t16 = lambda arr: torch.from_numpy(arr.view(np.int16)).to(dev)
+        st = dict(lin=lin, qw=qw, x=t16(x), a=t16(a), b=t16(b), dy=t16(dy),
+                  y=torch.empty(M, lin.n, dtype=torch.int16, device=dev),
+                  u=torch.empty(M, r, dtype=torch.float32, device=dev),
+                  dx=torch.empty(M, lin.k, dtype=torch.int16, device=dev),
+                  dA=torch.empty(r, lin.k, dtype=torch.float32, device=dev),
+                  dB=torch.empty(lin.n, r, dtype=torch.float32, device=dev))
+        lin_state.append(st)
+        ws_bytes = max(ws_bytes, q.qlora_workspace_bytes(M, lin.n, lin.k, r))
+        flops += flops_fwd_bwd(lin.n, lin.k, M, r)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(_i=0):
+        for st in lin_state:
+            q.qlora_linear_fwd(st["qw"], st["x"], st["a"], st["b"], s, st["y"], st["u"], ws=ws)
+            q.qlora_linear_bwd(st["qw"], st["x"], st["dy"], st["a"], st["b"], s, st["u"], st["dx"],
+                               st["dA"], st["dB"], ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = timed(step, args.steps, torch)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] step {ms_per_step:.3f} ms, {tflops:.1f} TFLOP/s")
+
+    # ------------------------------------------------ dominant kernel: fused forward GEMM, alone
+    gemm_flops = sum(2 * M * st["lin"].n * (st["lin"].k + r) for st in lin_state)
+
+    def recompute(_i=0):
+        for st in lin_state:
+            q.qlora_linear_fwd_recompute(st["qw"], st["x"], st["a"], st["b"], s, st["u"], st["y"])
+
+    recompute()
+    ms_recompute = timed(recompute, args.steps, torch)
+    launches = len(lin_state)
+    avg_launch_ms = ms_recompute / launches
+    gemm_achieved = gemm_flops / (ms_recompute * 1e-3) / 1e12
+    traffic = load_traffic("qlora_gemm_kernel<fwd,256>")
+    roofline = {"kernel": "qlora_gemm_kernel (forward, fused NF4 dequant + bf16 MFMA)",
+                "bound": "mfma", "achieved": round(gemm_achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(gemm_achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                "flops_per_launch": gemm_flops // launches}
+    log(f"[bench] fused fwd GEMM {gemm_achieved:.1f} TFLOP/s, {avg_launch_ms*1e3:.1f} us/launch")
+
+    paths = {}
+    dequant_gbps = None
+    if not args.no_paths:
+        paths, dequant_gbps = bandwidth_paths(torch, q, dev, args)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wk)
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; weights N(0,0.02^2), x and dY N(0,1), A and B N(0,0.01^2))",
+        "config": {"workload": f"{args.workload} layer set, all 7 linears NF4 + double quant, "
+                               f"fwd + bwd (dX, dA, dB)",
+                   "tokens": M, "rank": r, "alpha": wk.alpha,
+                   "linears": {l.name: [l.n, l.k] for l in wk.linears},
+                   "flops_per_step": flops},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "dequant_GBps": dequant_gbps,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "paths": paths,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bandwidth_paths(torch, q, dev, args):
+    """Quantise / double-quantise / dequantise over the 136-matrix stream, and the skinny forward."""
+    res = {}
+    n_rows, n_cols = wl.STREAM_SHAPE
+    numel = n_rows * n_cols
+    nb = numel // 64
+    log(f"[bench] stream pool: {wl.STREAM_POOL} x {n_rows}x{n_cols} fp32")
+    pool = [torch.from_numpy(wl.stream_weight(i)).to(dev) for i in range(wl.STREAM_POOL)]
+    qws = [q.empty_weight(n_rows, n_cols, dev) for _ in range(wl.STREAM_POOL)]
+    absmax = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(wl.STREAM_POOL)]
+    outs = [torch.empty(numel, dtype=torch.int16, device=dev) for _ in range(2)]
+    count = wl.STREAM_COUNT
+
+    def quant(i):
+        j = i % wl.STREAM_POOL
+        q.nf4_quantize(pool[j], qws[j].packed, absmax[j])
+
+    def dq(i):
+        j = i % wl.STREAM_POOL
+        q.nf4_double_quant(absmax[j], qws[j].scale_q, qws[j].scale_c2)
+
+    def deq(i):
+        q.nf4_dequant(qws[i % wl.STREAM_POOL], outs[i % 2])
+
+    for fn in (quant, dq, deq):
+        fn(0)
+    torch.cuda.synchronize()
+    total = count * numel
+    ng = (nb + 255) // 256
+    for name, fn, per_weight_bytes in (
+            ("quantize", quant, 4 + 0.5 + 4 / 64),
+            ("double_quant", dq, (4 * nb + nb + 4 * ng) / numel),
+            ("dequant", deq, nf4_bytes(numel) / numel + 2)):
+        ms = timed(fn, count, torch)
+        gbps = total * per_weight_bytes / (ms * count * 1e-3) / 1e9
+        res[name] = {"weights": total, "ms_total": round(ms * count, 3),
+                     "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                     "bytes_per_weight": round(per_weight_bytes, 4)}
+        log(f"[bench] {name}: {gbps:.0f} GB/s")
+    dequant_gbps = res["dequant"]["GBps"]
+    del pool, qws, absmax, outs
+    torch.cuda.empty_cache()
+
+    # skinny forward: 8192 x 28672, rank 16, 4 rotating copies of the quantised weight (> MALL)
+    sk = wl.SKINNY
+    lin = sk.linears[0]
+    log("[bench] skinny weight 8192x28672")
+    w = wl.weight("stream", 0, lin.n, lin.k, "gauss", 0.02)
+    base = q.quantize_weight(torch.from_numpy(w).to(dev))
+    del w
+    copies = [base] + [q.NF4Weight(base.packed.clone(), base.scale_q.clone(), base.scale_c2.clone(),
+                                   base.N, base.K) for _ in range(3)]
+    skinny = {}
+    for m in wl.SKINNY_MS:
+        _, x, a, b, _ = wl.linear_inputs(sk, 0, lin, m=m)
+        t16 = lambda arr: torch.from_numpy(arr.view(np.int16)).to(dev)
+        X, A, B = t16(x), t16(a), t16(b)
+        y = torch.empty(m, lin.n, dtype=torch.int16, device=dev)
+        u = torch.empty(m, sk.r, dtype=torch.float32, device=dev)
+        wsk = q.workspace(m, lin.n, lin.k, sk.r, dev)
+
+        def call(i):
+            q.qlora_linear_fwd(copies[i % len(copies)], X, A, B, sk.scale, y, u, ws=wsk)
+
+        call(0)
+        ms = timed(call, 200, torch)
+        nbytes = (nf4_bytes(lin.n * lin.k) + 2 * m * lin.k + 2 * sk.r * lin.k + 2 * lin.n * sk.r
+                  + 2 * m * lin.n + 4 * m * sk.r)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        skinny[f"M={m}"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                            "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "bytes": nbytes}
+        log(f"[bench] skinny M={m}: {ms*1e3:.1f} us, {gbps:.0f} GB/s")
+    res["skinny_fwd_8192x28672"] = skinny
+    return res, dequant_gbps
+
+
+def cpu_baseline(wk):
+    """The oracle, as it stands, on a bounded sample of the workload: quantise + double-quantise +
+    dequantise, forward and backward of every linear of the layer set at full token count."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    sample = list(range(len(wk.linears)))
+    flops = 0
+    secs = 0.0
+    for li in sample:
+        lin = wk.linears[li]
+        w, x, a, b, dy = wl.linear_inputs(wk, li, lin)     # input generation is not timed
+        t_start = time.perf_counter()
+        packed, c1 = oracle.quantize(w)
+        codes, c2 = oracle.double_quant(c1)
+        wt = oracle.dequant(packed, codes, c2, w.size).reshape(lin.n, lin.k)
+        oracle.linear_fwd(x, wt, a, b, wk.scale)
+        oracle.linear_bwd(x, dy, wt, a, b, wk.scale)
+        secs += time.perf_counter() - t_start
+        flops += flops_fwd_bwd(lin.n, lin.k, wk.m, wk.r)
+        log(f"[bench] cpu oracle {lin.name}: cumulative {secs:.1f} s")
+    return _cpu_result(flops, secs, threads, sample, wk)
+
+
+def _cpu_result(flops, secs, threads, sample, wk):
+    names = "+".join(wk.linears[i].name for i in sample)
+    return {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(secs, 2),
+            "sample": f"{names} linears of {wk.name} (M={wk.m}, r={wk.r}): NF4 quantise, double "
+                      f"quantise, dequantise, fp64 forward and backward; fwd+bwd flops / wall time"}
+
+
+if __name__ == "__main__":
+    main()

@@ -4,7 +4,7 @@ A thin ctypes layer over ``libqlora_nf4.so`` (the C ABI in ``include/qlora_nf4.h
 only checks tensor placement and marshals device pointers, sizes and the current HIP stream; all
 computation runs in the library's HIP kernels. PyTorch supplies device memory and streams.
 
-The library must have been built (``python -m bit_nf4_quantised_amd.build``); importing this
+The library must have been built (``python bit_nf4_quantised_amd/build.py``); importing this
 package without it raises ImportError, and there is no CPU fallback.
 
 Operations ("QLoRA, explained", pofe.ai): blockwise absmax NF4 quantisation with two indices per
@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first with "
-        "`python -m bit_nf4_quantised_amd.build` (hipcc, gfx950). There is no CPU fallback.")
+        "`python bit_nf4_quantised_amd/build.py` (hipcc, gfx950). There is no CPU fallback.")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -47,6 +47,8 @@ _SIGS = {
     "qlora_linear_fwd": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz, _p]),
     "qlora_linear_bwd": (ctypes.c_int, [_W, _p, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _p,
                                         ctypes.c_int, _p, _sz, _p]),
+    "qlora_linear_fwd_recompute": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz,
+                                                  _p]),
     "qlora_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "nf4_storage_bytes": (_i64, [_i64]),
     "nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
@@ -154,6 +156,27 @@ def qlora_linear_fwd(weight: NF4Weight, x, A, B, scale: float, y, u_out=None, ws
                                 _stream(stream)), "qlora_linear_fwd")
 
 
+def qlora_linear_fwd_recompute(weight: NF4Weight, x, A, B, scale: float, u, y, ws=None,
+                               stream=None) -> None:
+    """Forward with a known u = x A^T (gradient-checkpointing recompute); one fused kernel for
+    more than 16 tokens."""
+    for t in (x, A, B, y):
+        _dtype(t, *_BF16)
+    _dtype(u, torch.float32)
+    M = x.shape[0]
+    r = A.shape[0]
+    if x.shape != (M, weight.K) or A.shape != (r, weight.K) or B.shape != (weight.N, r) \
+            or y.shape != (M, weight.N) or u.numel() != M * r:
+        raise ValueError("shape mismatch")
+    if ws is None and M <= 16:
+        ws = workspace(M, weight.N, weight.K, r, x.device)
+    cw = weight.c_struct()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.qlora_linear_fwd_recompute(ctypes.byref(cw), _ptr(x), M, _ptr(A), _ptr(B), r, scale,
+                                          _ptr(u), _ptr(y), _ptr(ws), nbytes, _stream(stream)),
+           "qlora_linear_fwd_recompute")
+
+
 def qlora_linear_bwd(weight: NF4Weight, x, dy, A, B, scale: float, u, dx, dA, dB,
                      accumulate: bool = False, ws=None, stream=None) -> None:
     for t in (x, dy, A, B, dx):
@@ -215,6 +238,7 @@ def quantize_weight(w: torch.Tensor, stream=None, absmax: torch.Tensor | None = 
 
 
 __all__ = ["lib", "LIB_PATH", "EXPORTED", "NF4Error", "NF4Weight", "CNF4Weight", "nf4_quantize",
-           "nf4_double_quant", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_bwd",
+           "nf4_double_quant", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_fwd_recompute",
+           "qlora_linear_bwd",
            "qlora_workspace_bytes", "nf4_storage_bytes", "nf4_codebook", "workspace",
            "empty_weight", "quantize_weight"]

@@ -1,6 +1,7 @@
 """Build libqlora_nf4.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Usage: python -m bit_nf4_quantised_amd.build   (or __graft_entry__.build()).
+Usage: python bit_nf4_quantised_amd/build.py   (or __graft_entry__.build()). It does not import the
+package, whose import needs the library this script produces.
 Each translation unit is compiled to an object under bit_nf4_quantised_amd/_build/, then linked
 into bit_nf4_quantised_amd/libqlora_nf4.so.
 """

@@ -29,15 +29,17 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Workspace layout (bytes, each region 256-aligned):
 //   forward : [u (M*r fp32)] [partials: skinny splits or adapter down-projection chunks]
-//   backward: [v (M*r fp32)] [partials of v]
+//   backward: [v (M*r fp32)] [partials of v, then of dA, then of dB (the kernels run in order)]
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
   size_t part = nf4::skinny_eligible(M) ? nf4::skinny_workspace_floats(M, N, K, r)
                                         : (size_t)nf4::lora_down_chunks(M, K) * M * r;
   return align_up((size_t)M * r * 4) + align_up(part * 4);
 }
 size_t bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
-  (void)K;
   size_t part = (size_t)nf4::lora_down_chunks(M, N) * M * r;
+  const size_t ga = nf4::lora_grad_workspace_floats(M, K, r), gb = nf4::lora_grad_workspace_floats(M, N, r);
+  if (ga > part) part = ga;
+  if (gb > part) part = gb;
   return align_up((size_t)M * r * 4) + align_up(part * 4);
 }
 
@@ -125,6 +127,32 @@ int qlora_linear_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const ui
                                        y, stream));
 }
 
+int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A,
+                               const uint16_t* B, int32_t r, float scale, const float* u, uint16_t* y,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_weight(W);
+  if (st) return st;
+  if (M < 0) return NF4_ERR_SHAPE;
+  if ((st = check_rank(r))) return st;
+  if (M == 0) return NF4_OK;
+  if (!x || !A || !B || !u || !y) return NF4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(u) || !aligned16(y) ||
+      (ws && !aligned16(ws)))
+    return NF4_ERR_ALIGN;
+  const int64_t N = W->N, K = W->K;
+  if (nf4::skinny_eligible(M)) {
+    // the skinny path forms u itself from the adapter rows; it needs the workspace
+    const size_t need = fwd_ws(M, N, K, r);
+    if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
+    float* u_scratch = static_cast<float*>(ws);
+    return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, N, K, x, M, A, B, r,
+                                           scale, part, u_scratch, y, stream));
+  }
+  return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, N, K, x, M, u, B, r, scale,
+                                       y, stream));
+}
+
 int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy, int64_t M,
                      const uint16_t* A, const uint16_t* B, int32_t r, float scale, const float* u,
                      uint16_t* dx, float* dA, float* dB, int accumulate, void* ws, size_t ws_bytes,
@@ -149,9 +177,9 @@ int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy,
     e = nf4::launch_dx_gemm(W->packed, W->scale_q, W->scale_c2, N, K, dy, M, v, A, r, scale, dx, stream);
     if (e != hipSuccess) return NF4_ERR_HIP;
   }
-  e = nf4::launch_lora_grad(v, x, M, K, r, scale, dA, false, accumulate, stream);
+  e = nf4::launch_lora_grad(v, x, M, K, r, scale, dA, false, accumulate, part, stream);
   if (e != hipSuccess) return NF4_ERR_HIP;
-  return from_hip(nf4::launch_lora_grad(u, dy, M, N, r, scale, dB, true, accumulate, stream));
+  return from_hip(nf4::launch_lora_grad(u, dy, M, N, r, scale, dB, true, accumulate, part, stream));
 }
 
 }  // extern "C"

@@ -3,16 +3,24 @@
 // "QLoRA, explained", The forward pass and gradients / The algorithm, step by step:
 //   forward   y  = X W~^T + s (X A^T) B^T            (contraction over K)
 //   backward  dX = dY W~  + s (dY B) A               (contraction over N; W is read again)
-// W~ never exists in HBM: each workgroup dequantises a tile of packed NF4 codes into LDS with the
-// per-block bf16 lookup table and feeds it to v_mfma_f32_16x16x32_bf16. The adapter term rides on
-// the same accumulators as extra contraction steps: the operands are bf16(s * u) with B (forward)
-// or bf16(s * v) with A (backward), where u = X A^T and v = dY B come from the LoRA kernels.
+// W~ never exists in HBM: the packed NF4 codes of a tile are dequantised into LDS with the per-block
+// bf16 lookup table and fed to v_mfma_f32_16x16x32_bf16. The adapter term rides on the same
+// accumulators as extra contraction steps: operands bf16(s * u) with B (forward) or bf16(s * v) with
+// A (backward), where u = X A^T and v = dY B come from the LoRA kernels.
 //
-// Tile: BM activation rows x 128 output columns, contraction in steps of 64. The W tile in LDS is
-// stored [row of W][column of W] (K contiguous) for both directions: the forward reads it row-wise
-// with ds_read_b128, the backward reads it column-wise with ds_read_b64_tr_b16 (a 16-lane
-// transpose load: lane j of a 16-lane group receives element j%4 of the 8-byte rows addressed by
-// lanes j/4, j/4+4, j/4+8, j/4+12).
+// Workgroup = 8 waves on a BM x 128 output tile, contraction in steps of 64:
+//   * waves 0-3 (consumers) only read LDS and issue MFMAs; each owns a (BM/2) x 64 sub-tile;
+//   * waves 4-7 (producers) load the activation tile and the packed weight two steps ahead into
+//     registers, dequantise the weight and write both into the LDS stage the consumers will use
+//     next. With one consumer and one producer per SIMD, VALU dequantisation and global loads
+//     overlap the MFMA stream.
+// LDS holds two stages; one workgroup barrier per step separates "consumers read stage s" from
+// "producers write stage s+1".
+//
+// The W tile in LDS is stored [row of W][column of W] (K contiguous) for both directions: the
+// forward reads it row-wise with ds_read_b128, the backward reads it column-wise with
+// ds_read_b64_tr_b16 (within 16 lanes, lane j receives element j%4 of the 8-byte rows addressed by
+// lanes j/4, j/4+4, j/4+8 and j/4+12).
 #include "common.h"
 #include "launch.h"
 
@@ -32,33 +40,47 @@ struct GemmArgs {
   uint16_t* out;            // y [M x N] (forward) or dX [M x K] (backward), bf16
 };
 
-constexpr int kBN = 128;   // output columns per tile
-constexpr int kBK = 64;    // contraction per step
+constexpr int kBN = 128;      // output columns per tile
+constexpr int kBK = 64;       // contraction per step
 constexpr int kAP = kBK + 8;  // activation tile pitch (bf16 elements)
 
 template <bool DX>
 struct WTile {
-  static constexpr int rows = DX ? kBK : kBN;        // contraction rows (DX) or output rows
+  static constexpr int rows = DX ? kBK : kBN;            // contraction rows (DX) or output rows
   static constexpr int pitch = DX ? kBN + 8 : kBK + 8;
-  static constexpr int segs = DX ? kBN / 32 : kBK / 32;  // 32-element segments per row
+  static constexpr int segs = DX ? kBN / 32 : kBK / 32;  // 32-value segments per row
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <bool DX, int BM>
-__global__ __launch_bounds__(256) void qlora_gemm_kernel(const GemmArgs g) {
-  constexpr int WAVES_M = BM >= 128 ? 2 : 1;
-  constexpr int WAVES_N = 4 / WAVES_M;
-  constexpr int WM = BM / WAVES_M, WN = kBN / WAVES_N;
+struct Smem {
+  uint16_t A[2][BM][kAP];
+  uint16_t W[2][WTile<DX>::rows][WTile<DX>::pitch];
+};
+
+// Producer-side staging of one contraction step in registers.
+template <int NA>
+struct Staged {
+  u32x4 act[NA];
+  u32x4 wq;        // 32 packed codes
+  float wscale;    // c1' of their block
+  bool wvalid;
+};
+
+template <bool DX, int BM>
+__global__ __launch_bounds__(512) void qlora_gemm_kernel(const GemmArgs g) {
+  constexpr int WM = BM / 2, WN = kBN / 2;   // consumer sub-tile
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int NA = BM * kBK / 8 / 256;  // 16-byte activation chunks per thread per step
+  constexpr int NA = BM * kBK / 8 / 256;     // 16-byte activation chunks per producer thread
   using WT = WTile<DX>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][kAP];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][WT::rows][WT::pitch];
+  __shared__ __attribute__((aligned(16))) Smem<DX, BM> sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
+  const int tid = threadIdx.x;
+  const bool producer = tid >= 256;
+  const int lane = tid & 63, wave = (tid >> 6) & 3;
+  const int pt = tid - 256;  // producer thread index (valid if producer)
 
   // Tile coordinates; workgroups are dealt round-robin over the 8 XCDs, so give each XCD a
   // contiguous run of tiles that share an activation row block.
@@ -68,62 +90,49 @@ __global__ __launch_bounds__(256) void qlora_gemm_kernel(const GemmArgs g) {
   const int64_t col0 = (int64_t)(lin % gx) * kBN;
   const int64_t m0 = (int64_t)(lin / gx) * BM;
 
-  const int64_t Lc = DX ? g.N : g.K;           // contraction length
-  const int64_t Nout = DX ? g.K : g.N;         // output columns
-  const int64_t ld_act = Lc;
-  const int steps = (int)((Lc + kBK - 1) / kBK);
+  const int64_t Lc = DX ? g.N : g.K;       // contraction length
+  const int64_t Nout = DX ? g.K : g.N;     // output columns
+  const int main_steps = (int)((Lc + kBK - 1) / kBK);
+  const int lora_steps = (g.r + kBK - 1) / kBK;
+  const int steps = main_steps + lora_steps;
 
-  f32x4 acc[TN][TM];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ---------------------------------------------------------------- producer helpers
+  const int w_row = pt / WT::segs, w_seg = pt % WT::segs;
 
-  // ---- per-thread roles for staging
-  // activation: chunk q = tid + 256 * i covers row q / 8, columns (q % 8) * 8 .. +8
-  // W: thread covers one 32-element segment of one tile row
-  const int w_row = tid / WT::segs, w_seg = tid % WT::segs;
-
-  u32x4 areg[NA];
-  u32x4 wreg;
-  float wscale;
-  bool wvalid;
-
-  auto load_step = [&](int s) {
+  auto load_main = [&](int s, Staged<NA>& st) {
     const int64_t c0 = (int64_t)s * kBK;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const int q = tid + 256 * i;
+      const int q = pt + 256 * i;
       const int64_t row = m0 + (q >> 3), col = c0 + (q & 7) * 8;
-      if (row < g.M && col < Lc)
-        areg[i] = *reinterpret_cast<const u32x4*>(g.act + row * ld_act + col);
-      else
-        areg[i] = u32x4{0u, 0u, 0u, 0u};
+      st.act[i] = (row < g.M && col < Lc)
+                      ? *reinterpret_cast<const u32x4*>(g.act + row * Lc + col)
+                      : u32x4{0u, 0u, 0u, 0u};
     }
     int64_t n, k;
     if (DX) { n = c0 + w_row; k = col0 + 32 * w_seg; }
     else    { n = col0 + w_row; k = c0 + 32 * w_seg; }
-    wvalid = n < g.N && k < g.K;
-    if (wvalid) {
+    st.wvalid = n < g.N && k < g.K;
+    if (st.wvalid) {
       const int64_t e = n * g.K + k;
-      wreg = *reinterpret_cast<const u32x4*>(g.packed + e / 2);
-      wscale = block_scale(g.scale_q, g.scale_c2, e / kBlock);
+      st.wq = *reinterpret_cast<const u32x4*>(g.packed + e / 2);
+      st.wscale = block_scale(g.scale_q, g.scale_c2, e / kBlock);
     }
   };
 
-  auto store_step = [&](int buf) {
+  auto store_main = [&](int buf, const Staged<NA>& st) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const int q = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(&As[buf][q >> 3][(q & 7) * 8]) = areg[i];
+      const int q = pt + 256 * i;
+      *reinterpret_cast<u32x4*>(&sm.A[buf][q >> 3][(q & 7) * 8]) = st.act[i];
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(&Ws[buf][w_row][32 * w_seg]);
-    if (wvalid) {
-      const BlockLut t = make_lut(wscale);
+    u32x4* dst = reinterpret_cast<u32x4*>(&sm.W[buf][w_row][32 * w_seg]);
+    if (st.wvalid) {
+      const BlockLut t = make_lut(st.wscale);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t d[4];
-        dequant8(t, wreg[i], d);
+        dequant8(t, st.wq[i], d);
         dst[i] = u32x4{d[0], d[1], d[2], d[3]};
       }
     } else {
@@ -132,67 +141,25 @@ __global__ __launch_bounds__(256) void qlora_gemm_kernel(const GemmArgs g) {
     }
   };
 
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      bf16x8 bfr[TM], afr[TN];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-        bfr[tm] = *reinterpret_cast<const bf16x8*>(
-            &As[buf][wm0 + tm * 16 + (lane & 15)][kk + 8 * (lane >> 4)]);
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        if (DX) {
-          const int j = lane & 15, grp = lane >> 4;
-          const int col = wn0 + tn * 16 + 4 * (j & 3);
-          const int row = kk + 8 * grp + (j >> 2);
-          bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4*)(&Ws[buf][row][col]));
-          bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4*)(&Ws[buf][row + 4][col]));
-          afr[tn] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        } else {
-          afr[tn] = *reinterpret_cast<const bf16x8*>(
-              &Ws[buf][wn0 + tn * 16 + (lane & 15)][kk + 8 * (lane >> 4)]);
-        }
-      }
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-          acc[tn][tm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[tn], bfr[tm], acc[tn][tm], 0, 0, 0);
-    }
-  };
-
-  // ---- main contraction: double-buffered LDS, one barrier per step
-  load_step(0);
-  store_step(0);
-  __syncthreads();
-  for (int s = 0; s < steps; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < steps) load_step(s + 1);
-    compute(cur);
-    if (s + 1 < steps) store_step(cur ^ 1);
-    __syncthreads();
-  }
-
-  // ---- adapter term: contraction over the rank, 64 at a time, operands staged straight to LDS
-  for (int j0 = 0; j0 < g.r; j0 += kBK) {
+  // adapter step: contraction over rank columns j0 .. j0+63, loaded straight into LDS
+  auto store_lora = [&](int s, int buf) {
+    const int j0 = (s - main_steps) * kBK;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const int q = tid + 256 * i;
+      const int q = pt + 256 * i;
       const int64_t row = m0 + (q >> 3);
       const int col = j0 + (q & 7) * 8;
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
       if (row < g.M && col < g.r) {
         const f32x4* src = reinterpret_cast<const f32x4*>(g.lora_act + row * g.r + col);
         const f32x4 a = src[0], b = src[1];
-        v = u32x4{pack_bf16x2(g.scale * a[0], g.scale * a[1]), pack_bf16x2(g.scale * a[2], g.scale * a[3]),
-                  pack_bf16x2(g.scale * b[0], g.scale * b[1]), pack_bf16x2(g.scale * b[2], g.scale * b[3])};
+        const float sc = g.scale;
+        v = u32x4{pack_bf16x2(sc * a[0], sc * a[1]), pack_bf16x2(sc * a[2], sc * a[3]),
+                  pack_bf16x2(sc * b[0], sc * b[1]), pack_bf16x2(sc * b[2], sc * b[3])};
       }
-      *reinterpret_cast<u32x4*>(&As[0][q >> 3][(q & 7) * 8]) = v;
+      *reinterpret_cast<u32x4*>(&sm.A[buf][q >> 3][(q & 7) * 8]) = v;
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(&Ws[0][w_row][32 * w_seg]);
+    u32x4* dst = reinterpret_cast<u32x4*>(&sm.W[buf][w_row][32 * w_seg]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
@@ -206,12 +173,95 @@ __global__ __launch_bounds__(256) void qlora_gemm_kernel(const GemmArgs g) {
       }
       dst[i] = v;
     }
+  };
+
+  // ---------------------------------------------------------------- producer loop
+  // The two roles run separate loops that execute the same number of workgroup barriers, so
+  // each role's registers are live only in its own loop. Producers hold two register stages: at
+  // step s they write step s+1 to LDS and start loading step s+3 into the registers just freed;
+  // step s+2 is already in flight in the other set.
+  if (producer) {
+    Staged<NA> r0, r1;
+    load_main(0, r0);
+    store_main(0, r0);
+    if (1 < main_steps) load_main(1, r1);
+    if (2 < main_steps) load_main(2, r0);
     __syncthreads();
-    compute(0);
+    for (int s = 0; s < steps; s += 2) {
+      if (s + 1 < steps) {            // prepare step s+1 in stage 1 from r1
+        if (s + 1 < main_steps) {
+          store_main(1, r1);
+          if (s + 3 < main_steps) load_main(s + 3, r1);
+        } else {
+          store_lora(s + 1, 1);
+        }
+      }
+      __syncthreads();
+      if (s + 1 >= steps) break;
+      if (s + 2 < steps) {            // prepare step s+2 in stage 0 from r0
+        if (s + 2 < main_steps) {
+          store_main(0, r0);
+          if (s + 4 < main_steps) load_main(s + 4, r0);
+        } else {
+          store_lora(s + 2, 0);
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------------------------------------------------------- consumer loop
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  f32x4 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_frags = [&](int buf, int kk, bf16x8* afr, bf16x8* bfr) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+      bfr[tm] = *reinterpret_cast<const bf16x8*>(
+          &sm.A[buf][wm0 + tm * 16 + (lane & 15)][kk + 8 * (lane >> 4)]);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      if (DX) {
+        const int j = lane & 15, grp = lane >> 4;
+        const int col = wn0 + tn * 16 + 4 * (j & 3);
+        const int row = kk + 8 * grp + (j >> 2);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(&sm.W[buf][row][col]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(&sm.W[buf][row + 4][col]));
+        afr[tn] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
+        afr[tn] = *reinterpret_cast<const bf16x8*>(
+            &sm.W[buf][wn0 + tn * 16 + (lane & 15)][kk + 8 * (lane >> 4)]);
+      }
+    }
+  };
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < kBK; kk += 32) {
+      bf16x8 afr[TN], bfr[TM];
+      load_frags(buf, kk, afr, bfr);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+          acc[tn][tm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[tn], bfr[tm], acc[tn][tm], 0, 0, 0);
+      // keep the two sub-steps' fragments from being live at the same time
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    compute(s & 1);
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds 4 consecutive output columns of one row
+  // ---------------------------------------------------------------- epilogue
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
@@ -231,11 +281,16 @@ template <bool DX>
 static hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t stream) {
   const int64_t Nout = DX ? g.K : g.N;
   const int gx = (int)((Nout + kBN - 1) / kBN);
-  if (g.M > 64) {
+  const int64_t tiles256 = (int64_t)gx * ((g.M + 255) / 256);
+  if (g.M > 128 && tiles256 >= 192) {
     const int gy = (int)((g.M + 255) / 256);
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 256>), dim3(gx, gy), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 256>), dim3(gx, gy), dim3(512), 0, stream, g);
+  } else if (g.M > 64) {
+    const int gy = (int)((g.M + 127) / 128);
+    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 128>), dim3(gx, gy), dim3(512), 0, stream, g);
   } else {
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 64>), dim3(gx, 1), dim3(256), 0, stream, g);
+    const int gy = (int)((g.M + 63) / 64);
+    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 64>), dim3(gx, gy), dim3(512), 0, stream, g);
   }
   return hipGetLastError();
 }

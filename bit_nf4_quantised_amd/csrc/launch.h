@@ -24,8 +24,11 @@ hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const f
 int lora_down_chunks(int64_t M, int64_t L);
 hipError_t launch_lora_down(const uint16_t* P, int64_t M, int64_t L, const uint16_t* Q, bool q_is_lr,
                             int r, float* part, float* out, hipStream_t stream);
+// Adapter gradient out = scale * Q^T P (fp32); `part` holds lora_grad_workspace_floats(M, C, r) floats.
+size_t lora_grad_workspace_floats(int64_t M, int64_t C, int r);
 hipError_t launch_lora_grad(const float* P, const uint16_t* Q, int64_t M, int64_t C, int r,
-                            float scale, float* out, bool out_cr, int accumulate, hipStream_t stream);
+                            float scale, float* out, bool out_cr, int accumulate, float* part,
+                            hipStream_t stream);
 
 // Skinny forward (M <= 16): split-K dequant-GEMV on MFMA with a deterministic reduction.
 // `part` holds skinny_workspace_floats(M, N, K, r) floats; u_out receives u = x A^T [M x r].

@@ -106,18 +106,19 @@ __global__ __launch_bounds__(256) void lora_down_reduce_kernel(const float* __re
 
 // ------------------------------------------------------------------------------------------
 // Adapter gradients: D[c][j] = sum_m Q[m][c] * P[m][j] with P fp32 [M x r] split into bf16
-// hi + lo parts (P - hi rounded again), Q bf16 [M x C]. Workgroup: 64 columns c, all r; its four
-// waves take interleaved 32-row slices of M and are summed in wave order at the end.
+// hi + lo parts (P - hi rounded again), Q bf16 [M x C].
 //   OUT_CR = false: out is [r x C] (dA = s v^T X: P = v, Q = X)
 //   OUT_CR = true:  out is [C x r] (dB = s dY^T u: P = u, Q = dY)
+// Workgroup (blockIdx.x, blockIdx.y) = (64 columns c, one slice of M). Its four waves take
+// interleaved 32-row slices of that range, prefetching the next slice into registers while the
+// current one is multiplied; the waves are summed in wave order into part[slice][c][j], and
+// lora_grad_reduce_kernel sums the slices in order, scales and writes (or accumulates) the output.
 template <bool OUT_CR>
 __global__ __launch_bounds__(256) void lora_grad_kernel(const float* __restrict__ P,
                                                         const uint16_t* __restrict__ Q, int64_t M,
-                                                        int64_t C, int r, float scale,
-                                                        float* __restrict__ out, int accumulate) {
+                                                        int64_t C, int r, int64_t m_per_slice,
+                                                        float* __restrict__ part) {
   constexpr int QP = 64 + 8, PP = 128 + 8, RP = 128 + 1;
-  // The staging tiles (used in the main loop) and the cross-wave reduction buffer (used after it)
-  // share one LDS allocation.
   constexpr int kStage = 4 * 32 * QP * 2 + 2 * 4 * 32 * PP * 2;
   constexpr int kRed = 4 * 64 * RP * 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kStage > kRed ? kStage : kRed];
@@ -127,41 +128,68 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(const float* __restrict_
   auto Red = reinterpret_cast<float(*)[64][RP]>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int64_t m_begin = (int64_t)blockIdx.y * m_per_slice;
+  const int64_t m_end = min(M, m_begin + m_per_slice);
   const int RT = r / 16;
+  const int cols4 = r / 4;             // float4 chunks per P row
+  const int pchunks = 32 * cols4 / 64; // float4 chunks of a 32-row P slice per lane (2 .. 16)
   f32x4 acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t msteps = (M + 31) / 32;
-  const int64_t rounds = (msteps + 3) / 4;
-  for (int64_t rd = 0; rd < rounds; ++rd) {
-    const int64_t mb = (rd * 4 + wave) * 32;
-    // Q slice: 32 rows x 64 columns
+  u32x4 qreg[4];
+  f32x4 preg[16];
+  auto load = [&](int64_t mb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = lane + 64 * i;
       const int row = q >> 3, c8 = (q & 7) * 8;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (mb + row < M && c0 + c8 < C)
-        v = *reinterpret_cast<const u32x4*>(Q + (mb + row) * C + c0 + c8);
-      *reinterpret_cast<u32x4*>(&Qs[wave][row][c8]) = v;
+      qreg[i] = (mb + row < m_end && c0 + c8 < C)
+                    ? *reinterpret_cast<const u32x4*>(Q + (mb + row) * C + c0 + c8)
+                    : u32x4{0u, 0u, 0u, 0u};
     }
-    // P slice: 32 rows x r columns, hi/lo bf16
-    const int cols4 = r / 4;
-    for (int q = lane; q < 32 * cols4; q += 64) {
-      const int row = q / cols4, c4 = (q % cols4) * 4;
-      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (mb + row < M) v = *reinterpret_cast<const f32x4*>(P + (mb + row) * r + c4);
-      uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
-      float hv[4] = {__uint_as_float(h01 << 16), __uint_as_float(h01 & 0xFFFF0000u),
-                     __uint_as_float(h23 << 16), __uint_as_float(h23 & 0xFFFF0000u)};
-      uint32_t l01 = pack_bf16x2(v[0] - hv[0], v[1] - hv[1]);
-      uint32_t l23 = pack_bf16x2(v[2] - hv[2], v[3] - hv[3]);
-      *reinterpret_cast<u32x2*>(&Ph[wave][row][c4]) = u32x2{h01, h23};
-      *reinterpret_cast<u32x2*>(&Pl[wave][row][c4]) = u32x2{l01, l23};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < pchunks) {
+        const int q = lane + 64 * i;
+        const int row = q / cols4, c4 = (q % cols4) * 4;
+        preg[i] = (mb + row < m_end) ? *reinterpret_cast<const f32x4*>(P + (mb + row) * r + c4)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = lane + 64 * i;
+      *reinterpret_cast<u32x4*>(&Qs[wave][q >> 3][(q & 7) * 8]) = qreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < pchunks) {
+        const int q = lane + 64 * i;
+        const int row = q / cols4, c4 = (q % cols4) * 4;
+        const f32x4 v = preg[i];
+        const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+        const uint32_t l01 = pack_bf16x2(v[0] - __uint_as_float(h01 << 16),
+                                         v[1] - __uint_as_float(h01 & 0xFFFF0000u));
+        const uint32_t l23 = pack_bf16x2(v[2] - __uint_as_float(h23 << 16),
+                                         v[3] - __uint_as_float(h23 & 0xFFFF0000u));
+        *reinterpret_cast<u32x2*>(&Ph[wave][row][c4]) = u32x2{h01, h23};
+        *reinterpret_cast<u32x2*>(&Pl[wave][row][c4]) = u32x2{l01, l23};
+      }
+    }
+  };
+
+  // uniform trip count across waves: every wave runs `rounds` rounds (empty slices are zeros)
+  const int64_t rows = m_end > m_begin ? m_end - m_begin : 0;
+  const int64_t rounds = (rows + 127) / 128;
+  if (rounds > 0) load(m_begin + wave * 32);
+  for (int64_t rd = 0; rd < rounds; ++rd) {
+    stage();
+    if (rd + 1 < rounds) load(m_begin + ((rd + 1) * 4 + wave) * 32);
     __syncthreads();
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -183,8 +211,8 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(const float* __restrict_
     }
     __syncthreads();
   }
-  // lane layout of acc[ct][rt][i]: OUT_CR = false: c = ct*16 + 4*(lane/16) + i, j = rt*16 + lane%16
-  //                                 OUT_CR = true:  j = rt*16 + 4*(lane/16) + i, c = ct*16 + lane%16
+  // acc[ct][rt][i]: OUT_CR = false: c = ct*16 + 4*(lane/16) + i, j = rt*16 + lane%16
+  //                 OUT_CR = true:  j = rt*16 + 4*(lane/16) + i, c = ct*16 + lane%16
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -198,18 +226,32 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(const float* __restrict_
           Red[wave][c][j] = acc[ct][rt][i];
         }
   __syncthreads();
-  const int total = 64 * r;
-  for (int idx = tid; idx < total; idx += 256) {
-    int c, j;
-    if (OUT_CR) { c = idx / r; j = idx % r; }
-    else        { j = idx / 64; c = idx % 64; }
+  // part[slice][c][j] for the 64 columns of this workgroup
+  float* dst = part + (int64_t)blockIdx.y * C * r;
+  for (int idx = tid; idx < 64 * r; idx += 256) {
+    const int c = idx / r, j = idx % r;
     const int64_t cc = c0 + c;
-    if (cc >= C) continue;
-    float v = ((Red[0][c][j] + Red[1][c][j]) + Red[2][c][j]) + Red[3][c][j];
-    v *= scale;
-    float* o = OUT_CR ? out + cc * r + j : out + (int64_t)j * C + cc;
-    *o = accumulate ? *o + v : v;
+    if (cc < C) dst[cc * r + j] = ((Red[0][c][j] + Red[1][c][j]) + Red[2][c][j]) + Red[3][c][j];
   }
+}
+
+// out = scale * sum over slices (in slice order) [+ out]; out is [C x r] (OUT_CR) or [r x C].
+__global__ __launch_bounds__(256) void lora_grad_reduce_kernel(const float* __restrict__ part,
+                                                               int slices, int64_t C, int r,
+                                                               float scale, int out_cr,
+                                                               float* __restrict__ out,
+                                                               int accumulate) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = C * r;
+  if (idx >= total) return;
+  // idx walks the output in memory order
+  int64_t c, j;
+  if (out_cr) { c = idx / r; j = idx % r; }
+  else        { j = idx / C; c = idx % C; }
+  float v = 0.f;
+  for (int sl = 0; sl < slices; ++sl) v += part[(int64_t)sl * total + c * r + j];
+  v *= scale;
+  out[idx] = accumulate ? out[idx] + v : v;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -245,13 +287,35 @@ hipError_t launch_lora_down(const uint16_t* P, int64_t M, int64_t L, const uint1
   return hipGetLastError();
 }
 
+// Token slices of the gradient kernels: about 512 workgroups, slices of whole 128-row rounds.
+static int lora_grad_plan(int64_t M, int64_t C, int64_t* m_per_slice) {
+  const int64_t ctiles = (C + 63) / 64;
+  int64_t want = (512 + ctiles - 1) / ctiles;
+  const int64_t maxs = (M + 127) / 128;
+  if (want > maxs) want = maxs;
+  if (want < 1) want = 1;
+  *m_per_slice = ((M + want - 1) / want + 127) / 128 * 128;
+  return (int)((M + *m_per_slice - 1) / *m_per_slice);
+}
+
+size_t lora_grad_workspace_floats(int64_t M, int64_t C, int r) {
+  int64_t mps;
+  return (size_t)lora_grad_plan(M, C, &mps) * (size_t)C * (size_t)r;
+}
+
 hipError_t launch_lora_grad(const float* P, const uint16_t* Q, int64_t M, int64_t C, int r,
-                            float scale, float* out, bool out_cr, int accumulate, hipStream_t stream) {
-  dim3 grid((unsigned)((C + 63) / 64));
+                            float scale, float* out, bool out_cr, int accumulate, float* part,
+                            hipStream_t stream) {
+  int64_t mps;
+  const int slices = lora_grad_plan(M, C, &mps);
+  dim3 grid((unsigned)((C + 63) / 64), (unsigned)slices);
   if (out_cr)
-    hipLaunchKernelGGL((lora_grad_kernel<true>), grid, dim3(256), 0, stream, P, Q, M, C, r, scale, out, accumulate);
+    hipLaunchKernelGGL((lora_grad_kernel<true>), grid, dim3(256), 0, stream, P, Q, M, C, r, mps, part);
   else
-    hipLaunchKernelGGL((lora_grad_kernel<false>), grid, dim3(256), 0, stream, P, Q, M, C, r, scale, out, accumulate);
+    hipLaunchKernelGGL((lora_grad_kernel<false>), grid, dim3(256), 0, stream, P, Q, M, C, r, mps, part);
+  const int64_t total = C * r;
+  hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, part, slices, C, r, scale, out_cr ? 1 : 0, out, accumulate);
   return hipGetLastError();
 }
 

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(const u32x4* __restric
                                                           int64_t nchunks, u32x4* __restrict__ out) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
-    const u32x4 p = __builtin_nontemporal_load(packed + c);
+    const u32x4 p = packed[c];
     const BlockLut t = make_lut(block_scale(scale_q, scale_c2, c >> 1));
     u32x4 o[4];
 #pragma unroll
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(const u32x4* __restric
       o[i] = u32x4{d[0], d[1], d[2], d[3]};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(o[i], out + c * 4 + i);
+    for (int i = 0; i < 4; ++i) out[c * 4 + i] = o[i];
   }
 }
 

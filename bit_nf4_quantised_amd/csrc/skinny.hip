@@ -6,7 +6,8 @@
 // value). Layout of the work:
 //   * rows of W (N of them) followed by the r rows of A form the "row" axis, cut into tiles of 64;
 //     the k axis is cut into S splits of whole 256-column sub-chunks;
-//   * a workgroup (4 waves) takes one row tile and one split; wave w takes sub-chunks w, w+4, ...;
+//   * a workgroup (4 waves) takes one row tile and one split; wave w takes a contiguous quarter of
+//     the split's sub-chunks and keeps the next sub-chunk's packed codes in flight in registers;
 //     lane (row = lane % 16, grp = lane / 16) dequantises the 64-value block at column
 //     kb + 64 * grp of its row straight into MFMA operand registers (no LDS), and the same lane
 //     holds x[m = lane % 16][kb + 64 * grp ...] as the other operand, so v_mfma_f32_16x16x32_bf16
@@ -34,6 +35,12 @@ struct SkinnyArgs {
   float* part;         // [splits][M][N + r]
 };
 
+// One 16-row tile's packed codes for one sub-chunk, in registers.
+struct SkinnyStage {
+  u32x4 p[4][2];   // [tile][half of the lane's 64-value block]
+  float c1p[4];    // block scales
+};
+
 __global__ __launch_bounds__(256) void skinny_fwd_kernel(const SkinnyArgs g) {
   __shared__ float red[4][4][64][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -42,15 +49,42 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(const SkinnyArgs g) {
   const int64_t row_tile0 = (int64_t)blockIdx.x * 64;
   const int split = blockIdx.y;
   const int64_t nsub = (g.K + kSub - 1) / kSub;
-  const int64_t sub_begin = (int64_t)split * g.sub_per_split;
-  const int64_t sub_end = min(nsub, sub_begin + g.sub_per_split);
+  const int64_t split_begin = (int64_t)split * g.sub_per_split;
+  const int64_t split_end = min(nsub, split_begin + g.sub_per_split);
+  // wave w takes a contiguous quarter of the split's sub-chunks
+  const int64_t per_wave = (split_end - split_begin + 3) / 4;
+  const int64_t sub_begin = split_begin + wave * per_wave;
+  const int64_t sub_end = min(split_end, sub_begin + per_wave);
   const int64_t m = lane & 15;
+  // 16-row tiles of this workgroup: all NF4 rows, all adapter rows, or past the end
+  bool nf4_tile[4], live_tile[4];
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) {
+    const int64_t first = row_tile0 + tn * 16;
+    nf4_tile[tn] = first < g.N;
+    live_tile[tn] = first < rows;
+  }
 
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t sub = sub_begin + wave; sub < sub_end; sub += 4) {
+  auto load_stage = [&](int64_t sub, SkinnyStage& st) {
+    const int64_t kk = sub * kSub + 64 * grp;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      if (nf4_tile[tn] && kk < g.K) {
+        const int64_t row = row_tile0 + tn * 16 + (lane & 15);
+        const int64_t e = row * g.K + kk;
+        const u32x4* src = reinterpret_cast<const u32x4*>(g.packed + e / 2);
+        st.p[tn][0] = __builtin_nontemporal_load(src);
+        st.p[tn][1] = __builtin_nontemporal_load(src + 1);
+        st.c1p[tn] = block_scale(g.scale_q, g.scale_c2, e / kBlock);
+      }
+    }
+  };
+
+  auto process = [&](int64_t sub, const SkinnyStage& st) {
     const int64_t kk = sub * kSub + 64 * grp;
     const bool kvalid = kk < g.K;
     bf16x8 b[8];
@@ -61,34 +95,27 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(const SkinnyArgs g) {
     }
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn) {
-      const int64_t row = row_tile0 + tn * 16 + (lane & 15);
-      const int64_t tile_first = row_tile0 + tn * 16;
+      if (!live_tile[tn]) continue;
       uint32_t a[8][4];
-      if (tile_first < g.N) {
-        // NF4 rows (N % 16 == 0, so a 16-row tile is all NF4 or all adapter rows)
+      if (nf4_tile[tn]) {
         if (kvalid) {
-          const int64_t e = row * g.K + kk;
-          const u32x4* src = reinterpret_cast<const u32x4*>(g.packed + e / 2);
-          const u32x4 p0 = __builtin_nontemporal_load(src), p1 = __builtin_nontemporal_load(src + 1);
-          const BlockLut t = make_lut(block_scale(g.scale_q, g.scale_c2, e / kBlock));
+          const BlockLut t = make_lut(st.c1p[tn]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dequant8(t, p0[i], a[i]);
+          for (int i = 0; i < 4; ++i) dequant8(t, st.p[tn][0][i], a[i]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dequant8(t, p1[i], a[4 + i]);
+          for (int i = 0; i < 4; ++i) dequant8(t, st.p[tn][1][i], a[4 + i]);
         } else {
 #pragma unroll
           for (int i = 0; i < 8; ++i) a[i][0] = a[i][1] = a[i][2] = a[i][3] = 0u;
         }
-      } else if (tile_first < rows) {
-        const int64_t j = row - g.N;
+      } else {
+        const int64_t j = row_tile0 + tn * 16 + (lane & 15) - g.N;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           u32x4 v = u32x4{0u, 0u, 0u, 0u};
           if (kvalid && j < g.r) v = *reinterpret_cast<const u32x4*>(g.A + j * g.K + kk + 8 * i);
           a[i][0] = v[0]; a[i][1] = v[1]; a[i][2] = v[2]; a[i][3] = v[3];
         }
-      } else {
-        continue;
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -97,7 +124,19 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(const SkinnyArgs g) {
                                                           acc[tn], 0, 0, 0);
       }
     }
+  };
+
+  // two register stages: while sub-chunk i is dequantised, sub-chunk i+1 is in flight
+  SkinnyStage s0, s1;
+  if (sub_begin < sub_end) load_stage(sub_begin, s0);
+  for (int64_t sub = sub_begin; sub < sub_end; sub += 2) {
+    if (sub + 1 < sub_end) load_stage(sub + 1, s1);
+    process(sub, s0);
+    if (sub + 1 >= sub_end) break;
+    if (sub + 2 < sub_end) load_stage(sub + 2, s0);
+    process(sub + 1, s1);
   }
+
   // acc[tn][i]: row = tile row tn*16 + 4*grp + i, column m = lane % 16
 #pragma unroll
   for (int tn = 0; tn < 4; ++tn)
@@ -117,17 +156,17 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(const SkinnyArgs g) {
 }
 
 // y[m][n] = bf16(sum_s part[s][m][n] + scale * sum_j u[m][j] B[n][j]),  u[m][j] = sum_s part[s][m][N + j].
-// Each workgroup rebuilds u (M x r, at most 16 x 128) in LDS from the adapter-row partials, stages
-// its 256 columns of B, and sums the weight partials in split order.
+// Workgroup = 64 columns; it rebuilds u (M x r, at most 16 x 128) in LDS from the adapter-row
+// partials and stages its columns of B; thread t takes column t % 64 and tokens t / 64, +4, ...
 __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __restrict__ part, int splits,
                                                               int64_t M, int64_t N, int r,
                                                               const uint16_t* __restrict__ B, float scale,
                                                               float* __restrict__ u_out,
                                                               uint16_t* __restrict__ y) {
   __shared__ float us[16][128];
-  __shared__ uint16_t bs[128][256 + 2];
+  __shared__ float bs[128][64 + 1];
   const int64_t rows = N + r;
-  const int64_t n0 = (int64_t)blockIdx.x * 256;
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
   for (int idx = threadIdx.x; idx < M * r; idx += 256) {
     const int mm = idx / r, j = idx % r;
     float s = 0.f;
@@ -135,18 +174,19 @@ __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __res
     us[mm][j] = s;
     if (blockIdx.x == 0) u_out[(int64_t)mm * r + j] = s;
   }
-  for (int idx = threadIdx.x; idx < 256 * r; idx += 256) {
+  for (int idx = threadIdx.x; idx < 64 * r; idx += 256) {
     const int nl = idx / r, j = idx % r;
-    bs[j][nl] = (n0 + nl < N) ? B[(n0 + nl) * r + j] : (uint16_t)0;
+    bs[j][nl] = (n0 + nl < N) ? __uint_as_float((uint32_t)B[(n0 + nl) * r + j] << 16) : 0.f;
   }
   __syncthreads();
-  const int64_t n = n0 + threadIdx.x;
+  const int nl = threadIdx.x & 63;
+  const int64_t n = n0 + nl;
   if (n >= N) return;
-  for (int mm = 0; mm < M; ++mm) {
+  for (int mm = threadIdx.x >> 6; mm < M; mm += 4) {
     float s = 0.f;
     for (int sp = 0; sp < splits; ++sp) s += part[((int64_t)sp * M + mm) * rows + n];
     float l = 0.f;
-    for (int j = 0; j < r; ++j) l = fmaf(us[mm][j], __uint_as_float((uint32_t)bs[j][threadIdx.x] << 16), l);
+    for (int j = 0; j < r; ++j) l = fmaf(us[mm][j], bs[j][nl], l);
     const float v = s + scale * l;
     y[mm * N + n] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
   }
@@ -158,7 +198,7 @@ void skinny_plan(int64_t N, int64_t K, int r, int* splits, int* sub_per_split, i
   *row_tiles = (int)((N + r + 63) / 64);
   const int64_t nsub = (K + kSub - 1) / kSub;
   int64_t want = (1024 + *row_tiles - 1) / *row_tiles;
-  int64_t cap = nsub / 4;        // keep at least 4 sub-chunks (one per wave) per split
+  int64_t cap = nsub / 16;       // keep at least 16 sub-chunks (four per wave) per split
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
   if (want < 1) want = 1;
@@ -181,7 +221,7 @@ hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, cons
   SkinnyArgs g{packed, scale_q, scale_c2, N, K, x, M, A, r, splits, spp, part};
   hipLaunchKernelGGL(skinny_fwd_kernel, dim3((unsigned)row_tiles, (unsigned)splits), dim3(256), 0,
                      stream, g);
-  hipLaunchKernelGGL(skinny_epilogue_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(skinny_epilogue_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, stream,
                      part, splits, M, N, r, B, scale, u_out, y);
   return hipGetLastError();
 }

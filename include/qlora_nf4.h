@@ -109,6 +109,17 @@ int qlora_linear_bwd(const nf4_weight *W, const uint16_t *x, const uint16_t *dy,
                      uint16_t *dx, float *dA, float *dB, int accumulate, void *ws, size_t ws_bytes,
                      hipStream_t stream);
 
+/* Forward recompute with a known u = x A^T (as saved by qlora_linear_fwd): y = x W~^T + s u B^T.
+ * "QLoRA, explained", section "Compute and memory cost": when gradient checkpointing recomputes the
+ * forward, the weight is dequantised a third time per layer and step; the adapter down-projection
+ * saved by the first forward is reused rather than recomputed. For M > 16 this launches exactly one
+ * kernel (the fused dequantise + MFMA GEMM); for M <= 16 it runs the skinny path and needs ws.
+ *   u   [M x r] float32 input.  y [M x N] bf16 output.  ws as qlora_linear_fwd (may be NULL if M > 16).
+ * Errors as qlora_linear_fwd. */
+int qlora_linear_fwd_recompute(const nf4_weight *W, const uint16_t *x, int64_t M, const uint16_t *A,
+                               const uint16_t *B, int32_t r, float scale, const float *u, uint16_t *y,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes that qlora_linear_fwd and qlora_linear_bwd need for these sizes (the larger of
  * the two). Returns 0 for invalid sizes. */
 size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);

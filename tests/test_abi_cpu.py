@@ -106,6 +106,17 @@ def test_fwd_validation():
     assert f(None, FAKE, 64, FAKE, FAKE, 16, 2.0, FAKE, None, FAKE, ws, None) == q.NF4_ERR_NULL
 
 
+def test_recompute_validation():
+    w = ctypes.byref(_w())
+    f = lib.qlora_linear_fwd_recompute
+    assert f(w, FAKE, 64, FAKE, FAKE, 16, 2.0, None, FAKE, None, 0, None) == q.NF4_ERR_NULL
+    assert f(w, FAKE, 64, FAKE, FAKE, 20, 2.0, FAKE, FAKE, None, 0, None) == q.NF4_ERR_RANK
+    assert f(w, FAKE, 64, FAKE, FAKE, 16, 2.0, MISALIGNED, FAKE, None, 0, None) == q.NF4_ERR_ALIGN
+    # the skinny path (M <= 16) needs a workspace
+    assert f(w, FAKE, 8, FAKE, FAKE, 16, 2.0, FAKE, FAKE, None, 0, None) == q.NF4_ERR_WORKSPACE
+    assert f(w, FAKE, 0, FAKE, FAKE, 16, 2.0, FAKE, FAKE, None, 0, None) == q.NF4_OK
+
+
 def test_bwd_validation():
     w = ctypes.byref(_w())
     ws = q.qlora_workspace_bytes(64, 4096, 4096, 16)

@@ -122,3 +122,23 @@ def test_fwd_bwd_deterministic():
     r2 = gpu_fwd_bwd(qw, x, a, b, dy, 2.0)
     for p, q_ in zip(r1, r2):
         assert np.array_equal(p, q_)
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_forward_recompute_matches_forward(M):
+    """The recompute entry (u given) reproduces the forward's y bit for bit."""
+    import torch
+    import bit_nf4_quantised_amd as q
+    from gpu_helpers import bf16_to_dev, dev
+    N, K, r = 400, 960, 16
+    w, x, a, b, dy = _inputs(17 + M, M, N, K, r)
+    log(f"[linear] recompute M={M}")
+    qw = gpu_quantize(w)[0]
+    X, A, B = bf16_to_dev(x), bf16_to_dev(a), bf16_to_dev(b)
+    y1 = torch.empty(M, N, dtype=torch.int16, device=dev())
+    y2 = torch.empty(M, N, dtype=torch.int16, device=dev())
+    u = torch.empty(M, r, dtype=torch.float32, device=dev())
+    q.qlora_linear_fwd(qw, X, A, B, 2.0, y1, u)
+    q.qlora_linear_fwd_recompute(qw, X, A, B, 2.0, u, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)

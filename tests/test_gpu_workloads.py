@@ -14,8 +14,9 @@ from gpu_helpers import assert_close, f64_from_bits, gpu_dequant, gpu_fwd_bwd, g
 
 pytestmark = pytest.mark.gpu
 
-CASES = [(name, i) for name in ("llama8b", "llama65b", "llama70b")
-         for i in range(len(wl.WORKLOADS[name].linears))]
+# every linear of the 8B set; the distinct shapes (q, k, gate, down) of the 65B and 70B sets
+CASES = ([("llama8b", i) for i in range(7)] + [("llama65b", i) for i in (0, 1, 4, 6)]
+         + [("llama70b", i) for i in (0, 1, 4, 6)])
 
 
 def _oracle_quant(w):
