@@ -3,25 +3,32 @@
 // "QLoRA, explained", The forward pass and gradients / The algorithm, step by step:
 //   forward   y  = X W~^T + s (X A^T) B^T            (contraction over K)
 //   backward  dX = dY W~  + s (dY B) A               (contraction over N; W is read again)
-// W~ never exists in HBM: the packed NF4 codes of a tile are dequantised into LDS with the per-block
-// bf16 lookup table and fed to bf16 MFMAs. The adapter term rides on the same
-// accumulators as extra contraction steps: operands bf16(s * u) with B (forward) or bf16(s * v) with
-// A (backward), where u = X A^T and v = dY B come from the LoRA kernels.
+// W~ never exists in HBM: the packed NF4 codes of a tile are dequantised into LDS with a per-block
+// bf16 lookup table and fed to bf16 MFMAs. The adapter term rides on the same accumulators as extra
+// contraction steps: operands bf16(s * u) with B (forward) or bf16(s * v) with A (backward), where
+// u = X A^T and v = dY B come from the LoRA kernels.
 //
-// Workgroup = 8 waves on a BM x 128 output tile, contraction in steps of 64:
-//   * waves 0-3 (consumers) only read LDS and issue v_mfma_f32_32x32x16_bf16 (on gfx950 the
-//     16x16x32 form issues at half that rate); each owns a (BM/2) x 64 sub-tile;
-//   * waves 4-7 (producers) load the activation tile and the packed weight four steps ahead into
-//     registers, dequantise the weight and write both into the LDS stage the consumers will use
-//     next. With one consumer and one producer per SIMD, VALU dequantisation and global loads
-//     overlap the MFMA stream.
-// LDS holds two stages; one workgroup barrier per step separates "consumers read stage s" from
-// "producers write stage s+1".
+// Workgroup = 12 waves on a BM x 128 output tile, contraction in steps of 64:
+//   * waves 0-7 (consumers) only read LDS and issue v_mfma_f32_32x32x16_bf16. Two of them share
+//     each SIMD, so one issues MFMAs while the other waits on its LDS reads;
+//   * waves 8-11 (producers) stream the activation tile straight from global memory into LDS with
+//     16-byte LDS-DMA buffer loads (no registers, no VALU), load the packed weight, its scale codes
+//     and second-level constants three steps ahead into registers, dequantise the weight and write
+//     it to LDS. Their VALU work is the dequantisation alone, issued beside the MFMA stream.
+// LDS holds three activation stages and two weight stages; one workgroup barrier per step.
 //
-// The W tile in LDS is stored [row of W][column of W] (K contiguous) for both directions: the
-// forward reads it row-wise with ds_read_b128, the backward reads it column-wise with
+// Activation rows are 128 bytes in LDS (no padding, as DMA writes 64 lanes x 16 contiguous bytes);
+// the 16-byte chunk c of row r sits at slot c ^ ((r >> 1) & 7), which keeps the 16-lane groups of a
+// fragment read on distinct banks. The W tile is stored [row of W][column of W] (K contiguous) for
+// both directions: the forward reads it row-wise with ds_read_b128, the backward column-wise with
 // ds_read_b64_tr_b16 (within 16 lanes, lane j receives element j%4 of the 8-byte rows addressed by
 // lanes j/4, j/4+4, j/4+8 and j/4+12).
+//
+// Ragged edges need no per-element tests: buffer loads past the end of a tile's records return
+// zeros (activation rows past M, weight rows past N, their codes and constants), and the one
+// partial contraction step of the backward (N % 64 != 0) points its missing activation chunks past
+// the records. Weight rows past N dequantise to exact zeros there (code 0 and constant 0); in the
+// forward they only feed output columns that are not stored.
 #include "common.h"
 #include "launch.h"
 
@@ -41,9 +48,12 @@ struct GemmArgs {
   uint16_t* out;            // y [M x N] (forward) or dX [M x K] (backward), bf16
 };
 
-constexpr int kBN = 128;      // output columns per tile
-constexpr int kBK = 64;       // contraction per step
-constexpr int kAP = kBK + 8;  // activation tile pitch (bf16 elements)
+constexpr int kBN = 128;        // output columns per tile
+constexpr int kBK = 64;         // contraction per step
+constexpr int kXStages = 3;     // activation stages in LDS
+constexpr int kThreads = 768;   // 8 consumer + 4 producer waves
+constexpr int kRsrcFlags = 0x00020000;         // raw buffer, 32-bit data format
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past every record count used here
 
 template <bool DX>
 struct WTile {
@@ -54,37 +64,61 @@ struct WTile {
   static constexpr int segs = DX ? kBN / 32 : kBK / 32;  // 32-value segments per row
 };
 
+template <int BM>
+struct Waves {  // consumer layout: waves_m x waves_n waves, each on a WM x WN sub-tile
+  static constexpr int waves_m = BM == 64 ? 2 : 4;
+  static constexpr int waves_n = 8 / waves_m;
+  static constexpr int WM = BM / waves_m, WN = kBN / waves_n;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+};
+
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <bool DX, int BM>
-struct Smem {
-  uint16_t A[2][BM][kAP];
-  uint16_t W[2][WTile<DX>::rows][WTile<DX>::pitch];
+// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Producer-side barrier: the wave's LDS writes complete, then s_barrier. Written as inline asm so
+// that the compiler does not add a wait for every LDS-DMA load in flight (it cannot tell that
+// those target stages nobody reads this step); the producer waits for exactly the stage the
+// consumers read next with wait_vmcnt before calling this.
+__device__ __forceinline__ void producer_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Swap with the neighbouring lane (quad_perm [1,0,3,2]).
+__device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+
+// One packed weight chunk (32 values) of one step in registers: raw loaded words only, so issuing
+// the loads never waits for their arrival.
+struct WStage {
+  u32x4 wq;         // 32 packed codes
+  uint32_t code;    // aligned word holding the block's E4M3 scale code
+  uint32_t c2;      // the block's second-level constant (fp32 bits)
+  uint32_t shift;   // bit position of the code byte in `code`
 };
 
-// Producer-side staging of one contraction step in registers. Only raw loaded values are held
-// here (no arithmetic on them), so issuing the loads never waits for their arrival.
-template <int NA>
-struct Staged {
-  u32x4 act[NA];
-  u32x4 wq;        // 32 packed codes
-  uint32_t wcode;  // E4M3 code of their block's scale
-  float wc2;       // the block's second-level constant
-};
-
 template <bool DX, int BM>
-__global__ __launch_bounds__(512) void qlora_gemm_kernel(const GemmArgs g) {
-  constexpr int WM = BM / 2, WN = kBN / 2;   // consumer sub-tile
-  constexpr int TM = WM / 32, TN = WN / 32;  // 32 x 32 MFMA tiles per consumer
-  constexpr int NA = BM * kBK / 8 / 256;     // 16-byte activation chunks per producer thread
+__global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) {
   using WT = WTile<DX>;
+  using CW = Waves<BM>;
+  constexpr int TM = CW::TM, TN = CW::TN;
+  constexpr int NX = BM / 32;                 // activation DMA loads per producer wave per step
+  static_assert(NX <= 8, "activation DMA offsets");
+  constexpr int XSTAGE = BM * kBK;            // elements per activation stage
 
-  __shared__ __attribute__((aligned(16))) Smem<DX, BM> sm;
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[kXStages * XSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][WT::rows][WT::pitch];
 
   const int tid = threadIdx.x;
-  const bool producer = tid >= 256;
-  const int lane = tid & 63, wave = (tid >> 6) & 3;
-  const int pt = tid - 256;  // producer thread index (valid if producer)
+  const int lane = tid & 63;
 
   // Tile coordinates; workgroups are dealt round-robin over the 8 XCDs, so give each XCD a
   // contiguous run of tiles that share an activation row block.
@@ -100,145 +134,201 @@ __global__ __launch_bounds__(512) void qlora_gemm_kernel(const GemmArgs g) {
   const int lora_steps = (g.r + kBK - 1) / kBK;
   const int steps = main_steps + lora_steps;
 
-  // ---------------------------------------------------------------- producer helpers
-  // Loads are never predicated: addresses are clamped into range and the data of out-of-range
-  // chunks is zeroed when it is written to LDS. With straight-line loads the compiler can count
-  // outstanding loads exactly and waits only for the step being written, keeping the later
-  // steps in flight.
-  const int w_row = pt / WT::segs, w_seg = pt % WT::segs;
-
-  auto load_main = [&](int s, Staged<NA>& st) {
-    const int64_t c0 = (int64_t)s * kBK;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int q = pt + 256 * i;
-      const int64_t row = min(m0 + (q >> 3), g.M - 1);
-      const int64_t col = min(c0 + (q & 7) * 8, Lc - 8);
-      st.act[i] = *reinterpret_cast<const u32x4*>(g.act + row * Lc + col);
-    }
-    int64_t n, k;
-    if (DX) { n = c0 + w_row; k = col0 + 32 * w_seg; }
-    else    { n = col0 + w_row; k = c0 + 32 * w_seg; }
-    n = min(n, g.N - 1);
-    k = min(k, g.K - 32);
-    const int64_t e = n * g.K + k;
-    const int64_t b = e / kBlock;
-    st.wq = *reinterpret_cast<const u32x4*>(g.packed + e / 2);
-    st.wcode = g.scale_q[b];
-    st.wc2 = g.scale_c2[b / kGroup];
-  };
-
-  // whole-tile bounds tests are uniform across the workgroup; per-chunk tests only on edge tiles
-  const bool rows_full = m0 + BM <= g.M;
-  auto store_main = [&](int s, int buf, const Staged<NA>& st) {
-    const int64_t c0 = (int64_t)s * kBK;
-    const bool act_full = rows_full && c0 + kBK <= Lc;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int q = pt + 256 * i;
-      u32x4 v = st.act[i];
-      if (!act_full) {
-        const bool ok = m0 + (q >> 3) < g.M && c0 + (q & 7) * 8 < Lc;
-        if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-      }
-      *reinterpret_cast<u32x4*>(&sm.A[buf][q >> 3][(q & 7) * 8]) = v;
-    }
-    int64_t n, k;
-    if (DX) { n = c0 + w_row; k = col0 + 32 * w_seg; }
-    else    { n = col0 + w_row; k = c0 + 32 * w_seg; }
-    const bool w_full = DX ? (c0 + kBK <= g.N && col0 + kBN <= g.K) : (col0 + kBN <= g.N);
-    const bool wvalid = w_full || (n < g.N && k < g.K);
-    u32x4* dst = reinterpret_cast<u32x4*>(&sm.W[buf][w_row][32 * w_seg]);
-    const BlockLut t = make_lut(__fmul_rn(e4m3_decode(st.wcode), st.wc2));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t d[4];
-      dequant8(t, st.wq[i], d);
-      u32x4 v = u32x4{d[0], d[1], d[2], d[3]};
-      if (!w_full && !wvalid) v = u32x4{0u, 0u, 0u, 0u};
-      dst[i] = v;
-    }
-  };
-
-  // adapter step: contraction over rank columns j0 .. j0+63, loaded straight into LDS
-  auto store_lora = [&](int s, int buf) {
-    const int j0 = (s - main_steps) * kBK;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int q = pt + 256 * i;
-      const int64_t row = m0 + (q >> 3);
-      const int col = j0 + (q & 7) * 8;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (row < g.M && col < g.r) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(g.lora_act + row * g.r + col);
-        const f32x4 a = src[0], b = src[1];
-        const float sc = g.scale;
-        v = u32x4{pack_bf16x2(sc * a[0], sc * a[1]), pack_bf16x2(sc * a[2], sc * a[3]),
-                  pack_bf16x2(sc * b[0], sc * b[1]), pack_bf16x2(sc * b[2], sc * b[3])};
-      }
-      *reinterpret_cast<u32x4*>(&sm.A[buf][q >> 3][(q & 7) * 8]) = v;
-    }
-    u32x4* dst = reinterpret_cast<u32x4*>(&sm.W[buf][w_row][32 * w_seg]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (DX) {
-        const int64_t j = j0 + w_row, k = col0 + 32 * w_seg + 8 * i;
-        if (j < g.r && k < g.K) v = *reinterpret_cast<const u32x4*>(g.lora_w + j * g.K + k);
-      } else {
-        const int64_t n = col0 + w_row;
-        const int j = j0 + 32 * w_seg + 8 * i;
-        if (n < g.N && j < g.r) v = *reinterpret_cast<const u32x4*>(g.lora_w + n * g.r + j);
-      }
-      dst[i] = v;
-    }
-  };
-
-  // ---------------------------------------------------------------- producer loop
-  // The two roles run separate loops that execute the same number of workgroup barriers
-  // (1 + steps), so each role's registers are live only in its own loop. Producers keep a ring of
-  // four register stages (slot k holds main step t with t % 4 == k; loads past the last main step
-  // re-read it, unused): at step s they dequantise step s+1 into LDS and start loading step s+5
-  // into the slot just freed, so each load has about four steps to arrive.
-  if (producer) {
+  if (tid >= 512) {
+    // ================================================================ producers
+    const int pw = __builtin_amdgcn_readfirstlane(tid >> 6) - 8;   // producer wave 0..3 (uniform)
+    const int pt = tid - 512;        // producer thread 0..255
     const int last = main_steps - 1;
-    Staged<NA> r0, r1, r2, r3;
-    load_main(0, r0);
-    load_main(min(1, last), r1);
-    load_main(min(2, last), r2);
-    load_main(min(3, last), r3);
-    store_main(0, 0, r0);
-    load_main(min(4, last), r0);
-    __syncthreads();
-    auto body = [&](int s, Staged<NA>& next) {  // s + 1 < main_steps; `next` holds step s+1
-      store_main(s + 1, (s + 1) & 1, next);
-      load_main(min(s + 5, last), next);
-      __syncthreads();
+
+    // ---- activation tile by LDS DMA: instruction j of wave pw fills 16-byte slots
+    //      pw * 2BM + 64 j + lane of the stage; slot (row, s) holds logical chunk s ^ ((row>>1)&7)
+    const int64_t rows_valid = min(g.M - m0, (int64_t)BM);
+    uint32_t xoff[8];   // NX <= 8 entries used (a fixed size: lambdas that capture an array whose
+                        // size depends on a template parameter lose the kernel's host-side stub)
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+      const int slot = pw * 2 * BM + j * 64 + lane;
+      const int row = slot >> 3, c = (slot & 7) ^ ((row >> 1) & 7);
+      xoff[j] = (uint32_t)row * (uint32_t)(Lc * 2) + (uint32_t)c * 16u;
+    }
+    auto issue_x = [&](int t) {
+      const uint16_t* base = g.act + m0 * Lc + (int64_t)t * kBK;
+      const int nrec = (int)(rows_valid * Lc * 2 - (int64_t)t * kBK * 2);
+      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kRsrcFlags);
+      uint16_t* dst = Xs + (t % kXStages) * XSTAGE + (pw * 2 * BM) * 8;
+      if (__builtin_expect((int64_t)(t + 1) * kBK <= Lc, 1)) {
+#pragma unroll
+        for (int j = 0; j < NX; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + j * 64 * 8), 16, xoff[j], 0, 0, 0);
+      } else {   // a backward's last step with N % 64 != 0: chunks past N read zeros
+        const int valid_chunks = (int)(Lc - (int64_t)t * kBK) / 8;
+#pragma unroll
+        for (int j = 0; j < NX; ++j) {
+          const int slot = pw * 2 * BM + j * 64 + lane;
+          const int row = slot >> 3, c = (slot & 7) ^ ((row >> 1) & 7);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + j * 64 * 8), 16,
+                                                   c < valid_chunks ? xoff[j] : kOutOfRange, 0, 0, 0);
+        }
+      }
     };
-    for (int s = 0; s < last; s += 4) {
-      body(s, r1);
-      if (s + 1 >= last) break;
-      body(s + 1, r2);
-      if (s + 2 >= last) break;
-      body(s + 2, r3);
-      if (s + 3 >= last) break;
-      body(s + 3, r0);
+
+    // ---- packed weight chunk of this thread: 32 values of row w_row, segment w_seg of the W tile
+    const int w_row = pt / WT::segs, w_seg = pt % WT::segs;
+    const uint32_t kb = (uint32_t)(g.K / kBlock);         // blocks per row of W
+    const uint32_t wp_off = (uint32_t)w_row * (uint32_t)(g.K / 2) + (uint32_t)w_seg * 16u;
+    // block index of this thread's chunk at step t: b0 + t * b_step
+    const uint32_t b0 = DX ? (uint32_t)w_row * kb + (uint32_t)((col0 + 32 * w_seg) / kBlock)
+                           : (uint32_t)(col0 + w_row) * kb;
+    const uint32_t b_step = DX ? (uint32_t)kBK * kb : 1u;
+    const int64_t nblocks = g.N * (g.K / kBlock);
+    __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc((void*)g.scale_q, (short)0, (int)nblocks, kRsrcFlags);
+    __amdgpu_buffer_rsrc_t rs_c2 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.scale_c2, (short)0, (int)(((nblocks + kGroup - 1) / kGroup) * 4), kRsrcFlags);
+    auto load_w = [&](int t, WStage& st) {
+      const uint8_t* base;
+      int64_t nrec;
+      if (DX) {
+        base = g.packed + (int64_t)t * kBK * (g.K / 2) + col0 / 2;
+        nrec = (g.N - (int64_t)t * kBK) * (g.K / 2) - col0 / 2;
+      } else {
+        base = g.packed + col0 * (g.K / 2) + (int64_t)t * (kBK / 2);
+        nrec = min(g.N - col0, (int64_t)kBN) * (g.K / 2) - (int64_t)t * (kBK / 2);
+      }
+      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nrec, kRsrcFlags);
+      const uint32_t b = b0 + (uint32_t)t * b_step;
+      st.wq = __builtin_amdgcn_raw_buffer_load_b128(rs, wp_off, 0, 0);
+      st.code = __builtin_amdgcn_raw_buffer_load_b32(rs_q, b & ~3u, 0, 0);
+      st.c2 = __builtin_amdgcn_raw_buffer_load_b32(rs_c2, (b >> 8) * 4u, 0, 0);
+      st.shift = (b & 3u) * 8u;
+    };
+
+    // ---- dequantisation with a lookup table shared by the lane pair that holds one block: lane
+    // parity h computes the bf16 products of codes 8h .. 8h+7 and receives the other half from its
+    // neighbour. Odd lanes flip bit 3 of every index so that "own half" is entries 0..7 for both.
+    const uint32_t h = lane & 1;
+    float qv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = h ? code_value(8 + i) : code_value(i);
+    const uint32_t hx = h ? 0x88888888u : 0u, hx4 = hx >> 4;
+    auto dequant = [&](const WStage& st, int t) {
+      const float c1p = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)(st.code >> st.shift), 0),
+                                  __uint_as_float(st.c2));
+      uint32_t pp[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pp[k] = pack_bf16x2(__fmul_rn(qv[2 * k], c1p), __fmul_rn(qv[2 * k + 1], c1p));
+      BlockLut L;
+      L.lo[0] = __builtin_amdgcn_perm(pp[1], pp[0], 0x06040200u);
+      L.lo[1] = __builtin_amdgcn_perm(pp[3], pp[2], 0x06040200u);
+      L.hi[0] = __builtin_amdgcn_perm(pp[1], pp[0], 0x07050301u);
+      L.hi[1] = __builtin_amdgcn_perm(pp[3], pp[2], 0x07050301u);
+      L.lo[2] = swap_pair(L.lo[0]);
+      L.lo[3] = swap_pair(L.lo[1]);
+      L.hi[2] = swap_pair(L.hi[0]);
+      L.hi[3] = swap_pair(L.hi[1]);
+      u32x4* dst = reinterpret_cast<u32x4*>(&Ws[t & 1][w_row][32 * w_seg]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t p = st.wq[i];
+        const uint32_t odd = (p ^ hx) & 0x0F0F0F0Fu;           // elements 1,3,5,7
+        const uint32_t even = ((p >> 4) ^ hx4) & 0x0F0F0F0Fu;   // elements 0,2,4,6
+        const uint32_t s0 = __builtin_amdgcn_perm(odd, even, 0x05010400u);  // elements 0..3
+        const uint32_t s1 = __builtin_amdgcn_perm(odd, even, 0x07030602u);  // elements 4..7
+        uint32_t d[4];
+        lut4(L, s0, d[0], d[1]);
+        lut4(L, s1, d[2], d[3]);
+        dst[i] = u32x4{d[0], d[1], d[2], d[3]};
+      }
+    };
+
+    // ---- adapter steps: bf16(s * u) (or v) into the activation stage, B (or A) into the W stage
+    auto store_lora = [&](int t) {
+      const int j0 = (t - main_steps) * kBK;
+      uint16_t* xs = Xs + (t % kXStages) * XSTAGE;
+#pragma unroll
+      for (int i = 0; i < BM * 8 / 256; ++i) {
+        const int q = pt + 256 * i;
+        const int row = q >> 3, c = q & 7;
+        const int64_t m = m0 + row;
+        const int j = j0 + c * 8;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (m < g.M && j < g.r) {
+          const f32x4* src = reinterpret_cast<const f32x4*>(g.lora_act + m * g.r + j);
+          const f32x4 a = src[0], b = src[1];
+          const float sc = g.scale;
+          v = u32x4{pack_bf16x2(sc * a[0], sc * a[1]), pack_bf16x2(sc * a[2], sc * a[3]),
+                    pack_bf16x2(sc * b[0], sc * b[1]), pack_bf16x2(sc * b[2], sc * b[3])};
+        }
+        *reinterpret_cast<u32x4*>(xs + row * kBK + ((c ^ ((row >> 1) & 7)) * 8)) = v;
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(&Ws[t & 1][w_row][32 * w_seg]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (DX) {
+          const int64_t j = j0 + w_row, k = col0 + 32 * w_seg + 8 * i;
+          if (j < g.r && k < g.K) v = *reinterpret_cast<const u32x4*>(g.lora_w + j * g.K + k);
+        } else {
+          const int64_t n = col0 + w_row;
+          const int j = j0 + 32 * w_seg + 8 * i;
+          if (n < g.N && j < g.r) v = *reinterpret_cast<const u32x4*>(g.lora_w + n * g.r + j);
+        }
+        dst[i] = v;
+      }
+    };
+
+    // ---- schedule. Step s: load the weight of step s+3 into the ring slot just freed, start the
+    // activation DMA of step s+2, dequantise the weight of step s+1, then wait until the DMA of
+    // step s+1 has landed (the 3 weight loads and NX DMA loads issued this step may stay in
+    // flight; vector-memory loads complete in issue order) and meet the consumers at the barrier.
+    // The compiler's scheduling barriers keep that issue order fixed.
+    WStage r0, r1, r2;
+    load_w(0, r0);
+    load_w(min(1, last), r1);
+    load_w(min(2, last), r2);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_x(0);
+    if (main_steps > 1) issue_x(1);
+    __builtin_amdgcn_sched_barrier(0);
+    dequant(r0, 0);
+    if (main_steps > 1) wait_vmcnt<NX>();
+    else wait_vmcnt<0>();
+    producer_barrier();
+
+    auto body = [&](int s, WStage& nxt_load, const WStage& deq) {
+      load_w(min(s + 3, last), nxt_load);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool more_x = s + 2 < main_steps;
+      if (more_x) issue_x(s + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      dequant(deq, s + 1);
+      if (more_x) wait_vmcnt<3 + NX>();
+      else wait_vmcnt<0>();
+      producer_barrier();
+    };
+    int s = 0;
+    for (; s + 3 <= last; s += 3) {
+      body(s, r0, r1);
+      body(s + 1, r1, r2);
+      body(s + 2, r2, r0);
     }
-    // adapter steps, then the barrier of the final step
-    for (int s = last; s < steps - 1; ++s) {
-      store_lora(s + 1, (s + 1) & 1);
-      __syncthreads();
+    if (s < last) body(s, r0, r1);
+    if (s + 1 < last) body(s + 1, r1, r2);
+    for (int t = main_steps; t < steps; ++t) {   // adapter steps are written during step t - 1
+      wait_vmcnt<0>();
+      store_lora(t);
+      producer_barrier();
     }
-    __syncthreads();
+    producer_barrier();   // the barrier that ends the consumers' final step
     return;
   }
 
-  // ---------------------------------------------------------------- consumer loop
-  // v_mfma_f32_32x32x16_bf16 (the full-rate bf16 MFMA on gfx950): operand lane l holds row/column
-  // l % 32 and contraction 8 * (l / 32) .. +7; the result lane l holds column l % 32 and rows
-  // 8 * (q / 4) + 4 * (l / 32) + q % 4 for register q. The weight operand is the row side, so a lane
-  // ends up with four consecutive output columns of one activation row.
-  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  // ================================================================ consumers
+  // v_mfma_f32_32x32x16_bf16: operand lane l holds row/column l % 32 and contraction 8 * (l / 32)
+  // .. +7; the result lane l holds column l % 32 and rows 8 * (q / 4) + 4 * (l / 32) + q % 4 for
+  // register q. The weight operand is the row side, so a lane ends up with four consecutive output
+  // columns of one activation row.
+  const int cw = tid >> 6;
+  const int wm0 = (cw % CW::waves_m) * CW::WM, wn0 = (cw / CW::waves_m) * CW::WN;
   f32x16 acc[TN][TM];
 #pragma unroll
   for (int i = 0; i < TN; ++i)
@@ -247,34 +337,37 @@ __global__ __launch_bounds__(512) void qlora_gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  auto load_frags = [&](int buf, int kk, bf16x8* afr, bf16x8* bfr) {
+  // activation fragment of chunk pair kk: row wm0 + tm*32 + lane%32 (a multiple of 32 plus
+  // lane%32, so its swizzle is ((lane % 32) >> 1) & 7), logical chunk 2 kk + lane/32
+  int xaddr[4];
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-      bfr[tm] = *reinterpret_cast<const bf16x8*>(
-          &sm.A[buf][wm0 + tm * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      if (DX) {
-        // two 16-lane transpose loads per operand: lane group g16 covers output columns
-        // (g16 & 1) * 16 .. +15 and contraction rows 8 * (g16 >> 1) .. +7
-        const int j = lane & 15, g16 = lane >> 4;
-        const int col = wn0 + tn * 32 + (g16 & 1) * 16 + 4 * (j & 3);
-        const int row = kk + (g16 >> 1) * 8 + (j >> 2);
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(&sm.W[buf][row][col]));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(&sm.W[buf][row + 4][col]));
-        afr[tn] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      } else {
-        afr[tn] = *reinterpret_cast<const bf16x8*>(
-            &sm.W[buf][wn0 + tn * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
-      }
-    }
-  };
+  for (int kk = 0; kk < 4; ++kk)
+    xaddr[kk] = (wm0 + (lane & 31)) * kBK + (((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7)) * 8);
 
-  auto compute = [&](int buf) {
+  auto compute = [&](int s) {
+    const uint16_t* xs = Xs + (s % kXStages) * XSTAGE;
+    const int wb = s & 1;
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
+    for (int kk = 0; kk < 4; ++kk) {
       bf16x8 afr[TN], bfr[TM];
-      load_frags(buf, kk, afr, bfr);
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        bfr[tm] = *reinterpret_cast<const bf16x8*>(xs + xaddr[kk] + tm * 32 * kBK);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        if (DX) {
+          // two 16-lane transpose loads per operand: lane group g16 covers output columns
+          // (g16 & 1) * 16 .. +15 and contraction rows 8 * (g16 >> 1) .. +7
+          const int j = lane & 15, g16 = lane >> 4;
+          const int col = wn0 + tn * 32 + (g16 & 1) * 16 + 4 * (j & 3);
+          const int row = kk * 16 + (g16 >> 1) * 8 + (j >> 2);
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(&Ws[wb][row][col]));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(&Ws[wb][row + 4][col]));
+          afr[tn] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+          afr[tn] = *reinterpret_cast<const bf16x8*>(&Ws[wb][wn0 + tn * 32 + (lane & 31)][kk * 16 + 8 * (lane >> 5)]);
+        }
+      }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
@@ -285,7 +378,7 @@ __global__ __launch_bounds__(512) void qlora_gemm_kernel(const GemmArgs g) {
 
   __syncthreads();
   for (int s = 0; s < steps; ++s) {
-    compute(s & 1);
+    compute(s);
     __syncthreads();
   }
 
@@ -315,13 +408,13 @@ static hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t stream) {
   const int64_t tiles256 = (int64_t)gx * ((g.M + 255) / 256);
   if (g.M > 128 && tiles256 >= 192) {
     const int gy = (int)((g.M + 255) / 256);
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 256>), dim3(gx, gy), dim3(512), 0, stream, g);
+    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 256>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
   } else if (g.M > 64) {
     const int gy = (int)((g.M + 127) / 128);
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 128>), dim3(gx, gy), dim3(512), 0, stream, g);
+    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 128>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
   } else {
     const int gy = (int)((g.M + 63) / 64);
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 64>), dim3(gx, gy), dim3(512), 0, stream, g);
+    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 64>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
   }
   return hipGetLastError();
 }
