@@ -8,14 +8,19 @@
 // contraction steps: operands bf16(s * u) with B (forward) or bf16(s * v) with A (backward), where
 // u = X A^T and v = dY B come from the LoRA kernels.
 //
-// Workgroup = 12 waves on a BM x 128 output tile, contraction in steps of 64:
+// Workgroup = 16 waves on a BM x 128 output tile, contraction in steps of 64, three roles:
 //   * waves 0-7 (consumers) only read LDS and issue v_mfma_f32_32x32x16_bf16. Two of them share
 //     each SIMD, so one issues MFMAs while the other waits on its LDS reads;
-//   * waves 8-11 (producers) stream the activation tile straight from global memory into LDS with
-//     16-byte LDS-DMA buffer loads (no registers, no VALU), load the packed weight, its scale codes
-//     and second-level constants three steps ahead into registers, dequantise the weight and write
-//     it to LDS. Their VALU work is the dequantisation alone, issued beside the MFMA stream.
-// LDS holds three activation stages and two weight stages; one workgroup barrier per step.
+//   * waves 8-11 (dequantisers) turn the packed weight, its scale codes and second-level constants
+//     of a step (already in LDS) into the bf16 W tile: VALU work and LDS accesses only;
+//   * waves 12-15 (loaders) issue every global load as a 16-byte LDS-DMA buffer load: activation
+//     tiles one step ahead, packed weight tiles two steps ahead. The address unit takes a few tens
+//     of cycles per such load, so these waves spend most of their time waiting to issue; keeping
+//     that off the other waves' instruction streams is why they exist.
+// The roles meet at one workgroup barrier per phase. In phase q the loaders fetch activations of
+// step q+1 and packed weights of step q+2, the dequantisers build the W tile of step q and the
+// consumers multiply step q-1. LDS holds three activation stages, two W stages and three packed
+// weight stages.
 //
 // Activation rows are 128 bytes in LDS (no padding, as DMA writes 64 lanes x 16 contiguous bytes);
 // the 16-byte chunk c of row r sits at slot c ^ ((r >> 1) & 7), which keeps the 16-lane groups of a
@@ -51,7 +56,8 @@ struct GemmArgs {
 constexpr int kBN = 128;        // output columns per tile
 constexpr int kBK = 64;         // contraction per step
 constexpr int kXStages = 3;     // activation stages in LDS
-constexpr int kThreads = 768;   // 8 consumer + 4 producer waves
+constexpr int kPStages = 3;     // packed weight stages in LDS
+constexpr int kThreads = 1024;  // 8 consumer + 4 dequantiser + 4 loader waves
 constexpr int kRsrcFlags = 0x00020000;         // raw buffer, 32-bit data format
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past every record count used here
 
@@ -83,11 +89,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Producer-side barrier: the wave's LDS writes complete, then s_barrier. Written as inline asm so
-// that the compiler does not add a wait for every LDS-DMA load in flight (it cannot tell that
-// those target stages nobody reads this step); the producer waits for exactly the stage the
-// consumers read next with wait_vmcnt before calling this.
-__device__ __forceinline__ void producer_barrier() {
+// Workgroup barrier after the wave's LDS accesses complete. Written as inline asm so that the
+// compiler does not add a wait for every LDS-DMA load in flight (it cannot tell that those target
+// stages nobody reads in this phase); the loaders wait for exactly the loads read next with
+// wait_vmcnt before calling this.
+__device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
@@ -96,29 +102,24 @@ __device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
 }
 
-// One packed weight chunk (32 values) of one step in registers: raw loaded words only, so issuing
-// the loads never waits for their arrival.
-struct WStage {
-  u32x4 wq;         // 32 packed codes
-  uint32_t code;    // aligned word holding the block's E4M3 scale code
-  uint32_t c2;      // the block's second-level constant (fp32 bits)
-  uint32_t shift;   // bit position of the code byte in `code`
-};
-
 template <bool DX, int BM>
 __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) {
   using WT = WTile<DX>;
   using CW = Waves<BM>;
   constexpr int TM = CW::TM, TN = CW::TN;
-  constexpr int NX = BM / 32;                 // activation DMA loads per producer wave per step
+  constexpr int NX = BM / 32;                 // activation DMA loads per loader wave per phase
   static_assert(NX <= 8, "activation DMA offsets");
   constexpr int XSTAGE = BM * kBK;            // elements per activation stage
 
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kXStages * XSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t Ws[2][WT::rows][WT::pitch];
+  __shared__ __attribute__((aligned(16))) u32x4 Ps[kPStages][256];     // packed weight chunks
+  __shared__ __attribute__((aligned(16))) uint32_t Cs[kPStages][256];  // words holding scale codes
+  __shared__ __attribute__((aligned(16))) float Gs[kPStages][256];     // second-level constants
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // Tile coordinates; workgroups are dealt round-robin over the 8 XCDs, so give each XCD a
   // contiguous run of tiles that share an activation row block.
@@ -133,21 +134,19 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
   const int main_steps = (int)((Lc + kBK - 1) / kBK);
   const int lora_steps = (g.r + kBK - 1) / kBK;
   const int steps = main_steps + lora_steps;
+  const uint32_t kb = (uint32_t)(g.K / kBlock);   // blocks per row of W
 
-  if (tid >= 512) {
-    // ================================================================ producers
-    const int pw = __builtin_amdgcn_readfirstlane(tid >> 6) - 8;   // producer wave 0..3 (uniform)
-    const int pt = tid - 512;        // producer thread 0..255
-    const int last = main_steps - 1;
-
-    // ---- activation tile by LDS DMA: instruction j of wave pw fills 16-byte slots
-    //      pw * 2BM + 64 j + lane of the stage; slot (row, s) holds logical chunk s ^ ((row>>1)&7)
+  if (wave >= 12) {
+    // ================================================================ loaders
+    const int lw = wave - 12;
+    // ---- activation tile: instruction j of wave lw fills 16-byte slots lw * 2BM + 64 j + lane of
+    //      the stage; slot (row, s) holds logical chunk s ^ ((row >> 1) & 7)
     const int64_t rows_valid = min(g.M - m0, (int64_t)BM);
     uint32_t xoff[8];   // NX <= 8 entries used (a fixed size: lambdas that capture an array whose
                         // size depends on a template parameter lose the kernel's host-side stub)
 #pragma unroll
     for (int j = 0; j < NX; ++j) {
-      const int slot = pw * 2 * BM + j * 64 + lane;
+      const int slot = lw * 2 * BM + j * 64 + lane;
       const int row = slot >> 3, c = (slot & 7) ^ ((row >> 1) & 7);
       xoff[j] = (uint32_t)row * (uint32_t)(Lc * 2) + (uint32_t)c * 16u;
     }
@@ -155,36 +154,41 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
       const uint16_t* base = g.act + m0 * Lc + (int64_t)t * kBK;
       const int nrec = (int)(rows_valid * Lc * 2 - (int64_t)t * kBK * 2);
       __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kRsrcFlags);
-      uint16_t* dst = Xs + (t % kXStages) * XSTAGE + (pw * 2 * BM) * 8;
+      uint16_t* dst = Xs + (t % kXStages) * XSTAGE + (lw * 2 * BM) * 8;
       if (__builtin_expect((int64_t)(t + 1) * kBK <= Lc, 1)) {
 #pragma unroll
-        for (int j = 0; j < NX; ++j)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + j * 64 * 8), 16, xoff[j], 0, 0, 0);
+        for (int j = 0; j < NX; ++j) {
+          const uint32_t off = xoff[j];
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + j * 64 * 8), 16, off, 0, 0, 0);
+        }
       } else {   // a backward's last step with N % 64 != 0: chunks past N read zeros
         const int valid_chunks = (int)(Lc - (int64_t)t * kBK) / 8;
 #pragma unroll
         for (int j = 0; j < NX; ++j) {
-          const int slot = pw * 2 * BM + j * 64 + lane;
+          const int slot = lw * 2 * BM + j * 64 + lane;
           const int row = slot >> 3, c = (slot & 7) ^ ((row >> 1) & 7);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + j * 64 * 8), 16,
-                                                   c < valid_chunks ? xoff[j] : kOutOfRange, 0, 0, 0);
+          const uint32_t off = c < valid_chunks ? xoff[j] : kOutOfRange;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + j * 64 * 8), 16, off, 0, 0, 0);
         }
       }
     };
 
-    // ---- packed weight chunk of this thread: 32 values of row w_row, segment w_seg of the W tile
-    const int w_row = pt / WT::segs, w_seg = pt % WT::segs;
-    const uint32_t kb = (uint32_t)(g.K / kBlock);         // blocks per row of W
+    // ---- packed weight tile: slot lw * 64 + lane is the 32-value chunk the dequantiser thread of
+    //      the same index expands (row w_row, segment w_seg of the W tile)
+    const int pslot = lw * 64 + lane;
+    const int w_row = pslot / WT::segs, w_seg = pslot % WT::segs;
     const uint32_t wp_off = (uint32_t)w_row * (uint32_t)(g.K / 2) + (uint32_t)w_seg * 16u;
-    // block index of this thread's chunk at step t: b0 + t * b_step
-    const uint32_t b0 = DX ? (uint32_t)w_row * kb + (uint32_t)((col0 + 32 * w_seg) / kBlock)
-                           : (uint32_t)(col0 + w_row) * kb;
-    const uint32_t b_step = DX ? (uint32_t)kBK * kb : 1u;
     const int64_t nblocks = g.N * (g.K / kBlock);
     __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc((void*)g.scale_q, (short)0, (int)nblocks, kRsrcFlags);
     __amdgpu_buffer_rsrc_t rs_c2 = __builtin_amdgcn_make_buffer_rsrc(
         (void*)g.scale_c2, (short)0, (int)(((nblocks + kGroup - 1) / kGroup) * 4), kRsrcFlags);
-    auto load_w = [&](int t, WStage& st) {
+    // scales: forward, one block per W row and step (rows 0-63 by waves 0/2, 64-127 by 1/3: the
+    // word holding the code, then the constant); backward, two blocks per W row (wave 0: the 16
+    // bytes from the aligned word holding both codes, wave 1: 16 bytes of constants)
+    const int srow = DX ? lane : (lw & 1) * 64 + lane;
+    const uint32_t sb0 = DX ? (uint32_t)srow * kb + (uint32_t)(col0 / kBlock) : (uint32_t)(col0 + srow) * kb;
+    const uint32_t sb_step = DX ? (uint32_t)kBK * kb : 1u;
+    auto issue_p = [&](int t) {
       const uint8_t* base;
       int64_t nrec;
       if (DX) {
@@ -195,13 +199,51 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
         nrec = min(g.N - col0, (int64_t)kBN) * (g.K / 2) - (int64_t)t * (kBK / 2);
       }
       __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nrec, kRsrcFlags);
-      const uint32_t b = b0 + (uint32_t)t * b_step;
-      st.wq = __builtin_amdgcn_raw_buffer_load_b128(rs, wp_off, 0, 0);
-      st.code = __builtin_amdgcn_raw_buffer_load_b32(rs_q, b & ~3u, 0, 0);
-      st.c2 = __builtin_amdgcn_raw_buffer_load_b32(rs_c2, (b >> 8) * 4u, 0, 0);
-      st.shift = (b & 3u) * 8u;
+      const int ps = t % kPStages;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&Ps[ps][lw * 64]), 16, wp_off, 0, 0, 0);
+      const uint32_t b = sb0 + (uint32_t)t * sb_step;
+      if (DX) {
+        if (lw == 0) {
+          const uint32_t off = b & ~3u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_q, (lds_void*)(&Cs[ps][0]), 16, off, 0, 0, 0);
+        } else if (lw == 1) {
+          const uint32_t off = (b >> 8) * 4u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_c2, (lds_void*)(&Gs[ps][0]), 16, off, 0, 0, 0);
+        }
+      } else {
+        if (lw < 2) {
+          const uint32_t off = b & ~3u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_q, (lds_void*)(&Cs[ps][(lw & 1) * 64]), 4, off, 0, 0, 0);
+        } else {
+          const uint32_t off = (b >> 8) * 4u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_c2, (lds_void*)(&Gs[ps][(lw & 1) * 64]), 4, off, 0, 0, 0);
+        }
+      }
     };
 
+    // ---- schedule. Phase q issues the activations of step q+1, then the packed weights of step
+    // q+2, and waits until everything issued in phase q-1 has landed: at least NX + 1 loads were
+    // issued after it, and vector-memory loads complete in issue order.
+    issue_x(0);
+    issue_p(0);
+    if (main_steps > 1) issue_p(1);
+    wait_vmcnt<0>();
+    lds_barrier();
+    for (int q = 0; q <= steps; ++q) {
+      const bool more_x = q + 1 < main_steps, more_p = q + 2 < main_steps;
+      if (more_x) issue_x(q + 1);
+      if (more_p) issue_p(q + 2);
+      if (more_p) wait_vmcnt<NX + 1>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+    }
+    return;
+  }
+
+  if (wave >= 8) {
+    // ================================================================ dequantisers
+    const int dt = tid - 512;   // 0..255: the packed chunk of this thread
+    const int w_row = dt / WT::segs, w_seg = dt % WT::segs;
     // ---- dequantisation with a lookup table shared by the lane pair that holds one block: lane
     // parity h computes the bf16 products of codes 8h .. 8h+7 and receives the other half from its
     // neighbour. Odd lanes flip bit 3 of every index so that "own half" is entries 0..7 for both.
@@ -210,9 +252,27 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
 #pragma unroll
     for (int i = 0; i < 8; ++i) qv[i] = h ? code_value(8 + i) : code_value(i);
     const uint32_t hx = h ? 0x88888888u : 0u, hx4 = hx >> 4;
-    auto dequant = [&](const WStage& st, int t) {
-      const float c1p = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)(st.code >> st.shift), 0),
-                                  __uint_as_float(st.c2));
+    // block index of this thread's chunk at step t: b0 + t * b_step; where its code and constant
+    // sit in the scale stages
+    const uint32_t b0 = DX ? (uint32_t)w_row * kb + (uint32_t)((col0 + 32 * w_seg) / kBlock)
+                           : (uint32_t)(col0 + w_row) * kb;
+    const uint32_t b_step = DX ? (uint32_t)kBK * kb : 1u;
+    const uint32_t rb0 = DX ? (uint32_t)w_row * kb + (uint32_t)(col0 / kBlock) : b0;   // the row's first block
+    auto dequant = [&](int t) {
+      const int ps = t % kPStages;
+      const u32x4 wq = Ps[ps][dt];
+      const uint32_t b = b0 + (uint32_t)t * b_step;
+      uint32_t word, c2bits;
+      if (DX) {
+        const uint32_t rb = rb0 + (uint32_t)t * b_step;
+        const uint32_t byte = (rb & 3u) + (uint32_t)(w_seg >> 1);     // within the row's 16 bytes
+        word = Cs[ps][w_row * 4 + (int)(byte >> 2)] >> ((byte & 3u) * 8u);
+        c2bits = __float_as_uint(Gs[ps][w_row * 4 + (int)((b >> 8) - (rb >> 8))]);
+      } else {
+        word = Cs[ps][w_row] >> ((b & 3u) * 8u);
+        c2bits = __float_as_uint(Gs[ps][w_row]);
+      }
+      const float c1p = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)word, 0), __uint_as_float(c2bits));
       uint32_t pp[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) pp[k] = pack_bf16x2(__fmul_rn(qv[2 * k], c1p), __fmul_rn(qv[2 * k + 1], c1p));
@@ -228,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
       u32x4* dst = reinterpret_cast<u32x4*>(&Ws[t & 1][w_row][32 * w_seg]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t p = st.wq[i];
+        const uint32_t p = wq[i];
         const uint32_t odd = (p ^ hx) & 0x0F0F0F0Fu;           // elements 1,3,5,7
         const uint32_t even = ((p >> 4) ^ hx4) & 0x0F0F0F0Fu;   // elements 0,2,4,6
         const uint32_t s0 = __builtin_amdgcn_perm(odd, even, 0x05010400u);  // elements 0..3
@@ -246,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
       uint16_t* xs = Xs + (t % kXStages) * XSTAGE;
 #pragma unroll
       for (int i = 0; i < BM * 8 / 256; ++i) {
-        const int q = pt + 256 * i;
+        const int q = dt + 256 * i;
         const int row = q >> 3, c = q & 7;
         const int64_t m = m0 + row;
         const int j = j0 + c * 8;
@@ -276,49 +336,12 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
       }
     };
 
-    // ---- schedule. Step s: load the weight of step s+3 into the ring slot just freed, start the
-    // activation DMA of step s+2, dequantise the weight of step s+1, then wait until the DMA of
-    // step s+1 has landed (the 3 weight loads and NX DMA loads issued this step may stay in
-    // flight; vector-memory loads complete in issue order) and meet the consumers at the barrier.
-    // The compiler's scheduling barriers keep that issue order fixed.
-    WStage r0, r1, r2;
-    load_w(0, r0);
-    load_w(min(1, last), r1);
-    load_w(min(2, last), r2);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_x(0);
-    if (main_steps > 1) issue_x(1);
-    __builtin_amdgcn_sched_barrier(0);
-    dequant(r0, 0);
-    if (main_steps > 1) wait_vmcnt<NX>();
-    else wait_vmcnt<0>();
-    producer_barrier();
-
-    auto body = [&](int s, WStage& nxt_load, const WStage& deq) {
-      load_w(min(s + 3, last), nxt_load);
-      __builtin_amdgcn_sched_barrier(0);
-      const bool more_x = s + 2 < main_steps;
-      if (more_x) issue_x(s + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      dequant(deq, s + 1);
-      if (more_x) wait_vmcnt<3 + NX>();
-      else wait_vmcnt<0>();
-      producer_barrier();
-    };
-    int s = 0;
-    for (; s + 3 <= last; s += 3) {
-      body(s, r0, r1);
-      body(s + 1, r1, r2);
-      body(s + 2, r2, r0);
+    lds_barrier();
+    for (int q = 0; q <= steps; ++q) {
+      if (q < main_steps) dequant(q);
+      else if (q < steps) store_lora(q);
+      lds_barrier();
     }
-    if (s < last) body(s, r0, r1);
-    if (s + 1 < last) body(s + 1, r1, r2);
-    for (int t = main_steps; t < steps; ++t) {   // adapter steps are written during step t - 1
-      wait_vmcnt<0>();
-      store_lora(t);
-      producer_barrier();
-    }
-    producer_barrier();   // the barrier that ends the consumers' final step
     return;
   }
 
@@ -376,10 +399,11 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
     }
   };
 
-  __syncthreads();
-  for (int s = 0; s < steps; ++s) {
+  lds_barrier();   // step 0's loads have landed
+  lds_barrier();   // phase 0: step 0's W tile is built
+  for (int s = 0; s < steps; ++s) {   // phase s + 1
     compute(s);
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---------------------------------------------------------------- epilogue
