@@ -28,18 +28,17 @@ int from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Workspace layout (bytes, each region 256-aligned):
-//   forward : [u (M*r fp32)] [partials: skinny splits or adapter down-projection chunks]
-//   backward: [v (M*r fp32)] [partials of v, then of dA, then of dB (the kernels run in order)]
+//   forward : [u (M*r fp32)] [partials: skinny splits or the adapter pass over X]
+//   backward: [v (M*r fp32)] [partials of the pass over dY, then of the pass over X]
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
   size_t part = nf4::skinny_eligible(M) ? nf4::skinny_workspace_floats(M, N, K, r)
-                                        : (size_t)nf4::lora_down_chunks(M, K) * M * r;
+                                        : nf4::lora_pass_ws_floats(M, K, r, true, false);
   return align_up((size_t)M * r * 4) + align_up(part * 4);
 }
 size_t bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
-  size_t part = (size_t)nf4::lora_down_chunks(M, N) * M * r;
-  const size_t ga = nf4::lora_grad_workspace_floats(M, K, r), gb = nf4::lora_grad_workspace_floats(M, N, r);
+  size_t part = nf4::lora_pass_ws_floats(M, N, r, true, true);
+  const size_t ga = nf4::lora_pass_ws_floats(M, K, r, false, true);
   if (ga > part) part = ga;
-  if (gb > part) part = gb;
   return align_up((size_t)M * r * 4) + align_up(part * 4);
 }
 
@@ -121,7 +120,7 @@ int qlora_linear_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const ui
     return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, N, K, x, M, A, B, r,
                                            scale, part, u, y, stream));
   }
-  hipError_t e = nf4::launch_lora_down(x, M, K, A, false, r, part, u, stream);
+  hipError_t e = nf4::launch_lora_u(x, M, K, A, r, part, u, stream);
   if (e != hipSuccess) return NF4_ERR_HIP;
   return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, N, K, x, M, u, B, r, scale,
                                        y, stream));
@@ -171,15 +170,13 @@ int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy,
   if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;
   float* v = static_cast<float*>(ws);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
-  hipError_t e = nf4::launch_lora_down(dy, M, N, B, true, r, part, v, stream);
+  hipError_t e = nf4::launch_lora_dy(dy, M, N, B, u, r, scale, accumulate, part, v, dB, stream);
   if (e != hipSuccess) return NF4_ERR_HIP;
   if (dx) {
     e = nf4::launch_dx_gemm(W->packed, W->scale_q, W->scale_c2, N, K, dy, M, v, A, r, scale, dx, stream);
     if (e != hipSuccess) return NF4_ERR_HIP;
   }
-  e = nf4::launch_lora_grad(v, x, M, K, r, scale, dA, false, accumulate, part, stream);
-  if (e != hipSuccess) return NF4_ERR_HIP;
-  return from_hip(nf4::launch_lora_grad(u, dy, M, N, r, scale, dB, true, accumulate, part, stream));
+  return from_hip(nf4::launch_lora_dx(x, M, K, v, r, scale, accumulate, part, dA, stream));
 }
 
 }  // extern "C"

@@ -20,15 +20,26 @@ hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const f
                           int64_t N, int64_t K, const uint16_t* dy, int64_t M, const float* v,
                           const uint16_t* A, int r, float scale, uint16_t* dx, hipStream_t stream);
 
-// u = P Q^T-like down projections (see lora.hip); `part` holds lora_down_chunks(M, L) * M * r floats.
-int lora_down_chunks(int64_t M, int64_t L);
-hipError_t launch_lora_down(const uint16_t* P, int64_t M, int64_t L, const uint16_t* Q, bool q_is_lr,
-                            int r, float* part, float* out, hipStream_t stream);
-// Adapter gradient out = scale * Q^T P (fp32); `part` holds lora_grad_workspace_floats(M, C, r) floats.
-size_t lora_grad_workspace_floats(int64_t M, int64_t C, int r);
-hipError_t launch_lora_grad(const float* P, const uint16_t* Q, int64_t M, int64_t C, int r,
-                            float scale, float* out, bool out_cr, int accumulate, float* part,
-                            hipStream_t stream);
+// Adapter passes over one bf16 matrix (see lora.hip). Each writes partial results to `ws`
+// (lora_pass_ws_floats floats) and reduces them in a fixed order.
+struct LoraPassPlan {
+  int mb;           // rows per block
+  int mblocks;      // row blocks
+  int64_t crange;   // columns per column range
+  int cranges;      // column ranges
+};
+LoraPassPlan lora_pass_plan(int64_t M, int64_t C, int r);
+size_t lora_pass_ws_floats(int64_t M, int64_t C, int r, bool down, bool grad);
+// u = X A^T
+hipError_t launch_lora_u(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int r,
+                         float* ws, float* u, hipStream_t stream);
+// v = dY B and dB = scale * dY^T u (+ dB if accumulate), in one pass over dY
+hipError_t launch_lora_dy(const uint16_t* dY, int64_t M, int64_t N, const uint16_t* B, const float* u,
+                          int r, float scale, int accumulate, float* ws, float* v, float* dB,
+                          hipStream_t stream);
+// dA = scale * v^T X (+ dA if accumulate)
+hipError_t launch_lora_dx(const uint16_t* X, int64_t M, int64_t K, const float* v, int r, float scale,
+                          int accumulate, float* ws, float* dA, hipStream_t stream);
 
 // Skinny forward (M <= 16): split-K dequant-GEMV on MFMA with a deterministic reduction.
 // `part` holds skinny_workspace_floats(M, N, K, r) floats; u_out receives u = x A^T [M x r].

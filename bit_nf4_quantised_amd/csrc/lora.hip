@@ -6,13 +6,38 @@
 //   u  = X A^T   [M x r]   (forward; saved for the backward)
 //   v  = dY B    [M x r]   (backward)
 //   dA = s v^T X [r x K]   and   dB = s dY^T u [N x r]     (fp32, optionally accumulated)
-// All reductions run in a fixed order (no atomics), so results are bitwise reproducible.
+//
+// All four are passes over one bf16 matrix Q [M x C] (X or dY) that the pass reads once:
+//   down:  Dn[m][j] = sum_c Q[m][c] R(c, j)    R(c, j) = A[j][c] (A is r x C) or B[c][j] (B is C x r)
+//   grad:  Gr[c][j] = sum_m Q[m][c] P[m][j]    P = u or v, fp32, as a bf16 hi + lo pair
+// The backward's pass over dY does both at once (v and dB), so dY is read once for the adapter.
+// A workgroup takes 256 (or, above rank 32, 128) rows and a range of columns, streaming 64-column
+// steps of Q through LDS with LDS-DMA loads; the down products accumulate over its columns, the
+// grad products of each step are complete for its rows. Partial results go to a workspace and
+// lora_reduce_kernel sums them in a fixed order, so results are bitwise reproducible.
 #include "common.h"
 #include "launch.h"
 
 namespace nf4 {
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kStepC = 64;                     // Q columns per step
+constexpr int kLoraRsrcFlags = 0x00020000;     // raw buffer, 32-bit data format
+constexpr uint32_t kLoraOutOfRange = 0x80000000u;
+
+template <int N>
+__device__ __forceinline__ void lora_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier after the wave's LDS accesses complete, as raw s_barrier: the compiler would
+// otherwise wait for every LDS-DMA load in flight, including those for later steps.
+__device__ __forceinline__ void lora_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // 16-lane transpose read of an LDS tile stored [contraction][column] with pitch `pitch`:
 // returns, for lane (j = lane % 16, grp = lane / 16), the 8 contraction values
@@ -25,297 +50,363 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int pitch, int c
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// ------------------------------------------------------------------------------------------
-// Partial down-projection: part[c][m][j] = sum over l in chunk c of P[m][l] * Q(j, l), where
-// Q(j, l) = A[j][l] (A is r x L, QT = false) or B[l][j] (B is L x r, QT = true).
-// Workgroup: 64 activation rows (16 per wave) x one contraction chunk.
-template <bool QT>
-__global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restrict__ P, int64_t M,
-                                                        int64_t L, const uint16_t* __restrict__ Q,
-                                                        int r, int64_t chunk_len,
-                                                        float* __restrict__ part) {
-  constexpr int QP = 128 + 8;  // staged Q rows hold up to 128 rank columns
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[4][32][QP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m = (int64_t)blockIdx.x * 64 + wave * 16 + (lane & 15);
-  const int chunk = blockIdx.y;
-  const int64_t l_begin = (int64_t)chunk * chunk_len;
-  const int64_t l_end = min(L, l_begin + chunk_len);
-  const int RT = r / 16;
-  f32x4 acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+// Q tiles in LDS: rows of 64 bf16 (128 bytes); the 16-byte chunk c of row m sits at slot
+// c ^ ((m >> 1) & 7), so 16-lane groups reading one chunk of 16 consecutive rows hit distinct banks.
+__device__ __forceinline__ int q_elem(int m, int c) {
+  return m * kStepC + ((((c >> 3) ^ ((m >> 1) & 7)) << 3) | (c & 7));
+}
 
-  for (int64_t l0 = l_begin; l0 < l_end; l0 += 32) {
-    const int64_t l = l0 + 8 * (lane >> 4);
-    bf16x8 b = {};
-    if (m < M && l < l_end) b = *reinterpret_cast<const bf16x8*>(P + m * L + l);
-    if (QT) {
-      // stage B rows l0 .. l0+31 (r columns each) for this wave
-      const int cols8 = r / 8;
-      for (int q = lane; q < 32 * cols8; q += 64) {
-        const int row = q / cols8, c8 = (q % cols8) * 8;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (l0 + row < l_end) v = *reinterpret_cast<const u32x4*>(Q + (l0 + row) * r + c8);
-        *reinterpret_cast<u32x4*>(&Qs[wave][row][c8]) = v;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+// transpose read of the swizzled Q tile: lane (j, grp) receives rows m0 + 8*grp .. +7 of column
+// c0 + j (c0 a multiple of 16)
+__device__ __forceinline__ bf16x8 q_tr_frag(const uint16_t* tile, int m0, int c0, int lane) {
+  const int j = lane & 15, grp = lane >> 4;
+  const int m = m0 + 8 * grp + (j >> 2), c = c0 + 4 * (j & 3);
+  bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + q_elem(m, c)));
+  bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + q_elem(m + 4, c)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+struct LoraPassArgs {
+  const uint16_t* Q;        // [M x C] bf16
+  int64_t M, C;
+  const uint16_t* R;        // down operand: A [r x C] (RT = false) or B [C x r] (RT = true)
+  const float* P;           // grad operand [M x r] fp32
+  int r;
+  int64_t crange;           // columns per workgroup column range (a multiple of kStepC)
+  float* part_down;         // [column ranges][M][r]
+  float* part_grad;         // [row blocks][C][r]
+};
+
+// R16: the rank is exactly 16 (the common case): the grad operand fragments stay in registers.
+template <int MB, bool DOWN, bool GRAD, bool RT, bool R16>
+__global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
+  constexpr int QS = MB == 256 ? 3 : 2;                 // Q stages in LDS
+  constexpr int NQ = MB / 32;                           // Q DMA loads per wave per step
+  constexpr int RMAX = MB == 256 ? 32 : 128;            // largest rank handled
+  constexpr int RTILE = DOWN ? kStepC * RMAX : 8;       // R tile elements per stage
+  constexpr int PP = (GRAD ? RMAX : 0) + 8;             // pitch of the P tiles
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[QS][MB * kStepC];
+  __shared__ __attribute__((aligned(16))) uint16_t Rs[QS][RTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ph[GRAD ? MB : 1][PP];
+  __shared__ __attribute__((aligned(16))) uint16_t Pl[GRAD ? MB : 1][PP];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = R16 ? 16 : a.r, RT16 = r / 16;
+  const int64_t m0 = (int64_t)blockIdx.x * MB;
+  const int64_t rows_valid = min(a.M - m0, (int64_t)MB);
+  const int64_t c_begin = (int64_t)blockIdx.y * a.crange;
+  const int64_t c_end = min(a.C, c_begin + a.crange);
+  const int nsteps = (int)((c_end - c_begin + kStepC - 1) / kStepC);
+
+  // ---- DMA of one step: Q rows m0.., columns c0 .. c0+63 (swizzled), then the R tile
+  const int rdma = (r + 31) / 32;   // R loads per wave per step (waves past the tile repeat one)
+  auto issue = [&](int t) {
+    const int64_t c0 = c_begin + (int64_t)t * kStepC;
+    const int st = t % QS;
+    const int valid_chunks = (int)min((int64_t)8, (a.C - c0 + 7) / 8);
+    {
+      const uint16_t* base = a.Q + m0 * a.C + c0;
+      const int nrec = (int)(rows_valid * a.C * 2 - c0 * 2);
+      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kLoraRsrcFlags);
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      if (jt < RT) {
-        bf16x8 a;
-        if (QT) {
-          a = tr_frag(&Qs[wave][0][0], QP, jt * 16, lane);
+      for (int j = 0; j < NQ; ++j) {
+        const int slot = (wave * NQ + j) * 64 + lane;
+        const int row = slot >> 3, c = (slot & 7) ^ ((row >> 1) & 7);
+        const uint32_t off = c < valid_chunks ? (uint32_t)row * (uint32_t)(a.C * 2) + (uint32_t)c * 16u : kLoraOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&Qs[st][(wave * NQ + j) * 64 * 8]), 16, off, 0, 0, 0);
+      }
+    }
+    if (DOWN) {
+      // R tile of the step: RT = false, rows j < r of A, columns c0 .. c0+63, swizzled like Q;
+      // RT = true, rows c0 .. c0+63 of B (r columns each), contiguous. Either is r/8 loads of
+      // 64 lanes x 16 bytes; load i goes to wave i % 4.
+      for (int k = 0; k < rdma; ++k) {
+        int i = wave + 4 * k;
+        if (i >= r / 8) i = (r / 8) - 1 - ((i - r / 8) % (r / 8));   // repeat an existing load
+        const int slot = i * 64 + lane;
+        uint32_t off;
+        __amdgpu_buffer_rsrc_t rs;
+        if (RT) {
+          rs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.R + c0 * r), (short)0,
+                                                 (int)((a.C - c0) * r * 2), kLoraRsrcFlags);
+          off = (uint32_t)slot * 16u;
         } else {
-          a = bf16x8{};
-          if (l < l_end) a = *reinterpret_cast<const bf16x8*>(Q + (int64_t)(jt * 16 + (lane & 15)) * L + l);
+          rs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.R + c0), (short)0,
+                                                 (int)(r * a.C * 2 - c0 * 2), kLoraRsrcFlags);
+          const int row = slot >> 3, c = (slot & 7) ^ ((row >> 1) & 7);
+          off = c < valid_chunks ? (uint32_t)row * (uint32_t)(a.C * 2) + (uint32_t)c * 16u : kLoraOutOfRange;
         }
-        acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[jt], 0, 0, 0);
-      }
-    }
-    if (QT) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-  }
-  if (m < M) {
-#pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      if (jt < RT) {
-        const int j = jt * 16 + 4 * (lane >> 4);
-        *reinterpret_cast<f32x4*>(part + ((int64_t)chunk * M + m) * r + j) = acc[jt];
-      }
-    }
-  }
-}
-
-// out[m][j] = sum over chunks, in chunk order.
-__global__ __launch_bounds__(256) void lora_down_reduce_kernel(const float* __restrict__ part,
-                                                               int nchunks, int64_t count,
-                                                               float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= count) return;
-  float s = 0.f;
-  for (int c = 0; c < nchunks; ++c) s += part[(int64_t)c * count + i];
-  out[i] = s;
-}
-
-// ------------------------------------------------------------------------------------------
-// Adapter gradients: D[c][j] = sum_m Q[m][c] * P[m][j] with P fp32 [M x r] split into bf16
-// hi + lo parts (P - hi rounded again), Q bf16 [M x C].
-//   OUT_CR = false: out is [r x C] (dA = s v^T X: P = v, Q = X)
-//   OUT_CR = true:  out is [C x r] (dB = s dY^T u: P = u, Q = dY)
-// Workgroup (blockIdx.x, blockIdx.y) = (64 columns c, one slice of M). Its four waves take
-// interleaved 32-row slices of that range, prefetching the next slice into registers while the
-// current one is multiplied; the waves are summed in wave order into part[slice][c][j], and
-// lora_grad_reduce_kernel sums the slices in order, scales and writes (or accumulates) the output.
-template <bool OUT_CR>
-__global__ __launch_bounds__(256) void lora_grad_kernel(const float* __restrict__ P,
-                                                        const uint16_t* __restrict__ Q, int64_t M,
-                                                        int64_t C, int r, int64_t m_per_slice,
-                                                        float* __restrict__ part) {
-  constexpr int QP = 64 + 8, PP = 128 + 8, RP = 128 + 1;
-  constexpr int kStage = 4 * 32 * QP * 2 + 2 * 4 * 32 * PP * 2;
-  constexpr int kRed = 4 * 64 * RP * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kStage > kRed ? kStage : kRed];
-  auto Qs = reinterpret_cast<uint16_t(*)[32][QP]>(smem);
-  auto Ph = reinterpret_cast<uint16_t(*)[32][PP]>(smem + 4 * 32 * QP * 2);
-  auto Pl = reinterpret_cast<uint16_t(*)[32][PP]>(smem + 4 * 32 * QP * 2 + 4 * 32 * PP * 2);
-  auto Red = reinterpret_cast<float(*)[64][RP]>(smem);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t c0 = (int64_t)blockIdx.x * 64;
-  const int64_t m_begin = (int64_t)blockIdx.y * m_per_slice;
-  const int64_t m_end = min(M, m_begin + m_per_slice);
-  const int RT = r / 16;
-  const int cols4 = r / 4;             // float4 chunks per P row
-  const int pchunks = 32 * cols4 / 64; // float4 chunks of a 32-row P slice per lane (2 .. 16)
-  f32x4 acc[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 qreg[4];
-  f32x4 preg[16];
-  auto load = [&](int64_t mb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = lane + 64 * i;
-      const int row = q >> 3, c8 = (q & 7) * 8;
-      qreg[i] = (mb + row < m_end && c0 + c8 < C)
-                    ? *reinterpret_cast<const u32x4*>(Q + (mb + row) * C + c0 + c8)
-                    : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < pchunks) {
-        const int q = lane + 64 * i;
-        const int row = q / cols4, c4 = (q % cols4) * 4;
-        preg[i] = (mb + row < m_end) ? *reinterpret_cast<const f32x4*>(P + (mb + row) * r + c4)
-                                     : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = lane + 64 * i;
-      *reinterpret_cast<u32x4*>(&Qs[wave][q >> 3][(q & 7) * 8]) = qreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < pchunks) {
-        const int q = lane + 64 * i;
-        const int row = q / cols4, c4 = (q % cols4) * 4;
-        const f32x4 v = preg[i];
-        const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
-        const uint32_t l01 = pack_bf16x2(v[0] - __uint_as_float(h01 << 16),
-                                         v[1] - __uint_as_float(h01 & 0xFFFF0000u));
-        const uint32_t l23 = pack_bf16x2(v[2] - __uint_as_float(h23 << 16),
-                                         v[3] - __uint_as_float(h23 & 0xFFFF0000u));
-        *reinterpret_cast<u32x2*>(&Ph[wave][row][c4]) = u32x2{h01, h23};
-        *reinterpret_cast<u32x2*>(&Pl[wave][row][c4]) = u32x2{l01, l23};
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&Rs[st][i * 64 * 8]), 16, off, 0, 0, 0);
       }
     }
   };
 
-  // uniform trip count across waves: every wave runs `rounds` rounds (empty slices are zeros)
-  const int64_t rows = m_end > m_begin ? m_end - m_begin : 0;
-  const int64_t rounds = (rows + 127) / 128;
-  if (rounds > 0) load(m_begin + wave * 32);
-  for (int64_t rd = 0; rd < rounds; ++rd) {
-    stage();
-    if (rd + 1 < rounds) load(m_begin + ((rd + 1) * 4 + wave) * 32);
+  // ---- P rows of the block as bf16 hi + lo (grad)
+  if (GRAD) {
+    const int cols4 = r / 4;
+    for (int q = tid; q < MB * cols4; q += 256) {
+      const int row = q / cols4, c4 = (q % cols4) * 4;
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (row < rows_valid) v = *reinterpret_cast<const f32x4*>(a.P + (m0 + row) * r + c4);
+      const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+      const uint32_t l01 = pack_bf16x2(v[0] - __uint_as_float(h01 << 16), v[1] - __uint_as_float(h01 & 0xFFFF0000u));
+      const uint32_t l23 = pack_bf16x2(v[2] - __uint_as_float(h23 << 16), v[3] - __uint_as_float(h23 & 0xFFFF0000u));
+      *reinterpret_cast<u32x2*>(&Ph[row][c4]) = u32x2{h01, h23};
+      *reinterpret_cast<u32x2*>(&Pl[row][c4]) = u32x2{l01, l23};
+    }
+  }
+
+  // rank 16: every step multiplies by the same P fragments; read them once
+  bf16x8 pfr[R16 && GRAD ? MB / 32 : 1][2];
+  if (R16 && GRAD) {
     __syncthreads();
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const bf16x8 qf = tr_frag(&Qs[wave][0][0], QP, ct * 16, lane);
+    for (int kk = 0; kk < MB / 32; ++kk) {
+      pfr[kk][0] = tr_frag(&Ph[kk * 32][0], PP, 0, lane);
+      pfr[kk][1] = tr_frag(&Pl[kk * 32][0], PP, 0, lane);
+    }
+  }
+
+  // ---- accumulators. down: wave owns rows wave * MB/4 ..; grad: wave owns columns 16 wave .. of
+  // each step.
+  constexpr int MT = MB / 64;   // 16-row tiles of a wave (down)
+  f32x4 dacc[DOWN ? MT : 1][RMAX / 16];
+  f32x4 gacc[RMAX / 16];
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt) {
-        if (rt < RT) {
-          const bf16x8 ph = tr_frag(&Ph[wave][0][0], PP, rt * 16, lane);
-          const bf16x8 pl = tr_frag(&Pl[wave][0][0], PP, rt * 16, lane);
-          if (OUT_CR) {
-            acc[ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, qf, acc[ct][rt], 0, 0, 0);
-            acc[ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, qf, acc[ct][rt], 0, 0, 0);
-          } else {
-            acc[ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, ph, acc[ct][rt], 0, 0, 0);
-            acc[ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, pl, acc[ct][rt], 0, 0, 0);
+  for (int i = 0; i < (DOWN ? MT : 1); ++i)
+#pragma unroll
+    for (int j = 0; j < RMAX / 16; ++j) dacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int t) {
+    const int st = t % QS;
+    const uint16_t* qs = &Qs[st][0];
+    const int64_t c0 = c_begin + (int64_t)t * kStepC;
+    if (DOWN) {
+      // D lane l: column m = l % 16 of the row tile, rows j = jt*16 + 4 (l / 16) .. +3
+#pragma unroll
+      for (int kk = 0; kk < kStepC / 32; ++kk) {
+        bf16x8 bq[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = wave * (MB / 4) + mt * 16 + (lane & 15);
+          bq[mt] = *reinterpret_cast<const bf16x8*>(qs + q_elem(m, kk * 32 + 8 * (lane >> 4)));
+        }
+#pragma unroll
+        for (int jt = 0; jt < RMAX / 16; ++jt) {
+          if (jt < RT16) {
+            bf16x8 ar;
+            if (RT) {
+              ar = tr_frag(&Rs[st][kk * 32 * r], r, jt * 16, lane);
+            } else {
+              const int j = jt * 16 + (lane & 15);
+              ar = *reinterpret_cast<const bf16x8*>(&Rs[st][q_elem(j, kk * 32 + 8 * (lane >> 4))]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              dacc[mt][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, bq[mt], dacc[mt][jt], 0, 0, 0);
           }
         }
       }
     }
-    __syncthreads();
-  }
-  // acc[ct][rt][i]: OUT_CR = false: c = ct*16 + 4*(lane/16) + i, j = rt*16 + lane%16
-  //                 OUT_CR = true:  j = rt*16 + 4*(lane/16) + i, c = ct*16 + lane%16
+    if (GRAD) {
+      // D lane l: column c = 16 wave + l % 16 of the step, rows j = jt*16 + 4 (l / 16) .. +3
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+      for (int j = 0; j < RMAX / 16; ++j) gacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-      if (rt < RT)
+      for (int kk = 0; kk < MB / 32; ++kk) {
+        const bf16x8 bq = q_tr_frag(qs, kk * 32, wave * 16, lane);
+        if (R16) {
+          gacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pfr[kk][0], bq, gacc[0], 0, 0, 0);
+          gacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pfr[kk][1], bq, gacc[0], 0, 0, 0);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          int c, j;
-          if (OUT_CR) { j = rt * 16 + 4 * (lane >> 4) + i; c = ct * 16 + (lane & 15); }
-          else        { c = ct * 16 + 4 * (lane >> 4) + i; j = rt * 16 + (lane & 15); }
-          Red[wave][c][j] = acc[ct][rt][i];
+          for (int jt = 0; jt < RMAX / 16; ++jt) {
+            if (jt < RT16) {
+              const bf16x8 ph = tr_frag(&Ph[kk * 32][0], PP, jt * 16, lane);
+              const bf16x8 pl = tr_frag(&Pl[kk * 32][0], PP, jt * 16, lane);
+              gacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bq, gacc[jt], 0, 0, 0);
+              gacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bq, gacc[jt], 0, 0, 0);
+            }
+          }
         }
-  __syncthreads();
-  // part[slice][c][j] for the 64 columns of this workgroup
-  float* dst = part + (int64_t)blockIdx.y * C * r;
-  for (int idx = tid; idx < 64 * r; idx += 256) {
-    const int c = idx / r, j = idx % r;
-    const int64_t cc = c0 + c;
-    if (cc < C) dst[cc * r + j] = ((Red[0][c][j] + Red[1][c][j]) + Red[2][c][j]) + Red[3][c][j];
+      }
+      const int64_t c = c0 + wave * 16 + (lane & 15);
+      if (c < a.C) {
+        float* dst = a.part_grad + ((int64_t)blockIdx.x * a.C + c) * r + 4 * (lane >> 4);
+#pragma unroll
+        for (int jt = 0; jt < RMAX / 16; ++jt)
+          if (jt < RT16) *reinterpret_cast<f32x4*>(dst + jt * 16) = gacc[jt];
+      }
+    }
+  };
+
+  // ---- pipeline: QS-1 steps in flight. Step t: start the DMA of step t+QS-1, wait until step
+  // t's loads have landed (later steps' loads may stay in flight: vector-memory loads complete in
+  // issue order), barrier, compute, barrier (the stage is refilled next).
+  const int per_step = NQ + (DOWN ? rdma : 0);
+  for (int t = 0; t < QS - 1 && t < nsteps; ++t) issue(t);
+  for (int t = 0; t < nsteps; ++t) {
+    if (t + QS - 1 < nsteps) {
+      issue(t + QS - 1);
+      // allowance: the loads of steps t+1 .. t+QS-1
+      if (QS == 3) {
+        if (per_step == NQ) lora_wait_vmcnt<2 * NQ>();
+        else if (per_step == NQ + 1) lora_wait_vmcnt<2 * (NQ + 1)>();
+        else if (per_step == NQ + 2) lora_wait_vmcnt<2 * (NQ + 2)>();
+        else lora_wait_vmcnt<0>();
+      } else {
+        if (per_step == NQ) lora_wait_vmcnt<NQ>();
+        else if (per_step == NQ + 1) lora_wait_vmcnt<NQ + 1>();
+        else if (per_step == NQ + 2) lora_wait_vmcnt<NQ + 2>();
+        else if (per_step == NQ + 3) lora_wait_vmcnt<NQ + 3>();
+        else if (per_step == NQ + 4) lora_wait_vmcnt<NQ + 4>();
+        else lora_wait_vmcnt<0>();
+      }
+    } else {
+      lora_wait_vmcnt<0>();
+    }
+    lora_barrier();
+    compute(t);
+    lora_barrier();
+  }
+
+  if (DOWN) {
+    float* dst = a.part_down + (int64_t)blockIdx.y * a.M * r;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int64_t m = m0 + wave * (MB / 4) + mt * 16 + (lane & 15);
+      if (m < a.M) {
+#pragma unroll
+        for (int jt = 0; jt < RMAX / 16; ++jt)
+          if (jt < RT16) *reinterpret_cast<f32x4*>(dst + m * r + jt * 16 + 4 * (lane >> 4)) = dacc[mt][jt];
+      }
+    }
   }
 }
 
-// out = scale * sum over slices (in slice order) [+ out]; out is [C x r] (OUT_CR) or [r x C].
-__global__ __launch_bounds__(256) void lora_grad_reduce_kernel(const float* __restrict__ part,
-                                                               int slices, int64_t C, int r,
-                                                               float scale, int out_cr,
-                                                               float* __restrict__ out,
-                                                               int accumulate) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = C * r;
-  if (idx >= total) return;
-  // idx walks the output in memory order
-  int64_t c, j;
-  if (out_cr) { c = idx / r; j = idx % r; }
-  else        { j = idx / C; c = idx % C; }
-  float v = 0.f;
-  for (int sl = 0; sl < slices; ++sl) v += part[(int64_t)sl * total + c * r + j];
-  v *= scale;
-  out[idx] = accumulate ? out[idx] + v : v;
+// Ordered sums of partial results. A job: out[i] = scale * (sum over p < nparts, in order, of
+// part[p * count + i]) (+ out[i]); with `transpose`, part is [C][r] and out is [r][C]. One launch
+// serves two jobs (blocks [0, blocks0) take job 0). Threads take 4 consecutive outputs and issue
+// the loads of 8 partials at a time before adding them in order.
+struct ReduceJob {
+  const float* part;
+  int nparts;
+  int64_t count, C;
+  int r, transpose, accumulate;
+  float scale;
+  float* out;
+};
+
+__global__ __launch_bounds__(256) void lora_reduce_kernel(const ReduceJob j0, const ReduceJob j1, int blocks0) {
+  const bool second = (int)blockIdx.x >= blocks0;
+  const ReduceJob& jb = second ? j1 : j0;
+  const int64_t i4 = ((int64_t)(second ? blockIdx.x - blocks0 : blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i4 >= jb.count) return;
+  int64_t src[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t i = min(i4 + e, jb.count - 1);
+    src[e] = jb.transpose ? (i % jb.C) * jb.r + i / jb.C : i;
+  }
+  const bool vec = !jb.transpose && i4 + 4 <= jb.count;
+  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < jb.nparts; p0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int p = min(p0 + q, jb.nparts - 1);
+      const float* base = jb.part + (int64_t)p * jb.count;
+      if (vec) v[q] = *reinterpret_cast<const f32x4*>(base + i4);
+      else v[q] = f32x4{base[src[0]], base[src[1]], base[src[2]], base[src[3]]};
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (p0 + q < jb.nparts) s += v[q];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t i = i4 + e;
+    if (i < jb.count) {
+      const float x = s[e] * jb.scale;
+      jb.out[i] = jb.accumulate ? jb.out[i] + x : x;
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
-// Contraction chunking of the down-projection: about 512 workgroups, chunks of whole 32-column
-// steps, at least 256 columns each. Returns the chunk count and sets the chunk length.
-static int lora_down_plan(int64_t M, int64_t L, int64_t* chunk_len) {
-  const int64_t mtiles = (M + 63) / 64;
-  int64_t want = (512 + mtiles - 1) / mtiles;
-  const int64_t maxc = (L + 255) / 256;
-  if (want > maxc) want = maxc;
+// Work split of a pass: row blocks of 256 (128 above rank 32) and column ranges of whole steps,
+// about 256 workgroups in all with at least 4 steps per workgroup where the matrix allows it.
+LoraPassPlan lora_pass_plan(int64_t M, int64_t C, int r) {
+  LoraPassPlan p;
+  p.mb = r > 32 ? 128 : 256;
+  p.mblocks = (int)((M + p.mb - 1) / p.mb);
+  const int64_t steps = (C + kStepC - 1) / kStepC;
+  int64_t want = (256 + p.mblocks - 1) / p.mblocks;
+  if (want > (steps + 3) / 4) want = (steps + 3) / 4;
   if (want < 1) want = 1;
-  *chunk_len = ((L + want - 1) / want + 31) / 32 * 32;
-  return (int)((L + *chunk_len - 1) / *chunk_len);
+  const int64_t steps_per = (steps + want - 1) / want;
+  p.crange = steps_per * kStepC;
+  p.cranges = (int)((C + p.crange - 1) / p.crange);
+  return p;
 }
 
-int lora_down_chunks(int64_t M, int64_t L) {
-  int64_t len;
-  return lora_down_plan(M, L, &len);
+size_t lora_pass_ws_floats(int64_t M, int64_t C, int r, bool down, bool grad) {
+  const LoraPassPlan p = lora_pass_plan(M, C, r);
+  return (down ? (size_t)p.cranges * M * r : 0) + (grad ? (size_t)p.mblocks * C * r : 0);
 }
 
-hipError_t launch_lora_down(const uint16_t* P, int64_t M, int64_t L, const uint16_t* Q, bool q_is_lr,
-                            int r, float* part, float* out, hipStream_t stream) {
-  int64_t chunk_len;
-  const int nchunks = lora_down_plan(M, L, &chunk_len);
-  dim3 grid((unsigned)((M + 63) / 64), (unsigned)nchunks);
-  if (q_is_lr)
-    hipLaunchKernelGGL((lora_down_kernel<true>), grid, dim3(256), 0, stream, P, M, L, Q, r, chunk_len, part);
+template <bool DOWN, bool GRAD, bool RT>
+static void launch_pass(const LoraPassPlan& p, const LoraPassArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)p.mblocks, (unsigned)p.cranges);
+  if (p.mb == 256 && a.r == 16)
+    hipLaunchKernelGGL((lora_pass_kernel<256, DOWN, GRAD, RT, true>), grid, dim3(256), 0, stream, a);
+  else if (p.mb == 256)
+    hipLaunchKernelGGL((lora_pass_kernel<256, DOWN, GRAD, RT, false>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((lora_down_kernel<false>), grid, dim3(256), 0, stream, P, M, L, Q, r, chunk_len, part);
-  const int64_t count = M * r;
-  hipLaunchKernelGGL(lora_down_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
-                     stream, part, nchunks, count, out);
+    hipLaunchKernelGGL((lora_pass_kernel<128, DOWN, GRAD, RT, false>), grid, dim3(256), 0, stream, a);
+}
+
+static ReduceJob reduce_job(const float* part, int nparts, int64_t count, int64_t C, int r, bool transpose,
+                            float scale, int accumulate, float* out) {
+  return ReduceJob{part, nparts, count, C, r, transpose ? 1 : 0, accumulate, scale, out};
+}
+
+static void launch_reduce(const ReduceJob& j0, const ReduceJob* j1, hipStream_t stream) {
+  const int b0 = (int)((j0.count + 1023) / 1024);
+  const int b1 = j1 ? (int)((j1->count + 1023) / 1024) : 0;
+  hipLaunchKernelGGL(lora_reduce_kernel, dim3((unsigned)(b0 + b1)), dim3(256), 0, stream, j0, j1 ? *j1 : j0, b0);
+}
+
+hipError_t launch_lora_u(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int r,
+                         float* ws, float* u, hipStream_t stream) {
+  const LoraPassPlan p = lora_pass_plan(M, K, r);
+  LoraPassArgs a{X, M, K, A, nullptr, r, p.crange, ws, nullptr};
+  launch_pass<true, false, false>(p, a, stream);
+  launch_reduce(reduce_job(ws, p.cranges, M * r, 0, r, false, 1.f, 0, u), nullptr, stream);
   return hipGetLastError();
 }
 
-// Token slices of the gradient kernels: about 512 workgroups, slices of whole 128-row rounds.
-static int lora_grad_plan(int64_t M, int64_t C, int64_t* m_per_slice) {
-  const int64_t ctiles = (C + 63) / 64;
-  int64_t want = (512 + ctiles - 1) / ctiles;
-  const int64_t maxs = (M + 127) / 128;
-  if (want > maxs) want = maxs;
-  if (want < 1) want = 1;
-  *m_per_slice = ((M + want - 1) / want + 127) / 128 * 128;
-  return (int)((M + *m_per_slice - 1) / *m_per_slice);
+hipError_t launch_lora_dy(const uint16_t* dY, int64_t M, int64_t N, const uint16_t* B, const float* u,
+                          int r, float scale, int accumulate, float* ws, float* v, float* dB,
+                          hipStream_t stream) {
+  const LoraPassPlan p = lora_pass_plan(M, N, r);
+  float* part_down = ws;
+  float* part_grad = ws + (size_t)p.cranges * M * r;
+  LoraPassArgs a{dY, M, N, B, u, r, p.crange, part_down, part_grad};
+  launch_pass<true, true, true>(p, a, stream);
+  const ReduceJob jv = reduce_job(part_down, p.cranges, M * r, 0, r, false, 1.f, 0, v);
+  const ReduceJob jb = reduce_job(part_grad, p.mblocks, N * r, 0, r, false, scale, accumulate, dB);
+  launch_reduce(jv, &jb, stream);
+  return hipGetLastError();
 }
 
-size_t lora_grad_workspace_floats(int64_t M, int64_t C, int r) {
-  int64_t mps;
-  return (size_t)lora_grad_plan(M, C, &mps) * (size_t)C * (size_t)r;
-}
-
-hipError_t launch_lora_grad(const float* P, const uint16_t* Q, int64_t M, int64_t C, int r,
-                            float scale, float* out, bool out_cr, int accumulate, float* part,
-                            hipStream_t stream) {
-  int64_t mps;
-  const int slices = lora_grad_plan(M, C, &mps);
-  dim3 grid((unsigned)((C + 63) / 64), (unsigned)slices);
-  if (out_cr)
-    hipLaunchKernelGGL((lora_grad_kernel<true>), grid, dim3(256), 0, stream, P, Q, M, C, r, mps, part);
-  else
-    hipLaunchKernelGGL((lora_grad_kernel<false>), grid, dim3(256), 0, stream, P, Q, M, C, r, mps, part);
-  const int64_t total = C * r;
-  hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     stream, part, slices, C, r, scale, out_cr ? 1 : 0, out, accumulate);
+hipError_t launch_lora_dx(const uint16_t* X, int64_t M, int64_t K, const float* v, int r, float scale,
+                          int accumulate, float* ws, float* dA, hipStream_t stream) {
+  const LoraPassPlan p = lora_pass_plan(M, K, r);
+  LoraPassArgs a{X, M, K, nullptr, v, r, p.crange, nullptr, ws};
+  launch_pass<false, true, false>(p, a, stream);
+  launch_reduce(reduce_job(ws, p.mblocks, K * r, K, r, true, scale, accumulate, dA), nullptr, stream);
   return hipGetLastError();
 }
 
