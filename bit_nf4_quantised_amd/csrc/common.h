@@ -135,4 +135,26 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// ------------------------------------------------------------------------------------------
+// LDS-DMA plumbing (buffer loads that write LDS directly: lane i's 16 bytes land at M0 + 16 i).
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kRsrcFlags = 0x00020000;         // raw buffer, 32-bit data format
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past every record count used here
+
+// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier after the wave's LDS accesses complete. Written as inline asm so that the
+// compiler does not add a wait for every LDS-DMA load in flight (it cannot tell that those target
+// stages nobody reads before the next barrier); code that needs a DMA landed waits for it with
+// wait_vmcnt before calling this.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace nf4

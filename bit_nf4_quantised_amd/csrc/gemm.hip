@@ -14,13 +14,13 @@
 //   * waves 8-11 (dequantisers) turn the packed weight, its scale codes and second-level constants
 //     of a step (already in LDS) into the bf16 W tile: VALU work and LDS accesses only;
 //   * waves 12-15 (loaders) issue every global load as a 16-byte LDS-DMA buffer load: activation
-//     tiles one step ahead, packed weight tiles two steps ahead. The address unit takes a few tens
+//     tiles one step ahead, packed weight tiles three steps ahead. The address unit takes a few tens
 //     of cycles per such load, so these waves spend most of their time waiting to issue; keeping
 //     that off the other waves' instruction streams is why they exist.
 // The roles meet at one workgroup barrier per phase. In phase q the loaders fetch activations of
-// step q+1 and packed weights of step q+2, the dequantisers build the W tile of step q and the
-// consumers multiply step q-1. LDS holds three activation stages, two W stages and three packed
-// weight stages.
+// step q+1 and packed weights of step q+3, the dequantisers build the W tile of step q (from
+// registers) while reading the packed words of step q+1, and the consumers multiply step q-1.
+// LDS holds three activation stages, two W stages and four packed weight stages.
 //
 // Activation rows are 128 bytes in LDS (no padding, as DMA writes 64 lanes x 16 contiguous bytes);
 // the 16-byte chunk c of row r sits at slot c ^ ((r >> 1) & 7), which keeps the 16-lane groups of a
@@ -56,10 +56,8 @@ struct GemmArgs {
 constexpr int kBN = 128;        // output columns per tile
 constexpr int kBK = 64;         // contraction per step
 constexpr int kXStages = 3;     // activation stages in LDS
-constexpr int kPStages = 3;     // packed weight stages in LDS
+constexpr int kPStages = 4;     // packed weight stages in LDS
 constexpr int kThreads = 1024;  // 8 consumer + 4 dequantiser + 4 loader waves
-constexpr int kRsrcFlags = 0x00020000;         // raw buffer, 32-bit data format
-constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past every record count used here
 
 template <bool DX>
 struct WTile {
@@ -79,23 +77,12 @@ struct Waves {  // consumer layout: waves_m x waves_n waves, each on a WM x WN s
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
-// expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier after the wave's LDS accesses complete. Written as inline asm so that the
-// compiler does not add a wait for every LDS-DMA load in flight (it cannot tell that those target
-// stages nobody reads in this phase); the loaders wait for exactly the loads read next with
-// wait_vmcnt before calling this.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
+// The LDS words a dequantiser thread expands in one step: its 32-value packed chunk, the word
+// holding its block's scale code and the block's second-level constant.
+struct StepWords {
+  u32x4 wq;
+  uint32_t cw, c2;
+};
 
 // Swap with the neighbouring lane (quad_perm [1,0,3,2]).
 __device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
@@ -222,19 +209,29 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
     };
 
     // ---- schedule. Phase q issues the activations of step q+1, then the packed weights of step
-    // q+2, and waits until everything issued in phase q-1 has landed: at least NX + 1 loads were
-    // issued after it, and vector-memory loads complete in issue order.
+    // q+3, and waits until everything issued in phase q-1 has landed: the loads issued in phase q
+    // are the only ones allowed to stay in flight, and vector-memory loads complete in issue order.
+    // The packed weights of a step therefore sit in LDS one phase before they are expanded, which
+    // lets the dequantisers read them a phase ahead.
+    const bool two_p = !DX || lw < 2;   // issue_p makes two loads (chunk + code or constant)
     issue_x(0);
     issue_p(0);
     if (main_steps > 1) issue_p(1);
+    if (main_steps > 2) issue_p(2);
     wait_vmcnt<0>();
     lds_barrier();
     for (int q = 0; q <= steps; ++q) {
-      const bool more_x = q + 1 < main_steps, more_p = q + 2 < main_steps;
+      const bool more_x = q + 1 < main_steps, more_p = q + 3 < main_steps;
       if (more_x) issue_x(q + 1);
-      if (more_p) issue_p(q + 2);
-      if (more_p) wait_vmcnt<NX + 1>();
-      else wait_vmcnt<0>();
+      if (more_p) issue_p(q + 3);
+      if (more_p) {
+        if (two_p) wait_vmcnt<NX + 2>();
+        else wait_vmcnt<NX + 1>();
+      } else if (more_x) {
+        wait_vmcnt<NX>();
+      } else {
+        wait_vmcnt<0>();
+      }
       lds_barrier();
     }
     return;
@@ -258,21 +255,36 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
                            : (uint32_t)(col0 + w_row) * kb;
     const uint32_t b_step = DX ? (uint32_t)kBK * kb : 1u;
     const uint32_t rb0 = DX ? (uint32_t)w_row * kb + (uint32_t)(col0 / kBlock) : b0;   // the row's first block
-    auto dequant = [&](int t) {
+    // The LDS words of step t are read one phase before they are expanded (they landed a phase
+    // earlier still), so the reads wait behind the consumers' fragment reads off the critical path.
+    // Only raw loaded words cross the phase: anything computed from them would make the compiler
+    // wait for the reads in the phase that issues them.
+    auto fetch = [&](int t) {
       const int ps = t % kPStages;
-      const u32x4 wq = Ps[ps][dt];
-      const uint32_t b = b0 + (uint32_t)t * b_step;
-      uint32_t word, c2bits;
+      StepWords w;
+      w.wq = Ps[ps][dt];
+      if (DX) {
+        const uint32_t b = b0 + (uint32_t)t * b_step, rb = rb0 + (uint32_t)t * b_step;
+        const uint32_t byte = (rb & 3u) + (uint32_t)(w_seg >> 1);     // within the row's 16 bytes
+        w.cw = Cs[ps][w_row * 4 + (int)(byte >> 2)];
+        w.c2 = __float_as_uint(Gs[ps][w_row * 4 + (int)((b >> 8) - (rb >> 8))]);
+      } else {
+        w.cw = Cs[ps][w_row];
+        w.c2 = __float_as_uint(Gs[ps][w_row]);
+      }
+      return w;
+    };
+    auto dequant = [&](int t, const StepWords& sw) {
+      const u32x4 wq = sw.wq;
+      uint32_t shift;   // byte of the code within its word
       if (DX) {
         const uint32_t rb = rb0 + (uint32_t)t * b_step;
-        const uint32_t byte = (rb & 3u) + (uint32_t)(w_seg >> 1);     // within the row's 16 bytes
-        word = Cs[ps][w_row * 4 + (int)(byte >> 2)] >> ((byte & 3u) * 8u);
-        c2bits = __float_as_uint(Gs[ps][w_row * 4 + (int)((b >> 8) - (rb >> 8))]);
+        shift = (((rb & 3u) + (uint32_t)(w_seg >> 1)) & 3u) * 8u;
       } else {
-        word = Cs[ps][w_row] >> ((b & 3u) * 8u);
-        c2bits = __float_as_uint(Gs[ps][w_row]);
+        shift = ((b0 + (uint32_t)t) & 3u) * 8u;
       }
-      const float c1p = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)word, 0), __uint_as_float(c2bits));
+      const uint32_t word = sw.cw >> shift;
+      const float c1p = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)word, 0), __uint_as_float(sw.c2));
       uint32_t pp[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) pp[k] = pack_bf16x2(__fmul_rn(qv[2 * k], c1p), __fmul_rn(qv[2 * k + 1], c1p));
@@ -285,7 +297,10 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
       L.lo[3] = swap_pair(L.lo[1]);
       L.hi[2] = swap_pair(L.hi[0]);
       L.hi[3] = swap_pair(L.hi[1]);
-      u32x4* dst = reinterpret_cast<u32x4*>(&Ws[t & 1][w_row][32 * w_seg]);
+      // all 32 values are expanded before any is stored: an LDS write cannot issue while the
+      // consumers' fragment reads fill the LDS queue, and a stalled write would hold up the
+      // arithmetic behind it
+      uint32_t d[4][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t p = wq[i];
@@ -293,11 +308,13 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
         const uint32_t even = ((p >> 4) ^ hx4) & 0x0F0F0F0Fu;   // elements 0,2,4,6
         const uint32_t s0 = __builtin_amdgcn_perm(odd, even, 0x05010400u);  // elements 0..3
         const uint32_t s1 = __builtin_amdgcn_perm(odd, even, 0x07030602u);  // elements 4..7
-        uint32_t d[4];
-        lut4(L, s0, d[0], d[1]);
-        lut4(L, s1, d[2], d[3]);
-        dst[i] = u32x4{d[0], d[1], d[2], d[3]};
+        lut4(L, s0, d[i][0], d[i][1]);
+        lut4(L, s1, d[i][2], d[i][3]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4* dst = reinterpret_cast<u32x4*>(&Ws[t & 1][w_row][32 * w_seg]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = u32x4{d[i][0], d[i][1], d[i][2], d[i][3]};
     };
 
     // ---- adapter steps: bf16(s * u) (or v) into the activation stage, B (or A) into the W stage
@@ -337,9 +354,16 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
     };
 
     lds_barrier();
+    StepWords cur = fetch(0);
     for (int q = 0; q <= steps; ++q) {
-      if (q < main_steps) dequant(q);
-      else if (q < steps) store_lora(q);
+      if (q < main_steps) {
+        StepWords nxt = cur;
+        if (q + 1 < main_steps) nxt = fetch(q + 1);
+        dequant(q, cur);
+        cur = nxt;
+      } else if (q < steps) {
+        store_lora(q);
+      }
       lds_barrier();
     }
     return;

@@ -21,23 +21,7 @@
 namespace nf4 {
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
 constexpr int kStepC = 64;                     // Q columns per step
-constexpr int kLoraRsrcFlags = 0x00020000;     // raw buffer, 32-bit data format
-constexpr uint32_t kLoraOutOfRange = 0x80000000u;
-
-template <int N>
-__device__ __forceinline__ void lora_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier after the wave's LDS accesses complete, as raw s_barrier: the compiler would
-// otherwise wait for every LDS-DMA load in flight, including those for later steps.
-__device__ __forceinline__ void lora_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // 16-lane transpose read of an LDS tile stored [contraction][column] with pitch `pitch`:
 // returns, for lane (j = lane % 16, grp = lane / 16), the 8 contraction values
@@ -108,12 +92,12 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
     {
       const uint16_t* base = a.Q + m0 * a.C + c0;
       const int nrec = (int)(rows_valid * a.C * 2 - c0 * 2);
-      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kLoraRsrcFlags);
+      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kRsrcFlags);
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
         const int slot = (wave * NQ + j) * 64 + lane;
         const int row = slot >> 3, c = (slot & 7) ^ ((row >> 1) & 7);
-        const uint32_t off = c < valid_chunks ? (uint32_t)row * (uint32_t)(a.C * 2) + (uint32_t)c * 16u : kLoraOutOfRange;
+        const uint32_t off = c < valid_chunks ? (uint32_t)row * (uint32_t)(a.C * 2) + (uint32_t)c * 16u : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&Qs[st][(wave * NQ + j) * 64 * 8]), 16, off, 0, 0, 0);
       }
     }
@@ -129,13 +113,13 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
         __amdgpu_buffer_rsrc_t rs;
         if (RT) {
           rs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.R + c0 * r), (short)0,
-                                                 (int)((a.C - c0) * r * 2), kLoraRsrcFlags);
+                                                 (int)((a.C - c0) * r * 2), kRsrcFlags);
           off = (uint32_t)slot * 16u;
         } else {
           rs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.R + c0), (short)0,
-                                                 (int)(r * a.C * 2 - c0 * 2), kLoraRsrcFlags);
+                                                 (int)(r * a.C * 2 - c0 * 2), kRsrcFlags);
           const int row = slot >> 3, c = (slot & 7) ^ ((row >> 1) & 7);
-          off = c < valid_chunks ? (uint32_t)row * (uint32_t)(a.C * 2) + (uint32_t)c * 16u : kLoraOutOfRange;
+          off = c < valid_chunks ? (uint32_t)row * (uint32_t)(a.C * 2) + (uint32_t)c * 16u : kOutOfRange;
         }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&Rs[st][i * 64 * 8]), 16, off, 0, 0, 0);
       }
@@ -251,24 +235,24 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
       issue(t + QS - 1);
       // allowance: the loads of steps t+1 .. t+QS-1
       if (QS == 3) {
-        if (per_step == NQ) lora_wait_vmcnt<2 * NQ>();
-        else if (per_step == NQ + 1) lora_wait_vmcnt<2 * (NQ + 1)>();
-        else if (per_step == NQ + 2) lora_wait_vmcnt<2 * (NQ + 2)>();
-        else lora_wait_vmcnt<0>();
+        if (per_step == NQ) wait_vmcnt<2 * NQ>();
+        else if (per_step == NQ + 1) wait_vmcnt<2 * (NQ + 1)>();
+        else if (per_step == NQ + 2) wait_vmcnt<2 * (NQ + 2)>();
+        else wait_vmcnt<0>();
       } else {
-        if (per_step == NQ) lora_wait_vmcnt<NQ>();
-        else if (per_step == NQ + 1) lora_wait_vmcnt<NQ + 1>();
-        else if (per_step == NQ + 2) lora_wait_vmcnt<NQ + 2>();
-        else if (per_step == NQ + 3) lora_wait_vmcnt<NQ + 3>();
-        else if (per_step == NQ + 4) lora_wait_vmcnt<NQ + 4>();
-        else lora_wait_vmcnt<0>();
+        if (per_step == NQ) wait_vmcnt<NQ>();
+        else if (per_step == NQ + 1) wait_vmcnt<NQ + 1>();
+        else if (per_step == NQ + 2) wait_vmcnt<NQ + 2>();
+        else if (per_step == NQ + 3) wait_vmcnt<NQ + 3>();
+        else if (per_step == NQ + 4) wait_vmcnt<NQ + 4>();
+        else wait_vmcnt<0>();
       }
     } else {
-      lora_wait_vmcnt<0>();
+      wait_vmcnt<0>();
     }
-    lora_barrier();
+    lds_barrier();
     compute(t);
-    lora_barrier();
+    lds_barrier();
   }
 
   if (DOWN) {
