@@ -31,7 +31,7 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 //   forward : [u (M*r fp32)] [partials: skinny splits or the adapter pass over X]
 //   backward: [v (M*r fp32)] [partials of the pass over dY, then of the pass over X]
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
-  size_t part = nf4::skinny_eligible(M, K) ? nf4::skinny_workspace_floats(M, N, K, r)
+  size_t part = nf4::skinny_eligible(M, N, K) ? nf4::skinny_workspace_floats(M, N, K, r)
                                         : nf4::lora_pass_ws_floats(M, K, r, true, false);
   return align_up((size_t)M * r * 4) + align_up(part * 4);
 }
@@ -116,7 +116,7 @@ int qlora_linear_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const ui
   if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;
   float* u = u_out ? u_out : static_cast<float*>(ws);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
-  if (nf4::skinny_eligible(M, K)) {
+  if (nf4::skinny_eligible(M, N, K)) {
     return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, N, K, x, M, A, B, r,
                                            scale, part, u, y, stream));
   }
@@ -139,7 +139,7 @@ int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M
       (ws && !aligned16(ws)))
     return NF4_ERR_ALIGN;
   const int64_t N = W->N, K = W->K;
-  if (nf4::skinny_eligible(M, K)) {
+  if (nf4::skinny_eligible(M, N, K)) {
     // the skinny path forms u itself from the adapter rows; it needs the workspace
     const size_t need = fwd_ws(M, N, K, r);
     if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;

@@ -43,10 +43,9 @@ hipError_t launch_lora_dx(const uint16_t* X, int64_t M, int64_t K, const float* 
 
 // Skinny forward (M <= 16): split-K dequant-GEMV on MFMA with a deterministic reduction.
 // `part` holds skinny_workspace_floats(M, N, K, r) floats; u_out receives u = x A^T [M x r].
-bool skinny_eligible(int64_t M, int64_t K);
+bool skinny_eligible(int64_t M, int64_t N, int64_t K);
 struct SkinnyPlan {
-  int w_blocks, w_splits, w_sub;   // weight items: 512-row blocks x splits of w_sub sub-chunks
-  int a_items;                     // adapter-row items (16 sub-chunks each)
+  int w_blocks, w_splits, w_sub;   // items: 256-row blocks x splits of w_sub 512-column steps
 };
 SkinnyPlan skinny_plan(int64_t N, int64_t K, int r);
 size_t skinny_workspace_floats(int64_t M, int64_t N, int64_t K, int r);

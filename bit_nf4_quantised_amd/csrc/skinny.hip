@@ -4,38 +4,42 @@
 // y = x W~^T + s (x A^T) B^T. With M <= 16 the weight is read once and each dequantised value is
 // used M times, so the kernel is bound by HBM bandwidth on the packed weight (0.52 bytes per
 // value) and, behind it, by the dequantisation work. Layout of the work:
-//   * a workgroup of 16 waves owns 512 consecutive rows of W (32 per wave, two 16-row tiles) and
-//     one split of the k axis; the splits are whole 256-column sub-chunks, and their number is
-//     chosen so that the (row block, split) items fill the 256 CUs once;
-//   * lane (row = lane % 16, grp = lane / 16) dequantises the 64-value block at column
-//     kb + 64 * grp of its row straight into MFMA operand registers; the activation operand of
-//     v_mfma_f32_16x16x32_bf16 holds x[m = lane % 16][kb + 64 * grp ...], so the MFMA contracts
-//     over a permuted but consistent k order;
-//   * the activations of a sub-chunk (16 tokens x 256 columns) are shared by all waves: they are
-//     loaded one sub-chunk ahead and stored into LDS (chunk c of token t at slot c ^ t, which keeps
-//     the 16 token lanes of a fragment read in distinct banks; tokens past M and columns past K are
-//     zeros), and one workgroup barrier per sub-chunk hands them over;
-//   * the packed codes of the next sub-chunk are in flight in registers while a sub-chunk is
+//   * a workgroup of 16 waves owns 256 consecutive rows of W (one 16-row tile per wave) and one
+//     split of the k axis; a step covers 512 columns, and the number of splits is chosen so that
+//     the (row block, split) items fill the 256 CUs once;
+//   * lane (row = lane % 16, g = lane / 16) loads, with its instruction i, the 16 packed bytes at
+//     offset 64 i + 16 g of its row's 256-byte step (so the four lanes of a row read 64
+//     contiguous bytes per instruction): half g % 2 of block 2 i + g / 2. It dequantises them
+//     straight into MFMA operand registers; dword d of that half holds columns 128 i + 32 g + 8 d
+//     of the step, and the activation operand of v_mfma_f32_16x16x32_bf16 holds the same columns
+//     of x[m = lane % 16], so the MFMA contracts over a permuted but consistent k order;
+//   * the activations of a step (16 tokens x 512 columns) are shared by all waves: they are loaded
+//     one step ahead and stored into LDS (chunk c of token t at slot c ^ t, which keeps the 16
+//     token lanes of a fragment read in distinct banks; tokens past M and columns past K are
+//     zeros), and one workgroup barrier per step hands them over;
+//   * the packed codes, the row's eight scale codes of the step (one 16-byte load) and the
+//     second-level constants of the next step are in flight in registers while a step is
 //     dequantised (raw loaded words only, so issuing the loads never waits for them);
 //   * dequantisation reads both codes of a packed byte from an LDS pair table (256 entries of two
 //     fp32 codes, replicated 32 times so the 32 lanes of a half-wave read distinct banks): one
 //     v_perm forms the address (byte * 256 + copy * 8), then two fp32 products with the block
 //     scale and one bf16 pair conversion, giving bit for bit bf16(fl32(q[idx] * c1')). Four waves
 //     per SIMD keep enough of these lookups in flight;
-//   * every wave writes the fp32 partial sums of its own rows; the r rows of A (bf16, no
-//     dequantisation) are handled by separate small items, dispatched first, that write partial
-//     sums of u = x A^T;
-//   * skinny_epilogue_kernel sums the split partials in split order, forms u from its partials,
-//     adds s * u B^T in fp32 and rounds y to bf16.
+//   * the r rows of A (bf16) ride along: in the items of row block b < r / 16, wave w also
+//     multiplies one 32-column slice (i = w / 4, d = w % 4) of each step of A's tile b (one more
+//     MFMA per step), so u = x A^T is formed as 16 partial sums per split without separate work
+//     items;
+//   * every wave writes the fp32 partial sums of its own rows; skinny_epilogue_kernel sums the
+//     split partials in split order, forms u from its partials, adds s * u B^T in fp32 and rounds
+//     y to bf16.
 #include "common.h"
 #include "launch.h"
 
 namespace nf4 {
 
-constexpr int kSub = 256;                        // k columns per sub-chunk
+constexpr int kStep = 512;                       // k columns per step
 constexpr int kSkWaves = 16;                     // waves per workgroup
-constexpr int kSkTN = 2;                         // 16-row tiles per wave
-constexpr int kSkRows = kSkWaves * kSkTN * 16;   // rows of W per workgroup
+constexpr int kSkRows = kSkWaves * 16;           // rows of W per workgroup
 constexpr int kSkSlots = 256;                    // workgroups that occupy the MI355X once
 
 struct SkinnyArgs {
@@ -49,30 +53,36 @@ struct SkinnyArgs {
   int r;
   SkinnyPlan p;
   float* part;         // [w_splits][M][N]
-  float* upart;        // [a_items * 16][M][r]
+  float* upart;        // [w_splits * 16][M][r]
 };
 
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 
-// One sub-chunk of one lane's weight operands (raw loaded values only).
+// One step of one lane's packed weight (raw loaded values only): the bytes of instruction i are
+// half g % 2 of block 2 i + g / 2.
 struct SkinnyW {
-  u32x4 p[kSkTN][2];   // [tile][half of the lane's 64-value block]
-  uint32_t cw[kSkTN];  // aligned words holding the E4M3 codes of the block scales
-  float c2[kSkTN];     // second-level constants
+  u32x4 p[4];
+};
+// One step of one lane's small operands, single-buffered: each is reloaded for the next step as
+// soon as it has been consumed.
+struct SkinnyS {
+  u32x4 cw;        // 16 bytes from the aligned word holding the step's first scale code
+  u32x2 c2;        // second-level constants of the step's first group and the next one
+  u32x4 a;         // adapter fragment: 8 bf16 of A
 };
 
 __constant__ uint32_t kSkinnyCodes[16] = {NF4_CODE_BITS};
 
 __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyArgs g) {
   __shared__ __attribute__((aligned(16))) f32x2 tab[256 * 32];
-  // activation stages: 16 tokens x 32 chunks of 8 bf16
-  __shared__ __attribute__((aligned(16))) u32x4 xs[2][16 * 32];
+  // activation stages: 16 tokens x 64 chunks of 8 bf16
+  __shared__ __attribute__((aligned(16))) u32x4 xs[2][16 * 64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4;
   const int m = lane & 15;
   const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
-  const int64_t nsub = (g.K + kSub - 1) / kSub;
+  const int64_t nsteps = (g.K + kStep - 1) / kStep;
 
   // pair table: thread t fills copies 8 (t & 3) .. +7 of byte value t / 4
   {
@@ -85,145 +95,133 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
     for (int c = 0; c < 4; ++c) dst[c] = v;
   }
 
-  const int a_items = g.p.a_items;
-  if ((int)blockIdx.x < a_items) {
-    // ---------------------------------------------------------------- adapter rows: u partials
-    // wave w takes sub-chunk 16 * item + w of every 16-row tile of A; activations from global
-    const int64_t sub = (int64_t)blockIdx.x * kSkWaves + wave;
-    const int64_t kk0 = sub * kSub + 64 * grp;
-    const bool live = sub < nsub;
-    const int64_t kk = min(kk0, g.K - 64);
-    bf16x8 b[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = bf16x8{};
-    if (live && m < g.M && kk0 < g.K) {
-      const bf16x8* src = reinterpret_cast<const bf16x8*>(g.x + (int64_t)m * g.K + kk0);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = src[j];
-    }
-    float* dst = g.upart + ((int64_t)blockIdx.x * kSkWaves + wave) * g.M * g.r;
-    for (int t0 = 0; t0 < g.r; t0 += 16) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (live) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(g.A + (int64_t)(t0 + (lane & 15)) * g.K + kk);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, src[i]), b[i], acc, 0, 0, 0);
-      }
-      // acc[i]: row t0 + 4 grp + i of A, token m
-      if (m < g.M) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(int64_t)m * g.r + t0 + 4 * grp + i] = acc[i];
-      }
-    }
-    return;
-  }
+  const int rb = (int)blockIdx.x % g.p.w_blocks, split = (int)blockIdx.x / g.p.w_blocks;
+  const int s_begin = split * g.p.w_sub;
+  const int s_end = (int)min(nsteps, (int64_t)s_begin + g.p.w_sub);
+  const int64_t row = (int64_t)rb * kSkRows + wave * 16 + m;   // this lane's row of W
+  const int64_t rowc = min(row, g.N - 1);
+  const int64_t nblocks = g.N * (g.K / kBlock);
+  const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.scale_q, (short)0, (int)((nblocks + 3) & ~int64_t(3)), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rs_c2 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.scale_c2, (short)0, (int)(((nblocks + kGroup - 1) / kGroup) * 4), kRsrcFlags);
+  // adapter slice of this wave: tile rb of A, 32-column slice (ai, ad) = (w / 4, w % 4) of each step
+  const bool a_live = rb * 16 < g.r;
+  const int64_t arow = min((int64_t)rb * 16 + m, (int64_t)g.r - 1);
+  const int ai = wave >> 2, ad = wave & 3;
+  // per-lane bases, so that the step loop works with 32-bit offsets (the block count of W is
+  // below 2^31, so block indices fit)
+  const int kb = (int)(g.K / kBlock);                         // blocks per row
+  const uint32_t rowb = (uint32_t)(rowc * kb);                // first block of this lane's row
+  const uint8_t* prow = g.packed + (int64_t)rowb * 32 + 16 * (grp & 1);
+  const uint16_t* arp = g.A + arow * g.K;
+  // block of instruction i of this lane in step s, within the row (clamped: blocks past K re-read
+  // the row's last block, whose activations are zeros)
+  auto blk_of = [&](int s, int i) { return min(s * 8 + 2 * i + (grp >> 1), kb - 1); };
 
-  // ------------------------------------------------------------------ weight rows
-  const int it = (int)blockIdx.x - a_items;
-  const int rb = it % g.p.w_blocks, split = it / g.p.w_blocks;
-  const int64_t s_begin = (int64_t)split * g.p.w_sub;
-  const int64_t s_end = min(nsub, s_begin + g.p.w_sub);
-  const int64_t row0 = (int64_t)rb * kSkRows + wave * (kSkTN * 16);
-  const uint32_t kb = (uint32_t)(g.K / kBlock);
-  int64_t rowc[kSkTN];
+  auto load_w = [&](int s, SkinnyW& st) {
 #pragma unroll
-  for (int tn = 0; tn < kSkTN; ++tn) rowc[tn] = min(row0 + tn * 16 + (lane & 15), g.N - 1);
-
-  // activation copy: wave w moves tokens 2 (w % 8), +1 of a sub-chunk (lane i: token
-  // 2 (w % 8) + i / 32, slot i % 32 of the token's row, source chunk slot ^ token); tokens past M
-  // and columns past K are zeros. Waves w and w + 8 store the same values, so that every wave runs
-  // the same code. The copy goes through registers: loaded at the start of the phase before the
-  // sub-chunk is used, stored into LDS at its end.
-  // The load itself is unconditional (clamped into range) and the zeros are selected at the store:
-  // a load that some lanes skip would make the compiler wait for every load in flight.
-  const int xt = 2 * (wave & 7) + (lane >> 5), xslot = lane & 31, xchunk = xslot ^ (xt & 15);
-  const int64_t xrow = (int64_t)min(xt, (int)g.M - 1) * g.K;
-  auto load_x = [&](int64_t sub) {
-    const int64_t col = min(sub * kSub + 8 * xchunk, g.K - 8);
-    return *reinterpret_cast<const u32x4*>(g.x + xrow + col);
-  };
-  auto store_x = [&](int64_t sub, u32x4* stage, u32x4 v) {
-    const bool live = xt < g.M && sub * kSub + 8 * xchunk < g.K;
-    stage[xt * 32 + xslot] = live ? v : u32x4{0u, 0u, 0u, 0u};
-  };
-
-  // weight loads of one sub-chunk; blocks past K re-read the last block of the row (their
-  // activations are zeros)
-  auto load_w = [&](int64_t sub, SkinnyW& st) {
-    const int64_t kk = min(sub * kSub + 64 * grp, g.K - 64);
-#pragma unroll
-    for (int tn = 0; tn < kSkTN; ++tn) {
-      const int64_t e = rowc[tn] * g.K + kk;
-      const u32x4* src = reinterpret_cast<const u32x4*>(g.packed + e / 2);
-      st.p[tn][0] = __builtin_nontemporal_load(src);
-      st.p[tn][1] = __builtin_nontemporal_load(src + 1);
-      const int64_t b = e / kBlock;
-      // the aligned word holding the code (it never crosses a page, and its other bytes are
-      // ignored), so no byte extraction has to wait for the load
-      st.cw[tn] = *reinterpret_cast<const uint32_t*>(g.scale_q + (b & ~int64_t(3)));
-      st.c2[tn] = g.scale_c2[b / kGroup];
+    for (int i = 0; i < 4; ++i) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(prow + (uint32_t)blk_of(s, i) * 32u);
+      st.p[i] = __builtin_nontemporal_load(src);
     }
   };
+  auto load_scales = [&](int s, SkinnyS& ss) {
+    const uint32_t b0 = rowb + (uint32_t)min(s * 8, kb - 1);
+    ss.cw = __builtin_amdgcn_raw_buffer_load_b128(rs_q, b0 & ~3u, 0, 0);
+    ss.c2 = __builtin_amdgcn_raw_buffer_load_b64(rs_c2, (b0 >> 8) * 4u, 0, 0);
+  };
+  auto load_a = [&](int s, SkinnyS& ss) {
+    const uint32_t ak = (uint32_t)min((int64_t)s * kStep + 128 * ai + 32 * grp + 8 * ad, g.K - 8);
+    ss.a = *reinterpret_cast<const u32x4*>(arp + ak);
+  };
 
-  f32x4 acc[kSkTN];
-#pragma unroll
-  for (int i = 0; i < kSkTN; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // activation copy: thread t moves token t / 64, slot t % 64 (source chunk slot ^ token)
+  const int xt = tid >> 6, xslot = tid & 63, xchunk = xslot ^ xt;
+  const uint16_t* xp = g.x + (int64_t)min(xt, (int)g.M - 1) * g.K;
+  auto load_x = [&](int s) {
+    const uint32_t col = (uint32_t)min((int64_t)s * kStep + 8 * xchunk, g.K - 8);
+    return *reinterpret_cast<const u32x4*>(xp + col);
+  };
+  auto store_x = [&](int s, u32x4* stage, u32x4 v) {
+    const bool live = xt < g.M && (int64_t)s * kStep + 8 * xchunk < g.K;
+    stage[xt * 64 + xslot] = live ? v : u32x4{0u, 0u, 0u, 0u};
+  };
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accu = f32x4{0.f, 0.f, 0.f, 0.f};
   const char* tab_bytes = reinterpret_cast<const char*>(tab);
 
-  auto process = [&](int64_t sub, const SkinnyW& st, const u32x4* xsv) {
-    const int64_t kk = min(sub * kSub + 64 * grp, g.K - 64);
-    float c1p[kSkTN];
+  // process step s; with `more`, the small operands of step s + 1 are loaded as soon as those of
+  // step s have been consumed
+  auto process = [&](int s, const SkinnyW& st, SkinnyS& ss, const u32x4* xsv, bool more) {
+    const uint32_t b0 = rowb + (uint32_t)min(s * 8, kb - 1);
+    const uint32_t base = b0 & 3u;   // byte of the step's first code in the 16 loaded bytes
+    float c1p[4];
 #pragma unroll
-    for (int tn = 0; tn < kSkTN; ++tn) {
-      const uint32_t b = (uint32_t)rowc[tn] * kb + (uint32_t)(kk / kBlock);
-      c1p[tn] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)(st.cw[tn] >> ((b & 3u) * 8u)), 0), st.c2[tn]);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t b = rowb + (uint32_t)blk_of(s, i);
+      const uint32_t byte = base + (b - b0);   // < 16
+      const uint32_t word = byte < 4 ? ss.cw[0] : byte < 8 ? ss.cw[1] : byte < 12 ? ss.cw[2] : ss.cw[3];
+      const uint32_t code = word >> ((byte & 3u) * 8u);
+      const float c2 = (b >> 8) == (b0 >> 8) ? __uint_as_float(ss.c2[0]) : __uint_as_float(ss.c2[1]);
+      c1p[i] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)code, 0), c2);
     }
+    if (more) load_scales(s + 1, ss);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // activation fragment i: chunk 8 grp + i of token m
-      const bf16x8 bx = __builtin_bit_cast(bf16x8, xsv[m * 32 + ((8 * grp + i) ^ m)]);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int tn = 0; tn < kSkTN; ++tn) {
-        const uint32_t word = st.p[tn][i >> 2][i & 3];
+      for (int d = 0; d < 4; ++d) {
+        // activation fragment (i, d): chunk 16 i + 4 g + d of token m
+        const bf16x8 bx = __builtin_bit_cast(bf16x8, xsv[m * 64 + ((16 * i + 4 * grp + d) ^ m)]);
+        const uint32_t word = st.p[i][d];
         uint32_t a[4];
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          // byte bb of the word holds values 8 i + 2 bb (high nibble) and + 1
+          // byte bb of the word holds values 8 d + 2 bb (high nibble) and + 1 of the half block
           const uint32_t off = __builtin_amdgcn_perm(word, laneoff, 0x0C0C0000u | ((4u + bb) << 8));
           const f32x2 qv = *reinterpret_cast<const f32x2*>(tab_bytes + off);
-          a[bb] = pack_bf16x2(__fmul_rn(qv[0], c1p[tn]), __fmul_rn(qv[1], c1p[tn]));
+          a[bb] = pack_bf16x2(__fmul_rn(qv[0], c1p[i]), __fmul_rn(qv[1], c1p[i]));
         }
-        acc[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, (u32x4{a[0], a[1], a[2], a[3]})),
-                                                          bx, acc[tn], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, (u32x4{a[0], a[1], a[2], a[3]})),
+                                                      bx, acc, 0, 0, 0);
       }
+    if (a_live) {
+      const bf16x8 bx = __builtin_bit_cast(bf16x8, xsv[m * 64 + ((16 * ai + 4 * grp + ad) ^ m)]);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ss.a), bx, accu, 0, 0, 0);
     }
+    if (more) load_a(s + 1, ss);
   };
 
-  // Phase of sub-chunk s (parity p = (s - s_begin) % 2): the activations and weights of s + 1 are
+  // Phase of step s (parity p = (s - s_begin) % 2): the activations and packed weight of s + 1 are
   // loaded (into registers), s is dequantised and multiplied from w[p] and activation stage p, the
   // activations of s + 1 are stored into stage 1 - p (nobody reads it since the previous barrier),
   // and the barrier hands them over. Every load issued is consumed: the steady-state loop runs
-  // while both of its phases have a successor, and the last one or two phases are peeled.
+  // while both of its phases have a successor, and the last one or two phases are peeled (a load
+  // whose value is never used would make the compiler wait for it before reusing its registers).
   SkinnyW w[2];
+  SkinnyS ss;
   {
     const u32x4 x0 = load_x(s_begin);
     load_w(s_begin, w[0]);
+    load_scales(s_begin, ss);
+    load_a(s_begin, ss);
     store_x(s_begin, xs[0], x0);
   }
   __syncthreads();   // the pair table and the first activation stage are in place
-  auto phase = [&](int64_t sp, int p, bool more) {
+  auto phase = [&](int sp, int p, bool more) {
     u32x4 xn = u32x4{0u, 0u, 0u, 0u};
     if (more) {
       xn = load_x(sp + 1);
       load_w(sp + 1, w[1 - p]);
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the arithmetic
-    process(sp, w[p], xs[p]);
+    process(sp, w[p], ss, xs[p], more);
     if (more) store_x(sp + 1, xs[1 - p], xn);
     lds_barrier();
   };
-  int64_t sp = s_begin;
+  int sp = s_begin;
   for (; sp + 2 < s_end; sp += 2) {
     phase(sp, 0, true);
     phase(sp + 1, 1, true);
@@ -235,15 +233,18 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
     phase(sp, 0, false);
   }
 
-  // acc[tn][i]: row row0 + 16 tn + 4 grp + i, token m
+  // acc[i]: row (tile row 4 grp + i), token m
   if (m < g.M) {
 #pragma unroll
-    for (int tn = 0; tn < kSkTN; ++tn)
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r_out = (int64_t)rb * kSkRows + wave * 16 + 4 * grp + i;
+      if (r_out < g.N) g.part[((int64_t)split * g.M + m) * g.N + r_out] = acc[i];
+    }
+    if (a_live) {
+      float* dst = g.upart + ((int64_t)split * kSkWaves + wave) * g.M * g.r + (int64_t)m * g.r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = row0 + tn * 16 + 4 * grp + i;
-        if (row < g.N) g.part[((int64_t)split * g.M + m) * g.N + row] = acc[tn][i];
-      }
+      for (int i = 0; i < 4; ++i) dst[rb * 16 + 4 * grp + i] = accu[i];
+    }
   }
 }
 
@@ -297,20 +298,21 @@ __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __res
   y[mm * N + n] = (uint16_t)(pack_bf16x2(s + scale * l, 0.f) & 0xFFFFu);
 }
 
-// The activation copy addresses x with 32-bit buffer offsets.
-bool skinny_eligible(int64_t M, int64_t K) { return M >= 1 && M <= 16 && M * K * 2 < (int64_t(1) << 31); }
+// Scale codes and second-level constants are addressed with 32-bit buffer offsets.
+bool skinny_eligible(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= 16 && N * (K / kBlock) < (int64_t(1) << 31);
+}
 
 SkinnyPlan skinny_plan(int64_t N, int64_t K, int r) {
   SkinnyPlan p;
-  const int64_t nsub = (K + kSub - 1) / kSub;
-  p.w_blocks = (int)((N + kSkRows - 1) / kSkRows);
+  const int64_t nsteps = (K + kStep - 1) / kStep;
+  // every 16-row tile of A needs a row block to ride along with
+  p.w_blocks = (int)max((N + kSkRows - 1) / kSkRows, (int64_t)(r / 16));
   int64_t want = kSkSlots / p.w_blocks;
-  if (want > nsub) want = nsub;
+  if (want > nsteps) want = nsteps;
   if (want < 1) want = 1;
-  p.w_sub = (int)((nsub + want - 1) / want);
-  p.w_splits = (int)((nsub + p.w_sub - 1) / p.w_sub);
-  p.a_items = (int)((nsub + kSkWaves - 1) / kSkWaves);
-  (void)r;
+  p.w_sub = (int)((nsteps + want - 1) / want);
+  p.w_splits = (int)((nsteps + p.w_sub - 1) / p.w_sub);
   return p;
 }
 
@@ -321,7 +323,7 @@ static size_t skinny_wpart_floats(const SkinnyPlan& p, int64_t M, int64_t N) {
 
 size_t skinny_workspace_floats(int64_t M, int64_t N, int64_t K, int r) {
   const SkinnyPlan p = skinny_plan(N, K, r);
-  return skinny_wpart_floats(p, M, N) + (size_t)p.a_items * kSkWaves * (size_t)M * (size_t)r;
+  return skinny_wpart_floats(p, M, N) + (size_t)p.w_splits * kSkWaves * (size_t)M * (size_t)r;
 }
 
 hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
@@ -331,10 +333,10 @@ hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, cons
   const SkinnyPlan p = skinny_plan(N, K, r);
   float* upart = part + skinny_wpart_floats(p, M, N);
   SkinnyArgs g{packed, scale_q, scale_c2, N, K, x, M, A, r, p, part, upart};
-  const int items = p.a_items + p.w_blocks * p.w_splits;
+  const int items = p.w_blocks * p.w_splits;
   hipLaunchKernelGGL(skinny_fwd_kernel, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
   hipLaunchKernelGGL(skinny_epilogue_kernel, dim3((unsigned)((N + 255) / 256), (unsigned)M), dim3(256), 0,
-                     stream, part, p.w_splits, upart, p.a_items * kSkWaves, M, N, r, B, scale, u_out, y);
+                     stream, part, p.w_splits, upart, p.w_splits * kSkWaves, M, N, r, B, scale, u_out, y);
   return hipGetLastError();
 }
 
