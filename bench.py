@@ -115,6 +115,24 @@ def timed(fn, iters, torch):
     return s.elapsed_time(e) / iters
 
 
+def library_dense_gemm(torch, dev, m, lins, iters):
+    """TFLOP/s of torch.matmul (hipBLASLt) on plain bf16 operands of the same shapes, with no
+    quantisation: what a dense bf16 GEMM of these shapes sustains on this GPU. Context for the
+    roofline only; nothing on the measured path uses it."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    xs = [torch.randn(m, l.k, device=dev, dtype=torch.bfloat16, generator=g) for l in lins]
+    ws = [torch.randn(l.n, l.k, device=dev, dtype=torch.bfloat16, generator=g) * 0.02 for l in lins]
+
+    def run(_i=0):
+        for x, w in zip(xs, ws):
+            torch.matmul(x, w.t())
+
+    run()
+    ms = timed(run, iters, torch)
+    return sum(2 * m * l.n * l.k for l in lins) / (ms * 1e-3) / 1e12
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +221,13 @@ def main():
                 "flops_per_launch": gemm_flops // launches,
                 "linears": [st["lin"].name for st in big]}
     log(f"[bench] fused fwd GEMM {gemm_achieved:.1f} TFLOP/s, {avg_launch_ms*1e3:.1f} us/launch")
+    dense = library_dense_gemm(torch, dev, M, [st["lin"] for st in big], args.steps)
+    log(f"[bench] library dense bf16 GEMM, same shapes: {dense:.1f} TFLOP/s")
+    context = {"library_dense_bf16_gemm_TFLOPs": round(dense, 2),
+               "fused_vs_library_dense": round(gemm_achieved / dense, 4),
+               "what": "torch.matmul (hipBLASLt) on plain bf16 operands of the roofline kernel's "
+                       "shapes, no quantisation, timed the same way: the dense GEMM rate this GPU "
+                       "sustains at these shapes"}
 
     paths = {}
     dequant_gbps = None
@@ -224,6 +249,7 @@ def main():
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "dequant_GBps": dequant_gbps,
         "roofline": roofline,
+        "context": context,
         "cpu_baseline": cpu,
         "paths": paths,
     }

@@ -113,7 +113,9 @@ int qlora_linear_bwd(const nf4_weight *W, const uint16_t *x, const uint16_t *dy,
  * "QLoRA, explained", section "Compute and memory cost": when gradient checkpointing recomputes the
  * forward, the weight is dequantised a third time per layer and step; the adapter down-projection
  * saved by the first forward is reused rather than recomputed. For M > 16 this launches exactly one
- * kernel (the fused dequantise + MFMA GEMM); for M <= 16 it runs the skinny path and needs ws.
+ * kernel (the fused dequantise + MFMA GEMM); for M <= 16 it runs the skinny path (which forms u
+ * again from A) and needs ws, unless the weight holds 2^31 blocks of 64 or more, where the fused
+ * GEMM serves as well.
  *   u   [M x r] float32 input.  y [M x N] bf16 output.  ws as qlora_linear_fwd (may be NULL if M > 16).
  * Errors as qlora_linear_fwd. */
 int qlora_linear_fwd_recompute(const nf4_weight *W, const uint16_t *x, int64_t M, const uint16_t *A,
