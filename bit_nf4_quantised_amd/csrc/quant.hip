@@ -106,24 +106,32 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restri
 }
 
 // ------------------------------------------------------------------------------------------
-// Double quantisation. One wave per group of 256 scales, 4 per lane. c2 is the exact group
-// maximum; the code is the E4M3 value in [0, 1] nearest to the exact ratio c1 / c2 (ties to the
-// even code), found by binary search over the 56 midpoints with exact fp64 products.
-__device__ __forceinline__ double e4m3_mid(int j) {
-  return ((double)e4m3_decode(j) + (double)e4m3_decode(j + 1)) * 0.5;
-}
-
+// Double quantisation. One wave per group of 256 scales, 4 per lane; a wave walks groups with a
+// stride of the grid and has the next group's scales in flight while it encodes the current one.
+// c2 is the exact group maximum; the code is the E4M3 value in [0, 1] nearest to the exact ratio
+// c1 / c2, ties to the even code:
+//   x = fl32(c1 / c2) (correctly rounded) is within 2^-24 x of the ratio, far less than the gap
+//   between neighbouring E4M3 values, so truncating x to E4M3 gives the code just below the ratio
+//   or, when the ratio sits within that distance of an E4M3 value, that value's neighbour. Either
+//   way the nearest code is one of the truncation c and c + 1, and the exact test c1 > c2 * m
+//   against their midpoint m decides (exact in fp64: a 24-bit scale times a midpoint of at most 5
+//   significant bits), with equality going to the even code.
 __device__ __forceinline__ uint32_t e4m3_code_of_ratio(float c1, float c2) {
   if (c2 == 0.f) return 0;
-  const double a = c1, b = c2;
-  int lo = 0, hi = 56;  // count of midpoints strictly below c1 / c2
-  while (lo < hi) {
-    int mid = (lo + hi) >> 1;
-    if (a > b * e4m3_mid(mid)) lo = mid + 1;
-    else hi = mid;
+  const float x = __fdiv_rn(c1, c2);   // in [0, 1]
+  uint32_t c;
+  if (x < 0x1p-6f) {
+    c = (uint32_t)(x * 0x1p9f);          // subnormal codes m * 2^-9, m = 0..7 (exact scaling)
+  } else {
+    const uint32_t bits = __float_as_uint(x);
+    c = ((((bits >> 23) & 0xFFu) - 120u) << 3) | ((bits >> 20) & 7u);   // exponent field e + 7
   }
-  if (lo < 56 && (lo & 1) && a == b * e4m3_mid(lo)) ++lo;
-  return (uint32_t)lo;
+  if (c >= 0x38u) return 0x38u;          // 1.0, the largest value a ratio in [0, 1] can take
+  const double m = ((double)e4m3_decode(c) + (double)e4m3_decode(c + 1)) * 0.5;
+  const double a = c1, b = (double)c2 * m;
+  if (a > b) return c + 1;
+  if (a == b) return (c & 1u) ? c + 1 : c;
+  return c;
 }
 
 __global__ __launch_bounds__(256) void nf4_double_quant_kernel(const float* __restrict__ absmax,
@@ -131,25 +139,39 @@ __global__ __launch_bounds__(256) void nf4_double_quant_kernel(const float* __re
                                                                uint8_t* __restrict__ scale_q,
                                                                float* __restrict__ scale_c2) {
   const int lane = threadIdx.x & 63;
-  const int64_t g = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t gw = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
   const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
-  if (g >= ngroups) return;
-  const int64_t first = g * kGroup + lane * 4;
-  float c[4];
+  const int64_t full = nblocks / kGroup;   // groups without a ragged end
+  // full groups: branch-free 16-byte loads, the next group's in flight
+  auto load = [&](int64_t g) {
+    return *reinterpret_cast<const f32x4*>(absmax + g * kGroup + lane * 4);
+  };
+  int64_t g = gw;
+  if (g < full) {
+    f32x4 cur = load(g);
+    for (; g < full; g += nw) {
+      const f32x4 nxt = load(min(g + nw, full - 1));
+      const float c2 = wave_max(fmaxf(fmaxf(cur[0], cur[1]), fmaxf(cur[2], cur[3])));
+      uint32_t word = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) c[i] = (first + i < nblocks) ? absmax[first + i] : 0.f;
-  const float c2 = wave_max(fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])));
-  uint32_t code[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) code[i] = e4m3_code_of_ratio(c[i], c2);
-  if (first + 3 < nblocks) {
-    *reinterpret_cast<uint32_t*>(scale_q + first) =
-        code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-  } else {
-    for (int i = 0; i < 4; ++i)
-      if (first + i < nblocks) scale_q[first + i] = (uint8_t)code[i];
+      for (int i = 0; i < 4; ++i) word |= e4m3_code_of_ratio(cur[i], c2) << (8 * i);
+      *reinterpret_cast<uint32_t*>(scale_q + g * kGroup + lane * 4) = word;
+      if (lane == 0) scale_c2[g] = c2;
+      cur = nxt;
+    }
   }
-  if (lane == 0) scale_c2[g] = c2;
+  // the ragged last group, if any, by the wave whose turn it is
+  if (full < ngroups && gw == full % nw) {
+    const int64_t first = full * kGroup + lane * 4;
+    float c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = (first + i < nblocks) ? absmax[first + i] : 0.f;
+    const float c2 = wave_max(fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])));
+    for (int i = 0; i < 4; ++i)
+      if (first + i < nblocks) scale_q[first + i] = (uint8_t)e4m3_code_of_ratio(c[i], c2);
+    if (lane == 0) scale_c2[full] = c2;
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -245,7 +267,7 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, uint8_t* sc
                                float* scale_c2, hipStream_t stream) {
   if (nblocks == 0) return hipSuccess;
   const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
-  const int grid = (int)((ngroups + 3) / 4);
+  const int grid = grid_for(ngroups, 4, 256 * 8);   // 4 waves per workgroup, one group each
   hipLaunchKernelGGL(nf4_double_quant_kernel, dim3(grid), dim3(256), 0, stream, absmax, nblocks,
                      scale_q, scale_c2);
   return hipGetLastError();
