@@ -2,10 +2,10 @@
 
 A plain, slow, obviously correct reference of what the hot path computes, written from the pages'
 statement of the method (chiefly "QLoRA, explained": the sections on blockwise absmax quantisation,
-NormalFloat 4, double quantisation and the forward pass and gradients, plus its worked example and
-toy run). Floating point is float64 unless a step fixes a narrower type (the fp32 codebook, fp32
-scales, the bf16 dequantised weight), and the integer decisions (nearest code, nearest 8-bit float)
-are taken in exact arithmetic.
+NormalFloat 4, double quantisation, the forward pass and gradients and the quality loss at merge
+time, plus its worked example and toy run). Floating point is float64 unless a step fixes a
+narrower type (the fp32 codebook, fp32 scales, the bf16 dequantised weight), and the integer
+decisions (nearest code, nearest 8-bit float) are taken in exact arithmetic.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may import
 this package. It shares no code, header, table or constant with the HIP path
@@ -19,12 +19,13 @@ from .nf4 import (NF4_ZERO_INDEX, codebook, quantize_blocks, pack_nibbles, unpac
                   quantize, e4m3_value, e4m3_unit_values, double_quant, dequant_scales,
                   bf16_bits_from_f32, f32_from_bf16_bits, dequant, storage_bits)
 from .linear import linear_fwd, linear_bwd, linear_fwd_f64, linear_bwd_f64, linear_bwd_sampled
+from .merge import bf16_bits_from_f64, merge
 from .toy import int4_codebook, fp4_codebook, relative_mse, residual_capture
 
 __all__ = [
     "NF4_ZERO_INDEX", "codebook", "quantize_blocks", "pack_nibbles", "unpack_nibbles", "quantize",
     "e4m3_value", "e4m3_unit_values", "double_quant", "dequant_scales", "bf16_bits_from_f32",
     "f32_from_bf16_bits", "dequant", "storage_bits", "linear_fwd", "linear_bwd", "linear_fwd_f64",
-    "linear_bwd_f64", "linear_bwd_sampled", "int4_codebook",
+    "linear_bwd_f64", "linear_bwd_sampled", "bf16_bits_from_f64", "merge", "int4_codebook",
     "fp4_codebook", "relative_mse", "residual_capture",
 ]
