@@ -10,8 +10,9 @@ The same run also measures, each in its own timed loop:
   * the fused forward GEMM kernel alone (one launch per call through the forward-recompute entry),
     for the roofline against the bf16 dense MFMA peak;
   * quantise, double quantise and dequantise over 136 matrices of 4096 x 14336 (7.99e9 weights)
-    drawn from a pool of 8 distinct matrices, and the skinny forward of an 8192 x 28672 weight at
-    1, 4 and 16 tokens with 4 rotating weight copies, in HBM GB/s against 8 TB/s;
+    drawn from a pool of 8 distinct matrices, the skinny forward of an 8192 x 28672 weight at
+    1, 4 and 16 tokens with 4 rotating weight copies, and the adapter merge into that weight, in
+    HBM GB/s against 8 TB/s;
   * the CPU oracle on a bounded sample of the same workload (cpu_baseline).
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -329,6 +330,23 @@ def bandwidth_paths(torch, q, dev, args):
                             "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "bytes": nbytes}
         log(f"[bench] skinny M={m}: {ms*1e3:.1f} us, {gbps:.0f} GB/s")
     res["skinny_fwd_8192x28672"] = skinny
+
+    # adapter merge into the dequantised base, same weight (4 rotating copies), rank 16
+    _, _, a, b, _ = wl.linear_inputs(sk, 0, lin, m=1)
+    A = torch.from_numpy(a.view(np.int16)).to(dev)
+    B = torch.from_numpy(b.view(np.int16)).to(dev)
+    merged = torch.empty(lin.n * lin.k, dtype=torch.int16, device=dev)
+
+    def merge_call(i):
+        q.qlora_merge(copies[i % len(copies)], A, B, sk.scale, merged)
+
+    merge_call(0)
+    ms = timed(merge_call, 50, torch)
+    nbytes = nf4_bytes(lin.n * lin.k) + 2 * lin.n * lin.k + 2 * sk.r * lin.k + 2 * lin.n * sk.r
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    res["merge_8192x28672_r16"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                                   "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "bytes": nbytes}
+    log(f"[bench] merge: {ms*1e3:.1f} us, {gbps:.0f} GB/s")
     return res, dequant_gbps
 
 

@@ -49,6 +49,7 @@ _SIGS = {
                                         ctypes.c_int, _p, _sz, _p]),
     "qlora_linear_fwd_recompute": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz,
                                                   _p]),
+    "qlora_merge": (ctypes.c_int, [_W, _p, _p, _i32, _f32, _p, _p]),
     "qlora_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "nf4_storage_bytes": (_i64, [_i64]),
     "nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
@@ -154,6 +155,18 @@ def qlora_linear_fwd(weight: NF4Weight, x, A, B, scale: float, y, u_out=None, ws
     _check(lib.qlora_linear_fwd(ctypes.byref(cw), _ptr(x), M, _ptr(A), _ptr(B), r, scale, _ptr(y),
                                 _ptr(u_out), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "qlora_linear_fwd")
+
+
+def qlora_merge(weight: NF4Weight, A, B, scale: float, out, stream=None) -> None:
+    """Adapter merged into the dequantised base: out = bf16(W~ + s B A), [N x K]."""
+    for t in (A, B, out):
+        _dtype(t, *_BF16)
+    r = A.shape[0]
+    if A.shape != (r, weight.K) or B.shape != (weight.N, r) or out.numel() != weight.N * weight.K:
+        raise ValueError("shape mismatch")
+    cw = weight.c_struct()
+    _check(lib.qlora_merge(ctypes.byref(cw), _ptr(A), _ptr(B), r, scale, _ptr(out), _stream(stream)),
+           "qlora_merge")
 
 
 def qlora_linear_fwd_recompute(weight: NF4Weight, x, A, B, scale: float, u, y, ws=None,

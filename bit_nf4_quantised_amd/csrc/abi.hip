@@ -92,6 +92,17 @@ int nf4_dequant(const nf4_weight* W, uint16_t* out, hipStream_t stream) {
   return from_hip(nf4::launch_dequant(W->packed, W->scale_q, W->scale_c2, W->N * W->K, out, stream));
 }
 
+int qlora_merge(const nf4_weight* W, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                uint16_t* out, hipStream_t stream) {
+  int st = check_weight(W);
+  if (st) return st;
+  if ((st = check_rank(r))) return st;
+  if (!A || !B || !out) return NF4_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(out)) return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_merge(W->packed, W->scale_q, W->scale_c2, W->N, W->K, A, B, r, scale,
+                                    out, stream));
+}
+
 size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M < 0 || N < 16 || K < 64 || N % 16 || K % 64 || check_rank(r)) return 0;
   if (M == 0) return 0;

@@ -54,4 +54,9 @@ hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, cons
                              const uint16_t* B, int r, float scale, float* part, float* u_out,
                              uint16_t* y, hipStream_t stream);
 
+// Adapter merged into the dequantised base: out = bf16(W~ + s B A), [N x K].
+hipError_t launch_merge(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2, int64_t N,
+                        int64_t K, const uint16_t* A, const uint16_t* B, int r, float scale, uint16_t* out,
+                        hipStream_t stream);
+
 }  // namespace nf4

@@ -12,6 +12,8 @@
  *   qlora_linear_fwd  section "The algorithm, step by step": y = x W~^T + s x A^T B^T.
  *   qlora_linear_bwd  section "The forward pass and gradients": dX = dY (W~ + s B A),
  *                     dA = s B^T G, dB = s G A^T with G = dY^T X; W gets no gradient.
+ *   qlora_merge       section "Quality loss at merge time": the adapter merged into the
+ *                     dequantised base, W~ + s B A, served in bf16.
  *
  * Data formats (all little-endian, row-major):
  *   W        N x K (out x in, like nn.Linear), K % 64 == 0, N % 16 == 0. Blocks of 64 run along K.
@@ -121,6 +123,17 @@ int qlora_linear_bwd(const nf4_weight *W, const uint16_t *x, const uint16_t *dy,
 int qlora_linear_fwd_recompute(const nf4_weight *W, const uint16_t *x, int64_t M, const uint16_t *A,
                                const uint16_t *B, int32_t r, float scale, const float *u, uint16_t *y,
                                void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Adapter merged into the dequantised base weight, in bf16:
+ *   out = bf16_rne(fl32(W~ + fl32(s * (B A))))      [N x K] bf16 output (uint16 bit patterns),
+ * W~ exactly as nf4_dequant produces it, B A accumulated in fp32 from the exact bf16 products.
+ * "QLoRA, explained", section "Quality loss at merge time": the adapter was trained against W~,
+ * so merging into W~ (not into the original weight) keeps the trained model; the result is served
+ * in bf16 (re-quantising it, with nf4_quantize, adds a second rounding to the update).
+ *   A [r x K] bf16;  B [N x r] bf16;  scale = s.
+ * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_RANK, NF4_ERR_HIP. */
+int qlora_merge(const nf4_weight *W, const uint16_t *A, const uint16_t *B, int32_t r, float scale,
+                uint16_t *out, hipStream_t stream);
 
 /* Workspace bytes that qlora_linear_fwd and qlora_linear_bwd need for these sizes (the larger of
  * the two). Returns 0 for invalid sizes. */

@@ -89,6 +89,19 @@ def test_dequant_validation():
     assert lib.nf4_dequant(ctypes.byref(_w()), None, None) == q.NF4_ERR_NULL
 
 
+def test_merge_validation():
+    w = ctypes.byref(_w())
+    assert lib.qlora_merge(None, FAKE, FAKE, 16, 2.0, FAKE, None) == q.NF4_ERR_NULL
+    assert lib.qlora_merge(ctypes.byref(_w(K=4000)), FAKE, FAKE, 16, 2.0, FAKE, None) == q.NF4_ERR_SHAPE
+    assert lib.qlora_merge(w, FAKE, FAKE, 8, 2.0, FAKE, None) == q.NF4_ERR_RANK
+    assert lib.qlora_merge(w, FAKE, FAKE, 144, 2.0, FAKE, None) == q.NF4_ERR_RANK
+    assert lib.qlora_merge(w, None, FAKE, 16, 2.0, FAKE, None) == q.NF4_ERR_NULL
+    assert lib.qlora_merge(w, FAKE, None, 16, 2.0, FAKE, None) == q.NF4_ERR_NULL
+    assert lib.qlora_merge(w, FAKE, FAKE, 16, 2.0, None, None) == q.NF4_ERR_NULL
+    assert lib.qlora_merge(w, MISALIGNED, FAKE, 16, 2.0, FAKE, None) == q.NF4_ERR_ALIGN
+    assert lib.qlora_merge(w, FAKE, FAKE, 16, 2.0, MISALIGNED, None) == q.NF4_ERR_ALIGN
+
+
 def test_fwd_validation():
     w = ctypes.byref(_w())
     ws = q.qlora_workspace_bytes(64, 4096, 4096, 16)
