@@ -31,8 +31,8 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 //   forward : [u (M*r fp32)] [partials: skinny splits or the adapter pass over X]
 //   backward: [v (M*r fp32)] [partials of the pass over dY, then of the pass over X]
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
-  size_t part = nf4::skinny_eligible(M, N, K) ? nf4::skinny_workspace_floats(M, N, K, r)
-                                        : nf4::lora_pass_ws_floats(M, K, r, true, false);
+  // the forward's u needs no partial sums outside the skinny path
+  size_t part = nf4::skinny_eligible(M, N, K) ? nf4::skinny_workspace_floats(M, N, K, r) : 0;
   return align_up((size_t)M * r * 4) + align_up(part * 4);
 }
 size_t bwd_ws(int64_t M, int64_t N, int64_t K, int r) {

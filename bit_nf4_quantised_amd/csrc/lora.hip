@@ -362,12 +362,80 @@ static void launch_reduce(const ReduceJob& j0, const ReduceJob* j1, hipStream_t 
   hipLaunchKernelGGL(lora_reduce_kernel, dim3((unsigned)(b0 + b1)), dim3(256), 0, stream, j0, j1 ? *j1 : j0, b0);
 }
 
+// ------------------------------------------------------------------------------------------
+// u = X A^T in one launch, without partial sums in memory (its contraction runs over K only, so
+// a workgroup can own whole rows): a workgroup owns 16 rows of X and all of K. Its 8 waves take
+// interleaved 32-column chunks (wave w: chunks w, w + 8, ...), NB chunks at a time with every
+// load of a batch issued before its MFMAs; lane (row = lane % 16, g = lane / 16) holds columns
+// 8 g .. 8 g + 7 of the chunk of its row of X and of row 16 t + lane % 16 of A for each 16-row
+// tile t of A, and v_mfma_f32_16x16x32_bf16 accumulates u[row][16 t + j]. The workgroup then sums
+// the 8 waves in LDS in wave order.
+constexpr int kUWaves = 8;
+
+template <int NT>   // r / 16
+__global__ __launch_bounds__(kUWaves * 64) void lora_u_kernel(const uint16_t* __restrict__ X, int64_t M,
+                                                            int64_t K, const uint16_t* __restrict__ A,
+                                                            float* __restrict__ u) {
+  constexpr int NB = NT >= 8 ? 1 : 8 / NT;   // chunks per batch
+  constexpr int r = 16 * NT;
+  __shared__ f32x4 red[kUWaves][NT][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const uint16_t* xrow = X + min(m0 + (lane & 15), M - 1) * K + 8 * g;
+  const uint16_t* arow = A + (int64_t)(lane & 15) * K + 8 * g;
+  const int64_t nchunks = K / 32;
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t c0 = wave; c0 < nchunks; c0 += (int64_t)kUWaves * NB) {
+    bf16x8 xv[NB], av[NB][NT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      // chunks past the end re-read the last one and are not accumulated
+      const int64_t col = min(c0 + (int64_t)kUWaves * b, nchunks - 1) * 32;
+      xv[b] = *reinterpret_cast<const bf16x8*>(xrow + col);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) av[b][t] = *reinterpret_cast<const bf16x8*>(arow + (int64_t)t * 16 * K + col);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (c0 + (int64_t)kUWaves * b < nchunks) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[b], av[b][t], acc[t], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  // output o = (row, j): acc[t][i] of lane (row / 4) * 16 + j % 16 holds row 4 (lane / 16) + i
+  for (int o = tid; o < 16 * r; o += kUWaves * 64) {
+    const int row = o / r, j = o % r;
+    const int t = j >> 4, ln = (row >> 2) * 16 + (j & 15), i = row & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kUWaves; ++w) v += red[w][t][ln][i];
+    if (m0 + row < M) u[(m0 + row) * r + j] = v;
+  }
+}
+
 hipError_t launch_lora_u(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int r,
                          float* ws, float* u, hipStream_t stream) {
-  const LoraPassPlan p = lora_pass_plan(M, K, r);
-  LoraPassArgs a{X, M, K, A, nullptr, r, p.crange, ws, nullptr};
-  launch_pass<true, false, false>(p, a, stream);
-  launch_reduce(reduce_job(ws, p.cranges, M * r, 0, r, false, 1.f, 0, u), nullptr, stream);
+  (void)ws;
+  const dim3 grid((unsigned)((M + 15) / 16)), block(kUWaves * 64);
+  switch (r / 16) {
+    case 1: hipLaunchKernelGGL(lora_u_kernel<1>, grid, block, 0, stream, X, M, K, A, u); break;
+    case 2: hipLaunchKernelGGL(lora_u_kernel<2>, grid, block, 0, stream, X, M, K, A, u); break;
+    case 3: hipLaunchKernelGGL(lora_u_kernel<3>, grid, block, 0, stream, X, M, K, A, u); break;
+    case 4: hipLaunchKernelGGL(lora_u_kernel<4>, grid, block, 0, stream, X, M, K, A, u); break;
+    case 5: hipLaunchKernelGGL(lora_u_kernel<5>, grid, block, 0, stream, X, M, K, A, u); break;
+    case 6: hipLaunchKernelGGL(lora_u_kernel<6>, grid, block, 0, stream, X, M, K, A, u); break;
+    case 7: hipLaunchKernelGGL(lora_u_kernel<7>, grid, block, 0, stream, X, M, K, A, u); break;
+    default: hipLaunchKernelGGL(lora_u_kernel<8>, grid, block, 0, stream, X, M, K, A, u); break;
+  }
   return hipGetLastError();
 }
 
