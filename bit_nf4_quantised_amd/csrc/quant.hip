@@ -175,13 +175,14 @@ __global__ __launch_bounds__(256) void nf4_double_quant_kernel(const float* __re
 }
 
 // ------------------------------------------------------------------------------------------
-// Dequantise. A wave takes 64 consecutive blocks per iteration, lane l block l: it loads the 32
-// packed bytes, builds the block's 16-entry bf16 table and expands its 8 dwords into 8 pieces of
-// 8 bf16 (16 bytes each, 128 bytes per lane). The pieces go through a wave-private LDS region so
-// that every store instruction writes 1 KB of contiguous output (lane l: bytes 16 l + 1024 i of
-// the wave's 8 KB); piece j of lane l sits at slot 8 l + (j ^ (l % 8)), which keeps both the
-// writes and the reads of 8 consecutive lanes on distinct banks. The packed bytes and scales of
-// the next iteration are loaded before the current one is expanded.
+// Dequantise. A wave takes 64 consecutive blocks, lane l block l: it loads the 32 packed bytes,
+// builds the block's 16-entry bf16 table and expands its 8 dwords into 8 pieces of 8 bf16 (16 bytes
+// each, 128 bytes per lane). The pieces go through a wave-private LDS region so that every store
+// instruction writes 1 KB of contiguous output (lane l: bytes 16 l + 1024 i of the wave's 8 KB);
+// piece j of lane l sits at slot 8 l + (j ^ (l % 8)), which keeps both the writes and the reads of
+// 8 consecutive lanes on distinct banks. Every wave handles exactly one group of 64 blocks: with a
+// capped, persistent grid the group count rarely divides evenly, and the waves that take one
+// more group than the rest set the kernel's duration.
 constexpr int kDqWaves = 4;
 
 __global__ __launch_bounds__(kDqWaves * 64) void nf4_dequant_kernel(const uint8_t* __restrict__ packed,
@@ -191,56 +192,39 @@ __global__ __launch_bounds__(kDqWaves * 64) void nf4_dequant_kernel(const uint8_
   __shared__ __attribute__((aligned(16))) u32x4 stage[kDqWaves][64 * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   u32x4* st = stage[wave];
-  const int64_t gw = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const int64_t grp = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t groups = (nblocks + 63) / 64;
-
-  struct In {
-    u32x4 p0, p1;
-    uint32_t code;
-    float c2;
-  };
-  // branch-free loads: blocks past the end re-read the last block (never stored)
-  auto load = [&](int64_t grp) {
-    const int64_t b = min(grp * 64 + lane, nblocks - 1);
-    const u32x4* src = reinterpret_cast<const u32x4*>(packed + b * 32);
-    In in;
-    in.p0 = __builtin_nontemporal_load(src);
-    in.p1 = __builtin_nontemporal_load(src + 1);
-    in.code = scale_q[b];
-    in.c2 = scale_c2[b / kGroup];
-    return in;
-  };
-
-  int64_t grp = gw;
   if (grp >= groups) return;
-  In cur = load(grp);
-  for (; grp < groups; grp += nw) {
-    const In nxt = load(min(grp + nw, groups - 1));
-    const BlockLut t = make_lut(__fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)cur.code, 0), cur.c2));
+
+  // branch-free loads: blocks past the end re-read the last block
+  const int64_t b = min(grp * 64 + lane, nblocks - 1);
+  const u32x4* src = reinterpret_cast<const u32x4*>(packed + b * 32);
+  const u32x4 p0 = __builtin_nontemporal_load(src);
+  const u32x4 p1 = __builtin_nontemporal_load(src + 1);
+  const uint32_t code = scale_q[b];
+  const float c2 = scale_c2[b / kGroup];
+
+  const BlockLut t = make_lut(__fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)code, 0), c2));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t d[4];
-      dequant8(t, j < 4 ? cur.p0[j] : cur.p1[j - 4], d);
-      st[lane * 8 + (j ^ (lane & 7))] = u32x4{d[0], d[1], d[2], d[3]};
-    }
-    // read back and store coalesced: instruction i covers output bytes 1024 i .. +1023 of the
-    // group, i.e. piece lane % 8 of block 8 i + lane / 8. Slots of blocks past the end hold the
-    // last block's values (its packed bytes were re-read), so storing them over the last block
-    // writes identical bytes and every store stays unconditional (a store that some lanes skip
-    // would make the compiler wait for all stores before the next loads are used).
-    u32x4 v[8];
+  for (int j = 0; j < 8; ++j) {
+    uint32_t d[4];
+    dequant8(t, j < 4 ? p0[j] : p1[j - 4], d);
+    st[lane * 8 + (j ^ (lane & 7))] = u32x4{d[0], d[1], d[2], d[3]};
+  }
+  // read back and store coalesced: instruction i covers output bytes 1024 i .. +1023 of the
+  // group, i.e. piece lane % 8 of block 8 i + lane / 8. Slots of blocks past the end hold the
+  // last block's values (its packed bytes were re-read), so storing them over the last block
+  // writes identical bytes and every store stays unconditional.
+  u32x4 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int lb = 8 * i + (lane >> 3), pj = lane & 7;
-      v[i] = st[lb * 8 + (pj ^ (lb & 7))];
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int lb = 8 * i + (lane >> 3), pj = lane & 7;
+    v[i] = st[lb * 8 + (pj ^ (lb & 7))];
+  }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t b = min(grp * 64 + 8 * i + (lane >> 3), nblocks - 1);
-      __builtin_nontemporal_store(v[i], out + b * 8 + (lane & 7));
-    }
-    cur = nxt;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t bo = min(grp * 64 + 8 * i + (lane >> 3), nblocks - 1);
+    __builtin_nontemporal_store(v[i], out + bo * 8 + (lane & 7));
   }
 }
 
@@ -277,8 +261,8 @@ hipError_t launch_dequant(const uint8_t* packed, const uint8_t* scale_q, const f
                           int64_t numel, uint16_t* out, hipStream_t stream) {
   const int64_t nblocks = numel / kBlock;
   if (nblocks == 0) return hipSuccess;
-  const int64_t groups = (nblocks + 63) / 64;      // one wave iteration per 64 blocks
-  const int grid = grid_for(groups, kDqWaves, 256 * 8);
+  const int64_t groups = (nblocks + 63) / 64;      // one wave per 64 blocks
+  const int grid = (int)((groups + kDqWaves - 1) / kDqWaves);
   hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid), dim3(kDqWaves * 64), 0, stream, packed, scale_q,
                      scale_c2, nblocks, reinterpret_cast<u32x4*>(out));
   return hipGetLastError();
