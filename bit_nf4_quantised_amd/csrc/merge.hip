@@ -41,19 +41,24 @@ struct MergeArgs {
   uint16_t* out;        // [N x K] bf16
 };
 
+template <int NT>   // r / 16: the A strip holds exactly r rows, so small ranks leave room for more
+                    // workgroups per CU
 __global__ __launch_bounds__(256) void qlora_merge_kernel(const MergeArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t at[kMgCols * 128];      // A strip, [column][j]
+  // A strip, [column][j], columns padded to r + 4 values so that the 16 columns of an MFMA
+  // fragment read fall on distinct banks
+  constexpr int AP = 16 * NT + 4;
+  __shared__ __attribute__((aligned(16))) uint16_t at[kMgCols * AP];
   __shared__ __attribute__((aligned(16))) float ut[kMgRows * kMgPitch];    // s B A of one tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int strip = blockIdx.x / g.row_chunks, chunk = blockIdx.x % g.row_chunks;
   const int64_t k0 = (int64_t)strip * kMgCols;
   const int cols = (int)min((int64_t)kMgCols, g.K - k0);   // 128, or 64 for a last half strip
-  const int r = g.r;
+  constexpr int r = 16 * NT;
 
   // ---- A strip, transposed into LDS (columns past K as zeros)
   for (int idx = tid; idx < r * kMgCols; idx += 256) {
     const int j = idx / kMgCols, c = idx % kMgCols;
-    at[c * r + j] = c < cols ? g.A[(int64_t)j * g.K + k0 + c] : (uint16_t)0;
+    at[c * AP + j] = c < cols ? g.A[(int64_t)j * g.K + k0 + c] : (uint16_t)0;
   }
   __syncthreads();
 
@@ -76,7 +81,7 @@ __global__ __launch_bounds__(256) void qlora_merge_kernel(const MergeArgs g) {
       const s16x4 bf = *reinterpret_cast<const s16x4*>(g.B + (n0 + (lane & 15)) * r + jj);
 #pragma unroll
       for (int ct = 0; ct < kMgCols / 16; ++ct) {
-        const s16x4 af = *reinterpret_cast<const s16x4*>(at + (ct * 16 + (lane & 15)) * r + jj);
+        const s16x4 af = *reinterpret_cast<const s16x4*>(at + (ct * 16 + (lane & 15)) * AP + jj);
         acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bf, af, acc[ct], 0, 0, 0);
       }
     }
@@ -126,7 +131,17 @@ hipError_t launch_merge(const uint8_t* packed, const uint8_t* scale_q, const flo
   if (chunks > tiles) chunks = tiles;
   if (chunks < 1) chunks = 1;
   MergeArgs g{packed, scale_q, scale_c2, N, K, A, B, r, scale, (int)chunks, out};
-  hipLaunchKernelGGL(qlora_merge_kernel, dim3((unsigned)(strips * chunks)), dim3(256), 0, stream, g);
+  const dim3 grid((unsigned)(strips * chunks)), block(256);
+  switch (r / 16) {
+    case 1: hipLaunchKernelGGL(qlora_merge_kernel<1>, grid, block, 0, stream, g); break;
+    case 2: hipLaunchKernelGGL(qlora_merge_kernel<2>, grid, block, 0, stream, g); break;
+    case 3: hipLaunchKernelGGL(qlora_merge_kernel<3>, grid, block, 0, stream, g); break;
+    case 4: hipLaunchKernelGGL(qlora_merge_kernel<4>, grid, block, 0, stream, g); break;
+    case 5: hipLaunchKernelGGL(qlora_merge_kernel<5>, grid, block, 0, stream, g); break;
+    case 6: hipLaunchKernelGGL(qlora_merge_kernel<6>, grid, block, 0, stream, g); break;
+    case 7: hipLaunchKernelGGL(qlora_merge_kernel<7>, grid, block, 0, stream, g); break;
+    default: hipLaunchKernelGGL(qlora_merge_kernel<8>, grid, block, 0, stream, g); break;
+  }
   return hipGetLastError();
 }
 
