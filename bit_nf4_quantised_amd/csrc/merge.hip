@@ -10,13 +10,16 @@
 // tiles. The strip of A is staged once in LDS, transposed ([column][j]), so that an MFMA operand
 // fragment (4 consecutive j of one column) is one 8-byte read. Per tile, wave w takes rows
 // 16 w .. 16 w + 15:
-//   * v_mfma_f32_16x16x16_bf16 forms the 16 x 128 block of B A (operand lanes: row or column
-//     lane % 16, j = 4 (lane / 16) .. +3; result lanes: column lane % 16, rows 4 (lane / 16) + i),
-//     and s times it is written to the wave's rows of an LDS tile;
+//   * v_mfma_f32_16x16x16_bf16 forms the 16 x 128 block of B A with the A strip as the row side
+//     and B as the column side (operand lanes: row or column lane % 16, j = 4 (lane / 16) .. +3;
+//     result lanes: column lane % 16, rows 4 (lane / 16) + i), so a lane holds four consecutive
+//     columns of one row of B A, and s times it is written to the wave's rows of an LDS tile with
+//     16-byte writes;
 //   * lane l then takes row l / 4 of those 16 and the 32 columns 32 (l % 4) .. +31 (half a block):
 //     it dequantises them with the block's bf16 table, adds the update read back from LDS and
 //     stores 64 contiguous bytes (the four lanes of a row write the strip's 256 bytes).
 // Only the wave's own rows pass through its LDS rows, so no workgroup barrier is needed per tile.
+// The next tile's packed bytes, scales and B fragments are loaded while a tile is processed.
 #include "common.h"
 #include "launch.h"
 
@@ -68,58 +71,98 @@ __global__ __launch_bounds__(256) void qlora_merge_kernel(const MergeArgs g) {
   const int64_t kb = g.K / kBlock;
   float* urow = ut + (16 * wave) * kMgPitch;   // this wave's 16 rows of the update tile
 
-  for (int64_t t = t_begin; t < t_end; ++t) {
-    const int64_t n0 = t * kMgRows + 16 * wave;   // this wave's first row
-    if (n0 >= g.N) continue;                      // rows come in multiples of 16
-
+  // Lane l dequantises row l / 4 of the wave's 16 and columns 32 q .. +31, q = l % 4; in a last
+  // half strip the lanes past it redo their neighbour's columns, and a wave whose rows lie past N
+  // (rows come in 16s) redoes the last 16 rows, so that every load and store is unconditional
+  // (they write identical bytes).
+  const int rl = lane >> 2, q = lane & 3;
+  const int64_t col = k0 + 32 * (32 * q < cols ? q : q - 2);
+  auto first_row = [&](int64_t t) { return min(t * kMgRows + 16 * wave, g.N - 16); };
+  // A tile's inputs for this lane, loaded one tile ahead into one of two register slots (raw
+  // loaded values only, so issuing the loads never waits for them): the B fragments of the MFMA
+  // (row first + lane % 16, j = 16 s + 4 (lane / 16) ..), the 16 packed bytes, the aligned word
+  // holding the block's scale code (in range: the block count is a multiple of 16) and the
+  // block's second-level constant.
+  struct TileIn {
+    s16x4 bf[NT];
+    u32x4 p;
+    uint32_t cw;
+    float c2;
+  };
+  auto load_tile = [&](int64_t t, TileIn& in) {
+    const int64_t n0 = first_row(t);
+#pragma unroll
+    for (int s = 0; s < NT; ++s)
+      in.bf[s] = *reinterpret_cast<const s16x4*>(g.B + (n0 + (lane & 15)) * r + 16 * s + 4 * (lane >> 4));
+    const int64_t n = n0 + rl;
+    const int64_t b = n * kb + col / kBlock;
+    in.p = *reinterpret_cast<const u32x4*>(g.packed + (n * g.K + col) / 2);
+    in.cw = *reinterpret_cast<const uint32_t*>(g.scale_q + (b & ~int64_t(3)));
+    in.c2 = g.scale_c2[b / kGroup];
+  };
+  auto process = [&](int64_t t, const TileIn& in) {
+    const int64_t n0 = first_row(t);
     // ---- s B A for rows n0 .. n0 + 15, all 128 columns
     f32x4 acc[kMgCols / 16];
 #pragma unroll
     for (int ct = 0; ct < kMgCols / 16; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < r; j0 += 16) {
-      const int jj = j0 + 4 * (lane >> 4);
-      const s16x4 bf = *reinterpret_cast<const s16x4*>(g.B + (n0 + (lane & 15)) * r + jj);
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+      const int jj = 16 * s + 4 * (lane >> 4);
 #pragma unroll
       for (int ct = 0; ct < kMgCols / 16; ++ct) {
         const s16x4 af = *reinterpret_cast<const s16x4*>(at + (ct * 16 + (lane & 15)) * AP + jj);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bf, af, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(af, in.bf[s], acc[ct], 0, 0, 0);
       }
     }
+    // acc[ct][i] = (B A)[row lane % 16][column 16 ct + 4 (lane / 16) + i]: four consecutive columns
 #pragma unroll
     for (int ct = 0; ct < kMgCols / 16; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        urow[(4 * (lane >> 4) + i) * kMgPitch + ct * 16 + (lane & 15)] = __fmul_rn(g.scale, acc[ct][i]);
+      *reinterpret_cast<f32x4*>(urow + (lane & 15) * kMgPitch + ct * 16 + 4 * (lane >> 4)) =
+          f32x4{__fmul_rn(g.scale, acc[ct][0]), __fmul_rn(g.scale, acc[ct][1]), __fmul_rn(g.scale, acc[ct][2]),
+                __fmul_rn(g.scale, acc[ct][3])};
 
-    // ---- dequantise, add, round, store: row n0 + lane / 4, columns 32 (lane % 4) .. +31
-    const int rl = lane >> 2, q = lane & 3;
+    // ---- dequantise, add, round, store
     const int64_t n = n0 + rl;
-    if (32 * q < cols) {
-      const int64_t col = k0 + 32 * q;
-      const int64_t b = n * kb + col / kBlock;
-      const u32x4 p = *reinterpret_cast<const u32x4*>(g.packed + (n * g.K + col) / 2);
-      const BlockLut lut = make_lut(block_scale(g.scale_q, g.scale_c2, b));
-      const float* u = urow + rl * kMgPitch + 32 * q;
-      u32x4 o[4];
+    const int64_t b = n * kb + col / kBlock;
+    const uint32_t code = in.cw >> ((uint32_t)(b & 3) * 8u);   // e4m3_decode reads bits 0 .. 6
+    const BlockLut lut = make_lut(__fmul_rn(e4m3_decode(code), in.c2));
+    const float* u = urow + rl * kMgPitch + (col - k0);
+    u32x4 o[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t d[4];
-        dequant8(lut, p[i], d);   // values 8 i .. 8 i + 7 as 4 bf16 pairs
-        const f32x4 u0 = *reinterpret_cast<const f32x4*>(u + 8 * i);
-        const f32x4 u1 = *reinterpret_cast<const f32x4*>(u + 8 * i + 4);
-        const float uu[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+    for (int i = 0; i < 4; ++i) {
+      uint32_t d[4];
+      dequant8(lut, in.p[i], d);   // values 8 i .. 8 i + 7 as 4 bf16 pairs
+      const f32x4 u0 = *reinterpret_cast<const f32x4*>(u + 8 * i);
+      const f32x4 u1 = *reinterpret_cast<const f32x4*>(u + 8 * i + 4);
+      const float uu[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(d[e] << 16), hi = __uint_as_float(d[e] & 0xFFFF0000u);
-          d[e] = pack_bf16x2(__fadd_rn(lo, uu[2 * e]), __fadd_rn(hi, uu[2 * e + 1]));
-        }
-        o[i] = u32x4{d[0], d[1], d[2], d[3]};
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(d[e] << 16), hi = __uint_as_float(d[e] & 0xFFFF0000u);
+        d[e] = pack_bf16x2(__fadd_rn(lo, uu[2 * e]), __fadd_rn(hi, uu[2 * e + 1]));
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(g.out + n * g.K + col);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = o[i];
+      o[i] = u32x4{d[0], d[1], d[2], d[3]};
     }
+    u32x4* dst = reinterpret_cast<u32x4*>(g.out + n * g.K + col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = o[i];
+  };
+
+  // tiles in pairs, so that each slot stays one register set; the next tile's loads go out
+  // before the current tile's arithmetic (past the range they re-read the last tile)
+  if (t_begin >= t_end) return;
+  TileIn s0, s1;
+  load_tile(t_begin, s0);
+  int64_t t = t_begin;
+  for (; t + 1 < t_end; t += 2) {
+    load_tile(t + 1, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    process(t, s0);
+    load_tile(min(t + 2, t_end - 1), s0);
+    __builtin_amdgcn_sched_barrier(0);
+    process(t + 1, s1);
   }
+  if (t < t_end) process(t, s0);
 }
 
 hipError_t launch_merge(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2, int64_t N,
