@@ -84,7 +84,8 @@ __device__ __forceinline__ BlockLut make_lut(float c1p) {
 
 // Four selectors (one 4-bit index per byte, element order) -> two bf16 pairs.
 __device__ __forceinline__ void lut4(const BlockLut& t, uint32_t s, uint32_t& out01, uint32_t& out23) {
-  uint32_t sa = ((s << 3) & 0x40404040u) | s;
+  // sa = s | ((s << 3) & 0x40404040) as one v_bitop3 (truth table 0xEA: (a & b) | c)
+  uint32_t sa = __builtin_amdgcn_bitop3_b32(s << 3, 0x40404040u, s, 0xEA);
   uint32_t sb = sa ^ 0x48484848u;
   uint32_t lo = __builtin_amdgcn_perm(t.lo[1], t.lo[0], sa) & __builtin_amdgcn_perm(t.lo[3], t.lo[2], sb);
   uint32_t hi = __builtin_amdgcn_perm(t.hi[1], t.hi[0], sa) & __builtin_amdgcn_perm(t.hi[3], t.hi[2], sb);

@@ -305,7 +305,8 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
       for (int i = 0; i < 4; ++i) {
         const uint32_t p = wq[i];
         const uint32_t odd = (p ^ hx) & 0x0F0F0F0Fu;           // elements 1,3,5,7
-        const uint32_t even = ((p >> 4) ^ hx4) & 0x0F0F0F0Fu;   // elements 0,2,4,6
+        // elements 0,2,4,6: ((p >> 4) ^ hx4) & 0x0F0F0F0F as one v_bitop3 (truth table 0x28)
+        const uint32_t even = __builtin_amdgcn_bitop3_b32(p >> 4, hx4, 0x0F0F0F0Fu, 0x28);
         const uint32_t s0 = __builtin_amdgcn_perm(odd, even, 0x05010400u);  // elements 0..3
         const uint32_t s1 = __builtin_amdgcn_perm(odd, even, 0x07030602u);  // elements 4..7
         lut4(L, s0, d[i][0], d[i][1]);
