@@ -34,6 +34,8 @@
 // partial contraction step of the backward (N % 64 != 0) points its missing activation chunks past
 // the records. Weight rows past N dequantise to exact zeros there (code 0 and constant 0); in the
 // forward they only feed output columns that are not stored.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -392,9 +394,11 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
   for (int kk = 0; kk < 4; ++kk)
     xaddr[kk] = (wm0 + (lane & 31)) * kBK + (((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7)) * 8);
 
-  auto compute = [&](int s) {
-    const uint16_t* xs = Xs + (s % kXStages) * XSTAGE;
-    const int wb = s & 1;
+  // step s reads activation stage s % 3 and W buffer s % 2, passed as compile-time constants so
+  // that every LDS address is a fixed offset from a per-lane base
+  auto compute = [&](auto xs_t, auto wb_t) {
+    constexpr int XS = decltype(xs_t)::value, wb = decltype(wb_t)::value;
+    const uint16_t* xs = Xs + XS * XSTAGE;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 afr[TN], bfr[TM];
@@ -426,10 +430,24 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
 
   lds_barrier();   // step 0's loads have landed
   lds_barrier();   // phase 0: step 0's W tile is built
-  for (int s = 0; s < steps; ++s) {   // phase s + 1
-    compute(s);
-    lds_barrier();
+  // phase s + 1 computes step s; six steps per iteration cover every (stage, buffer) pair
+  const std::integral_constant<int, 0> c0{};
+  const std::integral_constant<int, 1> c1{};
+  const std::integral_constant<int, 2> c2{};
+  int s = 0;
+  for (; s + 6 <= steps; s += 6) {
+    compute(c0, c0); lds_barrier();
+    compute(c1, c1); lds_barrier();
+    compute(c2, c0); lds_barrier();
+    compute(c0, c1); lds_barrier();
+    compute(c1, c0); lds_barrier();
+    compute(c2, c1); lds_barrier();
   }
+  if (s < steps) { compute(c0, c0); lds_barrier(); }
+  if (s + 1 < steps) { compute(c1, c1); lds_barrier(); }
+  if (s + 2 < steps) { compute(c2, c0); lds_barrier(); }
+  if (s + 3 < steps) { compute(c0, c1); lds_barrier(); }
+  if (s + 4 < steps) { compute(c1, c0); lds_barrier(); }
 
   // ---------------------------------------------------------------- epilogue
 #pragma unroll
