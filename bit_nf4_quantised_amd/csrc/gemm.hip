@@ -139,12 +139,14 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
       const int row = slot >> 3, c = (slot & 7) ^ ((row >> 1) & 7);
       xoff[j] = (uint32_t)row * (uint32_t)(Lc * 2) + (uint32_t)c * 16u;
     }
-    auto issue_x = [&](int t) {
+    // `full`: the step is known to be a whole one (every step but the last), so the loop that
+    // issues those carries no per-chunk selects
+    auto issue_x = [&](int t, bool full) {
       const uint16_t* base = g.act + m0 * Lc + (int64_t)t * kBK;
       const int nrec = (int)(rows_valid * Lc * 2 - (int64_t)t * kBK * 2);
       __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kRsrcFlags);
       uint16_t* dst = Xs + (t % kXStages) * XSTAGE + (lw * 2 * BM) * 8;
-      if (__builtin_expect((int64_t)(t + 1) * kBK <= Lc, 1)) {
+      if (full || (int64_t)(t + 1) * kBK <= Lc) {
 #pragma unroll
         for (int j = 0; j < NX; ++j) {
           const uint32_t off = xoff[j];
@@ -216,15 +218,15 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
     // The packed weights of a step therefore sit in LDS one phase before they are expanded, which
     // lets the dequantisers read them a phase ahead.
     const bool two_p = !DX || lw < 2;   // issue_p makes two loads (chunk + code or constant)
-    issue_x(0);
+    issue_x(0, false);
     issue_p(0);
     if (main_steps > 1) issue_p(1);
     if (main_steps > 2) issue_p(2);
     wait_vmcnt<0>();
     lds_barrier();
-    for (int q = 0; q <= steps; ++q) {
+    auto phase = [&](int q, bool full) {
       const bool more_x = q + 1 < main_steps, more_p = q + 3 < main_steps;
-      if (more_x) issue_x(q + 1);
+      if (more_x) issue_x(q + 1, full);
       if (more_p) issue_p(q + 3);
       if (more_p) {
         if (two_p) wait_vmcnt<NX + 2>();
@@ -235,7 +237,10 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
         wait_vmcnt<0>();
       }
       lds_barrier();
-    }
+    };
+    int q = 0;
+    for (; q + 2 < main_steps; ++q) phase(q, true);   // step q + 1 is not the last one
+    for (; q <= steps; ++q) phase(q, false);
     return;
   }
 
