@@ -153,8 +153,12 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
   const char* tab_bytes = reinterpret_cast<const char*>(tab);
 
   // process step s; with `more`, the small operands of step s + 1 are loaded as soon as those of
-  // step s have been consumed
-  auto process = [&](int s, const SkinnyW& st, SkinnyS& ss, const u32x4* xsv, bool more) {
+  // step s have been consumed, and load i of step s + 1's packed weight goes out just before
+  // quarter i of step s is dequantised: a wave whose load has to wait for room in the CU's
+  // vector-memory queue then stalls between quarters while the other waves of its SIMD compute,
+  // instead of stalling before any of its arithmetic (16 waves issuing 4 loads each at the start
+  // of a step made the last waves wait about as long as the step's arithmetic)
+  auto process = [&](int s, const SkinnyW& st, SkinnyW& nx, SkinnyS& ss, const u32x4* xsv, bool more) {
     const uint32_t b0 = rowb + (uint32_t)min(s * 8, kb - 1);
     const uint32_t base = b0 & 3u;   // byte of the step's first code in the 16 loaded bytes
     float c1p[4];
@@ -170,7 +174,9 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
     if (more) load_scales(s + 1, ss);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      if (more) nx.p[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(prow + (uint32_t)blk_of(s + 1, i) * 32u));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         // activation fragment (i, d): chunk 16 i + 4 g + d of token m
@@ -187,6 +193,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, (u32x4{a[0], a[1], a[2], a[3]})),
                                                       bx, acc, 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (a_live) {
       const bf16x8 bx = __builtin_bit_cast(bf16x8, xsv[m * 64 + ((16 * ai + 4 * grp + ad) ^ m)]);
       accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ss.a), bx, accu, 0, 0, 0);
@@ -195,7 +203,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
   };
 
   // Phase of step s (parity p = (s - s_begin) % 2): the activations and packed weight of s + 1 are
-  // loaded (into registers), s is dequantised and multiplied from w[p] and activation stage p, the
+  // loaded (into registers; the weight a quarter at a time during the arithmetic), s is dequantised
+  // and multiplied from w[p] and activation stage p, the
   // activations of s + 1 are stored into stage 1 - p (nobody reads it since the previous barrier),
   // and the barrier hands them over. Every load issued is consumed: the steady-state loop runs
   // while both of its phases have a successor, and the last one or two phases are peeled (a load
@@ -214,10 +223,9 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
     u32x4 xn = u32x4{0u, 0u, 0u, 0u};
     if (more) {
       xn = load_x(sp + 1);
-      load_w(sp + 1, w[1 - p]);
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the arithmetic
-    process(sp, w[p], ss, xs[p], more);
+    process(sp, w[p], w[1 - p], ss, xs[p], more);
     if (more) store_x(sp + 1, xs[1 - p], xn);
     lds_barrier();
   };
