@@ -28,6 +28,8 @@ namespace nf4 {
 constexpr int kMgCols = 128;     // columns per strip
 constexpr int kMgRows = 64;      // rows per tile
 constexpr int kMgPitch = kMgCols + 4;   // fp32 pitch of the update tile (rows shift by 4 banks)
+constexpr int kMgStage = kMgCols + 8;   // bf16 pitch of the output staging rows (in the same LDS)
+static_assert(16 * kMgStage * 2 <= 16 * kMgPitch * 4, "staging fits in a wave's update rows");
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(256) void qlora_merge_kernel(const MergeArgs g) {
     in.cw = *reinterpret_cast<const uint32_t*>(g.scale_q + (b & ~int64_t(3)));
     in.c2 = g.scale_c2[b / kGroup];
   };
-  auto process = [&](int64_t t, const TileIn& in) {
+  auto process = [&](int64_t t, const TileIn& in, TileIn& nx, int64_t t_next) {
     const int64_t n0 = first_row(t);
     // ---- s B A for rows n0 .. n0 + 15, all 128 columns
     f32x4 acc[kMgCols / 16];
@@ -121,6 +123,11 @@ __global__ __launch_bounds__(256) void qlora_merge_kernel(const MergeArgs g) {
       *reinterpret_cast<f32x4*>(urow + (lane & 15) * kMgPitch + ct * 16 + 4 * (lane >> 4)) =
           f32x4{__fmul_rn(g.scale, acc[ct][0]), __fmul_rn(g.scale, acc[ct][1]), __fmul_rn(g.scale, acc[ct][2]),
                 __fmul_rn(g.scale, acc[ct][3])};
+
+    // the next tile's loads go out between this tile's MFMA part and its dequantisation, so that a
+    // wave waiting for room in the CU's vector-memory queue does so with half its tile still to do
+    load_tile(t_next, nx);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- dequantise, add, round, store
     const int64_t n = n0 + rl;
@@ -143,9 +150,22 @@ __global__ __launch_bounds__(256) void qlora_merge_kernel(const MergeArgs g) {
       }
       o[i] = u32x4{d[0], d[1], d[2], d[3]};
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(g.out + n * g.K + col);
+    // ---- coalesced stores through LDS: the results go into this wave's update rows (every lane
+    // has read its update values, and a wave's LDS accesses complete in order) as bf16 rows of
+    // kMgStage values, then store instruction i writes rows 4 i .. 4 i + 3, 16 bytes per lane and
+    // the 256 bytes of a row from 16 consecutive lanes (lanes past a half strip repeat the last
+    // 16 bytes of their row, identical writes)
+    uint16_t* stg = reinterpret_cast<uint16_t*>(urow);
+    u32x4* sdst = reinterpret_cast<u32x4*>(stg + rl * kMgStage + (col - k0));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = o[i];
+    for (int i = 0; i < 4; ++i) sdst[i] = o[i];
+    const int c16 = min(lane & 15, cols / 8 - 1);
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4*>(stg + (4 * i + (lane >> 4)) * kMgStage + 8 * c16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(g.out + (n0 + 4 * i + (lane >> 4)) * g.K + k0 + 8 * c16) = v[i];
   };
 
   // tiles in pairs, so that each slot stays one register set; the next tile's loads go out
@@ -155,14 +175,10 @@ __global__ __launch_bounds__(256) void qlora_merge_kernel(const MergeArgs g) {
   load_tile(t_begin, s0);
   int64_t t = t_begin;
   for (; t + 1 < t_end; t += 2) {
-    load_tile(t + 1, s1);
-    __builtin_amdgcn_sched_barrier(0);
-    process(t, s0);
-    load_tile(min(t + 2, t_end - 1), s0);
-    __builtin_amdgcn_sched_barrier(0);
-    process(t + 1, s1);
+    process(t, s0, s1, t + 1);
+    process(t + 1, s1, s0, min(t + 2, t_end - 1));
   }
-  if (t < t_end) process(t, s0);
+  if (t < t_end) process(t, s0, s1, t);
 }
 
 hipError_t launch_merge(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2, int64_t N,
