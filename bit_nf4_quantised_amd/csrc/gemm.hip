@@ -455,21 +455,33 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
   if (s + 4 < steps) { compute(c1, c0); lds_barrier(); }
 
   // ---------------------------------------------------------------- epilogue
+  // Every wave has passed the barrier after the last step, so the activation stages are free: wave
+  // cw stages its WM x WN sub-tile as bf16 rows of WN values (16-byte slot c of row q at
+  // c ^ ((q >> 1) & (C16 - 1))), then each store instruction writes 16 bytes per lane and whole
+  // rows of the sub-tile (128 bytes when WN = 64) from consecutive lanes.
+  constexpr int SUB = CW::WM * CW::WN;
+  static_assert(8 * SUB <= kXStages * XSTAGE, "sub-tiles fit in the activation stages");
+  constexpr int C16 = CW::WN / 8;           // 16-byte slots per row
+  constexpr int RPI = 64 / C16;             // rows per store instruction
+  uint16_t* stg = Xs + cw * SUB;
+  auto slot = [&](int q, int c16) { return q * CW::WN + ((c16 ^ ((q >> 1) & (C16 - 1))) * 8); };
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
+  for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-      const int64_t m = m0 + wm0 + tm * 32 + (lane & 31);
+      const f32x16& a = acc[tn][tm];
+      const int q = tm * 32 + (lane & 31);
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int64_t n = col0 + wn0 + tn * 32 + 8 * rq + 4 * (lane >> 5);
-        if (m < g.M && n < Nout) {
-          const f32x16& a = acc[tn][tm];
-          *reinterpret_cast<u32x2*>(g.out + m * Nout + n) =
-              u32x2{pack_bf16x2(a[4 * rq], a[4 * rq + 1]), pack_bf16x2(a[4 * rq + 2], a[4 * rq + 3])};
-        }
-      }
+      for (int rq = 0; rq < 4; ++rq)   // columns tn * 32 + 8 rq + 4 (lane / 32) .. +3
+        *reinterpret_cast<u32x2*>(stg + slot(q, 4 * tn + rq) + 4 * (lane >> 5)) =
+            u32x2{pack_bf16x2(a[4 * rq], a[4 * rq + 1]), pack_bf16x2(a[4 * rq + 2], a[4 * rq + 3])};
     }
+#pragma unroll
+  for (int j = 0; j < CW::WM / RPI; ++j) {
+    const int q = j * RPI + lane / C16, c16 = lane % C16;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + slot(q, c16));
+    const int64_t m = m0 + wm0 + q, n = col0 + wn0 + 8 * c16;
+    if (m < g.M && n < Nout) *reinterpret_cast<u32x4*>(g.out + m * Nout + n) = v;
   }
 }
 
