@@ -271,8 +271,9 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
 
 // Ordered sums of partial results. A job: out[i] = scale * (sum over p < nparts, in order, of
 // part[p * count + i]) (+ out[i]); with `transpose`, part is [C][r] and out is [r][C]. One launch
-// serves two jobs (blocks [0, blocks0) take job 0). Threads take 4 consecutive outputs and issue
-// the loads of 8 partials at a time before adding them in order.
+// serves two jobs (blocks [0, blocks0) take job 0). A thread takes one output and issues the loads
+// of 8 partials at a time before adding them in order; the sums are latency-bound chains, so
+// one output per thread gives the most chains in flight.
 struct ReduceJob {
   const float* part;
   int nparts;
@@ -285,37 +286,20 @@ struct ReduceJob {
 __global__ __launch_bounds__(256) void lora_reduce_kernel(const ReduceJob j0, const ReduceJob j1, int blocks0) {
   const bool second = (int)blockIdx.x >= blocks0;
   const ReduceJob& jb = second ? j1 : j0;
-  const int64_t i4 = ((int64_t)(second ? blockIdx.x - blocks0 : blockIdx.x) * 256 + threadIdx.x) * 4;
-  if (i4 >= jb.count) return;
-  int64_t src[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int64_t i = min(i4 + e, jb.count - 1);
-    src[e] = jb.transpose ? (i % jb.C) * jb.r + i / jb.C : i;
-  }
-  const bool vec = !jb.transpose && i4 + 4 <= jb.count;
-  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t i = (int64_t)(second ? blockIdx.x - blocks0 : blockIdx.x) * 256 + threadIdx.x;
+  if (i >= jb.count) return;
+  const int64_t src = jb.transpose ? (i % jb.C) * jb.r + i / jb.C : i;
+  float s = 0.f;
   for (int p0 = 0; p0 < jb.nparts; p0 += 8) {
-    f32x4 v[8];
+    float v[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int p = min(p0 + q, jb.nparts - 1);
-      const float* base = jb.part + (int64_t)p * jb.count;
-      if (vec) v[q] = *reinterpret_cast<const f32x4*>(base + i4);
-      else v[q] = f32x4{base[src[0]], base[src[1]], base[src[2]], base[src[3]]};
-    }
+    for (int q = 0; q < 8; ++q) v[q] = jb.part[(int64_t)min(p0 + q, jb.nparts - 1) * jb.count + src];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       if (p0 + q < jb.nparts) s += v[q];
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int64_t i = i4 + e;
-    if (i < jb.count) {
-      const float x = s[e] * jb.scale;
-      jb.out[i] = jb.accumulate ? jb.out[i] + x : x;
-    }
-  }
+  const float x = s * jb.scale;
+  jb.out[i] = jb.accumulate ? jb.out[i] + x : x;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -357,8 +341,8 @@ static ReduceJob reduce_job(const float* part, int nparts, int64_t count, int64_
 }
 
 static void launch_reduce(const ReduceJob& j0, const ReduceJob* j1, hipStream_t stream) {
-  const int b0 = (int)((j0.count + 1023) / 1024);
-  const int b1 = j1 ? (int)((j1->count + 1023) / 1024) : 0;
+  const int b0 = (int)((j0.count + 255) / 256);
+  const int b1 = j1 ? (int)((j1->count + 255) / 256) : 0;
   hipLaunchKernelGGL(lora_reduce_kernel, dim3((unsigned)(b0 + b1)), dim3(256), 0, stream, j0, j1 ? *j1 : j0, b0);
 }
 
