@@ -3,7 +3,7 @@
 A plain, slow, obviously correct reference of what the hot path computes, written from the pages'
 statement of the method (chiefly "QLoRA, explained": the sections on blockwise absmax quantisation,
 NormalFloat 4, double quantisation, the forward pass and gradients and the quality loss at merge
-time, plus its worked example and toy run). Floating point is float64 unless a step fixes a
+time and the training loop around the layer, plus its worked example and toy run). Floating point is float64 unless a step fixes a
 narrower type (the fp32 codebook, fp32 scales, the bf16 dequantised weight), and the integer
 decisions (nearest code, nearest 8-bit float) are taken in exact arithmetic.
 
@@ -20,12 +20,14 @@ from .nf4 import (NF4_ZERO_INDEX, codebook, quantize_blocks, pack_nibbles, unpac
                   bf16_bits_from_f32, f32_from_bf16_bits, dequant, storage_bits)
 from .linear import linear_fwd, linear_bwd, linear_fwd_f64, linear_bwd_f64, linear_bwd_sampled
 from .merge import bf16_bits_from_f64, merge
+from .optim import AdamWConfig, global_grad_norm, clip_coefficient, adamw_step
 from .toy import int4_codebook, fp4_codebook, relative_mse, residual_capture
 
 __all__ = [
     "NF4_ZERO_INDEX", "codebook", "quantize_blocks", "pack_nibbles", "unpack_nibbles", "quantize",
     "e4m3_value", "e4m3_unit_values", "double_quant", "dequant_scales", "bf16_bits_from_f32",
     "f32_from_bf16_bits", "dequant", "storage_bits", "linear_fwd", "linear_bwd", "linear_fwd_f64",
-    "linear_bwd_f64", "linear_bwd_sampled", "bf16_bits_from_f64", "merge", "int4_codebook",
+    "linear_bwd_f64", "linear_bwd_sampled", "bf16_bits_from_f64", "merge", "AdamWConfig",
+    "global_grad_norm", "clip_coefficient", "adamw_step", "int4_codebook",
     "fp4_codebook", "relative_mse", "residual_capture",
 ]
