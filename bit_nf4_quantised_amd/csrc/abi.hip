@@ -2,6 +2,7 @@
 // Declarations and the contract of every call are in include/qlora_nf4.h.
 #include "../../include/qlora_nf4.h"
 
+#include <math.h>
 #include <string.h>
 
 #include "common.h"
@@ -40,6 +41,28 @@ size_t bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
   const size_t ga = nf4::lora_pass_ws_floats(M, K, r, false, true);
   if (ga > part) part = ga;
   return align_up((size_t)M * r * 4) + align_up(part * 4);
+}
+
+// a tensor list of the adapter update: 1..kOptMaxTensors entries, each numel > 0 and a multiple
+// of 4, the whole list within one grid (4096 elements per workgroup)
+int check_opt_list(int32_t count, const int64_t* numel) {
+  if (count < 1 || count > nf4::kOptMaxTensors || !numel) return NF4_ERR_SHAPE;
+  int64_t wgs = 0;
+  for (int i = 0; i < count; ++i) {
+    if (numel[i] <= 0 || numel[i] % 4 || numel[i] > (int64_t(1) << 40)) return NF4_ERR_SHAPE;
+    wgs += (numel[i] + 4095) / 4096;
+  }
+  return wgs <= (int64_t(1) << 30) ? NF4_OK : NF4_ERR_SHAPE;
+}
+
+template <typename T>
+int check_ptr_list(int32_t count, T* const* ptrs) {
+  if (!ptrs) return NF4_ERR_NULL;
+  for (int i = 0; i < count; ++i) {
+    if (!ptrs[i]) return NF4_ERR_NULL;
+    if (!aligned16(ptrs[i])) return NF4_ERR_ALIGN;
+  }
+  return NF4_OK;
 }
 
 }  // namespace
@@ -188,6 +211,52 @@ int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy,
     if (e != hipSuccess) return NF4_ERR_HIP;
   }
   return from_hip(nf4::launch_lora_dx(x, M, K, v, r, scale, accumulate, part, dA, stream));
+}
+
+size_t qlora_grad_sqnorm_workspace_bytes(int32_t count, const int64_t* numel) {
+  if (check_opt_list(count, numel)) return 0;
+  return nf4::opt_workspace_bytes(count, numel);
+}
+
+int qlora_grad_sqnorm(int32_t count, const float* const* grads, const int64_t* numel, double* sqnorm,
+                      int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_opt_list(count, numel);
+  if (st) return st;
+  if ((st = check_ptr_list(count, grads))) return st;
+  if (!sqnorm) return NF4_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(sqnorm) & 7u) return NF4_ERR_ALIGN;
+  if (ws && !aligned16(ws)) return NF4_ERR_ALIGN;
+  if (!ws || ws_bytes < nf4::opt_workspace_bytes(count, numel)) return NF4_ERR_WORKSPACE;
+  return from_hip(nf4::launch_grad_sqnorm(count, grads, numel, static_cast<double*>(ws), sqnorm,
+                                          accumulate ? 1 : 0, stream));
+}
+
+int qlora_adamw_step(int32_t count, float* const* params, const float* const* grads, float* const* exp_avg,
+                     float* const* exp_avg_sq, uint16_t* const* params_bf16, const int64_t* numel,
+                     const qlora_adamw_config* cfg, int64_t step, const double* sqnorm, float* grad_norm,
+                     hipStream_t stream) {
+  int st = check_opt_list(count, numel);
+  if (st) return st;
+  if (!cfg || !sqnorm) return NF4_ERR_NULL;
+  if ((st = check_ptr_list(count, params)) || (st = check_ptr_list(count, grads)) ||
+      (st = check_ptr_list(count, exp_avg)) || (st = check_ptr_list(count, exp_avg_sq)))
+    return st;
+  if (params_bf16) {
+    for (int i = 0; i < count; ++i)
+      if (params_bf16[i] && (reinterpret_cast<uintptr_t>(params_bf16[i]) & 7u)) return NF4_ERR_ALIGN;
+  }
+  if ((reinterpret_cast<uintptr_t>(sqnorm) & 7u) || (reinterpret_cast<uintptr_t>(grad_norm) & 3u))
+    return NF4_ERR_ALIGN;
+  if (step < 1) return NF4_ERR_SHAPE;
+  const qlora_adamw_config& c = *cfg;
+  if (!isfinite(c.lr) || c.lr < 0.f || !(c.beta1 >= 0.f && c.beta1 < 1.f) ||
+      !(c.beta2 >= 0.f && c.beta2 < 1.f) || !(c.eps > 0.f) || !isfinite(c.eps) ||
+      !(c.weight_decay >= 0.f) || !isfinite(c.weight_decay) || isnan(c.max_grad_norm) ||
+      isinf(c.max_grad_norm))
+    return NF4_ERR_SHAPE;
+  return from_hip(nf4::launch_adamw(count, params, grads, exp_avg, exp_avg_sq, params_bf16, numel, c.lr,
+                                    c.beta1, c.beta2, c.eps, c.weight_decay, c.max_grad_norm, step,
+                                    sqnorm, grad_norm, stream));
 }
 
 }  // extern "C"

@@ -21,6 +21,10 @@ Workloads (sizes as out x in, i.e. W is N x K row-major like ``nn.Linear``):
 
 Adapters A (r x K) and B (N x r) are N(0, 0.01^2); activations X (M x K) and upstream gradients
 dY (M x N) are N(0, 1); all four are rounded to bf16.
+
+The adapter update draws fp32 master copies of A and B, N(0, 0.01^2), for every linear of
+``layers`` layers (Llama-3.1-8B: 32 layers, 448 tensors, 41.9 M values at rank 16), and fresh
+N(0, sigma^2) fp32 gradients per step (sigma 1e-3 puts the global norm above the 0.3 threshold).
 """
 from __future__ import annotations
 
@@ -30,7 +34,7 @@ from dataclasses import dataclass
 import numpy as np
 
 WORKLOAD_IDS = {"single": 1, "llama8b": 2, "llama65b": 3, "stream": 4, "llama70b": 5}
-TENSOR_IDS = {"w": 0, "x": 1, "a": 2, "b": 3, "dy": 4}
+TENSOR_IDS = {"w": 0, "x": 1, "a": 2, "b": 3, "dy": 4, "grad": 5, "master": 6}
 
 
 @dataclass(frozen=True)
@@ -126,6 +130,30 @@ def linear_inputs(wl: Workload, li: int, lin: Linear, m: int | None = None):
     b = gaussian_bf16(wl.name, li, "b", (lin.n, wl.r), 0.01)
     dy = gaussian_bf16(wl.name, li, "dy", (m, lin.n), 1.0)
     return w, x, a, b, dy
+
+
+LLAMA8B_LAYERS = 32
+
+
+def adapter_shapes(wl: Workload, layers: int = 1) -> list:
+    """Shapes of the trainable tensors, layer by layer: A (r x K) then B (N x r) of every linear."""
+    out = []
+    for _ in range(layers):
+        for lin in wl.linears:
+            out += [(wl.r, lin.k), (lin.n, wl.r)]
+    return out
+
+
+def adapter_masters(workload: str, shapes, sigma: float = 0.01) -> list:
+    """fp32 master weights of the adapters, one seeded stream per tensor."""
+    return [rng_for(workload, i, "master").standard_normal(s, dtype=np.float32) * np.float32(sigma)
+            for i, s in enumerate(shapes)]
+
+
+def adapter_grads(workload: str, shapes, step: int, sigma: float = 1e-3) -> list:
+    """fp32 adapter gradients of one step, one seeded stream per tensor and step."""
+    return [rng_for(workload, i, "grad", step).standard_normal(s, dtype=np.float32) * np.float32(sigma)
+            for i, s in enumerate(shapes)]
 
 
 def stream_weight(i: int) -> np.ndarray:
