@@ -355,9 +355,10 @@ def bandwidth_paths(torch, q, dev, args):
 
 def adapter_update_path(torch, q, dev, iters=50):
     """The adapter update of a training step over every adapter of a 32-layer Llama-3.1-8B at
-    rank 16 (448 tensors, 41.9 M values): the global gradient norm, then clipped AdamW with fp32
-    state and bf16 copies of the new weights. Per value 34 bytes: the norm pass reads the gradient
-    (4); the step reads p, g, m, v (16) and writes p, m, v (12) and the bf16 copy (2)."""
+    rank 16 (448 tensors, 41.9 M values), through one plan: the global gradient norm, then clipped
+    AdamW with fp32 state and bf16 copies of the new weights. Per value 34 bytes: the norm pass
+    reads the gradient (4); the step reads p, g, m, v (16) and writes p, m, v (12) and the bf16
+    copy (2)."""
     shapes = wl.adapter_shapes(wl.WORKLOADS["llama8b"], wl.LLAMA8B_LAYERS)
     log(f"[bench] adapter update: {len(shapes)} tensors")
     p = [torch.from_numpy(x).to(dev) for x in wl.adapter_masters("llama8b", shapes)]
@@ -365,17 +366,17 @@ def adapter_update_path(torch, q, dev, iters=50):
     m = [torch.zeros_like(x) for x in p]
     v = [torch.zeros_like(x) for x in p]
     pb = [torch.empty(x.numel(), dtype=torch.int16, device=dev) for x in p]
-    norm = torch.empty(1, dtype=torch.float32, device=dev)
-    upd = q.AdamWUpdate(p, g, m, v, q.AdamWConfig(), pb)
-    upd(1, norm)
-    ms = timed(lambda i: upd(i + 2, norm), iters, torch)
-    values = sum(x.numel() for x in p)
+    norm = torch.empty(1, dtype=torch.float64, device=dev)
+    plan = q.AdamWPlan(p, g, m, v, pb, q.AdamWConfig())
+    plan.step(1, norm)
+    ms = timed(lambda i: plan.step(i + 2, norm), iters, torch)
+    values = plan.values
     nbytes = 34 * values
     gbps = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] adapter update: {ms*1e3:.1f} us, {gbps:.0f} GB/s, grad norm {float(norm.cpu()):.3f}")
+    plan.close()
     return {"tensors": len(shapes), "values": values, "us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
-            "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "bytes": nbytes,
-            "launches": 3 * len(upd.lists)}
+            "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "bytes": nbytes, "launches": 3}
 
 
 def cpu_baseline(wk, min_seconds: float = 10.0):

@@ -59,10 +59,10 @@ _SIGS = {
     "qlora_linear_fwd_recompute": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz,
                                                   _p]),
     "qlora_merge": (ctypes.c_int, [_W, _p, _p, _i32, _f32, _p, _p]),
-    "qlora_grad_sqnorm_workspace_bytes": (_sz, [_i32, _p]),
-    "qlora_grad_sqnorm": (ctypes.c_int, [_i32, _p, _p, _p, ctypes.c_int, _p, _sz, _p]),
-    "qlora_adamw_step": (ctypes.c_int, [_i32, _p, _p, _p, _p, _p, _p, ctypes.POINTER(CAdamWConfig),
-                                        _i64, _p, _p, _p]),
+    "qlora_adamw_plan_create": (ctypes.c_int, [_i64, _p, _p, _p, _p, _p, _p,
+                                               ctypes.POINTER(ctypes.c_void_p)]),
+    "qlora_adamw_plan_step": (ctypes.c_int, [_p, ctypes.POINTER(CAdamWConfig), _i64, _p, _p]),
+    "qlora_adamw_plan_destroy": (ctypes.c_int, [_p]),
     "qlora_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "nf4_storage_bytes": (_i64, [_i64]),
     "nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
@@ -225,9 +225,6 @@ def qlora_linear_bwd(weight: NF4Weight, x, dy, A, B, scale: float, u, dx, dA, dB
 
 
 # ------------------------------------------------------------------------- the adapter update
-OPT_MAX_TENSORS = 32     # tensors per qlora_grad_sqnorm / qlora_adamw_step call
-
-
 @dataclass(frozen=True)
 class AdamWConfig:
     """Hyper-parameters of the adapter update; lr and the clipping threshold are the paper's,
@@ -255,65 +252,14 @@ def _ptr_array(tensors, dtypes, allow_none=False):
     return arr
 
 
-def _numel_array(tensors):
-    return (ctypes.c_int64 * len(tensors))(*[t.numel() for t in tensors])
+class AdamWPlan:
+    """qlora_adamw_plan over a set of adapter tensors (fp32 master weights, gradients, first and
+    second moments, optional bf16 copies): one call runs the clipped AdamW step over all of them
+    in three kernel launches. The tensors must stay alive, at the same storage, while the plan is
+    used; the plan keeps references to them."""
 
-
-def qlora_grad_sqnorm_workspace_bytes(numels) -> int:
-    arr = (ctypes.c_int64 * len(numels))(*numels)
-    return int(lib.qlora_grad_sqnorm_workspace_bytes(len(numels), arr))
-
-
-def qlora_grad_sqnorm(grads, sqnorm, accumulate: bool = False, ws=None, stream=None) -> None:
-    """sqnorm (one float64 on the device) = [sqnorm +] the sum of squares of every gradient
-    element; at most OPT_MAX_TENSORS fp32 tensors per call."""
-    _dtype(sqnorm, torch.float64)
-    if sqnorm.numel() != 1:
-        raise ValueError("sqnorm must hold one float64")
-    ptrs = _ptr_array(grads, (torch.float32,))
-    numel = _numel_array(grads)
-    need = int(lib.qlora_grad_sqnorm_workspace_bytes(len(grads), numel))
-    if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=sqnorm.device)
-    _check(lib.qlora_grad_sqnorm(len(grads), ptrs, numel, _ptr(sqnorm), int(bool(accumulate)),
-                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "qlora_grad_sqnorm")
-
-
-def qlora_adamw_step(params, grads, exp_avg, exp_avg_sq, step: int, sqnorm,
-                     cfg: AdamWConfig = AdamWConfig(), params_bf16=None, grad_norm=None,
-                     stream=None) -> None:
-    """One clipped AdamW step, in place, over at most OPT_MAX_TENSORS fp32 tensors; sqnorm is the
-    global squared gradient norm from qlora_grad_sqnorm. params_bf16 (a list, entries may be None)
-    receives the new weights in bf16."""
-    n = len(params)
-    if not (len(grads) == len(exp_avg) == len(exp_avg_sq) == n) or \
-            (params_bf16 is not None and len(params_bf16) != n):
-        raise ValueError("tensor lists differ in length")
-    for i in range(n):
-        shapes = [grads[i].numel(), exp_avg[i].numel(), exp_avg_sq[i].numel()]
-        if params_bf16 is not None and params_bf16[i] is not None:
-            shapes.append(params_bf16[i].numel())
-        if any(k != params[i].numel() for k in shapes):
-            raise ValueError(f"tensor {i}: sizes differ")
-    _dtype(sqnorm, torch.float64)
-    _dtype(grad_norm, torch.float32)
-    f32 = (torch.float32,)
-    pb = None if params_bf16 is None else _ptr_array(params_bf16, _BF16, allow_none=True)
-    c = cfg.c_struct()
-    _check(lib.qlora_adamw_step(n, _ptr_array(params, f32), _ptr_array(grads, f32),
-                                _ptr_array(exp_avg, f32), _ptr_array(exp_avg_sq, f32), pb,
-                                _numel_array(params), ctypes.byref(c), int(step), _ptr(sqnorm),
-                                _ptr(grad_norm), _stream(stream)), "qlora_adamw_step")
-
-
-class AdamWUpdate:
-    """The whole adapter update for any number of tensors, marshalled once: the global squared
-    norm over lists of OPT_MAX_TENSORS (accumulated on the device), then the AdamW step list by
-    list. Holds the pointer arrays and the workspace, so a call only issues the C calls."""
-
-    def __init__(self, params, grads, exp_avg, exp_avg_sq, cfg: AdamWConfig = AdamWConfig(),
-                 params_bf16=None, sqnorm=None):
+    def __init__(self, params, grads, exp_avg, exp_avg_sq, params_bf16=None,
+                 cfg: AdamWConfig = AdamWConfig()):
         n = len(params)
         if not (len(grads) == len(exp_avg) == len(exp_avg_sq) == n) or n == 0 or \
                 (params_bf16 is not None and len(params_bf16) != n):
@@ -324,42 +270,39 @@ class AdamWUpdate:
                 sizes.append(params_bf16[i].numel())
             if any(k != params[i].numel() for k in sizes):
                 raise ValueError(f"tensor {i}: sizes differ")
-        dev = params[0].device
-        self.sqnorm = torch.empty(1, dtype=torch.float64, device=dev) if sqnorm is None else sqnorm
-        _dtype(self.sqnorm, torch.float64)
-        self.cfg = cfg.c_struct()
-        self._keep = (params, grads, exp_avg, exp_avg_sq, params_bf16)
+        self._keep = (list(params), list(grads), list(exp_avg), list(exp_avg_sq),
+                      None if params_bf16 is None else list(params_bf16))
+        self.cfg = cfg
+        self._ccfg = cfg.c_struct()
         f32 = (torch.float32,)
-        self.lists = []
-        need = 16
-        for i in range(0, n, OPT_MAX_TENSORS):
-            sl = slice(i, i + OPT_MAX_TENSORS)
-            numel = _numel_array(params[sl])
-            k = len(params[sl])
-            need = max(need, int(lib.qlora_grad_sqnorm_workspace_bytes(k, numel)))
-            pb = None if params_bf16 is None else _ptr_array(params_bf16[sl], _BF16, allow_none=True)
-            self.lists.append((k, _ptr_array(params[sl], f32), _ptr_array(grads[sl], f32),
-                               _ptr_array(exp_avg[sl], f32), _ptr_array(exp_avg_sq[sl], f32), pb,
-                               numel))
-        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        pb = None if params_bf16 is None else _ptr_array(params_bf16, _BF16, allow_none=True)
+        numel = (ctypes.c_int64 * n)(*[t.numel() for t in params])
+        handle = ctypes.c_void_p()
+        with torch.cuda.device(params[0].device):
+            _check(lib.qlora_adamw_plan_create(n, _ptr_array(params, f32), _ptr_array(grads, f32),
+                                               _ptr_array(exp_avg, f32), _ptr_array(exp_avg_sq, f32),
+                                               pb, numel, ctypes.byref(handle)),
+                   "qlora_adamw_plan_create")
+        self._handle = handle
+        self.values = sum(t.numel() for t in params)
 
-    def __call__(self, step: int, grad_norm=None, stream=None) -> None:
-        _dtype(grad_norm, torch.float32)
-        s = _stream(stream)
-        sq, ws, nbytes = _ptr(self.sqnorm), _ptr(self.ws), self.ws.numel()
-        for j, (k, _, g, _, _, _, numel) in enumerate(self.lists):
-            _check(lib.qlora_grad_sqnorm(k, g, numel, sq, int(j > 0), ws, nbytes, s),
-                   "qlora_grad_sqnorm")
-        gn = _ptr(grad_norm)
-        for j, (k, p, g, m, v, pb, numel) in enumerate(self.lists):
-            _check(lib.qlora_adamw_step(k, p, g, m, v, pb, numel, ctypes.byref(self.cfg), int(step), sq,
-                                        gn if j == 0 else None, s), "qlora_adamw_step")
+    def step(self, step: int, grad_norm=None, stream=None) -> None:
+        """AdamW step number `step` (from 1); grad_norm (one float64 on the device) receives the
+        gradient norm before clipping."""
+        _dtype(grad_norm, torch.float64)
+        _check(lib.qlora_adamw_plan_step(self._handle, ctypes.byref(self._ccfg), int(step),
+                                         _ptr(grad_norm), _stream(stream)), "qlora_adamw_plan_step")
 
+    def close(self) -> None:
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            lib.qlora_adamw_plan_destroy(self._handle)
+        self._handle = None
 
-def adamw_update(params, grads, exp_avg, exp_avg_sq, step: int, cfg: AdamWConfig = AdamWConfig(),
-                 params_bf16=None, grad_norm=None, sqnorm=None, stream=None) -> None:
-    """One-off form of AdamWUpdate: marshal, then run one step."""
-    AdamWUpdate(params, grads, exp_avg, exp_avg_sq, cfg, params_bf16, sqnorm)(step, grad_norm, stream)
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
 
 
 # ------------------------------------------------------------------------- helpers
@@ -403,7 +346,6 @@ def quantize_weight(w: torch.Tensor, stream=None, absmax: torch.Tensor | None = 
 
 __all__ = ["lib", "LIB_PATH", "EXPORTED", "NF4Error", "NF4Weight", "CNF4Weight", "nf4_quantize",
            "nf4_double_quant", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_fwd_recompute",
-           "qlora_linear_bwd", "qlora_merge", "AdamWConfig", "CAdamWConfig", "OPT_MAX_TENSORS",
-           "qlora_grad_sqnorm_workspace_bytes", "qlora_grad_sqnorm", "qlora_adamw_step", "AdamWUpdate", "adamw_update",
+           "qlora_linear_bwd", "qlora_merge", "AdamWConfig", "CAdamWConfig", "AdamWPlan",
            "qlora_workspace_bytes", "nf4_storage_bytes", "nf4_codebook", "workspace",
            "empty_weight", "quantize_weight"]

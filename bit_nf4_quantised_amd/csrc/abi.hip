@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <new>
+
 #include "common.h"
 #include "launch.h"
 
@@ -43,29 +45,27 @@ size_t bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
   return align_up((size_t)M * r * 4) + align_up(part * 4);
 }
 
-// a tensor list of the adapter update: 1..kOptMaxTensors entries, each numel > 0 and a multiple
-// of 4, the whole list within one grid (4096 elements per workgroup)
-int check_opt_list(int32_t count, const int64_t* numel) {
-  if (count < 1 || count > nf4::kOptMaxTensors || !numel) return NF4_ERR_SHAPE;
-  int64_t wgs = 0;
-  for (int i = 0; i < count; ++i) {
-    if (numel[i] <= 0 || numel[i] % 4 || numel[i] > (int64_t(1) << 40)) return NF4_ERR_SHAPE;
-    wgs += (numel[i] + 4095) / 4096;
-  }
-  return wgs <= (int64_t(1) << 30) ? NF4_OK : NF4_ERR_SHAPE;
-}
-
 template <typename T>
-int check_ptr_list(int32_t count, T* const* ptrs) {
+int check_ptr_list(int64_t count, T* const* ptrs, uintptr_t align_mask, bool entries_may_be_null) {
   if (!ptrs) return NF4_ERR_NULL;
-  for (int i = 0; i < count; ++i) {
-    if (!ptrs[i]) return NF4_ERR_NULL;
-    if (!aligned16(ptrs[i])) return NF4_ERR_ALIGN;
+  for (int64_t i = 0; i < count; ++i) {
+    if (!ptrs[i]) {
+      if (entries_may_be_null) continue;
+      return NF4_ERR_NULL;
+    }
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) & align_mask) return NF4_ERR_ALIGN;
   }
   return NF4_OK;
 }
 
 }  // namespace
+
+// the opaque plan of the adapter update: device memory holding the chunk table and scratch
+struct qlora_adamw_plan {
+  void* mem = nullptr;
+  int64_t chunks = 0;
+  int device = -1;
+};
 
 extern "C" {
 
@@ -213,40 +213,37 @@ int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy,
   return from_hip(nf4::launch_lora_dx(x, M, K, v, r, scale, accumulate, part, dA, stream));
 }
 
-size_t qlora_grad_sqnorm_workspace_bytes(int32_t count, const int64_t* numel) {
-  if (check_opt_list(count, numel)) return 0;
-  return nf4::opt_workspace_bytes(count, numel);
-}
-
-int qlora_grad_sqnorm(int32_t count, const float* const* grads, const int64_t* numel, double* sqnorm,
-                      int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = check_opt_list(count, numel);
-  if (st) return st;
-  if ((st = check_ptr_list(count, grads))) return st;
-  if (!sqnorm) return NF4_ERR_NULL;
-  if (reinterpret_cast<uintptr_t>(sqnorm) & 7u) return NF4_ERR_ALIGN;
-  if (ws && !aligned16(ws)) return NF4_ERR_ALIGN;
-  if (!ws || ws_bytes < nf4::opt_workspace_bytes(count, numel)) return NF4_ERR_WORKSPACE;
-  return from_hip(nf4::launch_grad_sqnorm(count, grads, numel, static_cast<double*>(ws), sqnorm,
-                                          accumulate ? 1 : 0, stream));
-}
-
-int qlora_adamw_step(int32_t count, float* const* params, const float* const* grads, float* const* exp_avg,
-                     float* const* exp_avg_sq, uint16_t* const* params_bf16, const int64_t* numel,
-                     const qlora_adamw_config* cfg, int64_t step, const double* sqnorm, float* grad_norm,
-                     hipStream_t stream) {
-  int st = check_opt_list(count, numel);
-  if (st) return st;
-  if (!cfg || !sqnorm) return NF4_ERR_NULL;
-  if ((st = check_ptr_list(count, params)) || (st = check_ptr_list(count, grads)) ||
-      (st = check_ptr_list(count, exp_avg)) || (st = check_ptr_list(count, exp_avg_sq)))
+int qlora_adamw_plan_create(int64_t count, float* const* params, const float* const* grads,
+                            float* const* exp_avg, float* const* exp_avg_sq, uint16_t* const* params_bf16,
+                            const int64_t* numel, qlora_adamw_plan** out) {
+  if (!out) return NF4_ERR_NULL;
+  *out = nullptr;
+  if (count < 1 || count > (int64_t(1) << 31)) return NF4_ERR_SHAPE;
+  if (!numel) return NF4_ERR_NULL;
+  for (int64_t i = 0; i < count; ++i)
+    if (numel[i] <= 0 || numel[i] % 4 || numel[i] > (int64_t(1) << 40)) return NF4_ERR_SHAPE;
+  if (nf4::opt_chunk_count(count, numel) > (int64_t(1) << 30)) return NF4_ERR_SHAPE;
+  int st;
+  if ((st = check_ptr_list(count, params, 15, false)) || (st = check_ptr_list(count, grads, 15, false)) ||
+      (st = check_ptr_list(count, exp_avg, 15, false)) || (st = check_ptr_list(count, exp_avg_sq, 15, false)))
     return st;
-  if (params_bf16) {
-    for (int i = 0; i < count; ++i)
-      if (params_bf16[i] && (reinterpret_cast<uintptr_t>(params_bf16[i]) & 7u)) return NF4_ERR_ALIGN;
+  if (params_bf16 && (st = check_ptr_list(count, params_bf16, 7, true))) return st;
+  qlora_adamw_plan* plan = new (std::nothrow) qlora_adamw_plan;
+  if (!plan) return NF4_ERR_HIP;
+  if (hipGetDevice(&plan->device) != hipSuccess ||
+      nf4::opt_plan_create(count, params, grads, exp_avg, exp_avg_sq, params_bf16, numel, &plan->mem,
+                           &plan->chunks) != hipSuccess) {
+    delete plan;
+    return NF4_ERR_HIP;
   }
-  if ((reinterpret_cast<uintptr_t>(sqnorm) & 7u) || (reinterpret_cast<uintptr_t>(grad_norm) & 3u))
-    return NF4_ERR_ALIGN;
+  *out = plan;
+  return NF4_OK;
+}
+
+int qlora_adamw_plan_step(const qlora_adamw_plan* plan, const qlora_adamw_config* cfg, int64_t step,
+                          double* grad_norm, hipStream_t stream) {
+  if (!plan || !cfg) return NF4_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(grad_norm) & 7u) return NF4_ERR_ALIGN;
   if (step < 1) return NF4_ERR_SHAPE;
   const qlora_adamw_config& c = *cfg;
   if (!isfinite(c.lr) || c.lr < 0.f || !(c.beta1 >= 0.f && c.beta1 < 1.f) ||
@@ -254,9 +251,17 @@ int qlora_adamw_step(int32_t count, float* const* params, const float* const* gr
       !(c.weight_decay >= 0.f) || !isfinite(c.weight_decay) || isnan(c.max_grad_norm) ||
       isinf(c.max_grad_norm))
     return NF4_ERR_SHAPE;
-  return from_hip(nf4::launch_adamw(count, params, grads, exp_avg, exp_avg_sq, params_bf16, numel, c.lr,
-                                    c.beta1, c.beta2, c.eps, c.weight_decay, c.max_grad_norm, step,
-                                    sqnorm, grad_norm, stream));
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return NF4_ERR_HIP;
+  return from_hip(nf4::opt_plan_step(plan->mem, plan->chunks, c.lr, c.beta1, c.beta2, c.eps,
+                                     c.weight_decay, c.max_grad_norm, step, grad_norm, stream));
+}
+
+int qlora_adamw_plan_destroy(qlora_adamw_plan* plan) {
+  if (!plan) return NF4_OK;
+  const hipError_t e = hipFree(plan->mem);
+  delete plan;
+  return from_hip(e);
 }
 
 }  // extern "C"

@@ -59,19 +59,16 @@ hipError_t launch_merge(const uint8_t* packed, const uint8_t* scale_q, const flo
                         int64_t K, const uint16_t* A, const uint16_t* B, int r, float scale, uint16_t* out,
                         hipStream_t stream);
 
-// Adapter update: squared gradient norm (fixed-order partial sums in double) and AdamW over a list
-// of at most kOptMaxTensors fp32 tensors, each a multiple of 4 elements.
-constexpr int kOptMaxTensors = 32;
-size_t opt_workspace_bytes(int count, const int64_t* numel);
-// *sqnorm = (accumulate ? *sqnorm : 0) + sum of squares of every element; ws holds
-// opt_workspace_bytes(count, numel) bytes
-hipError_t launch_grad_sqnorm(int count, const float* const* grads, const int64_t* numel, double* ws,
-                              double* sqnorm, int accumulate, hipStream_t stream);
-// clipped AdamW step (see optim.hip); params_bf16 may be null, or hold null entries
-hipError_t launch_adamw(int count, float* const* params, const float* const* grads, float* const* exp_avg,
-                        float* const* exp_avg_sq, uint16_t* const* params_bf16, const int64_t* numel,
-                        float lr, float beta1, float beta2, float eps, float weight_decay,
-                        float max_norm, int64_t step, const double* sqnorm, float* grad_norm,
-                        hipStream_t stream);
+// Adapter update over a plan: a device table of 4096-value chunk descriptors of every tensor.
+int64_t opt_chunk_count(int64_t count, const int64_t* numel);
+// allocates the plan's device memory (hipMalloc) and uploads the table (hipMemcpy, blocking)
+hipError_t opt_plan_create(int64_t count, float* const* params, const float* const* grads,
+                           float* const* exp_avg, float* const* exp_avg_sq,
+                           uint16_t* const* params_bf16, const int64_t* numel, void** dev_mem,
+                           int64_t* chunks_out);
+// global squared norm, then the clipped AdamW step: three kernels on `stream`
+hipError_t opt_plan_step(void* dev_mem, int64_t chunks, float lr, float beta1, float beta2, float eps,
+                         float weight_decay, float max_norm, int64_t step, double* grad_norm,
+                         hipStream_t stream);
 
 }  // namespace nf4

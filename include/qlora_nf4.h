@@ -14,8 +14,8 @@
  *                     dA = s B^T G, dB = s G A^T with G = dY^T X; W gets no gradient.
  *   qlora_merge       section "Quality loss at merge time": the adapter merged into the
  *                     dequantised base, W~ + s B A, served in bf16.
- *   qlora_grad_sqnorm, qlora_adamw_step   sections "The algorithm, step by step" and "Minimal
- *                     implementation": global gradient-norm clipping, then AdamW over A and B.
+ *   qlora_adamw_plan_*   sections "The algorithm, step by step" and "Minimal implementation":
+ *                     global gradient-norm clipping, then AdamW over A and B.
  *
  * Data formats (all little-endian, row-major):
  *   W        N x K (out x in, like nn.Linear), K % 64 == 0, N % 16 == 0. Blocks of 64 run along K.
@@ -143,43 +143,49 @@ int qlora_merge(const nf4_weight *W, const uint16_t *A, const uint16_t *B, int32
  * (decoupled weight decay); for clipped gradient g = c * grad at step t = 1, 2, ...:
  *   p <- p * (1 - lr*weight_decay);  m <- beta1*m + (1-beta1)*g;  v <- beta2*v + (1-beta2)*g^2;
  *   p <- p - (lr / (1 - beta1^t)) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps),
- * c = min(1, max_grad_norm / (norm + 1e-6)) (1 when max_grad_norm <= 0), norm = sqrt(*sqnorm).
- * Tensor lists are HOST arrays of `count` device pointers (1 <= count <= 32), each tensor fp32 with
- * numel[i] > 0 a multiple of 4 elements and 16-byte aligned. A model with more adapter tensors
- * calls qlora_grad_sqnorm once per list with accumulate = 1 after the first, then
- * qlora_adamw_step once per list with the same sqnorm. Paged and 8-bit optimiser state are not
+ * c = min(1, max_grad_norm / (norm + 1e-6)) (1 when max_grad_norm <= 0), norm the L2 norm over
+ * every gradient value of every tensor of the plan. Paged and 8-bit optimiser state are not
  * provided. */
 typedef struct {
-  float lr;             /* learning rate (the pages use 2e-4) */
+  float lr;             /* learning rate (the pages use 2e-4); >= 0 */
   float beta1, beta2;   /* in [0, 1) */
   float eps;            /* > 0 */
   float weight_decay;   /* >= 0 */
   float max_grad_norm;  /* clipping threshold; <= 0 disables clipping */
 } qlora_adamw_config;
 
-/* Workspace bytes qlora_grad_sqnorm needs for this list (8 bytes per 4096 elements, rounded up per
- * tensor); 0 if the list is invalid. numel is a host array. */
-size_t qlora_grad_sqnorm_workspace_bytes(int32_t count, const int64_t *numel);
+/* Opaque: the device pointers and sizes of a set of adapter tensors, as a table of 4096-value
+ * chunk descriptors in device memory, so that one step over any number of tensors is three
+ * kernel launches. */
+typedef struct qlora_adamw_plan qlora_adamw_plan;
 
-/* *sqnorm = (accumulate ? *sqnorm : 0) + the sum of squares of every element of grads[0..count).
- *   sqnorm  one double in device memory, 8-byte aligned.  ws  device workspace, 16-byte aligned.
- * The sum runs in double over fixed 4096-element chunks and a fixed order, so it is reproducible.
- * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (count or numel), NF4_ERR_ALIGN, NF4_ERR_WORKSPACE. */
-int qlora_grad_sqnorm(int32_t count, const float *const *grads, const int64_t *numel, double *sqnorm,
-                      int accumulate, void *ws, size_t ws_bytes, hipStream_t stream);
+/* Build a plan over `count` tensors (count >= 1). The arguments are HOST arrays of `count` entries:
+ *   params      fp32 master weights (A and B of every adapted linear), updated in place
+ *   grads       fp32 gradients of the same sizes
+ *   exp_avg, exp_avg_sq   fp32 first and second moments, updated in place (zero before step 1)
+ *   params_bf16 NULL, or bf16 buffers that receive the new weights rounded to nearest even (the A
+ *               and B the next forward reads); entries may be NULL
+ *   numel       values per tensor: > 0 and a multiple of 4
+ * Every pointer 16-byte aligned (bf16 buffers: 8-byte). The tensors must stay allocated at these
+ * addresses while the plan is used. Allocates device memory on the current device (about 12 bytes
+ * per 1024 values) and blocks until the table is uploaded. *out receives the plan, or NULL.
+ * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (count or numel), NF4_ERR_ALIGN, NF4_ERR_HIP (allocation). */
+int qlora_adamw_plan_create(int64_t count, float *const *params, const float *const *grads,
+                            float *const *exp_avg, float *const *exp_avg_sq, uint16_t *const *params_bf16,
+                            const int64_t *numel, qlora_adamw_plan **out);
 
-/* One clipped AdamW step over params[i] (fp32 master weights, updated in place) with gradients
- * grads[i] and moments exp_avg[i], exp_avg_sq[i] (fp32, updated in place; zero before step 1).
- * params_bf16 may be NULL; otherwise params_bf16[i] (may itself be NULL) receives the new weights
- * rounded to bf16 (nearest even), the A or B the next forward reads. sqnorm is the device total
- * from qlora_grad_sqnorm over every adapter gradient of the model. grad_norm (device float, may be
- * NULL) receives sqrt(*sqnorm) for logging. step counts from 1.
- * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (count, numel, step or a config value out of range),
- * NF4_ERR_ALIGN. */
-int qlora_adamw_step(int32_t count, float *const *params, const float *const *grads, float *const *exp_avg,
-                     float *const *exp_avg_sq, uint16_t *const *params_bf16, const int64_t *numel,
-                     const qlora_adamw_config *cfg, int64_t step, const double *sqnorm, float *grad_norm,
-                     hipStream_t stream);
+/* One clipped AdamW step over every tensor of the plan, on `stream`, on the plan's device:
+ * the squared gradient norm (partial sums in double over 16384-value groups, added in a fixed
+ * order, so it is reproducible bit for bit), then the elementwise update. grad_norm (device
+ * double, may be NULL) receives the norm before clipping. step counts from 1. Steps on one plan
+ * must not overlap (they share the plan's scratch).
+ * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (step < 1 or a config value out of range), NF4_ERR_ALIGN,
+ * NF4_ERR_HIP (launch failure, or a device other than the plan's is current). */
+int qlora_adamw_plan_step(const qlora_adamw_plan *plan, const qlora_adamw_config *cfg, int64_t step,
+                          double *grad_norm, hipStream_t stream);
+
+/* Free the plan (its device memory). No step on it may still be running. NULL is a no-op. */
+int qlora_adamw_plan_destroy(qlora_adamw_plan *plan);
 
 /* Workspace bytes that qlora_linear_fwd and qlora_linear_bwd need for these sizes (the larger of
  * the two). Returns 0 for invalid sizes. */

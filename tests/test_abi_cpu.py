@@ -162,55 +162,38 @@ def _numels(*vals):
     return (ctypes.c_int64 * len(vals))(*vals)
 
 
-def test_grad_sqnorm_workspace_and_validation():
-    ws_bytes = lib.qlora_grad_sqnorm_workspace_bytes
-    # one double per 4096-element chunk, rounded up per tensor
-    assert ws_bytes(2, _numels(4096, 4100)) == 8 * 3
-    assert ws_bytes(1, _numels(16 * 4096 * 8)) == 8 * 128
-    assert ws_bytes(0, _numels(4)) == 0
-    assert ws_bytes(33, _numels(*([4] * 33))) == 0
-    assert ws_bytes(1, _numels(6)) == 0          # not a multiple of 4
-    assert ws_bytes(1, _numels(0)) == 0
-    f = lib.qlora_grad_sqnorm
-    n2, g2 = _numels(4096, 8192), _ptrs(FAKE, FAKE)
-    assert f(0, g2, n2, FAKE, 0, FAKE, 1 << 20, None) == q.NF4_ERR_SHAPE
-    assert f(33, _ptrs(*([FAKE] * 33)), _numels(*([4] * 33)), FAKE, 0, FAKE, 1 << 20, None) == q.NF4_ERR_SHAPE
-    assert f(2, g2, _numels(4096, 10), FAKE, 0, FAKE, 1 << 20, None) == q.NF4_ERR_SHAPE
-    assert f(2, g2, _numels(-4, 8), FAKE, 0, FAKE, 1 << 20, None) == q.NF4_ERR_SHAPE
-    assert f(2, None, n2, FAKE, 0, FAKE, 1 << 20, None) == q.NF4_ERR_NULL
-    assert f(2, _ptrs(FAKE, None), n2, FAKE, 0, FAKE, 1 << 20, None) == q.NF4_ERR_NULL
-    assert f(2, _ptrs(FAKE, MISALIGNED), n2, FAKE, 0, FAKE, 1 << 20, None) == q.NF4_ERR_ALIGN
-    assert f(2, g2, n2, None, 0, FAKE, 1 << 20, None) == q.NF4_ERR_NULL
-    assert f(2, g2, n2, FAKE + 4, 0, FAKE, 1 << 20, None) == q.NF4_ERR_ALIGN
-    assert f(2, g2, n2, FAKE, 0, MISALIGNED, 1 << 20, None) == q.NF4_ERR_ALIGN
-    assert f(2, g2, n2, FAKE, 0, None, 1 << 20, None) == q.NF4_ERR_WORKSPACE
-    assert f(2, g2, n2, FAKE, 0, FAKE, 8 * 3 - 1, None) == q.NF4_ERR_WORKSPACE
+def test_adamw_plan_create_validation():
+    f = lib.qlora_adamw_plan_create
+    l2, n2 = _ptrs(FAKE, FAKE), _numels(4096, 8192)
+    out = ctypes.c_void_p(FAKE)
 
+    def call(count=2, params=l2, grads=l2, m=l2, v=l2, pb=None, numel=n2, out_ref=True):
+        return f(count, params, grads, m, v, pb, numel, ctypes.byref(out) if out_ref else None)
 
-def test_adamw_step_validation():
-    f = lib.qlora_adamw_step
-    good = q.AdamWConfig().c_struct()
-    n2, l2 = _numels(4096, 8192), _ptrs(FAKE, FAKE)
-
-    def call(count=2, params=l2, grads=l2, m=l2, v=l2, pb=None, numel=n2, cfg=good, step=1,
-             sqnorm=FAKE, norm=None):
-        return f(count, params, grads, m, v, pb, numel, None if cfg is None else ctypes.byref(cfg),
-                 step, sqnorm, norm, None)
-
+    assert call(out_ref=False) == q.NF4_ERR_NULL
     assert call(count=0) == q.NF4_ERR_SHAPE
-    assert call(count=33, numel=_numels(*([4] * 33))) == q.NF4_ERR_SHAPE
-    assert call(numel=_numels(4096, 2)) == q.NF4_ERR_SHAPE
-    assert call(cfg=None) == q.NF4_ERR_NULL
-    assert call(sqnorm=None) == q.NF4_ERR_NULL
+    assert out.value is None                      # cleared on every error
+    assert call(numel=None) == q.NF4_ERR_NULL
+    assert call(numel=_numels(4096, 10)) == q.NF4_ERR_SHAPE
+    assert call(numel=_numels(0, 8)) == q.NF4_ERR_SHAPE
+    assert call(numel=_numels(-4, 8)) == q.NF4_ERR_SHAPE
     for key in ("params", "grads", "m", "v"):
-        assert call(**{key: _ptrs(FAKE, None)}) == q.NF4_ERR_NULL
         assert call(**{key: None}) == q.NF4_ERR_NULL
+        assert call(**{key: _ptrs(FAKE, None)}) == q.NF4_ERR_NULL
         assert call(**{key: _ptrs(MISALIGNED, FAKE)}) == q.NF4_ERR_ALIGN
     assert call(pb=_ptrs(FAKE, FAKE + 2)) == q.NF4_ERR_ALIGN
-    assert call(sqnorm=FAKE + 4) == q.NF4_ERR_ALIGN
-    assert call(norm=FAKE + 2) == q.NF4_ERR_ALIGN
-    assert call(step=0) == q.NF4_ERR_SHAPE
+
+
+def test_adamw_plan_step_validation():
+    # every check below returns before the plan is dereferenced, so a fake handle is safe
+    f = lib.qlora_adamw_plan_step
+    good = q.AdamWConfig().c_struct()
+    assert f(None, ctypes.byref(good), 1, None, None) == q.NF4_ERR_NULL
+    assert f(FAKE, None, 1, None, None) == q.NF4_ERR_NULL
+    assert f(FAKE, ctypes.byref(good), 1, FAKE + 4, None) == q.NF4_ERR_ALIGN
+    assert f(FAKE, ctypes.byref(good), 0, None, None) == q.NF4_ERR_SHAPE
     for bad in (dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0), dict(lr=-1.0),
                 dict(weight_decay=-0.5), dict(lr=float("nan")), dict(max_grad_norm=float("inf"))):
         cfg = q.AdamWConfig(**{**q.AdamWConfig().__dict__, **bad}).c_struct()
-        assert call(cfg=cfg) == q.NF4_ERR_SHAPE, bad
+        assert f(FAKE, ctypes.byref(cfg), 1, None, None) == q.NF4_ERR_SHAPE, bad
+    assert lib.qlora_adamw_plan_destroy(None) == q.NF4_OK

@@ -9,8 +9,9 @@ v is a sum of non-negative terms, so its error is relative: |dv| <= 8u v. m can 
 error is bounded by the magnitudes that enter it: |dm| <= 8u (beta1 |m0| + (1 - beta1) c |g|).
 The step divides by sqrt(v)/sqrt(1 - beta2^t) + eps (positive terms, a relative error) and
 subtracts from the decayed weight: |dp| <= 16u (|p0| (1 - lr wd) + lr/(1 - beta1^t) mag_m / denom).
-The squared norm is a double sum of exact squares (relative 1e-12), the reported norm its float
-rounding, and the bf16 copy must equal torch's round-to-nearest-even of the GPU's fp32 weights.
+The norm is a double sum of exact squares (relative 1e-12), and the bf16 copy must equal torch's
+round-to-nearest-even of the GPU's fp32 weights. Every call goes through one plan
+(qlora_adamw_plan_*), which covers any number of tensors.
 """
 import numpy as np
 import pytest
@@ -37,32 +38,31 @@ def _cfgs(lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad
 
 
 class _State:
-    def __init__(self, masters, with_bf16=True):
+    def __init__(self, masters, cfg, with_bf16=True, bf16_none=()):
         import torch
+        import bit_nf4_quantised_amd as q
         self.p = [to_dev(x) for x in masters]
         self.m = [torch.zeros_like(x) for x in self.p]
         self.v = [torch.zeros_like(x) for x in self.p]
         self.g = [torch.empty_like(x) for x in self.p]
-        self.pb = [torch.full((x.numel(),), 0x7fc1, dtype=torch.int16, device=dev()) for x in self.p] \
-            if with_bf16 else None
-        self.sq = torch.full((1,), -1.0, dtype=torch.float64, device=dev())
-        self.norm = torch.full((1,), -1.0, dtype=torch.float32, device=dev())
+        self.pb = None
+        if with_bf16:
+            self.pb = [None if i in bf16_none else
+                       torch.full((x.numel(),), 0x7fc1, dtype=torch.int16, device=dev())
+                       for i, x in enumerate(self.p)]
+        self.norm = torch.full((1,), -1.0, dtype=torch.float64, device=dev())
+        self.plan = q.AdamWPlan(self.p, self.g, self.m, self.v, self.pb, cfg)
 
     def host(self):
         f = lambda ts: [t.cpu().numpy().astype(np.float64) for t in ts]  # noqa: E731
         return f(self.p), f(self.m), f(self.v)
 
 
-def _step_gpu(st, grads, step, cfg, helper):
+def _step_gpu(st, grads, step):
     import torch
-    import bit_nf4_quantised_amd as q
     for t, g in zip(st.g, grads):
-        t.copy_(torch.from_numpy(g))
-    if helper:
-        q.adamw_update(st.p, st.g, st.m, st.v, step, cfg, st.pb, st.norm, st.sq)
-    else:
-        q.qlora_grad_sqnorm(st.g, st.sq)
-        q.qlora_adamw_step(st.p, st.g, st.m, st.v, step, st.sq, cfg, st.pb, st.norm)
+        t.copy_(torch.from_numpy(g).reshape(t.shape))
+    st.plan.step(step, st.norm)
     torch.cuda.synchronize()
 
 
@@ -91,21 +91,19 @@ def _check_step(name, prev, grads, got, ref, ocfg, step, norm):
         f"m {worst[0]:.3f} v {worst[1]:.3f} p {worst[2]:.3f}")
 
 
-def _run(name, shapes, cfg_kw, steps, sigma, helper=False, with_bf16=True, workload="llama8b"):
+def _run(name, shapes, cfg_kw, steps, sigma, with_bf16=True, workload="llama8b"):
     import torch
     cfg, ocfg = _cfgs(**cfg_kw)
-    st = _State(wl.adapter_masters(workload, shapes), with_bf16)
+    st = _State(wl.adapter_masters(workload, shapes), cfg, with_bf16)
     for step in range(1, steps + 1):
         grads = wl.adapter_grads(workload, shapes, step, sigma)
         prev = st.host()
-        _step_gpu(st, grads, step, cfg, helper)
+        _step_gpu(st, grads, step)
         g64 = [g.astype(np.float64) for g in grads]
         ref = oracle.adamw_step(prev[0], g64, prev[1], prev[2], step, ocfg)
         sq_ref = sum(float(np.sum(g * g)) for g in g64)
-        sq = float(st.sq.cpu()[0])
-        assert sq == pytest.approx(sq_ref, rel=1e-12)
         assert ref[3] == pytest.approx(np.sqrt(sq_ref), rel=1e-15)
-        assert float(st.norm.cpu()[0]) == _f32(np.sqrt(sq))
+        assert float(st.norm.cpu()[0]) == pytest.approx(ref[3], rel=1e-12)
         got = st.host()
         _check_step(name, prev, grads, got, ref, ocfg, step, ref[3])
         if st.pb is not None:
@@ -130,38 +128,52 @@ def test_llama70b_layer_rank64():
     _run("llama70b-layer", shapes, dict(lr=1e-4, weight_decay=0.0), 2, 2e-4, workload="llama70b")
 
 
-def test_ragged_tensors_and_many_lists():
-    # sizes that end inside a 4096-element chunk and inside a float4, 40 tensors (two lists of at
-    # most 32, the squared norm accumulated across them), no bf16 copies
-    shapes = [(16, 40), (24, 16), (4100, 1), (1, 4), (3, 4), (4096, 1), (8196, 1), (16, 8)] * 5
-    log(f"[optim] ragged: {len(shapes)} tensors through the list-splitting helper")
-    _run("ragged", shapes, dict(lr=3e-3, weight_decay=0.05), 4, 0.05, helper=True, with_bf16=False)
+def test_ragged_and_tiny_tensors():
+    # sizes that end inside a 4096-value chunk and inside a float4, and a chunk count that leaves the
+    # last norm group of four partly empty (1 + 6 + 2 + 1 + 1 + 1 + 3 + 1 chunks per pattern, x 5
+    # = 80, plus 3 single-chunk tensors: 83 chunks in 21 groups); no bf16 copies
+    shapes = [(16, 40), (24, 1024), (4100, 1), (1, 4), (3, 4), (4096, 1), (8196, 1), (16, 8)] * 5 + \
+        [(4, 1)] * 3
+    log(f"[optim] ragged: {len(shapes)} tensors")
+    _run("ragged", shapes, dict(lr=3e-3, weight_decay=0.05), 4, 0.05, with_bf16=False)
 
 
 def test_zero_gradient_and_large_step():
-    import bit_nf4_quantised_amd as q
     import torch
     shapes = [(16, 4096), (4096, 16)]
     cfg, ocfg = _cfgs(lr=1e-3, weight_decay=0.1)
-    st = _State(wl.adapter_masters("llama8b", shapes))
+    st = _State(wl.adapter_masters("llama8b", shapes), cfg, bf16_none=(1,))
     p0 = st.host()
     zeros = [np.zeros(s, dtype=np.float32) for s in shapes]
-    _step_gpu(st, zeros, 1000, cfg, False)
-    assert float(st.sq.cpu()[0]) == 0.0 and float(st.norm.cpu()[0]) == 0.0
+    _step_gpu(st, zeros, 1000)
+    assert float(st.norm.cpu()[0]) == 0.0
     got = st.host()
     ref = oracle.adamw_step(p0[0], [z.astype(np.float64) for z in zeros], p0[1], p0[2], 1000, ocfg)
     _check_step("zero-grad", p0, zeros, got, ref, ocfg, 1000, 0.0)
     assert all(np.all(x == 0) for x in got[1] + got[2])
-    # a None entry in the bf16 list leaves that buffer alone
-    before = st.pb[1].clone()
-    q.qlora_adamw_step(st.p, st.g, st.m, st.v, 1001, st.sq, cfg, [st.pb[0], None], None)
-    torch.cuda.synchronize()
-    assert torch.equal(st.pb[1], before)
+    assert torch.equal(st.pb[0].cpu(), st.p[0].cpu().to(torch.bfloat16).view(torch.int16).reshape(-1))
+
+
+def test_norm_is_reproducible_and_scales_exactly():
+    # the same gradients give the same norm bit for bit; doubling every gradient (exact in fp32)
+    # doubles the norm exactly (sqrt(4 s) = 2 sqrt(s) in IEEE arithmetic)
+    shapes = wl.adapter_shapes(wl.WORKLOADS["llama8b"])
+    cfg, _ = _cfgs()
+    st = _State(wl.adapter_masters("llama8b", shapes), cfg)
+    grads = wl.adapter_grads("llama8b", shapes, 9)
+    _step_gpu(st, grads, 1)
+    first = float(st.norm.cpu()[0])
+    _step_gpu(st, grads, 2)
+    assert float(st.norm.cpu()[0]) == first
+    _step_gpu(st, [2 * g for g in grads], 3)
+    assert float(st.norm.cpu()[0]) == 2 * first
+    ref = np.sqrt(sum(float(np.sum(g.astype(np.float64) ** 2)) for g in grads))
+    assert first == pytest.approx(ref, rel=1e-12)
 
 
 def test_full_model_adapters_one_step():
     # the launch configuration the benchmark times: every adapter of a 32-layer Llama-3.1-8B at
-    # rank 16 (448 tensors, 41.9 M values), one step, every element against the oracle
+    # rank 16 (448 tensors, 41.9 M values) in one plan, one step, every value against the oracle
     shapes = wl.adapter_shapes(wl.WORKLOADS["llama8b"], wl.LLAMA8B_LAYERS)
     log(f"[optim] full model: {len(shapes)} tensors")
-    _run("llama8b-model", shapes, {}, 1, 1e-3, helper=True)
+    _run("llama8b-model", shapes, {}, 1, 1e-3)
