@@ -80,12 +80,18 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# what the dominant kernel (the fused GEMM) is built from: its sources and the compile flags
+ROOFLINE_KERNEL_SOURCES = ("gemm.hip", "common.h")
+
+
 def kernel_source_hash() -> str:
+    from bit_nf4_quantised_amd import build as nf4_build
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_nf4_quantised_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in ROOFLINE_KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
+    h.update(" ".join(nf4_build.COMMON).encode())
     return h.hexdigest()[:16]
 
 
