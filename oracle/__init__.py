@@ -17,7 +17,8 @@ torch's own float8/bfloat16 casts, closed forms and finite differences. None is 
 """
 from .nf4 import (NF4_ZERO_INDEX, codebook, quantize_blocks, pack_nibbles, unpack_nibbles,
                   quantize, e4m3_value, e4m3_unit_values, double_quant, dequant_scales,
-                  bf16_bits_from_f32, f32_from_bf16_bits, dequant, storage_bits)
+                  bf16_bits_from_f32, f32_from_bf16_bits, dequant, storage_bits, quantize_with,
+                  dequant_blocks)
 from .linear import linear_fwd, linear_bwd, linear_fwd_f64, linear_bwd_f64, linear_bwd_sampled
 from .merge import bf16_bits_from_f64, merge
 from .optim import AdamWConfig, global_grad_norm, clip_coefficient, adamw_step
@@ -26,7 +27,7 @@ from .toy import int4_codebook, fp4_codebook, relative_mse, residual_capture
 __all__ = [
     "NF4_ZERO_INDEX", "codebook", "quantize_blocks", "pack_nibbles", "unpack_nibbles", "quantize",
     "e4m3_value", "e4m3_unit_values", "double_quant", "dequant_scales", "bf16_bits_from_f32",
-    "f32_from_bf16_bits", "dequant", "storage_bits", "linear_fwd", "linear_bwd", "linear_fwd_f64",
+    "f32_from_bf16_bits", "dequant", "storage_bits", "quantize_with", "dequant_blocks", "linear_fwd", "linear_bwd", "linear_fwd_f64",
     "linear_bwd_f64", "linear_bwd_sampled", "bf16_bits_from_f64", "merge", "AdamWConfig",
     "global_grad_norm", "clip_coefficient", "adamw_step", "int4_codebook",
     "fp4_codebook", "relative_mse", "residual_capture",

@@ -214,6 +214,28 @@ def dequant(packed, codes, c2, numel: int) -> np.ndarray:
     return bf16_bits_from_f32(w32).reshape(-1)
 
 
+def quantize_with(w, codes, blocksize: int):
+    """Blockwise absmax quantisation with any ascending codebook and blocksize, packed two indices
+    per byte: the format the toy run compares ("QLoRA, explained", A toy run; the blocksize
+    discussion). Returns (packed uint8 [numel/2], absmax float32 [numel/blocksize])."""
+    idx, absmax = quantize_blocks(w, blocksize, codes)
+    return pack_nibbles(idx), absmax
+
+
+def dequant_blocks(packed, scales, codes, blocksize: int, numel: int) -> np.ndarray:
+    """bf16(fl32(q[idx] * s_b)) with one fp32 scale s_b per block of ``blocksize`` values; returns
+    uint16 bit patterns [numel]. The scale is the fp32 absmax itself when the scales are not double
+    quantised ("QLoRA, explained", Double quantisation: the baseline that stores fp32 scales), or
+    c1' = fl32(e4m3 * c2) from ``dequant_scales`` when they are."""
+    codes = np.asarray(codes, dtype=np.float32)
+    idx = unpack_nibbles(packed, numel).reshape(-1, blocksize)
+    if idx.max(initial=0) >= codes.size:
+        raise ValueError("index outside the codebook")
+    s = np.asarray(scales, dtype=np.float32).reshape(-1)
+    w32 = (codes[idx] * s[:, None]).astype(np.float32)      # one IEEE float32 multiply, RNE
+    return bf16_bits_from_f32(w32).reshape(-1)
+
+
 def storage_bits(blocksize: int = BLOCK, double_quantised: bool = True, group: int = DQ_GROUP) -> float:
     """Bits per parameter: 4-bit index + scale storage ("QLoRA, explained", Double quantisation and
     the toy run's blocksize discussion): fp32 scales cost 32/B; with double quantisation 8/B plus

@@ -260,3 +260,47 @@ def test_storage_bits_match_pages():
     assert oracle.storage_bits(16, False) == g["bs16_no_dq"]
     assert round(oracle.storage_bits(16), 3) == g["bs16_dq"]
     assert oracle.storage_bits(64, False) - 4 == g["bs64_fp32_scales_overhead"]
+
+
+# ---------------------------------------------------------------- codebook and blocksize variants
+@pytest.mark.parametrize("book,bs", [("fp4", 16), ("int4", 256), ("nf4", 32), ("fp4", 4096)])
+def test_dequant_blocks_matches_torch_composition(book, bs):
+    """bf16(fl32(q[idx] * absmax)) rebuilt with float32 torch tensors and torch's bf16 cast, for
+    the toy's other codebooks and other blocksizes, with fp32 scales (no double quantisation)."""
+    from oracle import toy
+    codes = {"nf4": oracle.codebook(), "fp4": toy.fp4_codebook(), "int4": toy.int4_codebook()}[book]
+    rng = np.random.default_rng(bs)
+    w = (rng.standard_normal(8192) * 0.03).astype(np.float32)
+    w[:bs] = 0.0                                                   # one all-zero block
+    packed, absmax = oracle.quantize_with(w, codes, bs)
+    got = oracle.dequant_blocks(packed, absmax, codes, bs, w.size)
+    idx = torch.from_numpy(oracle.unpack_nibbles(packed).astype(np.int64))
+    q = torch.from_numpy(codes)
+    ref = (q[idx].view(-1, bs) * torch.from_numpy(absmax)[:, None]).to(torch.bfloat16)
+    assert np.array_equal(got, ref.view(torch.int16).numpy().view(np.uint16).reshape(-1))
+    assert np.all(got[:bs] == 0)
+
+
+def test_dequant_blocks_reduces_to_the_nf4_path():
+    """NF4, blocksize 64, double-quantised scales: the generic dequantisation is the two-level one."""
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal(64 * 520) * 0.02).astype(np.float32)
+    packed, c1 = oracle.quantize_with(w, oracle.codebook(), 64)
+    assert np.array_equal(packed, oracle.quantize(w)[0])
+    codes, c2 = oracle.double_quant(c1)
+    got = oracle.dequant_blocks(packed, oracle.dequant_scales(codes, c2), oracle.codebook(), 64, w.size)
+    assert np.array_equal(got, oracle.dequant(packed, codes, c2, w.size))
+
+
+@pytest.mark.parametrize("bs", [16, 32, 128, 1024])
+def test_quantize_with_blocksizes_matches_brute_force(bs):
+    from oracle import toy
+    rng = np.random.default_rng(bs + 1)
+    for codes in (oracle.codebook(), toy.fp4_codebook(), toy.int4_codebook()):
+        w = rng.standard_normal(2 * bs).astype(np.float32)
+        packed, absmax = oracle.quantize_with(w, codes, bs)
+        idx = oracle.unpack_nibbles(packed)
+        for bi in range(2):
+            want, c = brute_nearest(w[bi * bs:(bi + 1) * bs], codes)
+            assert list(idx[bi * bs:(bi + 1) * bs]) == want
+            assert Fraction(float(absmax[bi])) == c
