@@ -303,6 +303,36 @@ def bandwidth_paths(torch, q, dev, args):
                      "bytes_per_weight": round(per_weight_bytes, 4)}
         log(f"[bench] {name}: {gbps:.0f} GB/s")
     dequant_gbps = res["dequant"]["GBps"]
+
+    # codebook and blocksize variants over the same pool: quantise, and dequantise with fp32 scales
+    # (no double quantisation), 16 launches each (two passes over the pool)
+    variants = {}
+    nvar = 16
+    for book, bs in (("nf4", 64), ("fp4", 64), ("int4", 64), ("nf4", 16), ("nf4", 4096)):
+        am = [torch.empty(numel // bs, dtype=torch.float32, device=dev) for _ in range(wl.STREAM_POOL)]
+
+        def vq(i, book=book, bs=bs, am=am):
+            j = i % wl.STREAM_POOL
+            q.q4_quantize(pool[j], book, bs, qws[j].packed, am[j])
+
+        def vd(i, book=book, bs=bs, am=am):
+            j = i % wl.STREAM_POOL
+            q.q4_dequant(qws[j].packed, numel, book, bs, outs[i % 2], absmax=am[j])
+
+        for i in range(wl.STREAM_POOL):
+            vq(i)
+        torch.cuda.synchronize()
+        ent = {}
+        for name, fn, per_weight in (("quantize", vq, 4 + 0.5 + 4 / bs), ("dequant_fp32_scales", vd, 0.5 + 4 / bs + 2)):
+            ms = timed(fn, nvar, torch)
+            gbps = numel * per_weight / (ms * 1e-3) / 1e9
+            ent[name] = {"GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                         "bytes_per_weight": round(per_weight, 4), "us_per_matrix": round(ms * 1e3, 2)}
+        variants[f"{book}_bs{bs}"] = ent
+        log(f"[bench] variant {book} bs {bs}: quantise {ent['quantize']['GBps']:.0f} GB/s, "
+            f"dequantise {ent['dequant_fp32_scales']['GBps']:.0f} GB/s")
+        del am
+    res["variants_4096x14336"] = variants
     del pool, qws, absmax, outs
     torch.cuda.empty_cache()
 

@@ -59,6 +59,9 @@ _SIGS = {
     "qlora_linear_fwd_recompute": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz,
                                                   _p]),
     "qlora_merge": (ctypes.c_int, [_W, _p, _p, _i32, _f32, _p, _p]),
+    "q4_codebook_values": (ctypes.c_int, [_i32, ctypes.POINTER(ctypes.c_float)]),
+    "q4_quantize": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _p]),
+    "q4_dequant": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _p, _p, _p]),
     "qlora_adamw_plan_create": (ctypes.c_int, [_i64, _p, _p, _p, _p, _p, _p,
                                                ctypes.POINTER(ctypes.c_void_p)]),
     "qlora_adamw_plan_step": (ctypes.c_int, [_p, ctypes.POINTER(CAdamWConfig), _i64, _p, _p]),
@@ -224,6 +227,52 @@ def qlora_linear_bwd(weight: NF4Weight, x, dy, A, B, scale: float, u, dx, dA, dB
            "qlora_linear_bwd")
 
 
+# ------------------------------------------------------------------------- format variants
+Q4_CODEBOOKS = {"nf4": 0, "fp4": 1, "int4": 2}
+
+
+def _book(codebook) -> int:
+    if isinstance(codebook, str):
+        if codebook not in Q4_CODEBOOKS:
+            raise ValueError(f"codebook must be one of {sorted(Q4_CODEBOOKS)}")
+        return Q4_CODEBOOKS[codebook]
+    return int(codebook)
+
+
+def q4_codebook_values(codebook) -> list:
+    out = (ctypes.c_float * 16)()
+    n = lib.q4_codebook_values(_book(codebook), out)
+    if n < 0:
+        raise NF4Error(-n, "q4_codebook_values")
+    return list(out)[:n]
+
+
+def q4_quantize(w, codebook, blocksize: int, packed, absmax, stream=None) -> None:
+    """Blockwise absmax quantisation with the NF4, FP4 or INT4 codebook and blocksize 16..4096."""
+    _dtype(w, torch.float32); _dtype(packed, torch.uint8); _dtype(absmax, torch.float32)
+    n = w.numel()
+    if packed.numel() * 2 != n or absmax.numel() * blocksize != n:
+        raise ValueError("output sizes must be numel/2 and numel/blocksize")
+    _check(lib.q4_quantize(_ptr(w), n, _book(codebook), blocksize, _ptr(packed), _ptr(absmax),
+                           _stream(stream)), "q4_quantize")
+
+
+def q4_dequant(packed, numel: int, codebook, blocksize: int, out, absmax=None, scale_q=None,
+               scale_c2=None, stream=None) -> None:
+    """bf16 weights from packed indices and either fp32 scales (absmax) or double-quantised ones
+    (scale_q, scale_c2)."""
+    _dtype(packed, torch.uint8); _dtype(out, *_BF16); _dtype(absmax, torch.float32)
+    _dtype(scale_q, torch.uint8); _dtype(scale_c2, torch.float32)
+    if packed.numel() * 2 != numel or out.numel() != numel:
+        raise ValueError("packed must hold numel/2 bytes and out numel values")
+    nb = numel // blocksize
+    if (absmax is not None and absmax.numel() != nb) or (scale_q is not None and scale_q.numel() != nb) \
+            or (scale_c2 is not None and scale_c2.numel() != (nb + 255) // 256):
+        raise ValueError("scale sizes do not match numel / blocksize")
+    _check(lib.q4_dequant(_ptr(packed), numel, _book(codebook), blocksize, _ptr(absmax), _ptr(scale_q),
+                          _ptr(scale_c2), _ptr(out), _stream(stream)), "q4_dequant")
+
+
 # ------------------------------------------------------------------------- the adapter update
 @dataclass(frozen=True)
 class AdamWConfig:
@@ -347,5 +396,6 @@ def quantize_weight(w: torch.Tensor, stream=None, absmax: torch.Tensor | None = 
 __all__ = ["lib", "LIB_PATH", "EXPORTED", "NF4Error", "NF4Weight", "CNF4Weight", "nf4_quantize",
            "nf4_double_quant", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_fwd_recompute",
            "qlora_linear_bwd", "qlora_merge", "AdamWConfig", "CAdamWConfig", "AdamWPlan",
+           "Q4_CODEBOOKS", "q4_codebook_values", "q4_quantize", "q4_dequant",
            "qlora_workspace_bytes", "nf4_storage_bytes", "nf4_codebook", "workspace",
            "empty_weight", "quantize_weight"]

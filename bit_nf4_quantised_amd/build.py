@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqlora_nf4.so")
-SOURCES = ["quant.hip", "gemm.hip", "lora.hip", "skinny.hip", "merge.hip", "optim.hip", "abi.hip"]
+SOURCES = ["quant.hip", "gemm.hip", "lora.hip", "skinny.hip", "merge.hip", "optim.hip", "variants.hip", "abi.hip"]
 ARCH = os.environ.get("NF4_OFFLOAD_ARCH", "gfx950")
 
 

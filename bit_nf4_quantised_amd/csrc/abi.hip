@@ -213,6 +213,46 @@ int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy,
   return from_hip(nf4::launch_lora_dx(x, M, K, v, r, scale, accumulate, part, dA, stream));
 }
 
+int q4_codebook_values(int32_t codebook, float out[16]) {
+  if (!out) return NF4_ERR_NULL;
+  int count = 0;
+  return nf4::q4_codebook(codebook, out, &count) ? count : -NF4_ERR_SHAPE;
+}
+
+static int check_q4(int64_t numel, int32_t codebook, int32_t blocksize) {
+  float q[16];
+  int count = 0;
+  if (!nf4::q4_codebook(codebook, q, &count)) return NF4_ERR_SHAPE;
+  if (blocksize < 16 || blocksize > 4096 || (blocksize & (blocksize - 1))) return NF4_ERR_SHAPE;
+  if (numel < 0 || numel % 64 || numel % blocksize || numel > (int64_t(1) << 42)) return NF4_ERR_SHAPE;
+  return NF4_OK;
+}
+
+int q4_quantize(const float* w, int64_t numel, int32_t codebook, int32_t blocksize, uint8_t* packed,
+                float* absmax, hipStream_t stream) {
+  int st = check_q4(numel, codebook, blocksize);
+  if (st) return st;
+  if (numel == 0) return NF4_OK;
+  if (!w || !packed || !absmax) return NF4_ERR_NULL;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(absmax)) return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_q4_quantize(w, numel, codebook, blocksize, packed, absmax, stream));
+}
+
+int q4_dequant(const uint8_t* packed, int64_t numel, int32_t codebook, int32_t blocksize, const float* absmax,
+               const uint8_t* scale_q, const float* scale_c2, uint16_t* out, hipStream_t stream) {
+  int st = check_q4(numel, codebook, blocksize);
+  if (st) return st;
+  if (numel == 0) return NF4_OK;
+  if (!packed || !out) return NF4_ERR_NULL;
+  const bool dq = scale_q || scale_c2;
+  if (absmax ? dq : !(scale_q && scale_c2)) return NF4_ERR_NULL;   // exactly one kind of scales
+  if (!aligned16(packed) || !aligned16(out) || (absmax && !aligned16(absmax)) ||
+      (scale_q && !aligned16(scale_q)) || (scale_c2 && !aligned16(scale_c2)))
+    return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_q4_dequant(packed, absmax, scale_q, scale_c2, numel, codebook, blocksize, out,
+                                         stream));
+}
+
 int qlora_adamw_plan_create(int64_t count, float* const* params, const float* const* grads,
                             float* const* exp_avg, float* const* exp_avg_sq, uint16_t* const* params_bf16,
                             const int64_t* numel, qlora_adamw_plan** out) {

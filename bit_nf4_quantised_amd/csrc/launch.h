@@ -71,4 +71,13 @@ hipError_t opt_plan_step(void* dev_mem, int64_t chunks, float lr, float beta1, f
                          float weight_decay, float max_norm, int64_t step, double* grad_norm,
                          hipStream_t stream);
 
+// Codebook (0 NF4, 1 FP4 E2M1, 2 INT4) and blocksize (16..4096, a power of two) variants; the
+// dequantisation takes fp32 scales (absmax != null) or double-quantised ones (scale_q, scale_c2).
+bool q4_codebook(int id, float out[16], int* count);
+hipError_t launch_q4_quantize(const float* w, int64_t numel, int book, int blocksize, uint8_t* packed,
+                              float* absmax, hipStream_t stream);
+hipError_t launch_q4_dequant(const uint8_t* packed, const float* absmax, const uint8_t* scale_q,
+                             const float* scale_c2, int64_t numel, int book, int blocksize, uint16_t* out,
+                             hipStream_t stream);
+
 }  // namespace nf4

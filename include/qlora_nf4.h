@@ -16,6 +16,8 @@
  *                     dequantised base, W~ + s B A, served in bf16.
  *   qlora_adamw_plan_*   sections "The algorithm, step by step" and "Minimal implementation":
  *                     global gradient-norm clipping, then AdamW over A and B.
+ *   q4_*              sections "A toy run" and "Double quantisation": FP4 and INT4 codebooks,
+ *                     blocksizes 16..4096, and fp32 scales without double quantisation.
  *
  * Data formats (all little-endian, row-major):
  *   W        N x K (out x in, like nn.Linear), K % 64 == 0, N % 16 == 0. Blocks of 64 run along K.
@@ -136,6 +138,38 @@ int qlora_linear_fwd_recompute(const nf4_weight *W, const uint16_t *x, int64_t M
  * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_RANK, NF4_ERR_HIP. */
 int qlora_merge(const nf4_weight *W, const uint16_t *A, const uint16_t *B, int32_t r, float scale,
                 uint16_t *out, hipStream_t stream);
+
+/* ---- Codebook and blocksize variants, and scales without double quantisation ("QLoRA, explained",
+ * A toy run, which compares NF4 with a symmetric 15-level INT4 grid and E2M1 FP4 scaled to [-1, 1],
+ * and discusses blocksizes from 16 to 4096; Double quantisation, whose baseline keeps one fp32
+ * absmax per block). The same storage layout as above with another codebook and blocksize:
+ * packed[j] holds the indices of elements 2j (high nibble) and 2j+1 (low nibble); one fp32 absmax
+ * per block of `blocksize` consecutive values. Double quantisation of those scales is
+ * nf4_double_quant on the absmax array (any length; groups of 256 blocks). */
+enum {
+  Q4_CODEBOOK_NF4 = 0,    /* the 16 NF4 codes above */
+  Q4_CODEBOOK_FP4 = 1,    /* E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} / 6, both signs: 15 codes */
+  Q4_CODEBOOK_INT4 = 2    /* k / 7 for k = -7..7: 15 codes */
+};
+
+/* Writes the codebook's values, ascending, as fp32 (out[15] repeats the last code when there are
+ * 15) and returns how many there are (15 or 16); a negative status for an unknown codebook. */
+int q4_codebook_values(int32_t codebook, float out[16]);
+
+/* Blockwise absmax quantisation to the exact nearest code (ties to the lower index; an all-zero
+ * block takes the exact-zero code). numel a multiple of 64 and of blocksize; blocksize a power of
+ * two in 16..4096. packed: numel/2 bytes; absmax: numel/blocksize floats. Inputs finite.
+ * Errors: NF4_ERR_SHAPE (codebook, blocksize or numel), NF4_ERR_NULL, NF4_ERR_ALIGN. */
+int q4_quantize(const float *w, int64_t numel, int32_t codebook, int32_t blocksize, uint8_t *packed,
+                float *absmax, hipStream_t stream);
+
+/* out[i] = bf16(fl32(q[idx_i] * s_b)), b the block of element i. Exactly one kind of scales:
+ *   absmax != NULL, scale_q == scale_c2 == NULL: s_b = absmax[b] (fp32, no double quantisation);
+ *   absmax == NULL: s_b = fl32(e4m3(scale_q[b]) * scale_c2[b / 256]) (double quantised).
+ * Indices must be below the codebook's size. Errors: NF4_ERR_SHAPE, NF4_ERR_NULL (missing or
+ * both kinds of scales), NF4_ERR_ALIGN. */
+int q4_dequant(const uint8_t *packed, int64_t numel, int32_t codebook, int32_t blocksize, const float *absmax,
+               const uint8_t *scale_q, const float *scale_c2, uint16_t *out, hipStream_t stream);
 
 /* ---- The adapter update of a training step ("QLoRA, explained", The algorithm, step by step, and
  * Minimal implementation): the adapter gradients are clipped by their global L2 norm (0.3 in the

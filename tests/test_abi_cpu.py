@@ -197,3 +197,33 @@ def test_adamw_plan_step_validation():
         cfg = q.AdamWConfig(**{**q.AdamWConfig().__dict__, **bad}).c_struct()
         assert f(FAKE, ctypes.byref(cfg), 1, None, None) == q.NF4_ERR_SHAPE, bad
     assert lib.qlora_adamw_plan_destroy(None) == q.NF4_OK
+
+
+def test_q4_codebooks_equal_oracle():
+    from oracle import toy
+    for book, ref in ((0, oracle.codebook()), (1, toy.fp4_codebook()), (2, toy.int4_codebook())):
+        out = (ctypes.c_float * 16)()
+        n = lib.q4_codebook_values(book, out)
+        assert n == ref.size
+        assert np.array_equal(np.array(out[:n], dtype=np.float32), ref)
+    assert lib.q4_codebook_values(3, (ctypes.c_float * 16)()) < 0
+
+
+def test_q4_validation():
+    f, g = lib.q4_quantize, lib.q4_dequant
+    assert f(FAKE, 4096, 3, 64, FAKE, FAKE, None) == q.NF4_ERR_SHAPE          # codebook
+    for bs in (8, 48, 8192):
+        assert f(FAKE, 8192, 1, bs, FAKE, FAKE, None) == q.NF4_ERR_SHAPE      # blocksize
+    assert f(FAKE, 4096 + 32, 0, 32, FAKE, FAKE, None) == q.NF4_ERR_SHAPE     # numel % 64
+    assert f(FAKE, 4096 + 64, 0, 128, FAKE, FAKE, None) == q.NF4_ERR_SHAPE    # numel % blocksize
+    assert f(FAKE, -64, 0, 64, FAKE, FAKE, None) == q.NF4_ERR_SHAPE
+    assert f(None, 0, 0, 64, None, None, None) == q.NF4_OK                    # empty
+    assert f(None, 4096, 0, 64, FAKE, FAKE, None) == q.NF4_ERR_NULL
+    assert f(FAKE, 4096, 0, 64, FAKE, MISALIGNED, None) == q.NF4_ERR_ALIGN
+    assert g(FAKE, 4096, 2, 16, None, None, None, FAKE, None) == q.NF4_ERR_NULL     # no scales
+    assert g(FAKE, 4096, 2, 16, FAKE, FAKE, FAKE, FAKE, None) == q.NF4_ERR_NULL     # both kinds
+    assert g(FAKE, 4096, 2, 16, None, FAKE, None, FAKE, None) == q.NF4_ERR_NULL     # half of DQ
+    assert g(FAKE, 4096, 2, 16, FAKE, None, None, None, None) == q.NF4_ERR_NULL
+    assert g(FAKE, 4096, 2, 16, MISALIGNED, None, None, FAKE, None) == q.NF4_ERR_ALIGN
+    assert g(FAKE, 4096, 2, 24, FAKE, None, None, FAKE, None) == q.NF4_ERR_SHAPE
+    assert g(None, 0, 1, 4096, None, None, None, None, None) == q.NF4_OK
