@@ -49,7 +49,7 @@ def nf4_bytes(numel: int) -> int:
     return numel // 2 + nb + 4 * ((nb + 255) // 256)
 
 
-ROOFLINE_KERNEL = "qlora_gemm_kernel<false, 256>"
+ROOFLINE_KERNEL = "qlora_gemm_kernel<false, 256, false>"
 
 
 def fwd_tile_rows(m: int, n: int) -> int:
@@ -206,7 +206,7 @@ def main():
 
     # ------------------------------------------------ dominant kernel: fused forward GEMM, alone
     # Timed over the linears whose forward runs the 256-row tile instantiation
-    # qlora_gemm_kernel<false, 256>, so that the average launch matches that kernel's entry in a
+    # qlora_gemm_kernel<false, 256, false>, so that the average launch matches that kernel's entry in a
     # rocprofv3 kernel-trace summary of this same command.
     big = [st for st in lin_state if fwd_tile_rows(M, st["lin"].n) == 256]
     gemm_flops = sum(2 * M * st["lin"].n * (st["lin"].k + r) for st in big)
@@ -228,6 +228,26 @@ def main():
                 "flops_per_launch": gemm_flops // launches,
                 "linears": [st["lin"].name for st in big]}
     log(f"[bench] fused fwd GEMM {gemm_achieved:.1f} TFLOP/s, {avg_launch_ms*1e3:.1f} us/launch")
+    # the same forward GEMMs on weights that keep fp32 scales (no double quantisation)
+    f32s = {}
+    for st in big:
+        li = wk.linears.index(st["lin"])
+        wt = torch.from_numpy(wl.linear_inputs(wk, li, st["lin"], m=1)[0]).to(dev)
+        f32s[st["lin"].name] = q.quantize_weight(wt, double_quant=False)
+        del wt
+
+    def recompute_f32s(_i=0):
+        for st in big:
+            q.qlora_linear_fwd_recompute(f32s[st["lin"].name], st["x"], st["a"], st["b"], s, st["u"], st["y"])
+
+    recompute_f32s()
+    ms_f32s = timed(recompute_f32s, args.steps, torch)
+    fwd_f32s = {"TFLOPs": round(gemm_flops / (ms_f32s * 1e-3) / 1e12, 2),
+                "vs_double_quantised": round(ms_recompute / ms_f32s, 4),
+                "what": "the roofline kernel's forward GEMMs with fp32 absmax scales instead of "
+                        "double-quantised ones (4.5 instead of 4.127 bits per weight)"}
+    log(f"[bench] fused fwd GEMM, fp32 scales: {fwd_f32s['TFLOPs']:.1f} TFLOP/s")
+    del f32s
     dense = library_dense_gemm(torch, dev, M, [st["lin"] for st in big], args.steps)
     log(f"[bench] library dense bf16 GEMM, same shapes: {dense:.1f} TFLOP/s")
     context = {"library_dense_bf16_gemm_TFLOPs": round(dense, 2),
@@ -259,6 +279,7 @@ def main():
         "context": context,
         "cpu_baseline": cpu,
         "paths": paths,
+        "fwd_gemm_fp32_scales": fwd_f32s,
     }
     print(json.dumps(out), flush=True)
 

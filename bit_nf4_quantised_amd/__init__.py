@@ -37,7 +37,8 @@ NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_RANK, NF4_ERR_WORKSP
 class CNF4Weight(ctypes.Structure):
     """Mirror of ``nf4_weight`` in include/qlora_nf4.h."""
     _fields_ = [("packed", ctypes.c_void_p), ("scale_q", ctypes.c_void_p),
-                ("scale_c2", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+                ("scale_c2", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("absmax", ctypes.c_void_p)]
 
 
 class CAdamWConfig(ctypes.Structure):
@@ -118,15 +119,18 @@ _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 @dataclass
 class NF4Weight:
-    """A quantised, double-quantised N x K weight held in three device tensors."""
-    packed: torch.Tensor     # uint8 [N*K/2]
-    scale_q: torch.Tensor    # uint8 [N*K/64]
-    scale_c2: torch.Tensor   # float32 [ceil(N*K/16384)]
+    """A quantised N x K weight in device tensors: double-quantised scales (scale_q, scale_c2) or,
+    without double quantisation, the fp32 absmax (scale_q and scale_c2 None)."""
+    packed: torch.Tensor           # uint8 [N*K/2]
+    scale_q: torch.Tensor | None   # uint8 [N*K/64]
+    scale_c2: torch.Tensor | None  # float32 [ceil(N*K/16384)]
     N: int
     K: int
+    absmax: torch.Tensor | None = None   # float32 [N*K/64]
 
     def c_struct(self) -> CNF4Weight:
-        return CNF4Weight(_ptr(self.packed), _ptr(self.scale_q), _ptr(self.scale_c2), self.N, self.K)
+        return CNF4Weight(_ptr(self.packed), _ptr(self.scale_q), _ptr(self.scale_c2), self.N, self.K,
+                          _ptr(self.absmax))
 
 
 # ------------------------------------------------------------------------- the five calls
@@ -382,12 +386,18 @@ def empty_weight(N: int, K: int, device="cuda") -> NF4Weight:
                      torch.empty((nb + 255) // 256, dtype=torch.float32, device=device), N, K)
 
 
-def quantize_weight(w: torch.Tensor, stream=None, absmax: torch.Tensor | None = None) -> NF4Weight:
-    """Quantise a float32 N x K device tensor: nf4_quantize followed by nf4_double_quant."""
+def quantize_weight(w: torch.Tensor, stream=None, absmax: torch.Tensor | None = None,
+                    double_quant: bool = True) -> NF4Weight:
+    """Quantise a float32 N x K device tensor: nf4_quantize followed by nf4_double_quant, or with
+    double_quant=False a weight that keeps the fp32 absmax as its scales."""
     N, K = w.shape
-    qw = empty_weight(N, K, w.device)
     if absmax is None:
         absmax = torch.empty(N * K // 64, dtype=torch.float32, device=w.device)
+    if not double_quant:
+        qw = NF4Weight(torch.empty(N * K // 2, dtype=torch.uint8, device=w.device), None, None, N, K, absmax)
+        nf4_quantize(w, qw.packed, absmax, stream)
+        return qw
+    qw = empty_weight(N, K, w.device)
     nf4_quantize(w, qw.packed, absmax, stream)
     nf4_double_quant(absmax, qw.scale_q, qw.scale_c2, stream)
     return qw

@@ -17,10 +17,13 @@ constexpr uint32_t kCodeBits[16] = {NF4_CODE_BITS};
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_weight(const nf4_weight* W) {
-  if (!W || !W->packed || !W->scale_q || !W->scale_c2) return NF4_ERR_NULL;
+  if (!W || !W->packed) return NF4_ERR_NULL;
+  // exactly one kind of scales: double-quantised (scale_q and scale_c2) or fp32 (absmax)
+  if (W->absmax ? (W->scale_q || W->scale_c2) : !(W->scale_q && W->scale_c2)) return NF4_ERR_NULL;
   if (W->N < 16 || W->K < 64 || W->N % 16 || W->K % 64) return NF4_ERR_SHAPE;
   if (W->N > (int64_t(1) << 31) || W->K > (int64_t(1) << 31)) return NF4_ERR_SHAPE;
-  if (!aligned16(W->packed) || !aligned16(W->scale_q) || !aligned16(W->scale_c2)) return NF4_ERR_ALIGN;
+  if (!aligned16(W->packed) || !aligned16(W->scale_q) || !aligned16(W->scale_c2) || !aligned16(W->absmax))
+    return NF4_ERR_ALIGN;
   return NF4_OK;
 }
 
@@ -112,6 +115,9 @@ int nf4_dequant(const nf4_weight* W, uint16_t* out, hipStream_t stream) {
   if (st) return st;
   if (!out) return NF4_ERR_NULL;
   if (!aligned16(out)) return NF4_ERR_ALIGN;
+  if (W->absmax)
+    return from_hip(nf4::launch_q4_dequant(W->packed, W->absmax, nullptr, nullptr, W->N * W->K, 0, 64, out,
+                                           stream));
   return from_hip(nf4::launch_dequant(W->packed, W->scale_q, W->scale_c2, W->N * W->K, out, stream));
 }
 
@@ -120,6 +126,7 @@ int qlora_merge(const nf4_weight* W, const uint16_t* A, const uint16_t* B, int32
   int st = check_weight(W);
   if (st) return st;
   if ((st = check_rank(r))) return st;
+  if (W->absmax) return NF4_ERR_SHAPE;   // the merge reads double-quantised scales only
   if (!A || !B || !out) return NF4_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(out)) return NF4_ERR_ALIGN;
   return from_hip(nf4::launch_merge(W->packed, W->scale_q, W->scale_c2, W->N, W->K, A, B, r, scale,
@@ -150,14 +157,14 @@ int qlora_linear_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const ui
   if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;
   float* u = u_out ? u_out : static_cast<float*>(ws);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
-  if (nf4::skinny_eligible(M, N, K)) {
+  if (!W->absmax && nf4::skinny_eligible(M, N, K)) {
     return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, N, K, x, M, A, B, r,
                                            scale, part, u, y, stream));
   }
   hipError_t e = nf4::launch_lora_u(x, M, K, A, r, part, u, stream);
   if (e != hipSuccess) return NF4_ERR_HIP;
-  return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, N, K, x, M, u, B, r, scale,
-                                       y, stream));
+  return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, u, B,
+                                       r, scale, y, stream));
 }
 
 int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A,
@@ -173,7 +180,7 @@ int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M
       (ws && !aligned16(ws)))
     return NF4_ERR_ALIGN;
   const int64_t N = W->N, K = W->K;
-  if (nf4::skinny_eligible(M, N, K)) {
+  if (!W->absmax && nf4::skinny_eligible(M, N, K)) {
     // the skinny path forms u itself from the adapter rows; it needs the workspace
     const size_t need = fwd_ws(M, N, K, r);
     if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;
@@ -182,8 +189,8 @@ int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M
     return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, N, K, x, M, A, B, r,
                                            scale, part, u_scratch, y, stream));
   }
-  return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, N, K, x, M, u, B, r, scale,
-                                       y, stream));
+  return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, u, B,
+                                       r, scale, y, stream));
 }
 
 int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy, int64_t M,
@@ -207,7 +214,8 @@ int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy,
   hipError_t e = nf4::launch_lora_dy(dy, M, N, B, u, r, scale, accumulate, part, v, dB, stream);
   if (e != hipSuccess) return NF4_ERR_HIP;
   if (dx) {
-    e = nf4::launch_dx_gemm(W->packed, W->scale_q, W->scale_c2, N, K, dy, M, v, A, r, scale, dx, stream);
+    e = nf4::launch_dx_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, dy, M, v, A, r, scale, dx,
+                            stream);
     if (e != hipSuccess) return NF4_ERR_HIP;
   }
   return from_hip(nf4::launch_lora_dx(x, M, K, v, r, scale, accumulate, part, dA, stream));

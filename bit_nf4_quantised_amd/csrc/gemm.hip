@@ -34,6 +34,10 @@
 // partial contraction step of the backward (N % 64 != 0) points its missing activation chunks past
 // the records. Weight rows past N dequantise to exact zeros there (code 0 and constant 0); in the
 // forward they only feed output columns that are not stored.
+//
+// With F32S the weight keeps one fp32 absmax per block instead of double-quantised scales (the
+// baseline of "QLoRA, explained", Double quantisation): the loaders bring that scale where they
+// bring the E4M3 code word otherwise, there is no second-level constant, and c1' is the scale.
 #include <type_traits>
 
 #include "common.h"
@@ -45,6 +49,7 @@ struct GemmArgs {
   const uint8_t* packed;
   const uint8_t* scale_q;
   const float* scale_c2;
+  const float* absmax;      // fp32 scales (F32S) instead of scale_q and scale_c2
   int64_t N, K;             // W is N x K
   const uint16_t* act;      // X [M x K] (forward) or dY [M x N] (backward), bf16
   int64_t M;
@@ -91,7 +96,7 @@ __device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
 }
 
-template <bool DX, int BM>
+template <bool DX, int BM, bool F32S>
 __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) {
   using WT = WTile<DX>;
   using CW = Waves<BM>;
@@ -170,7 +175,9 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
     const int w_row = pslot / WT::segs, w_seg = pslot % WT::segs;
     const uint32_t wp_off = (uint32_t)w_row * (uint32_t)(g.K / 2) + (uint32_t)w_seg * 16u;
     const int64_t nblocks = g.N * (g.K / kBlock);
-    __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc((void*)g.scale_q, (short)0, (int)nblocks, kRsrcFlags);
+    __amdgpu_buffer_rsrc_t rs_q = F32S
+        ? __builtin_amdgcn_make_buffer_rsrc((void*)g.absmax, (short)0, (int)(nblocks * 4), kRsrcFlags)
+        : __builtin_amdgcn_make_buffer_rsrc((void*)g.scale_q, (short)0, (int)nblocks, kRsrcFlags);
     __amdgpu_buffer_rsrc_t rs_c2 = __builtin_amdgcn_make_buffer_rsrc(
         (void*)g.scale_c2, (short)0, (int)(((nblocks + kGroup - 1) / kGroup) * 4), kRsrcFlags);
     // scales: forward, one block per W row and step (rows 0-63 by waves 0/2, 64-127 by 1/3: the
@@ -193,7 +200,18 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
       const int ps = t % kPStages;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&Ps[ps][lw * 64]), 16, wp_off, 0, 0, 0);
       const uint32_t b = sb0 + (uint32_t)t * sb_step;
-      if (DX) {
+      if (F32S) {
+        // forward: the block's scale for rows 0-63 (wave 0) and 64-127 (wave 1); backward: the
+        // row's two blocks, the first by wave 0 and the second by wave 1
+        if (DX) {
+          if (lw == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_q, (lds_void*)(&Cs[ps][0]), 4, b * 4u, 0, 0, 0);
+          else if (lw == 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_q, (lds_void*)(&Gs[ps][0]), 4, (b + 1u) * 4u, 0, 0, 0);
+        } else if (lw < 2) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_q, (lds_void*)(&Cs[ps][(lw & 1) * 64]), 4, b * 4u, 0, 0, 0);
+        }
+      } else if (DX) {
         if (lw == 0) {
           const uint32_t off = b & ~3u;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_q, (lds_void*)(&Cs[ps][0]), 16, off, 0, 0, 0);
@@ -217,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
     // are the only ones allowed to stay in flight, and vector-memory loads complete in issue order.
     // The packed weights of a step therefore sit in LDS one phase before they are expanded, which
     // lets the dequantisers read them a phase ahead.
-    const bool two_p = !DX || lw < 2;   // issue_p makes two loads (chunk + code or constant)
+    const bool two_p = (!DX && !F32S) || lw < 2;   // issue_p makes two loads (chunk + a scale word)
     issue_x(0, false);
     issue_p(0);
     if (main_steps > 1) issue_p(1);
@@ -270,7 +288,10 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
       const int ps = t % kPStages;
       StepWords w;
       w.wq = Ps[ps][dt];
-      if (DX) {
+      if (F32S) {
+        w.cw = DX && (w_seg >> 1) ? __float_as_uint(Gs[ps][w_row]) : Cs[ps][w_row];
+        w.c2 = 0u;
+      } else if (DX) {
         const uint32_t b = b0 + (uint32_t)t * b_step, rb = rb0 + (uint32_t)t * b_step;
         const uint32_t byte = (rb & 3u) + (uint32_t)(w_seg >> 1);     // within the row's 16 bytes
         w.cw = Cs[ps][w_row * 4 + (int)(byte >> 2)];
@@ -291,7 +312,8 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
         shift = ((b0 + (uint32_t)t) & 3u) * 8u;
       }
       const uint32_t word = sw.cw >> shift;
-      const float c1p = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)word, 0), __uint_as_float(sw.c2));
+      const float c1p = F32S ? __uint_as_float(sw.cw)
+                             : __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)word, 0), __uint_as_float(sw.c2));
       uint32_t pp[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) pp[k] = pack_bf16x2(__fmul_rn(qv[2 * k], c1p), __fmul_rn(qv[2 * k + 1], c1p));
@@ -485,36 +507,38 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
   }
 }
 
-template <bool DX>
+template <bool DX, bool F32S>
 static hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t stream) {
   const int64_t Nout = DX ? g.K : g.N;
   const int gx = (int)((Nout + kBN - 1) / kBN);
   const int64_t tiles256 = (int64_t)gx * ((g.M + 255) / 256);
   if (g.M > 128 && tiles256 >= 192) {
     const int gy = (int)((g.M + 255) / 256);
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 256>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
+    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 256, F32S>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
   } else if (g.M > 64) {
     const int gy = (int)((g.M + 127) / 128);
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 128>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
+    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 128, F32S>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
   } else {
     const int gy = (int)((g.M + 63) / 64);
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 64>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
+    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 64, F32S>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
-                           int64_t N, int64_t K, const uint16_t* x, int64_t M, const float* u,
-                           const uint16_t* B, int r, float scale, uint16_t* y, hipStream_t stream) {
-  GemmArgs g{packed, scale_q, scale_c2, N, K, x, M, u, B, r, scale, y};
-  return launch_gemm_t<false>(g, stream);
+                           const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                           const float* u, const uint16_t* B, int r, float scale, uint16_t* y,
+                           hipStream_t stream) {
+  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, x, M, u, B, r, scale, y};
+  return absmax ? launch_gemm_t<false, true>(g, stream) : launch_gemm_t<false, false>(g, stream);
 }
 
 hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
-                          int64_t N, int64_t K, const uint16_t* dy, int64_t M, const float* v,
-                          const uint16_t* A, int r, float scale, uint16_t* dx, hipStream_t stream) {
-  GemmArgs g{packed, scale_q, scale_c2, N, K, dy, M, v, A, r, scale, dx};
-  return launch_gemm_t<true>(g, stream);
+                          const float* absmax, int64_t N, int64_t K, const uint16_t* dy, int64_t M,
+                          const float* v, const uint16_t* A, int r, float scale, uint16_t* dx,
+                          hipStream_t stream) {
+  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, dy, M, v, A, r, scale, dx};
+  return absmax ? launch_gemm_t<true, true>(g, stream) : launch_gemm_t<true, false>(g, stream);
 }
 
 }  // namespace nf4

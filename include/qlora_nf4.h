@@ -62,12 +62,18 @@ typedef enum {
   NF4_ERR_HIP = 6         /* the HIP runtime rejected a kernel launch */
 } nf4_status;
 
-/* A quantised, double-quantised weight W (N x K). All three arrays are device memory. */
+/* A quantised weight W (N x K), device memory. Its block scales are either double quantised
+ * (scale_q and scale_c2 set, absmax NULL: 4.127 bits per weight) or the fp32 absmax itself
+ * (absmax set, scale_q and scale_c2 NULL: the 4.5-bit baseline without double quantisation,
+ * "QLoRA, explained", Double quantisation). nf4_dequant and the linear calls take either; with
+ * fp32 scales the forward runs the fused GEMM at every token count (no skinny path) and
+ * qlora_merge is not available (NF4_ERR_SHAPE). */
 typedef struct {
   const uint8_t *packed;    /* [N*K/2]                 */
   const uint8_t *scale_q;   /* [N*K/64]                */
   const float *scale_c2;    /* [ceil(N*K/64/256)]      */
   int64_t N, K;
+  const float *absmax;      /* [N*K/64] or NULL        */
 } nf4_weight;
 
 /* Blockwise absmax NF4 quantisation of a float32 array (any shape, flattened row-major).
@@ -135,7 +141,8 @@ int qlora_linear_fwd_recompute(const nf4_weight *W, const uint16_t *x, int64_t M
  * so merging into W~ (not into the original weight) keeps the trained model; the result is served
  * in bf16 (re-quantising it, with nf4_quantize, adds a second rounding to the update).
  *   A [r x K] bf16;  B [N x r] bf16;  scale = s.
- * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_RANK, NF4_ERR_HIP. */
+ * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (also a weight with fp32 scales), NF4_ERR_ALIGN,
+ * NF4_ERR_RANK, NF4_ERR_HIP. */
 int qlora_merge(const nf4_weight *W, const uint16_t *A, const uint16_t *B, int32_t r, float scale,
                 uint16_t *out, hipStream_t stream);
 

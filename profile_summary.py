@@ -53,7 +53,7 @@ def ktrace(tag, bench_json):
         lines.append(f"| `{k[0]}` | {k[1]} x {k[2]} | {len(v)} | {v2[len(v2)//2]:.1f} | {v2[0]:.1f} | "
                      f"{sum(v):.1f} |")
     rl = b["roofline"]
-    st = [s for s in stats if short(s["Name"]) == "qlora_gemm_kernel<false, 256>"][0]
+    st = [s for s in stats if short(s["Name"]) == "qlora_gemm_kernel<false, 256, false>"][0]
     lines += ["", "## Agreement with the benchmark's live measurement", "",
               f"`bench.py` (default run, HIP events over its timed forward loop) reports "
               f"{rl['avg_launch_us']} us per launch of `{bench.ROOFLINE_KERNEL}` averaged over "
@@ -131,7 +131,7 @@ def counters(tag, bench_json):
     rl = b["roofline"]
     wk = bench.wl.WORKLOADS["llama8b"]
     big = [l for l in wk.linears if bench.fwd_tile_rows(wk.m, l.n) == 256]
-    key = "qlora_gemm_kernel<false, 256>"
+    key = "qlora_gemm_kernel<false, 256, false>"
     # q, o and down share one grid size; their mean stands for each of them
     tot_f = tot_w = 0.0
     for l in big:
@@ -195,14 +195,14 @@ def clock(tag):
         lines.append(f"| `{k[0]}` | {k[1]} | {len(g)} | {dur:.1f} | {cyc:.0f} | {cyc/dur/1e3:.2f} | "
                      f"{100*mfb/(cyc*1024):.1f} |")
     # the same kernel at two launch sizes gives the clock without the fixed overhead
-    a = d.get(("qlora_gemm_kernel<false, 256>", 256)); b = d.get(("qlora_gemm_kernel<false, 256>", 896))
+    a = d.get(("qlora_gemm_kernel<false, 256, false>", 256)); b = d.get(("qlora_gemm_kernel<false, 256, false>", 896))
     if a and b:
         ca = sum(x for x, _ in a["GRBM_GUI_ACTIVE"]) / len(a["GRBM_GUI_ACTIVE"]) / 8
         ta = sum(t for _, t in a["GRBM_GUI_ACTIVE"]) / len(a["GRBM_GUI_ACTIVE"])
         cb = sum(x for x, _ in b["GRBM_GUI_ACTIVE"]) / len(b["GRBM_GUI_ACTIVE"]) / 8
         tb = sum(t for _, t in b["GRBM_GUI_ACTIVE"]) / len(b["GRBM_GUI_ACTIVE"])
         slope = (cb - ca) / (tb - ta) / 1e3
-        lines += ["", f"Fit over the two launch sizes of `qlora_gemm_kernel<false, 256>` (256 and 896 "
+        lines += ["", f"Fit over the two launch sizes of `qlora_gemm_kernel<false, 256, false>` (256 and 896 "
                       f"workgroups): {slope:.2f} GHz sustained, {ca - slope*1e3*ta:.0f} cycles of fixed "
                       f"overhead per dispatch.", ""]
     return "\n".join(lines)

@@ -89,6 +89,18 @@ def test_dequant_validation():
     assert lib.nf4_dequant(ctypes.byref(_w()), None, None) == q.NF4_ERR_NULL
 
 
+def test_weight_scale_kinds():
+    # exactly one kind of scales: double quantised, or fp32 absmax
+    both = q.CNF4Weight(FAKE, FAKE, FAKE, 4096, 4096, FAKE)
+    assert lib.nf4_dequant(ctypes.byref(both), FAKE, None) == q.NF4_ERR_NULL
+    half = q.CNF4Weight(FAKE, None, FAKE, 4096, 4096, None)
+    assert lib.nf4_dequant(ctypes.byref(half), FAKE, None) == q.NF4_ERR_NULL
+    mis = q.CNF4Weight(FAKE, None, None, 4096, 4096, MISALIGNED)
+    assert lib.nf4_dequant(ctypes.byref(mis), FAKE, None) == q.NF4_ERR_ALIGN
+    f32s = q.CNF4Weight(FAKE, None, None, 4096, 4096, FAKE)
+    assert lib.qlora_merge(ctypes.byref(f32s), FAKE, FAKE, 16, 2.0, FAKE, None) == q.NF4_ERR_SHAPE
+
+
 def test_merge_validation():
     w = ctypes.byref(_w())
     assert lib.qlora_merge(None, FAKE, FAKE, 16, 2.0, FAKE, None) == q.NF4_ERR_NULL

@@ -142,3 +142,68 @@ def test_forward_recompute_matches_forward(M):
     q.qlora_linear_fwd_recompute(qw, X, A, B, 2.0, u, y2)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+# ---------------------------------------------------------------- fp32 scales (no double quantisation)
+def _f32s_weight(w):
+    import bit_nf4_quantised_amd as q
+    from gpu_helpers import to_dev
+    import torch
+    qw = q.quantize_weight(to_dev(w.astype(np.float32)), double_quant=False)
+    torch.cuda.synchronize()
+    packed, absmax = oracle.quantize(w)
+    wt = oracle.dequant_blocks(packed, absmax, oracle.codebook(), 64, w.size).reshape(w.shape)
+    return qw, wt
+
+
+@pytest.mark.parametrize("M,N,K,r,s", [
+    (300, 400, 960, 16, 2.0),      # ragged in every tile dimension, K % 128 == 64
+    (513, 128, 128, 64, 0.25),     # three row tiles, the last with one row
+    (77, 1040, 1088, 128, 0.5),
+    (8, 400, 960, 16, 2.0),        # few tokens: the fused GEMM, not the skinny path
+    (2048, 4096, 4096, 16, 2.0),   # the q/o shape of the 8B layer set
+])
+def test_fp32_scale_weight_matches_oracle(M, N, K, r, s):
+    from gpu_helpers import gpu_dequant
+    w, x, a, b, dy = _inputs(M + N + r, M, N, K, r)
+    log(f"[linear] fp32 scales M={M} N={N} K={K} r={r}")
+    qw, wt = _f32s_weight(w)
+    assert np.array_equal(gpu_dequant(qw).reshape(N, K), wt)
+    y, u, dx, dA, dB = gpu_fwd_bwd(qw, x, a, b, dy, s)
+    yr, ur = oracle.linear_fwd(x, wt, a, b, s)
+    dxr, dar, dbr = oracle.linear_bwd(x, dy, wt, a, b, s)
+    assert_close("y", f64_from_bits(y), yr)
+    assert_close("dx", f64_from_bits(dx), dxr)
+    assert_close("dA", dA, dar)
+    assert_close("dB", dB, dbr)
+
+
+def test_fp32_scale_weight_one_hot_and_recompute():
+    # with B = 0, one-hot rows of x give y rows equal to columns of W~ bit for bit, one-hot rows of
+    # dY give dX rows equal to rows of W~; the recompute forward equals the forward
+    import torch
+    import bit_nf4_quantised_amd as q
+    from gpu_helpers import bf16_to_dev, bits_from_dev, dev
+    M, N, K, r = 200, 384, 960, 16
+    w, x, a, b, dy = _inputs(5, M, N, K, r)
+    qw, wt = _f32s_weight(w)
+    x = np.zeros((M, K), np.uint16)
+    dy = np.zeros((M, N), np.uint16)
+    for i in range(M):
+        x[i, (7 * i) % K] = 0x3F80
+        dy[i, (5 * i) % N] = 0x3F80
+    b0 = np.zeros_like(b)
+    y, u, dx, dA, dB = gpu_fwd_bwd(qw, x, a, b0, dy, 2.0)
+    for i in range(M):
+        assert np.array_equal(y[i], wt[:, (7 * i) % K]), i
+        assert np.array_equal(dx[i], wt[(5 * i) % N]), i
+    X, A, B = bf16_to_dev(x), bf16_to_dev(a), bf16_to_dev(b)
+    U = torch.empty(M, r, dtype=torch.float32, device=dev())
+    y1 = torch.empty(M, N, dtype=torch.int16, device=dev())
+    y2 = torch.empty(M, N, dtype=torch.int16, device=dev())
+    q.qlora_linear_fwd(qw, X, A, B, 2.0, y1, U)
+    q.qlora_linear_fwd_recompute(qw, X, A, B, 2.0, U, y2)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_from_dev(y1), bits_from_dev(y2))
+    with pytest.raises(q.NF4Error):
+        q.qlora_merge(qw, A, B, 2.0, torch.empty(N * K, dtype=torch.int16, device=dev()))
