@@ -76,6 +76,11 @@ PATH_KERNELS = {
     "grad_sqnorm_partial_kernel": "adapter update, norm partial sums (448 tensors, 41.9 M values)",
     "grad_sqnorm_final_kernel": "adapter update, norm total",
     "adamw_kernel": "adapter update, clipped AdamW",
+    "q4_quantize_kernel<16>": "variant quantise, blocksize 16 (NF4), 4096x14336 pool",
+    "q4_quantize_kernel<64>": "variant quantise, blocksize 64 (NF4, FP4, INT4), 4096x14336 pool",
+    "q4_quantize_kernel<4096>": "variant quantise, blocksize 4096 (NF4), 4096x14336 pool",
+    "q4_dequant_kernel<4, false>": "variant dequantise, fp32 scales, blocksize 16",
+    "q4_dequant_kernel<1, false>": "variant dequantise, fp32 scales, blocksizes 64 and 4096",
 }
 
 
