@@ -63,6 +63,8 @@ def test_single_linear_workload():
     (4, 400, 960, 64, 0.25),
     (16, 416, 1024, 16, 2.0),
     (16, 64, 64, 16, 2.0),         # one block per row
+    (1800, 14336, 128, 16, 2.0),   # forward: 896 tiles of 256 rows, ragged last row block
+    (1800, 128, 14336, 16, 2.0),   # the same for the dX GEMM (14336 output columns)
 ])
 def test_ragged_shapes(M, N, K, r, s):
     check_full(*_inputs(M * 7 + r, M, N, K, r), s, "ragged")
