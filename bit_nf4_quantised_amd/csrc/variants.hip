@@ -11,9 +11,9 @@
 //                               fl32(e4m3 * c2) when the scales are double quantised.
 //
 // Exact nearest code for any such codebook: x = w * fl32(1 / c) is within 2^-23 of w / c. A table
-// of 256 bins of width 1/128 over [-1, 1], built in LDS at the start of each workgroup from the
-// codebook, holds per bin the number of decision midpoints below it and the midpoint inside it (at
-// most one: the codebooks' midpoints are at least 0.04 apart). Then idx = base + (x > mid) is the
+// of 256 bins of width 1/128 over [-1, 1], built once on the host from the codebook and copied
+// into LDS by each workgroup, holds per bin the number of decision midpoints below it and the
+// midpoint inside it (at most one: the codebooks' midpoints are at least 0.04 apart). Then idx = base + (x > mid) is the
 // exact count of midpoints below x, and it equals the count below w / c unless x lies within 2^-20
 // of the bin's midpoint or of one of its edges (or the scale is below 2^-100): such values count
 // the midpoints m with w > c * m in fp64, where the product of a 24-bit scale and a midpoint of at
@@ -42,6 +42,10 @@ constexpr float kQMargin = 0x1p-20f;
 struct QBin {
   float mid;         // the midpoint inside the bin, or +inf
   uint32_t base;     // midpoints below the bin's lower edge
+};
+
+struct QBinTable {
+  QBin bin[kQBins];
 };
 
 // Maximum over the B / 16 threads of a block: a butterfly within the wave, then (B > 1024) the
@@ -77,22 +81,12 @@ __device__ uint32_t exact_index(float w, float c, const Q4Book& cb) {
 
 template <int B>
 __global__ __launch_bounds__(256) void q4_quantize_kernel(const f32x4* __restrict__ w, int64_t numel,
-                                                          const Q4Book cb, u32x2* __restrict__ packed,
+                                                          const Q4Book cb, const QBinTable table,
+                                                          u32x2* __restrict__ packed,
                                                           float* __restrict__ absmax) {
   __shared__ QBin bins[kQBins];
   __shared__ float wmax[4];
-  {
-    const int t = threadIdx.x;
-    const double lo = -1.0 + t / 128.0, hi = -1.0 + (t + 1) / 128.0;
-    uint32_t base = 0;
-    float mid = __builtin_huge_valf();
-    for (int i = 0; i + 1 < cb.count; ++i) {
-      const double m = ((double)cb.q[i] + (double)cb.q[i + 1]) * 0.5;
-      if (m < lo) ++base;
-      else if (m < hi) mid = (float)m;
-    }
-    bins[t] = QBin{mid, base};
-  }
+  bins[threadIdx.x] = table.bin[threadIdx.x];
   const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
   const bool valid = e0 < numel;
   const int64_t ec = valid ? e0 : numel - 16;      // blocks past the end re-read the last values
@@ -249,24 +243,54 @@ bool q4_codebook(int id, float out[16], int* count) {
   return true;
 }
 
+// The bin table of a codebook: per bin [lo, hi) of width 1/128, the midpoints below lo and the one
+// in [lo, hi) (each midpoint the exact fp64 mean of two fp32 codes, stored rounded to fp32; the
+// kernel's 2^-20 margin around it covers that rounding).
+static void make_bins(const Q4Book& cb, QBinTable& t) {
+  for (int b = 0; b < kQBins; ++b) {
+    const double lo = -1.0 + b / 128.0, hi = -1.0 + (b + 1) / 128.0;
+    uint32_t base = 0;
+    float mid = __builtin_huge_valf();
+    for (int i = 0; i + 1 < cb.count; ++i) {
+      const double m = ((double)cb.q[i] + (double)cb.q[i + 1]) * 0.5;
+      if (m < lo) ++base;
+      else if (m < hi) mid = (float)m;
+    }
+    t.bin[b] = QBin{mid, base};
+  }
+}
+
 hipError_t launch_q4_quantize(const float* w, int64_t numel, int book, int blocksize, uint8_t* packed,
                               float* absmax, hipStream_t stream) {
   if (numel == 0) return hipSuccess;
   Q4Book cb;
   if (!make_book(book, cb)) return hipErrorInvalidValue;
+  // built once, on first use, by a thread-safe static initialiser; constant afterwards
+  struct Tables {
+    QBinTable t[3];
+    Tables() {
+      for (int id = 0; id < 3; ++id) {
+        Q4Book b;
+        make_book(id, b);
+        make_bins(b, t[id]);
+      }
+    }
+  };
+  static const Tables tables;
+  const QBinTable& tb = tables.t[book];
   const dim3 grid((unsigned)((numel + 4095) / 4096)), block(256);
   const f32x4* src = reinterpret_cast<const f32x4*>(w);
   u32x2* dst = reinterpret_cast<u32x2*>(packed);
   switch (blocksize) {
-    case 16: hipLaunchKernelGGL(q4_quantize_kernel<16>, grid, block, 0, stream, src, numel, cb, dst, absmax); break;
-    case 32: hipLaunchKernelGGL(q4_quantize_kernel<32>, grid, block, 0, stream, src, numel, cb, dst, absmax); break;
-    case 64: hipLaunchKernelGGL(q4_quantize_kernel<64>, grid, block, 0, stream, src, numel, cb, dst, absmax); break;
-    case 128: hipLaunchKernelGGL(q4_quantize_kernel<128>, grid, block, 0, stream, src, numel, cb, dst, absmax); break;
-    case 256: hipLaunchKernelGGL(q4_quantize_kernel<256>, grid, block, 0, stream, src, numel, cb, dst, absmax); break;
-    case 512: hipLaunchKernelGGL(q4_quantize_kernel<512>, grid, block, 0, stream, src, numel, cb, dst, absmax); break;
-    case 1024: hipLaunchKernelGGL(q4_quantize_kernel<1024>, grid, block, 0, stream, src, numel, cb, dst, absmax); break;
-    case 2048: hipLaunchKernelGGL(q4_quantize_kernel<2048>, grid, block, 0, stream, src, numel, cb, dst, absmax); break;
-    case 4096: hipLaunchKernelGGL(q4_quantize_kernel<4096>, grid, block, 0, stream, src, numel, cb, dst, absmax); break;
+    case 16: hipLaunchKernelGGL(q4_quantize_kernel<16>, grid, block, 0, stream, src, numel, cb, tb, dst, absmax); break;
+    case 32: hipLaunchKernelGGL(q4_quantize_kernel<32>, grid, block, 0, stream, src, numel, cb, tb, dst, absmax); break;
+    case 64: hipLaunchKernelGGL(q4_quantize_kernel<64>, grid, block, 0, stream, src, numel, cb, tb, dst, absmax); break;
+    case 128: hipLaunchKernelGGL(q4_quantize_kernel<128>, grid, block, 0, stream, src, numel, cb, tb, dst, absmax); break;
+    case 256: hipLaunchKernelGGL(q4_quantize_kernel<256>, grid, block, 0, stream, src, numel, cb, tb, dst, absmax); break;
+    case 512: hipLaunchKernelGGL(q4_quantize_kernel<512>, grid, block, 0, stream, src, numel, cb, tb, dst, absmax); break;
+    case 1024: hipLaunchKernelGGL(q4_quantize_kernel<1024>, grid, block, 0, stream, src, numel, cb, tb, dst, absmax); break;
+    case 2048: hipLaunchKernelGGL(q4_quantize_kernel<2048>, grid, block, 0, stream, src, numel, cb, tb, dst, absmax); break;
+    case 4096: hipLaunchKernelGGL(q4_quantize_kernel<4096>, grid, block, 0, stream, src, numel, cb, tb, dst, absmax); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
