@@ -191,8 +191,8 @@ def qlora_merge(weight: NF4Weight, A, B, scale: float, out, stream=None) -> None
 
 def qlora_linear_fwd_recompute(weight: NF4Weight, x, A, B, scale: float, u, y, ws=None,
                                stream=None) -> None:
-    """Forward with a known u = x A^T (gradient-checkpointing recompute); one fused kernel for
-    more than 16 tokens."""
+    """Forward with a known u = x A^T (gradient-checkpointing recompute): the forward's GEMM
+    without the pass that forms u."""
     for t in (x, A, B, y):
         _dtype(t, *_BF16)
     _dtype(u, torch.float32)
@@ -201,7 +201,7 @@ def qlora_linear_fwd_recompute(weight: NF4Weight, x, A, B, scale: float, u, y, w
     if x.shape != (M, weight.K) or A.shape != (r, weight.K) or B.shape != (weight.N, r) \
             or y.shape != (M, weight.N) or u.numel() != M * r:
         raise ValueError("shape mismatch")
-    if ws is None and M <= 16:
+    if ws is None:   # with the forward's workspace the launches (and y) are the forward's own
         ws = workspace(M, weight.N, weight.K, r, x.device)
     cw = weight.c_struct()
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()

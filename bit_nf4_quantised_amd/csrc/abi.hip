@@ -34,12 +34,15 @@ int from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Workspace layout (bytes, each region 256-aligned):
-//   forward : [u (M*r fp32)] [partials: skinny splits or the adapter pass over X]
+//   forward : [u (M*r fp32)] [partials: the skinny path's splits, or the GEMM's contraction ranges]
 //   backward: [v (M*r fp32)] [partials of the pass over dY, then of the pass over X]
+size_t fwd_part_floats(int64_t M, int64_t N, int64_t K, int r) {
+  if (nf4::skinny_eligible(M, N, K)) return nf4::skinny_workspace_floats(M, N, K, r);
+  const int ks = nf4::fwd_gemm_splits(M, N, K);
+  return ks > 1 ? (size_t)ks * M * N : 0;
+}
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
-  // the forward's u needs no partial sums outside the skinny path
-  size_t part = nf4::skinny_eligible(M, N, K) ? nf4::skinny_workspace_floats(M, N, K, r) : 0;
-  return align_up((size_t)M * r * 4) + align_up(part * 4);
+  return align_up((size_t)M * r * 4) + align_up(fwd_part_floats(M, N, K, r) * 4);
 }
 size_t bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
   size_t part = nf4::lora_pass_ws_floats(M, N, r, true, true);
@@ -164,7 +167,7 @@ int qlora_linear_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const ui
   hipError_t e = nf4::launch_lora_u(x, M, K, A, r, part, u, stream);
   if (e != hipSuccess) return NF4_ERR_HIP;
   return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, u, B,
-                                       r, scale, y, stream));
+                                       r, scale, y, part, stream));
 }
 
 int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A,
@@ -189,8 +192,13 @@ int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M
     return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, N, K, x, M, A, B, r,
                                            scale, part, u_scratch, y, stream));
   }
+  // with a workspace of the forward's size, the same launches as qlora_linear_fwd (and the same
+  // output bit for bit); without one, the GEMM in one pass over the contraction
+  float* gpart = nullptr;
+  if (ws && ws_bytes >= fwd_ws(M, N, K, r) && fwd_part_floats(M, N, K, r) > 0)
+    gpart = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
   return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, u, B,
-                                       r, scale, y, stream));
+                                       r, scale, y, gpart, stream));
 }
 
 int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy, int64_t M,

@@ -35,6 +35,13 @@
 // the records. Weight rows past N dequantise to exact zeros there (code 0 and constant 0); in the
 // forward they only feed output columns that are not stored.
 //
+// Split contraction (ksplit > 1, forward only): when a launch would leave most CUs idle (few
+// output tiles), each tile's contraction is cut into ksplit ranges taken by separate workgroups.
+// A tile's time is set by its number of steps (a step costs the dequantisers' work on one W tile,
+// whatever the tile's height), so halving the steps per workgroup halves it. Each range writes
+// fp32 partial sums; gemm_ksum_kernel adds them in range order and rounds to bf16. The adapter
+// steps ride with the last range.
+//
 // With F32S the weight keeps one fp32 absmax per block instead of double-quantised scales (the
 // baseline of "QLoRA, explained", Double quantisation): the loaders bring that scale where they
 // bring the E4M3 code word otherwise, there is no second-level constant, and c1' is the scale.
@@ -58,6 +65,8 @@ struct GemmArgs {
   int r;
   float scale;
   uint16_t* out;            // y [M x N] (forward) or dX [M x K] (backward), bf16
+  int ksplit;               // contraction ranges (1: none)
+  float* part;              // ksplit x M x Nout fp32 partial sums when ksplit > 1
 };
 
 constexpr int kBN = 128;        // output columns per tile
@@ -117,16 +126,23 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
 
   // Tile coordinates; workgroups are dealt round-robin over the 8 XCDs, so give each XCD a
   // contiguous run of tiles that share an activation row block.
+  // The contraction range is the slowest index, so the ranges of a tile go to different XCDs.
   const int gx = gridDim.x, total = gridDim.x * gridDim.y;
   int lin = blockIdx.x + gx * blockIdx.y;
   if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  const int tiles = total / g.ksplit;
+  const int split = lin / tiles;
+  lin %= tiles;
   const int64_t col0 = (int64_t)(lin % gx) * kBN;
   const int64_t m0 = (int64_t)(lin / gx) * BM;
 
   const int64_t Lc = DX ? g.N : g.K;       // contraction length
   const int64_t Nout = DX ? g.K : g.N;     // output columns
-  const int main_steps = (int)((Lc + kBK - 1) / kBK);
-  const int lora_steps = (g.r + kBK - 1) / kBK;
+  const int main_total = (int)((Lc + kBK - 1) / kBK);
+  const int per_split = (main_total + g.ksplit - 1) / g.ksplit;
+  const int T0 = split * per_split;        // first contraction step of this range
+  const int main_steps = min(per_split, main_total - T0);
+  const int lora_steps = split == g.ksplit - 1 ? (g.r + kBK - 1) / kBK : 0;
   const int steps = main_steps + lora_steps;
   const uint32_t kb = (uint32_t)(g.K / kBlock);   // blocks per row of W
 
@@ -147,18 +163,19 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
     // `full`: the step is known to be a whole one (every step but the last), so the loop that
     // issues those carries no per-chunk selects
     auto issue_x = [&](int t, bool full) {
-      const uint16_t* base = g.act + m0 * Lc + (int64_t)t * kBK;
-      const int nrec = (int)(rows_valid * Lc * 2 - (int64_t)t * kBK * 2);
+      const int tg = t + T0;
+      const uint16_t* base = g.act + m0 * Lc + (int64_t)tg * kBK;
+      const int nrec = (int)(rows_valid * Lc * 2 - (int64_t)tg * kBK * 2);
       __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kRsrcFlags);
       uint16_t* dst = Xs + (t % kXStages) * XSTAGE + (lw * 2 * BM) * 8;
-      if (full || (int64_t)(t + 1) * kBK <= Lc) {
+      if (full || (int64_t)(tg + 1) * kBK <= Lc) {
 #pragma unroll
         for (int j = 0; j < NX; ++j) {
           const uint32_t off = xoff[j];
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + j * 64 * 8), 16, off, 0, 0, 0);
         }
       } else {   // a backward's last step with N % 64 != 0: chunks past N read zeros
-        const int valid_chunks = (int)(Lc - (int64_t)t * kBK) / 8;
+        const int valid_chunks = (int)(Lc - (int64_t)tg * kBK) / 8;
 #pragma unroll
         for (int j = 0; j < NX; ++j) {
           const int slot = lw * 2 * BM + j * 64 + lane;
@@ -187,19 +204,20 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
     const uint32_t sb0 = DX ? (uint32_t)srow * kb + (uint32_t)(col0 / kBlock) : (uint32_t)(col0 + srow) * kb;
     const uint32_t sb_step = DX ? (uint32_t)kBK * kb : 1u;
     auto issue_p = [&](int t) {
+      const int tg = t + T0;
       const uint8_t* base;
       int64_t nrec;
       if (DX) {
-        base = g.packed + (int64_t)t * kBK * (g.K / 2) + col0 / 2;
-        nrec = (g.N - (int64_t)t * kBK) * (g.K / 2) - col0 / 2;
+        base = g.packed + (int64_t)tg * kBK * (g.K / 2) + col0 / 2;
+        nrec = (g.N - (int64_t)tg * kBK) * (g.K / 2) - col0 / 2;
       } else {
-        base = g.packed + col0 * (g.K / 2) + (int64_t)t * (kBK / 2);
-        nrec = min(g.N - col0, (int64_t)kBN) * (g.K / 2) - (int64_t)t * (kBK / 2);
+        base = g.packed + col0 * (g.K / 2) + (int64_t)tg * (kBK / 2);
+        nrec = min(g.N - col0, (int64_t)kBN) * (g.K / 2) - (int64_t)tg * (kBK / 2);
       }
       __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nrec, kRsrcFlags);
       const int ps = t % kPStages;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(&Ps[ps][lw * 64]), 16, wp_off, 0, 0, 0);
-      const uint32_t b = sb0 + (uint32_t)t * sb_step;
+      const uint32_t b = sb0 + (uint32_t)tg * sb_step;
       if (F32S) {
         // forward: the block's scale for rows 0-63 (wave 0) and 64-127 (wave 1); backward: the
         // row's two blocks, the first by wave 0 and the second by wave 1
@@ -292,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
         w.cw = DX && (w_seg >> 1) ? __float_as_uint(Gs[ps][w_row]) : Cs[ps][w_row];
         w.c2 = 0u;
       } else if (DX) {
-        const uint32_t b = b0 + (uint32_t)t * b_step, rb = rb0 + (uint32_t)t * b_step;
+        const uint32_t b = b0 + (uint32_t)(t + T0) * b_step, rb = rb0 + (uint32_t)(t + T0) * b_step;
         const uint32_t byte = (rb & 3u) + (uint32_t)(w_seg >> 1);     // within the row's 16 bytes
         w.cw = Cs[ps][w_row * 4 + (int)(byte >> 2)];
         w.c2 = __float_as_uint(Gs[ps][w_row * 4 + (int)((b >> 8) - (rb >> 8))]);
@@ -306,10 +324,10 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
       const u32x4 wq = sw.wq;
       uint32_t shift;   // byte of the code within its word
       if (DX) {
-        const uint32_t rb = rb0 + (uint32_t)t * b_step;
+        const uint32_t rb = rb0 + (uint32_t)(t + T0) * b_step;
         shift = (((rb & 3u) + (uint32_t)(w_seg >> 1)) & 3u) * 8u;
       } else {
-        shift = ((b0 + (uint32_t)t) & 3u) * 8u;
+        shift = ((b0 + (uint32_t)(t + T0)) & 3u) * 8u;
       }
       const uint32_t word = sw.cw >> shift;
       const float c1p = F32S ? __uint_as_float(sw.cw)
@@ -477,6 +495,25 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
   if (s + 4 < steps) { compute(c1, c0); lds_barrier(); }
 
   // ---------------------------------------------------------------- epilogue
+  if (g.ksplit > 1) {
+    // fp32 partial sums of this contraction range, straight from the accumulators (lane: one row,
+    // four consecutive columns per group of four registers)
+    float* pp = g.part + (int64_t)split * g.M * Nout;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const f32x16& a = acc[tn][tm];
+        const int64_t m = m0 + wm0 + tm * 32 + (lane & 31);
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int64_t n = col0 + wn0 + tn * 32 + 8 * rq + 4 * (lane >> 5);
+          if (m < g.M && n < Nout)
+            *reinterpret_cast<f32x4*>(pp + m * Nout + n) = f32x4{a[4 * rq], a[4 * rq + 1], a[4 * rq + 2], a[4 * rq + 3]};
+        }
+      }
+    return;
+  }
   // Every wave has passed the barrier after the last step, so the activation stages are free: wave
   // cw stages its WM x WN sub-tile as bf16 rows of WN values (16-byte slot c of row q at
   // c ^ ((q >> 1) & (C16 - 1))), then each store instruction writes 16 bytes per lane and whole
@@ -507,6 +544,29 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
   }
 }
 
+// Sum of the contraction ranges' partial sums, in range order, rounded to bf16.
+__global__ __launch_bounds__(256) void gemm_ksum_kernel(const f32x4* __restrict__ part, int64_t n4, int ksplit,
+                                                        u32x2* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 a = part[i];
+  for (int s = 1; s < ksplit; ++s) {
+    const f32x4 b = part[(int64_t)s * n4 + i];
+    a = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+  }
+  out[i] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+}
+
+// Contraction ranges of a forward launch: two when the 128-row tiles would number at most 128
+// (at most half of MI355X's 256 CUs busy) and there are at least 8 steps to share; else one. The
+// rule depends on the shapes only, so the workspace size and the launch always agree.
+int fwd_gemm_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t gx = (N + kBN - 1) / kBN;
+  if ((M > 128 && gx * ((M + 255) / 256) >= 192) || M <= 64) return 1;
+  const int64_t tiles = gx * ((M + 127) / 128);
+  return (tiles <= 128 && (K + kBK - 1) / kBK >= 8) ? 2 : 1;
+}
+
 template <bool DX, bool F32S>
 static hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t stream) {
   const int64_t Nout = DX ? g.K : g.N;
@@ -517,7 +577,12 @@ static hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t stream) {
     hipLaunchKernelGGL((qlora_gemm_kernel<DX, 256, F32S>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
   } else if (g.M > 64) {
     const int gy = (int)((g.M + 127) / 128);
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 128, F32S>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
+    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 128, F32S>), dim3(gx, gy * g.ksplit), dim3(kThreads), 0, stream, g);
+    if (g.ksplit > 1) {
+      const int64_t n4 = g.M * Nout / 4;
+      hipLaunchKernelGGL(gemm_ksum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                         (const f32x4*)g.part, n4, g.ksplit, reinterpret_cast<u32x2*>(g.out));
+    }
   } else {
     const int gy = (int)((g.M + 63) / 64);
     hipLaunchKernelGGL((qlora_gemm_kernel<DX, 64, F32S>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
@@ -528,8 +593,9 @@ static hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t stream) {
 hipError_t launch_fwd_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                            const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                            const float* u, const uint16_t* B, int r, float scale, uint16_t* y,
-                           hipStream_t stream) {
-  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, x, M, u, B, r, scale, y};
+                           float* part, hipStream_t stream) {
+  const int ks = part ? fwd_gemm_splits(M, N, K) : 1;
+  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, x, M, u, B, r, scale, y, ks, part};
   return absmax ? launch_gemm_t<false, true>(g, stream) : launch_gemm_t<false, false>(g, stream);
 }
 
@@ -537,7 +603,7 @@ hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const f
                           const float* absmax, int64_t N, int64_t K, const uint16_t* dy, int64_t M,
                           const float* v, const uint16_t* A, int r, float scale, uint16_t* dx,
                           hipStream_t stream) {
-  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, dy, M, v, A, r, scale, dx};
+  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, dy, M, v, A, r, scale, dx, 1, nullptr};
   return absmax ? launch_gemm_t<true, true>(g, stream) : launch_gemm_t<true, false>(g, stream);
 }
 

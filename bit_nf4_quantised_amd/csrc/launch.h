@@ -13,11 +13,13 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, uint8_t* sc
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                           int64_t numel, uint16_t* out, hipStream_t stream);
 
-// absmax != null: fp32 scales per block instead of scale_q / scale_c2
+// absmax != null: fp32 scales per block instead of scale_q / scale_c2. part: room for
+// fwd_gemm_splits(M, N, K) x M x N fp32 partial sums, or null (then the launch does not split)
+int fwd_gemm_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fwd_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                            const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                            const float* u, const uint16_t* B, int r, float scale, uint16_t* y,
-                           hipStream_t stream);
+                           float* part, hipStream_t stream);
 hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                           const float* absmax, int64_t N, int64_t K, const uint16_t* dy, int64_t M,
                           const float* v, const uint16_t* A, int r, float scale, uint16_t* dx,

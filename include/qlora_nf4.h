@@ -124,11 +124,14 @@ int qlora_linear_bwd(const nf4_weight *W, const uint16_t *x, const uint16_t *dy,
 /* Forward recompute with a known u = x A^T (as saved by qlora_linear_fwd): y = x W~^T + s u B^T.
  * "QLoRA, explained", section "Compute and memory cost": when gradient checkpointing recomputes the
  * forward, the weight is dequantised a third time per layer and step; the adapter down-projection
- * saved by the first forward is reused rather than recomputed. For M > 16 this launches exactly one
- * kernel (the fused dequantise + MFMA GEMM); for M <= 16 it runs the skinny path (which forms u
- * again from A) and needs ws, unless the weight holds 2^31 blocks of 64 or more, where the fused
- * GEMM serves as well.
- *   u   [M x r] float32 input.  y [M x N] bf16 output.  ws as qlora_linear_fwd (may be NULL if M > 16).
+ * saved by the first forward is reused rather than recomputed. For M > 16 this runs the fused
+ * dequantise + MFMA GEMM alone: one launch, or, when the output has too few tiles to fill the GPU
+ * and ws holds qlora_workspace_bytes(M, N, K, r) bytes, the GEMM split over two contraction ranges
+ * plus a launch that adds the two halves, exactly as qlora_linear_fwd does (so y equals its output
+ * bit for bit). For M <= 16 it runs the skinny path (which forms u again from A) and needs ws,
+ * unless the weight holds 2^31 blocks of 64 or more or has fp32 scales, where the fused GEMM serves.
+ *   u   [M x r] float32 input.  y [M x N] bf16 output.  ws as qlora_linear_fwd (may be NULL if M > 16:
+ *   then the GEMM is never split, same tolerance).
  * Errors as qlora_linear_fwd. */
 int qlora_linear_fwd_recompute(const nf4_weight *W, const uint16_t *x, int64_t M, const uint16_t *A,
                                const uint16_t *B, int32_t r, float scale, const float *u, uint16_t *y,
