@@ -78,9 +78,9 @@ constexpr int kThreads = 1024;  // 8 consumer + 4 dequantiser + 4 loader waves
 template <bool DX>
 struct WTile {
   static constexpr int rows = DX ? kBK : kBN;            // contraction rows (DX) or output rows
-  // pitches keep the rows of one 16-lane LDS access in distinct banks (dX: 288-byte rows, so the
-  // four rows a transpose read touches sit 32 bytes apart modulo 128)
-  static constexpr int pitch = DX ? kBN + 16 : kBK + 8;
+  // forward: 144-byte rows put 16 consecutive rows in 16 distinct 16-byte slots of the 64-bank
+  // (256-byte) LDS. dX: unpadded 256-byte rows with the 16-byte chunks swizzled (wswz)
+  static constexpr int pitch = DX ? kBN : kBK + 8;
   static constexpr int segs = DX ? kBN / 32 : kBK / 32;  // 32-value segments per row
 };
 
@@ -99,6 +99,16 @@ struct StepWords {
   u32x4 wq;
   uint32_t cw, c2;
 };
+
+// Element offset of (row, col) within a row of the dX W tile: chunk k (8 values, 16 bytes) of row r
+// sits at chunk k ^ 5 (r & 3). A transpose read (lanes 0-31: four rows r..r+3, r % 4 == 0, times
+// four aligned chunks) then meets 16 distinct chunk positions (the XOR's upper two bits differ per
+// row), and so does a dequantiser store (four rows times one chunk in each of four 64-byte
+// segments: the XOR's lower two bits differ per row). With padded 288-byte rows instead, the reads
+// overlapped in the bank window and 17 % of the GEMM's cycles stalled on bank conflicts.
+__device__ __forceinline__ int wswz(int row, int col) {
+  return ((((col >> 3) ^ (5 * (row & 3))) << 3) | (col & 7));
+}
 
 // Swap with the neighbouring lane (quad_perm [1,0,3,2]).
 __device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
@@ -360,9 +370,16 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
         lut4(L, s1, d[i][2], d[i][3]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      u32x4* dst = reinterpret_cast<u32x4*>(&Ws[t & 1][w_row][32 * w_seg]);
+      if (DX) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = u32x4{d[i][0], d[i][1], d[i][2], d[i][3]};
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<u32x4*>(&Ws[t & 1][w_row][wswz(w_row, 32 * w_seg + 8 * i)]) =
+              u32x4{d[i][0], d[i][1], d[i][2], d[i][3]};
+      } else {
+        u32x4* dst = reinterpret_cast<u32x4*>(&Ws[t & 1][w_row][32 * w_seg]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = u32x4{d[i][0], d[i][1], d[i][2], d[i][3]};
+      }
     };
 
     // ---- adapter steps: bf16(s * u) (or v) into the activation stage, B (or A) into the W stage
@@ -385,7 +402,6 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
         }
         *reinterpret_cast<u32x4*>(xs + row * kBK + ((c ^ ((row >> 1) & 7)) * 8)) = v;
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(&Ws[t & 1][w_row][32 * w_seg]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
@@ -397,7 +413,8 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
           const int j = j0 + 32 * w_seg + 8 * i;
           if (n < g.N && j < g.r) v = *reinterpret_cast<const u32x4*>(g.lora_w + n * g.r + j);
         }
-        dst[i] = v;
+        const int wc = DX ? wswz(w_row, 32 * w_seg + 8 * i) : 32 * w_seg + 8 * i;
+        *reinterpret_cast<u32x4*>(&Ws[t & 1][w_row][wc]) = v;
       }
     };
 
@@ -456,8 +473,8 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
           // two 16-lane transpose loads per operand: lane group g16 covers output columns
           // (g16 & 1) * 16 .. +15 and contraction rows 8 * (g16 >> 1) .. +7
           const int j = lane & 15, g16 = lane >> 4;
-          const int col = wn0 + tn * 32 + (g16 & 1) * 16 + 4 * (j & 3);
           const int row = kk * 16 + (g16 >> 1) * 8 + (j >> 2);
+          const int col = wswz(row, wn0 + tn * 32 + (g16 & 1) * 16 + 4 * (j & 3));   // rows row, row + 4
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(&Ws[wb][row][col]));
           const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(&Ws[wb][row + 4][col]));
           afr[tn] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
