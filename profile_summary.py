@@ -213,6 +213,45 @@ def clock(tag):
     return "\n".join(lines)
 
 
+LDS_CMD = ("timeout -s KILL 240 rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT "
+           "SQ_LDS_DATA_FIFO_FULL SQ_LDS_ADDR_CONFLICT SQ_BUSY_CU_CYCLES SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS "
+           "--output-format csv -d gpurun_out/pmc_lds -o run -- python3 bench.py --steps 2 --warmup 0 "
+           "--no-cpu-baseline --no-paths")
+
+
+def lds(tag):
+    rows = list(csv.DictReader(open(f"{OUT}/pmc_lds/run_counter_collection.csv")))
+    d = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in rows:
+        name = short(r["Kernel_Name"])
+        if name.startswith("Custom_Cijk"):
+            name = "hipBLASLt Custom_" + name.split("_MT")[1].split("_")[0]
+        elif name.startswith("Cijk"):
+            name = "hipBLASLt " + name.split("_MT")[1].split("_")[0]
+        d[(name, int(r["Grid_Size"]) // int(r["Workgroup_Size"]))][r["Counter_Name"]].append(
+            float(r["Counter_Value"]))
+    lines = [f"# LDS activity of the fused GEMMs: {tag}", "",
+             "Command (from the repository root, on one MI355X):", "", "```", LDS_CMD, "```", "",
+             "Per dispatch, averaged over the dispatches of each kernel and grid. GRBM_GUI_ACTIVE is summed "
+             "over the 8 XCD instances, so cycles per instance are the value / 8; LDS active = "
+             "SQ_LDS_IDX_ACTIVE / (cycles x 256 CUs), and likewise the bank-conflict and data-FIFO-full "
+             "stall cycles (the tool's own LDS utilisation and bank-conflict metrics). The `hipBLASLt` "
+             "rows are the library's dense bf16 GEMM that bench.py times on the same shapes.", "",
+             "| kernel | grid WGs | dispatches | cycles per XCD | LDS active % | bank-conflict stall % | "
+             "data FIFO full % |", "|---|---|---|---|---|---|---|"]
+    for k in sorted(d):
+        if not (k[0].startswith("qlora_gemm") or k[0].startswith("hipBLASLt")):
+            continue
+        c = {n: sum(v) / len(v) for n, v in d[k].items()}
+        g = c["GRBM_GUI_ACTIVE"] / 8
+        lines.append(f"| `{k[0]}` | {k[1]} | {len(d[k]['GRBM_GUI_ACTIVE'])} | {g:.0f} | "
+                     f"{100 * c['SQ_LDS_IDX_ACTIVE'] / (g * 256):.1f} | "
+                     f"{100 * c['SQ_LDS_BANK_CONFLICT'] / (g * 256):.1f} | "
+                     f"{100 * c['SQ_LDS_DATA_FIFO_FULL'] / (g * 256):.1f} |")
+    lines.append("")
+    return "\n".join(lines)
+
+
 if __name__ == "__main__":
     tag = sys.argv[1]
     bench_json = f"{OUT}/bench.json"
@@ -228,6 +267,9 @@ if __name__ == "__main__":
     if os.path.exists(f"{OUT}/ktrace_paths/run_kernel_stats.csv"):
         open(f"{PROF}/bandwidth_paths_kernel_trace.md", "w").write(paths_trace(tag))
         print(open(f"{PROF}/bandwidth_paths_kernel_trace.md").read())
+    if os.path.exists(f"{OUT}/pmc_lds/run_counter_collection.csv"):
+        open(f"{PROF}/fused_gemm_llama8b_lds_counters.md", "w").write(lds(tag))
+        print(open(f"{PROF}/fused_gemm_llama8b_lds_counters.md").read())
     if os.path.exists(f"{OUT}/pmc_clock/run_counter_collection.csv"):
         open(f"{PROF}/fused_gemm_llama8b_clock_mfma.md", "w").write(clock(tag))
         print(open(f"{PROF}/fused_gemm_llama8b_clock_mfma.md").read())
