@@ -1,7 +1,7 @@
-"""Turn the rocprofv3 CSV output of the profiling commands below (written under gpurun_out/ on the
-GPU machine) into the text summaries under profiles/, and record the fused GEMM's HBM bytes per
-launch in profiles/traffic.json with a hash of that kernel's sources, which bench.py reads for its
-roofline's traffic field.
+"""Turn the rocprofv3 CSV output of the profiling commands below (each writes into the directory
+its -d option names) into the text summaries under profiles/, and record the fused GEMM's HBM bytes
+per launch in profiles/traffic.json with a hash of that kernel's sources, which bench.py reads for
+its roofline's traffic field.
 
     python3 profile_summary.py "<workload description>"
 """
