@@ -50,9 +50,10 @@ hipError_t launch_lora_dx(const uint16_t* X, int64_t M, int64_t K, const float* 
 // `part` holds skinny_workspace_floats(M, N, K, r) floats; u_out receives u = x A^T [M x r].
 bool skinny_eligible(int64_t M, int64_t N, int64_t K);
 struct SkinnyPlan {
-  int w_blocks, w_splits, w_sub;   // items: 256-row blocks x splits of w_sub 512-column steps
+  int w_blocks, w_splits, w_sub;   // items: row blocks x splits of w_sub steps
+  int narrow;                      // M <= 4: 64-row blocks, 2048-column steps; else 256 rows, 512
 };
-SkinnyPlan skinny_plan(int64_t N, int64_t K, int r);
+SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r);
 size_t skinny_workspace_floats(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                              int64_t N, int64_t K, const uint16_t* x, int64_t M, const uint16_t* A,

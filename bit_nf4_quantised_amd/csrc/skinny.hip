@@ -256,6 +256,229 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// M <= 4 tokens: four rows x four column chunks per MFMA.
+//
+// How a wave's loads map onto HBM sets the read rate of this regime: one load instruction that
+// touches 16 rows (64 bytes each, the lane order of an MFMA operand) reads the weight at about
+// 5.1 TB/s, one that touches 4 rows with two whole 128-byte lines each at about 6.3 TB/s. With at
+// most four tokens the MFMA's 16 x 16 output can afford the second: its rows i = (rho, c) are 4
+// weight rows x 4 column chunks and its columns j = (t, c') 4 tokens x the same 4 chunks, the
+// chunks of an operand lane being chosen so that A row (rho, c) and B column (t, c') contract over
+// the same columns exactly when c == c'. The diagonal entries c == c' are partial dot products of
+// row rho with token t; the other 12 of every 16 are discarded, which costs nothing as long as
+// M <= 4 (the 16-row layout wastes 16 - M of its 16 token columns just the same). After the last
+// step, every lane keeps its diagonal entry and a quad of lanes sums the four chunks.
+//   * a workgroup of 16 waves owns 64 rows (4 per wave) and one split of the k axis; a step is
+//     2048 columns (1 KB of codes per row);
+//   * lane (kg = lane / 16, rho = lane % 16 / 4, c = lane % 4), h = kg / 2: in window q = 0..3
+//     of a step it loads the 16 bytes at 128 (q + 4 h) + 64 (kg % 2) + 16 c of row rho, so one
+//     load instruction covers 4 rows x two whole 128-byte lines; dword d of them holds columns
+//     256 (q + 4 h) + 128 (kg % 2) + 32 c + 8 d .. + 7, which is also what the activation operand
+//     of (q, d) holds for token t = rho and chunk c' = c;
+//   * the lane's four blocks of a step (one per window) lie 4 apart in one 16-byte window of scale
+//     codes (whose start is shifted per lane by a whole dword so that it covers them); blocks past
+//     the row's end get a zero scale (their activation columns are zeros as well);
+//   * activations (4 tokens x 2048 columns, 16 KB) go through LDS one step ahead, as in the 16-row
+//     kernel; the r rows of A ride along in the items of row block b < r / 16: wave w multiplies
+//     the A rows 16 b + 4 (w / 4) .. + 3 against the activation fragment (q, d = w % 4) of every
+//     window, with the same diagonal layout;
+//   * the split partials go to the 16-row kernel's epilogue.
+constexpr int kS4Step = 2048;                    // k columns per step
+constexpr int kS4Rows = kSkWaves * 4;            // rows of W per workgroup
+
+struct Skinny4W {
+  u32x4 p[4];      // window q of the step
+};
+struct Skinny4S {
+  u32x4 cw;        // 16 scale codes: the lane's block of window q is byte p + 4 q
+  u32x2 c2;        // second-level constants of the step's first group and the next one
+  u32x4 a[4];      // adapter fragments of the four windows
+};
+
+__global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const SkinnyArgs g) {
+  __shared__ __attribute__((aligned(16))) f32x2 tab[256 * 32];
+  // activation stages: 4 tokens x 256 chunks of 8 bf16; chunk k of token t sits at slot k ^ t
+  __shared__ __attribute__((aligned(16))) u32x4 xs[2][4 * 256];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = lane >> 4, hh = kg >> 1, kb2 = kg & 1;
+  const int rho = (lane & 15) >> 2, c = lane & 3;
+  const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
+  const int64_t nsteps = (g.K + kS4Step - 1) / kS4Step;
+
+  {
+    const int byte = tid >> 2;
+    const float hi = __uint_as_float(kSkinnyCodes[byte >> 4]);
+    const float lo = __uint_as_float(kSkinnyCodes[byte & 15]);
+    const u32x4 v = u32x4{__float_as_uint(hi), __float_as_uint(lo), __float_as_uint(hi), __float_as_uint(lo)};
+    u32x4* dst = reinterpret_cast<u32x4*>(&tab[byte * 32 + (tid & 3) * 8]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[k] = v;
+  }
+
+  const int rb = (int)blockIdx.x % g.p.w_blocks, split = (int)blockIdx.x / g.p.w_blocks;
+  const int s_begin = split * g.p.w_sub;
+  const int s_end = (int)min(nsteps, (int64_t)s_begin + g.p.w_sub);
+  const int64_t row = (int64_t)rb * kS4Rows + wave * 4 + rho;   // the row this lane loads
+  const int64_t rowc = min(row, g.N - 1);
+  const int64_t nblocks = g.N * (g.K / kBlock);
+  const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.scale_q, (short)0, (int)((nblocks + 3) & ~int64_t(3)), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rs_c2 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.scale_c2, (short)0, (int)(((nblocks + kGroup - 1) / kGroup) * 4), kRsrcFlags);
+  const int kb = (int)(g.K / kBlock);
+  const uint32_t rowb = (uint32_t)(rowc * kb);
+  const int blk0 = 16 * hh + 2 * kb2 + (c >> 1);              // block of window 0 within a step
+  const uint8_t* prow = g.packed + (int64_t)rowb * 32 + 16 * (c & 1);
+  auto blk_of = [&](int s, int q) { return min(s * 32 + blk0 + 4 * q, kb - 1); };
+  // scale window: 16 bytes from the dword holding the block of window 0 minus 0..3 bytes; since
+  // 32 s + 16 hh is a multiple of 4, the lane's byte p within each dword is the same every step
+  const uint32_t e0 = (rowb & 3u) + (uint32_t)(2 * kb2 + (c >> 1));   // 0..6
+  const uint32_t wsh = (e0 >> 2) * 4u, pbyte = e0 & 3u;
+  const uint32_t gsel = pbyte | ((pbyte + 4u) << 8);                  // bytes p of two dwords
+  // adapter rows of this wave (items of row block rb < r / 16)
+  const bool a_live = rb * 16 < g.r;
+  const int64_t arow = min((int64_t)rb * 16 + 4 * (wave >> 2) + rho, (int64_t)g.r - 1);
+  const int dA = wave & 3;
+  const uint16_t* arp = g.A + arow * g.K;
+
+  auto load_w = [&](int s, Skinny4W& st) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      st.p[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(prow + (uint32_t)blk_of(s, q) * 32u));
+  };
+  auto load_scales = [&](int s, Skinny4S& ss) {
+    const uint32_t w0 = ((rowb + (uint32_t)(32 * s + 16 * hh)) & ~3u) + wsh;
+    ss.cw = __builtin_amdgcn_raw_buffer_load_b128(rs_q, w0, 0, 0);
+    ss.c2 = __builtin_amdgcn_raw_buffer_load_b64(rs_c2, ((rowb + (uint32_t)(32 * s)) >> 8) * 4u, 0, 0);
+  };
+  auto a_col = [&](int s, int q) {
+    return (uint32_t)min((int64_t)s * kS4Step + 256 * (q + 4 * hh) + 128 * kb2 + 32 * c + 8 * dA, g.K - 8);
+  };
+  auto load_a = [&](int s, int q, Skinny4S& ss) {
+    ss.a[q] = *reinterpret_cast<const u32x4*>(arp + a_col(s, q));
+  };
+
+  // activation copy: thread t moves token t / 256, chunk t % 256 (slot chunk ^ token)
+  const int xt = tid >> 8, xch = tid & 255;
+  const uint16_t* xp = g.x + (int64_t)min(xt, (int)g.M - 1) * g.K;
+  auto load_x = [&](int s) {
+    const uint32_t col = (uint32_t)min((int64_t)s * kS4Step + 8 * xch, g.K - 8);
+    return *reinterpret_cast<const u32x4*>(xp + col);
+  };
+  auto store_x = [&](int s, u32x4* stage, u32x4 v) {
+    const bool live = xt < g.M && (int64_t)s * kS4Step + 8 * xch < g.K;
+    stage[xt * 256 + (xch ^ xt)] = live ? v : u32x4{0u, 0u, 0u, 0u};
+  };
+  // activation fragment (q, d) of this lane: token rho, chunk 32 (q + 4 hh) + 16 kb2 + 4 c + d
+  const int xbase = rho * 256 + 128 * hh + 16 * kb2 + 4 * c;
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accu = f32x4{0.f, 0.f, 0.f, 0.f};
+  const char* tab_bytes = reinterpret_cast<const char*>(tab);
+
+  auto process = [&](int s, const Skinny4W& st, Skinny4W& nx, Skinny4S& ss, const u32x4* xsv, bool more) {
+    // block scales of the four windows
+    float c1p[4];
+    {
+      const uint32_t lo = __builtin_amdgcn_perm(ss.cw[1], ss.cw[0], gsel);
+      const uint32_t hi = __builtin_amdgcn_perm(ss.cw[3], ss.cw[2], gsel);
+      const uint32_t codes = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      // blocks of this step before the next group boundary
+      const int bnd = 256 - (int)((rowb + (uint32_t)(32 * s)) & 255u);
+      const float c2a = __uint_as_float(ss.c2[0]), c2b = __uint_as_float(ss.c2[1]);
+      c1p[0] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)codes, 0), blk0 >= bnd ? c2b : c2a);
+      c1p[1] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)codes, 1), blk0 + 4 >= bnd ? c2b : c2a);
+      c1p[2] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)codes, 2), blk0 + 8 >= bnd ? c2b : c2a);
+      c1p[3] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)codes, 3), blk0 + 12 >= bnd ? c2b : c2a);
+      if (32 * s + 32 > kb) {   // the step runs past the row's end (wave-uniform)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (32 * s + blk0 + 4 * q >= kb) c1p[q] = 0.f;
+      }
+    }
+    if (more) load_scales(s + 1, ss);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (more) nx.p[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(prow + (uint32_t)blk_of(s + 1, q) * 32u));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16x8 bx = __builtin_bit_cast(bf16x8, xsv[xbase + 32 * q + (d ^ rho)]);
+        const uint32_t word = st.p[q][d];
+        uint32_t a[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const uint32_t off = __builtin_amdgcn_perm(word, laneoff, 0x0C0C0000u | ((4u + bb) << 8));
+          const f32x2 qv = *reinterpret_cast<const f32x2*>(tab_bytes + off);
+          a[bb] = pack_bf16x2(__fmul_rn(qv[0], c1p[q]), __fmul_rn(qv[1], c1p[q]));
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, (u32x4{a[0], a[1], a[2], a[3]})),
+                                                      bx, acc, 0, 0, 0);
+      }
+      if (a_live) {
+        const bf16x8 bx = __builtin_bit_cast(bf16x8, xsv[xbase + 32 * q + (dA ^ rho)]);
+        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ss.a[q]), bx, accu, 0, 0, 0);
+        if (more) load_a(s + 1, q, ss);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  Skinny4W w[2];
+  Skinny4S ss;
+  {
+    const u32x4 x0 = load_x(s_begin);
+    load_w(s_begin, w[0]);
+    load_scales(s_begin, ss);
+    if (a_live) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) load_a(s_begin, q, ss);
+    }
+    store_x(s_begin, xs[0], x0);
+  }
+  __syncthreads();   // the pair table and the first activation stage are in place
+  auto phase = [&](int sp, int p, bool more) {
+    u32x4 xn = u32x4{0u, 0u, 0u, 0u};
+    if (more) xn = load_x(sp + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    process(sp, w[p], w[1 - p], ss, xs[p], more);
+    if (more) store_x(sp + 1, xs[1 - p], xn);
+    lds_barrier();
+  };
+  int sp = s_begin;
+  for (; sp + 2 < s_end; sp += 2) {
+    phase(sp, 0, true);
+    phase(sp + 1, 1, true);
+  }
+  if (sp + 1 < s_end) {
+    phase(sp, 0, true);
+    phase(sp + 1, 1, false);
+  } else {
+    phase(sp, 0, false);
+  }
+
+  // lane keeps D[(kg, c)][(rho, c)]: row 4 wave + kg, token rho, chunk c; a quad sums the chunks
+  auto diag_sum = [&](const f32x4& v) {
+    float d = c == 0 ? v[0] : c == 1 ? v[1] : c == 2 ? v[2] : v[3];
+    d += dpp_f<0xB1>(d);   // quad_perm [1,0,3,2]
+    d += dpp_f<0x4E>(d);   // quad_perm [2,3,0,1]
+    return d;
+  };
+  const float yv = diag_sum(acc);
+  const float uv = diag_sum(accu);
+  if (c == 0 && rho < g.M) {
+    const int64_t r_out = (int64_t)rb * kS4Rows + wave * 4 + kg;
+    if (r_out < g.N) g.part[((int64_t)split * g.M + rho) * g.N + r_out] = yv;
+    if (a_live) {
+      const int ar = rb * 16 + 4 * (wave >> 2) + kg;
+      g.upart[(((int64_t)split * 4 + dA) * g.M + rho) * g.r + ar] = uv;
+    }
+  }
+}
+
 // y[m][n] = bf16(sum_s part[s][m][n] + scale * sum_j u[m][j] B[n][j]),  u[m][j] = sum_p upart[p][m][j].
 // Workgroup (x, y) = columns 256 x .. +255 of token y. It rebuilds u[y][:] in LDS: thread t sums
 // the contiguous run t / r of the u partials for j = t % r, then thread j adds the runs in order,
@@ -311,11 +534,14 @@ bool skinny_eligible(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 16 && N * (K / kBlock) < (int64_t(1) << 31);
 }
 
-SkinnyPlan skinny_plan(int64_t N, int64_t K, int r) {
+SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r) {
   SkinnyPlan p;
-  const int64_t nsteps = (K + kStep - 1) / kStep;
+  p.narrow = M <= 4 ? 1 : 0;
+  const int rows = p.narrow ? kS4Rows : kSkRows;
+  const int64_t step = p.narrow ? kS4Step : kStep;
+  const int64_t nsteps = (K + step - 1) / step;
   // every 16-row tile of A needs a row block to ride along with
-  p.w_blocks = (int)max((N + kSkRows - 1) / kSkRows, (int64_t)(r / 16));
+  p.w_blocks = (int)max((N + rows - 1) / rows, (int64_t)(r / 16));
   int64_t want = kSkSlots / p.w_blocks;
   if (want > nsteps) want = nsteps;
   if (want < 1) want = 1;
@@ -324,27 +550,33 @@ SkinnyPlan skinny_plan(int64_t N, int64_t K, int r) {
   return p;
 }
 
+// u partial sums per split: one per wave (16-row kernel) or one per activation dword (M <= 4)
+static int skinny_u_parts(const SkinnyPlan& p) { return p.w_splits * (p.narrow ? 4 : kSkWaves); }
+
 static size_t skinny_wpart_floats(const SkinnyPlan& p, int64_t M, int64_t N) {
   // the u partials start on a 16-byte boundary
   return ((size_t)p.w_splits * (size_t)M * (size_t)N + 3) & ~size_t(3);
 }
 
 size_t skinny_workspace_floats(int64_t M, int64_t N, int64_t K, int r) {
-  const SkinnyPlan p = skinny_plan(N, K, r);
-  return skinny_wpart_floats(p, M, N) + (size_t)p.w_splits * kSkWaves * (size_t)M * (size_t)r;
+  const SkinnyPlan p = skinny_plan(M, N, K, r);
+  return skinny_wpart_floats(p, M, N) + (size_t)skinny_u_parts(p) * (size_t)M * (size_t)r;
 }
 
 hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                              int64_t N, int64_t K, const uint16_t* x, int64_t M, const uint16_t* A,
                              const uint16_t* B, int r, float scale, float* part, float* u_out,
                              uint16_t* y, hipStream_t stream) {
-  const SkinnyPlan p = skinny_plan(N, K, r);
+  const SkinnyPlan p = skinny_plan(M, N, K, r);
   float* upart = part + skinny_wpart_floats(p, M, N);
   SkinnyArgs g{packed, scale_q, scale_c2, N, K, x, M, A, r, p, part, upart};
   const int items = p.w_blocks * p.w_splits;
-  hipLaunchKernelGGL(skinny_fwd_kernel, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
+  if (p.narrow)
+    hipLaunchKernelGGL(skinny4_fwd_kernel, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
+  else
+    hipLaunchKernelGGL(skinny_fwd_kernel, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
   hipLaunchKernelGGL(skinny_epilogue_kernel, dim3((unsigned)((N + 255) / 256), (unsigned)M), dim3(256), 0,
-                     stream, part, p.w_splits, upart, p.w_splits * kSkWaves, M, N, r, B, scale, u_out, y);
+                     stream, part, p.w_splits, upart, skinny_u_parts(p), M, N, r, B, scale, u_out, y);
   return hipGetLastError();
 }
 

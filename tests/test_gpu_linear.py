@@ -63,6 +63,12 @@ def test_single_linear_workload():
     (4, 400, 960, 64, 0.25),
     (16, 416, 1024, 16, 2.0),
     (16, 64, 64, 16, 2.0),         # one block per row
+    (2, 400, 960, 16, 2.0),        # M <= 4: four rows x four chunks per MFMA
+    (3, 1040, 1088, 128, 0.5),     #   rank 128, ragged rows
+    (1, 64, 64, 16, 2.0),          #   one block per row
+    (4, 96, 4160, 32, 1.0),        #   65 blocks per row: a 64-column last step, odd scale offsets
+    (1, 16, 2048, 64, 1.0),        #   fewer rows than one row block; the adapter needs four blocks
+    (4, 208, 16448, 16, 2.0),      #   257 blocks per row: groups of 256 blocks split steps
     (1800, 14336, 128, 16, 2.0),   # forward: 896 tiles of 256 rows, ragged last row block
     (1800, 128, 14336, 16, 2.0),   # the same for the dX GEMM (14336 output columns)
 ])
@@ -79,7 +85,7 @@ def test_accumulate_mode():
     check_full(w, x, a, b, dy, 2.0, "accumulate", accumulate=True, dA0=dA0, dB0=dB0)
 
 
-@pytest.mark.parametrize("M", [8, 200])
+@pytest.mark.parametrize("M", [1, 3, 8, 200])
 def test_one_hot_rows_are_exact(M):
     """B = 0 and one-hot rows: y rows are columns of W~ and dX rows are rows of W~, bit for bit."""
     N, K, r = 256, 512, 16
