@@ -131,6 +131,34 @@ def test_fwd_validation():
     assert f(None, FAKE, 64, FAKE, FAKE, 16, 2.0, FAKE, None, FAKE, ws, None) == q.NF4_ERR_NULL
 
 
+def _skinny_fwd_bytes(M, N, K, r):
+    """Forward workspace of the few-token path, from its documented plan: M <= 4 takes 64-row
+    blocks and 2048-column steps with one u partial per activation dword (4 per split), larger M
+    256-row blocks and 512-column steps with one u partial per wave (16 per split); the row blocks
+    times the k splits fill 256 workgroups at most, and u plus the partials come first."""
+    rows, step, uper = (64, 2048, 4) if M <= 4 else (256, 512, 16)
+    nsteps = -(-K // step)
+    blocks = max(-(-N // rows), r // 16)
+    want = min(max(256 // blocks, 1), nsteps)
+    sub = -(-nsteps // want)
+    splits = -(-nsteps // sub)
+    part = ((splits * M * N + 3) // 4) * 4 + splits * uper * M * r
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    return up(M * r * 4) + up(part * 4)
+
+
+@pytest.mark.parametrize("M,N,K,r", [(1, 8192, 28672, 16), (4, 8192, 28672, 16), (5, 8192, 28672, 16),
+                                     (16, 8192, 28672, 16), (3, 1040, 1088, 128), (4, 96, 4160, 32),
+                                     (1, 16, 2048, 64), (2, 14336, 4096, 64)])
+def test_skinny_workspace_follows_the_plan(M, N, K, r):
+    need = _skinny_fwd_bytes(M, N, K, r)
+    assert q.qlora_workspace_bytes(M, N, K, r) >= need
+    # one byte less than the plan's partial sums is refused before any launch
+    w = ctypes.byref(_w(N=N, K=K))
+    assert lib.qlora_linear_fwd(w, FAKE, M, FAKE, FAKE, r, 2.0, FAKE, None, FAKE, need - 1, None) == \
+        q.NF4_ERR_WORKSPACE
+
+
 def test_recompute_validation():
     w = ctypes.byref(_w())
     f = lib.qlora_linear_fwd_recompute
