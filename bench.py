@@ -363,6 +363,7 @@ def bandwidth_paths(torch, q, dev, args):
     log("[bench] skinny weight 8192x28672")
     w = wl.weight("stream", 0, lin.n, lin.k, "gauss", 0.02)
     base = q.quantize_weight(torch.from_numpy(w).to(dev))
+    base_f32 = q.quantize_weight(torch.from_numpy(w).to(dev), double_quant=False)
     del w
     copies = [base] + [q.NF4Weight(base.packed.clone(), base.scale_q.clone(), base.scale_c2.clone(),
                                    base.N, base.K) for _ in range(3)]
@@ -386,7 +387,24 @@ def bandwidth_paths(torch, q, dev, args):
         skinny[f"M={m}"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
                             "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "bytes": nbytes}
         log(f"[bench] skinny M={m}: {ms*1e3:.1f} us, {gbps:.0f} GB/s")
+        if m == 1:
+            # the same forward with fp32 block scales (no double quantisation), 4 rotating copies
+            fcopies = [base_f32] + [q.NF4Weight(base_f32.packed.clone(), None, None, base_f32.N, base_f32.K,
+                                                absmax=base_f32.absmax.clone()) for _ in range(3)]
+
+            def fcall(i):
+                q.qlora_linear_fwd(fcopies[i % len(fcopies)], X, A, B, sk.scale, y, u, ws=wsk)
+
+            fcall(0)
+            fms = timed(fcall, 200, torch)
+            fbytes = nbytes - nf4_bytes(lin.n * lin.k) + lin.n * lin.k // 2 + 4 * (lin.n * lin.k // 64)
+            skinny["M=1 fp32 scales"] = {"us": round(fms * 1e3, 2), "GBps": round(fbytes / (fms * 1e-3) / 1e9, 1),
+                                         "frac_hbm": round(fbytes / (fms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                                         "bytes": fbytes}
+            log(f"[bench] skinny M=1, fp32 scales: {fms*1e3:.1f} us")
+            del fcopies
     res["skinny_fwd_8192x28672"] = skinny
+    del base_f32
 
     # adapter merge into the dequantised base, same weight (4 rotating copies), rank 16
     _, _, a, b, _ = wl.linear_inputs(sk, 0, lin, m=1)

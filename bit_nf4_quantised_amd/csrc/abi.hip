@@ -160,8 +160,8 @@ int qlora_linear_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const ui
   if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;
   float* u = u_out ? u_out : static_cast<float*>(ws);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
-  if (!W->absmax && nf4::skinny_eligible(M, N, K)) {
-    return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, N, K, x, M, A, B, r,
+  if (nf4::skinny_eligible(M, N, K) && (!W->absmax || M <= 4)) {
+    return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, A, B, r,
                                            scale, part, u, y, stream));
   }
   hipError_t e = nf4::launch_lora_u(x, M, K, A, r, part, u, stream);
@@ -183,13 +183,13 @@ int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M
       (ws && !aligned16(ws)))
     return NF4_ERR_ALIGN;
   const int64_t N = W->N, K = W->K;
-  if (!W->absmax && nf4::skinny_eligible(M, N, K)) {
+  if (nf4::skinny_eligible(M, N, K) && (!W->absmax || M <= 4)) {
     // the skinny path forms u itself from the adapter rows; it needs the workspace
     const size_t need = fwd_ws(M, N, K, r);
     if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;
     float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
     float* u_scratch = static_cast<float*>(ws);
-    return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, N, K, x, M, A, B, r,
+    return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, A, B, r,
                                            scale, part, u_scratch, y, stream));
   }
   // with a workspace of the forward's size, the same launches as qlora_linear_fwd (and the same

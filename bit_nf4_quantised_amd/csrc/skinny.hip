@@ -53,7 +53,8 @@ struct SkinnyArgs {
   int r;
   SkinnyPlan p;
   float* part;         // [w_splits][M][N]
-  float* upart;        // [w_splits * 16][M][r]
+  float* upart;        // [u parts][M][r]
+  const float* absmax; // fp32 block scales instead of scale_q / scale_c2 (M <= 4 kernel only)
 };
 
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
@@ -283,6 +284,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
 //     kernel; the r rows of A ride along in the items of row block b < r / 16: wave w multiplies
 //     the A rows 16 b + 4 (w / 4) .. + 3 against the activation fragment (q, d = w % 4) of every
 //     window, with the same diagonal layout;
+//   * with fp32 block scales (no double quantisation) the lane loads its four blocks' scales
+//     directly (F32S);
 //   * the split partials go to the 16-row kernel's epilogue.
 constexpr int kS4Step = 2048;                    // k columns per step
 constexpr int kS4Rows = kSkWaves * 4;            // rows of W per workgroup
@@ -296,6 +299,7 @@ struct Skinny4S {
   u32x4 a[4];      // adapter fragments of the four windows
 };
 
+template <bool F32S>
 __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const SkinnyArgs g) {
   __shared__ __attribute__((aligned(16))) f32x2 tab[256 * 32];
   // activation stages: 4 tokens x 256 chunks of 8 bf16; chunk k of token t sits at slot k ^ t
@@ -327,6 +331,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
       (void*)g.scale_q, (short)0, (int)((nblocks + 3) & ~int64_t(3)), kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rs_c2 = __builtin_amdgcn_make_buffer_rsrc(
       (void*)g.scale_c2, (short)0, (int)(((nblocks + kGroup - 1) / kGroup) * 4), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rs_am = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.absmax, (short)0, (int)(nblocks * 4), kRsrcFlags);
   const int kb = (int)(g.K / kBlock);
   const uint32_t rowb = (uint32_t)(rowc * kb);
   const int blk0 = 16 * hh + 2 * kb2 + (c >> 1);              // block of window 0 within a step
@@ -349,9 +355,16 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
       st.p[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(prow + (uint32_t)blk_of(s, q) * 32u));
   };
   auto load_scales = [&](int s, Skinny4S& ss) {
-    const uint32_t w0 = ((rowb + (uint32_t)(32 * s + 16 * hh)) & ~3u) + wsh;
-    ss.cw = __builtin_amdgcn_raw_buffer_load_b128(rs_q, w0, 0, 0);
-    ss.c2 = __builtin_amdgcn_raw_buffer_load_b64(rs_c2, ((rowb + (uint32_t)(32 * s)) >> 8) * 4u, 0, 0);
+    if constexpr (F32S) {
+      // the fp32 scales of the lane's four blocks (blocks past the row's end re-read its last one)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        ss.cw[q] = __builtin_amdgcn_raw_buffer_load_b32(rs_am, (rowb + (uint32_t)blk_of(s, q)) * 4u, 0, 0);
+    } else {
+      const uint32_t w0 = ((rowb + (uint32_t)(32 * s + 16 * hh)) & ~3u) + wsh;
+      ss.cw = __builtin_amdgcn_raw_buffer_load_b128(rs_q, w0, 0, 0);
+      ss.c2 = __builtin_amdgcn_raw_buffer_load_b64(rs_c2, ((rowb + (uint32_t)(32 * s)) >> 8) * 4u, 0, 0);
+    }
   };
   auto a_col = [&](int s, int q) {
     return (uint32_t)min((int64_t)s * kS4Step + 256 * (q + 4 * hh) + 128 * kb2 + 32 * c + 8 * dA, g.K - 8);
@@ -381,7 +394,15 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
   auto process = [&](int s, const Skinny4W& st, Skinny4W& nx, Skinny4S& ss, const u32x4* xsv, bool more) {
     // block scales of the four windows
     float c1p[4];
-    {
+    if constexpr (F32S) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) c1p[q] = __uint_as_float(ss.cw[q]);
+      if (32 * s + 32 > kb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (32 * s + blk0 + 4 * q >= kb) c1p[q] = 0.f;
+      }
+    } else {
       const uint32_t lo = __builtin_amdgcn_perm(ss.cw[1], ss.cw[0], gsel);
       const uint32_t hi = __builtin_amdgcn_perm(ss.cw[3], ss.cw[2], gsel);
       const uint32_t codes = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
@@ -564,15 +585,18 @@ size_t skinny_workspace_floats(int64_t M, int64_t N, int64_t K, int r) {
 }
 
 hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
-                             int64_t N, int64_t K, const uint16_t* x, int64_t M, const uint16_t* A,
-                             const uint16_t* B, int r, float scale, float* part, float* u_out,
-                             uint16_t* y, hipStream_t stream) {
+                             const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                             const uint16_t* A, const uint16_t* B, int r, float scale, float* part,
+                             float* u_out, uint16_t* y, hipStream_t stream) {
   const SkinnyPlan p = skinny_plan(M, N, K, r);
+  if (absmax && !p.narrow) return hipErrorInvalidValue;   // fp32 scales: the M <= 4 kernel only
   float* upart = part + skinny_wpart_floats(p, M, N);
-  SkinnyArgs g{packed, scale_q, scale_c2, N, K, x, M, A, r, p, part, upart};
+  SkinnyArgs g{packed, scale_q, scale_c2, N, K, x, M, A, r, p, part, upart, absmax};
   const int items = p.w_blocks * p.w_splits;
-  if (p.narrow)
-    hipLaunchKernelGGL(skinny4_fwd_kernel, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
+  if (p.narrow && absmax)
+    hipLaunchKernelGGL(skinny4_fwd_kernel<true>, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
+  else if (p.narrow)
+    hipLaunchKernelGGL(skinny4_fwd_kernel<false>, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
   else
     hipLaunchKernelGGL(skinny_fwd_kernel, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
   hipLaunchKernelGGL(skinny_epilogue_kernel, dim3((unsigned)((N + 255) / 256), (unsigned)M), dim3(256), 0,

@@ -66,7 +66,7 @@ typedef enum {
  * (scale_q and scale_c2 set, absmax NULL: 4.127 bits per weight) or the fp32 absmax itself
  * (absmax set, scale_q and scale_c2 NULL: the 4.5-bit baseline without double quantisation,
  * "QLoRA, explained", Double quantisation). nf4_dequant and the linear calls take either; with
- * fp32 scales the forward runs the fused GEMM at every token count (no skinny path) and
+ * fp32 scales the few-token forward path serves M <= 4 only (the fused GEMM above) and
  * qlora_merge is not available (NF4_ERR_SHAPE). */
 typedef struct {
   const uint8_t *packed;    /* [N*K/2]                 */
@@ -129,7 +129,8 @@ int qlora_linear_bwd(const nf4_weight *W, const uint16_t *x, const uint16_t *dy,
  * and ws holds qlora_workspace_bytes(M, N, K, r) bytes, the GEMM split over two contraction ranges
  * plus a launch that adds the two halves, exactly as qlora_linear_fwd does (so y equals its output
  * bit for bit). For M <= 16 it runs the skinny path (which forms u again from A) and needs ws,
- * unless the weight holds 2^31 blocks of 64 or more or has fp32 scales, where the fused GEMM serves.
+ * unless the weight holds 2^31 blocks of 64 or more, or has fp32 scales and M > 4, where the fused
+ * GEMM serves.
  *   u   [M x r] float32 input.  y [M x N] bf16 output.  ws as qlora_linear_fwd (may be NULL if M > 16:
  *   then the GEMM is never split, same tolerance).
  * Errors as qlora_linear_fwd. */

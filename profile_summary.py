@@ -70,7 +70,8 @@ PATH_KERNELS = {
                            "setup quantisations of other shapes",
     "nf4_double_quant_kernel": "double quantise: same stream (per weight 0.0784 B), plus setup",
     "nf4_dequant_kernel": "dequantise, same stream (per weight 2.5159 B)",
-    "skinny4_fwd_kernel": "skinny forward, 8192x28672 at M = 1 and 4 (four rows x four chunks per MFMA)",
+    "skinny4_fwd_kernel<false>": "skinny forward, 8192x28672 at M = 1 and 4 (four rows x four chunks per MFMA)",
+    "skinny4_fwd_kernel<true>": "the same at M = 1 with fp32 block scales (no double quantisation)",
     "skinny_fwd_kernel": "skinny forward, 8192x28672 at M = 16",
     "skinny_epilogue_kernel": "its split-K epilogue",
     "qlora_merge_kernel<1>": "adapter merge, 8192x28672, rank 16",

@@ -169,6 +169,9 @@ def _f32s_weight(w):
     (513, 128, 128, 64, 0.25),     # three row tiles, the last with one row
     (77, 1040, 1088, 128, 0.5),
     (8, 400, 960, 16, 2.0),        # few tokens: the fused GEMM, not the skinny path
+    (1, 400, 960, 16, 2.0),        # M <= 4: the few-token kernel with fp32 scales
+    (4, 96, 4160, 32, 1.0),        #   65 blocks per row, a 64-column last step
+    (3, 1040, 1088, 128, 0.5),     #   rank 128, ragged rows
     (2048, 4096, 4096, 16, 2.0),   # the q/o shape of the 8B layer set
 ])
 def test_fp32_scale_weight_matches_oracle(M, N, K, r, s):
@@ -186,13 +189,15 @@ def test_fp32_scale_weight_matches_oracle(M, N, K, r, s):
     assert_close("dB", dB, dbr)
 
 
-def test_fp32_scale_weight_one_hot_and_recompute():
+@pytest.mark.parametrize("M", [3, 200])
+def test_fp32_scale_weight_one_hot_and_recompute(M):
     # with B = 0, one-hot rows of x give y rows equal to columns of W~ bit for bit, one-hot rows of
-    # dY give dX rows equal to rows of W~; the recompute forward equals the forward
+    # dY give dX rows equal to rows of W~; the recompute forward equals the forward (M = 3: the
+    # few-token kernel, M = 200: the fused GEMM)
     import torch
     import bit_nf4_quantised_amd as q
     from gpu_helpers import bf16_to_dev, bits_from_dev, dev
-    M, N, K, r = 200, 384, 960, 16
+    N, K, r = 384, 960, 16
     w, x, a, b, dy = _inputs(5, M, N, K, r)
     qw, wt = _f32s_weight(w)
     x = np.zeros((M, K), np.uint16)
