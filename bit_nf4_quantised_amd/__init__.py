@@ -22,7 +22,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
+# NF4_LIBRARY names another build of the same library (the host-sanitised one the CPU tests use)
+LIB_PATH = os.environ.get("NF4_LIBRARY") or os.path.join(_HERE, "libqlora_nf4.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

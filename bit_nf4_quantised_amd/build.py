@@ -47,6 +47,49 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C ABI layer (argument
+# validation and kernel sequencing). Each -fsanitize= applies to the host compilation only; the
+# device code is unchanged. The library leaves the sanitizer runtime unresolved: a process that
+# loads it preloads libclang_rt.asan (which carries the UBSan handlers too).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(BUILD, "libqlora_nf4_san.so")
+
+
+def asan_runtime() -> str:
+    """Path of clang's shared AddressSanitizer runtime next to hipcc."""
+    root = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "lib", "clang")
+    for base in (root, "/opt/rocm/lib/llvm/lib/clang"):
+        if os.path.isdir(base):
+            for ver in sorted(os.listdir(base), reverse=True):
+                cand = os.path.join(base, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+                if os.path.exists(cand):
+                    return os.path.realpath(cand)
+    raise RuntimeError("clang's AddressSanitizer runtime (libclang_rt.asan-x86_64.so) not found")
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """Build _build/libqlora_nf4_san.so: abi.hip with host sanitizers, the kernels as usual."""
+    os.makedirs(BUILD, exist_ok=True)
+    others = [s for s in SOURCES if s != "abi.hip"]
+    with ThreadPoolExecutor(max_workers=min(len(others), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, others))
+    san_obj = os.path.join(BUILD, "abi_san.o")
+    cmd = [hipcc()] + COMMON + ["-g"] + SANITIZE + ["-c", os.path.join(CSRC, "abi.hip"), "-o", san_obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stderr}")
+    tmp = SAN_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, san_obj] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:

@@ -29,6 +29,18 @@ int check_weight(const nf4_weight* W) {
 
 int check_rank(int32_t r) { return (r >= 16 && r <= 128 && r % 16 == 0) ? NF4_OK : NF4_ERR_RANK; }
 
+// Sizes the linear calls' kernels can address. Their buffer records and offsets are 32-bit: the
+// backward's packed-weight record spans up to N*K/2 bytes, an activation tile up to 256 rows of a
+// matrix with N or K bf16 columns (512 * max(N, K) bytes), each below 2^31; a launch counts its
+// workgroups, ceil(M / 64) * ceil(max(N, K) / 128), in 32 bits.
+bool linear_shape_ok(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || M >= (int64_t(1) << 31)) return false;
+  if (N >= (int64_t(1) << 22) || K >= (int64_t(1) << 22)) return false;
+  if (N * K >= (int64_t(1) << 32)) return false;
+  const int64_t mx = N > K ? N : K;
+  return ((M + 63) / 64) * ((mx + 127) / 128) < (int64_t(1) << 31);
+}
+
 int from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
@@ -138,6 +150,7 @@ int qlora_merge(const nf4_weight* W, const uint16_t* A, const uint16_t* B, int32
 
 size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M < 0 || N < 16 || K < 64 || N % 16 || K % 64 || check_rank(r)) return 0;
+  if (!linear_shape_ok(M, N, K)) return 0;
   if (M == 0) return 0;
   size_t a = fwd_ws(M, N, K, r), b = bwd_ws(M, N, K, r);
   return a > b ? a : b;
@@ -148,7 +161,7 @@ int qlora_linear_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const ui
                      size_t ws_bytes, hipStream_t stream) {
   int st = check_weight(W);
   if (st) return st;
-  if (M < 0) return NF4_ERR_SHAPE;
+  if (!linear_shape_ok(M, W->N, W->K)) return NF4_ERR_SHAPE;
   if ((st = check_rank(r))) return st;
   if (M == 0) return NF4_OK;
   if (!x || !A || !B || !y) return NF4_ERR_NULL;
@@ -175,7 +188,7 @@ int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M
                                void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_weight(W);
   if (st) return st;
-  if (M < 0) return NF4_ERR_SHAPE;
+  if (!linear_shape_ok(M, W->N, W->K)) return NF4_ERR_SHAPE;
   if ((st = check_rank(r))) return st;
   if (M == 0) return NF4_OK;
   if (!x || !A || !B || !u || !y) return NF4_ERR_NULL;
@@ -207,7 +220,7 @@ int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy,
                      hipStream_t stream) {
   int st = check_weight(W);
   if (st) return st;
-  if (M < 0) return NF4_ERR_SHAPE;
+  if (!linear_shape_ok(M, W->N, W->K)) return NF4_ERR_SHAPE;
   if ((st = check_rank(r))) return st;
   if (M == 0) return NF4_OK;
   if (!x || !dy || !A || !B || !u || !dA || !dB) return NF4_ERR_NULL;

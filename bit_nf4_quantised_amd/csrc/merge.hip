@@ -1,8 +1,8 @@
 // Adapter merged into the dequantised base weight, in bf16 (gfx950).
 //
-// "QLoRA, explained", Quality loss at merge time: the adapter was trained against the dequantised
-// weight W~, so the merge that keeps what was trained is out = W~ + s B A, served in bf16 (s =
-// lora_alpha / r, as in the forward). Here: W~ exactly as the dequantisation kernels produce it,
+// "QLoRA, explained", Quality loss at merge time: training saw W~, the dequantised weight, never the
+// original one, so the merge that preserves the trained model is out = W~ + s B A, served in bf16
+// (s = lora_alpha / r, as in the forward). Here: W~ exactly as the dequantisation kernels produce it,
 // the rank-r product B A in fp32 on MFMA (bf16 products are exact, fp32 accumulation), then
 // fl32(W~ + fl32(s * (B A))) rounded once to bf16, nearest even.
 //

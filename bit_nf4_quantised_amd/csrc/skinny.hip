@@ -514,7 +514,9 @@ __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __res
   __shared__ float us[128];
   const int64_t mm = blockIdx.y;
   const int tid = threadIdx.x;
-  const int nruns = 256 / r;                          // r divides 256 (r % 16 == 0, r <= 128)
+  // nruns * r <= 256 and nruns * per_run >= u_parts: threads past nruns * r (r = 48, 80, 96, 112)
+  // form a run past the last partial, which sums nothing and is never read
+  const int nruns = 256 / r;
   const int per_run = (u_parts + nruns - 1) / nruns;
   {
     const int j = tid % r, run = tid / r;

@@ -1,7 +1,7 @@
 // Codebook and blocksize variants of the 4-bit format, and scales without double quantisation
 // (gfx950).
 //
-// "QLoRA, explained", A toy run (NF4 against a symmetric 15-level INT4 grid and E2M1 FP4 scaled to
+// "QLoRA, explained", A toy run (NF4 beside an INT4 grid of 15 levels k/7 and E2M1 FP4 rescaled to
 // [-1, 1]), its blocksize discussion (16 to 4096 values per absmax) and Double quantisation (whose
 // baseline keeps one fp32 absmax per block):
 //   q4_quantize_kernel<B>       blockwise absmax over blocks of B values and, per value, the exact

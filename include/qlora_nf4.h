@@ -2,9 +2,9 @@
  *
  * The operations follow the method as stated on "QLoRA, explained" (pofe.ai):
  *   nf4_quantize      sections "Blockwise absmax quantisation" and "NormalFloat 4 (NF4)": a weight is
- *                     flattened row-major and cut into blocks of 64; each block stores its absmax and
- *                     each value the index of the nearest of 16 NF4 codes; "Minimal implementation":
- *                     two indices per byte.
+ *                     flattened row-major and cut into blocks of 64; a block keeps its absmax, and
+ *                     every value becomes the position of its closest NF4 code (16 codes);
+ *                     "Minimal implementation": two indices per byte.
  *   nf4_double_quant  section "Double quantisation": the block scales are quantised to 8-bit floats
  *                     in groups of 256 with one fp32 constant per group.
  *   nf4_dequant       section "The forward pass and gradients": first the 8-bit scales are restored
@@ -32,8 +32,10 @@
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers to caller-owned memory (except nf4_codebook's output, a host
- *     array), each 16-byte aligned. The library never allocates or frees device memory, never
- *     synchronises and keeps no mutable global state; calls are thread-safe.
+ *     array), each 16-byte aligned. Apart from qlora_adamw_plan_create (which allocates the plan's
+ *     device memory and blocks until its table is uploaded) and qlora_adamw_plan_destroy (which
+ *     frees it), the library never allocates or frees device memory and never synchronises; it
+ *     keeps no mutable global state and its calls are thread-safe.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the default stream).
  *     The return value reports argument validation and launch status; faults inside kernels
  *     surface at the caller's next synchronisation.
@@ -98,7 +100,12 @@ int nf4_double_quant(const float *absmax, int64_t nblocks, uint8_t *scale_q, flo
  * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (N % 16, K % 64, N < 16, K < 64), NF4_ERR_ALIGN. */
 int nf4_dequant(const nf4_weight *W, uint16_t *out, hipStream_t stream);
 
-/* Forward of the adapted linear: y = x W~^T + s (x A^T) B^T, bf16 inputs, fp32 accumulation,
+/* Size limits of the three linear calls (their kernels address buffers with 32-bit offsets):
+ * N < 2^22, K < 2^22, N*K < 2^32 and 0 <= M < 2^31, with ceil(M/64) * ceil(max(N, K)/128) < 2^31.
+ * Larger sizes are refused with NF4_ERR_SHAPE (and qlora_workspace_bytes returns 0 for them);
+ * nf4_quantize, nf4_dequant and qlora_merge index in 64 bits and take the weight whole.
+ *
+ * Forward of the adapted linear: y = x W~^T + s (x A^T) B^T, bf16 inputs, fp32 accumulation,
  * W~ dequantised on the fly (never written to memory).
  *   x      [M x K] bf16;  A [r x K] bf16;  B [N x r] bf16;  scale = s.
  *   y      [M x N] bf16 output.
@@ -129,8 +136,7 @@ int qlora_linear_bwd(const nf4_weight *W, const uint16_t *x, const uint16_t *dy,
  * and ws holds qlora_workspace_bytes(M, N, K, r) bytes, the GEMM split over two contraction ranges
  * plus a launch that adds the two halves, exactly as qlora_linear_fwd does (so y equals its output
  * bit for bit). For M <= 16 it runs the skinny path (which forms u again from A) and needs ws,
- * unless the weight holds 2^31 blocks of 64 or more, or has fp32 scales and M > 4, where the fused
- * GEMM serves.
+ * unless the weight has fp32 scales and M > 4, where the fused GEMM serves.
  *   u   [M x r] float32 input.  y [M x N] bf16 output.  ws as qlora_linear_fwd (may be NULL if M > 16:
  *   then the GEMM is never split, same tolerance).
  * Errors as qlora_linear_fwd. */
@@ -141,9 +147,9 @@ int qlora_linear_fwd_recompute(const nf4_weight *W, const uint16_t *x, int64_t M
 /* Adapter merged into the dequantised base weight, in bf16:
  *   out = bf16_rne(fl32(W~ + fl32(s * (B A))))      [N x K] bf16 output (uint16 bit patterns),
  * W~ exactly as nf4_dequant produces it, B A accumulated in fp32 from the exact bf16 products.
- * "QLoRA, explained", section "Quality loss at merge time": the adapter was trained against W~,
- * so merging into W~ (not into the original weight) keeps the trained model; the result is served
- * in bf16 (re-quantising it, with nf4_quantize, adds a second rounding to the update).
+ * "QLoRA, explained", section "Quality loss at merge time": training saw W~, never the original
+ * weight, so adding the adapter to W~ preserves the trained model; the result is served in bf16
+ * (re-quantising it, with nf4_quantize, rounds the update a second time).
  *   A [r x K] bf16;  B [N x r] bf16;  scale = s.
  * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (also a weight with fp32 scales), NF4_ERR_ALIGN,
  * NF4_ERR_RANK, NF4_ERR_HIP. */
@@ -151,7 +157,7 @@ int qlora_merge(const nf4_weight *W, const uint16_t *A, const uint16_t *B, int32
                 uint16_t *out, hipStream_t stream);
 
 /* ---- Codebook and blocksize variants, and scales without double quantisation ("QLoRA, explained",
- * A toy run, which compares NF4 with a symmetric 15-level INT4 grid and E2M1 FP4 scaled to [-1, 1],
+ * A toy run, which sets NF4 beside an INT4 grid of 15 levels k/7 and E2M1 FP4 rescaled to [-1, 1],
  * and discusses blocksizes from 16 to 4096; Double quantisation, whose baseline keeps one fp32
  * absmax per block). The same storage layout as above with another codebook and blocksize:
  * packed[j] holds the indices of elements 2j (high nibble) and 2j+1 (low nibble); one fp32 absmax

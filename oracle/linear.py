@@ -17,8 +17,8 @@ def linear_fwd(x_bits, w_bits, a_bits, b_bits, scale: float):
     """Forward of an adapted linear: y = X W~^T + s (X A^T) B^T; also returns u = X A^T.
 
     "QLoRA, explained", The forward pass and gradients (its display equation was lost) and
-    The algorithm, step by step, whose forward line reads y = x W_tilde^T + gamma x A^T B^T, with
-    gamma = s = lora_alpha / r. No bias and no dropout.
+    The algorithm, step by step (the forward line of its pseudo-code): the frozen dequantised
+    weight's product plus the adapter product scaled by s = lora_alpha / r. No bias and no dropout.
 
     Shapes: X [M, K], W~ [N, K] (the dequantised bf16 weight), A [r, K], B [N, r].
     Returns (y [M, N], u [M, r]) in float64.

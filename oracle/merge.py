@@ -1,8 +1,8 @@
 """The adapter merged into the dequantised base weight, in bf16. TEST INFRASTRUCTURE ONLY.
 
-"QLoRA, explained", Quality loss at merge time: the adapter was trained against the dequantised
-weight W~, so a merge that keeps what was trained adds the adapter to W~ (not to the original
-weight) and serves the sum in bf16. The pages fix no arithmetic for the sum; the reading taken is
+"QLoRA, explained", Quality loss at merge time: training saw W~, the dequantised weight, never the
+original one, so the merge that preserves the trained model adds the adapter to W~ and serves the
+sum in bf16. The pages fix no arithmetic for the sum; the reading taken is
 the plainest one: the exact value W~ + s B A (s = lora_alpha / r, as in the forward), rounded once
 to bf16 (round to nearest, ties to even). Here the sum is formed in float64 from the exact bf16
 values of W~, A and B, whose error is far below half a bf16 unit.

@@ -21,8 +21,8 @@ def codebook() -> np.ndarray:
     """The 16 NF4 codes as float32, ascending (index 0 is -1, index 7 is 0, index 15 is +1).
 
     "QLoRA, explained", NormalFloat 4 (NF4): the codes sit at standard-normal quantiles (k = 4), the
-    negative and positive halves are built separately so that an exact zero exists (8 levels on one
-    side, 9 on the other, sharing zero), and the set is renormalised into [-1, 1]. The page's formula
+    negative and positive halves are built separately so that an exact zero exists (the halves hold 8
+    and 9 codes, zero being in both), and the set is renormalised into [-1, 1]. The page's formula
     and printed table did not survive; the reading taken here, which reproduces every code the
     worked example prints, is:
 
@@ -138,8 +138,9 @@ def double_quant(absmax, group: int = DQ_GROUP):
     """Double quantisation of the first-level scales.
 
     "QLoRA, explained", Double quantisation, and The algorithm, step by step: the fp32
-    block scales are themselves quantised to 8-bit floats in blocks of 256, keeping one fp32
-    second-level constant per 256 scales. Readings taken where the page is silent:
+    block scales go through a second quantisation, to an 8-bit float format, in groups of 256
+    scales, each group also storing a single fp32 constant. Readings taken where the page is
+    silent:
 
     * the second-level constant of a group is its largest scale, c2 = max c1 (all scales are >= 0),
       so every ratio c1 / c2 lies in [0, 1]; the last group may hold fewer than 256 scales;
@@ -175,8 +176,8 @@ def double_quant(absmax, group: int = DQ_GROUP):
 def dequant_scales(codes, c2, group: int = DQ_GROUP) -> np.ndarray:
     """First dequantisation level: c1' = fl32(e4m3(code) * c2), one float32 product per block.
 
-    "QLoRA, explained", The forward pass and gradients: dDQ first restores the 8-bit scales with the
-    fp32 second-level constants."""
+    "QLoRA, explained", The forward pass and gradients: dDQ's first level turns each 8-bit scale code
+    back into a float with its group's fp32 constant."""
     codes = np.asarray(codes, dtype=np.uint8).reshape(-1)
     vals = e4m3_unit_values().astype(np.float32)            # <= 4 significant bits: exact
     c2 = np.asarray(c2, dtype=np.float32).reshape(-1)
@@ -203,8 +204,8 @@ def f32_from_bf16_bits(b) -> np.ndarray:
 def dequant(packed, codes, c2, numel: int) -> np.ndarray:
     """Two-level dequantisation to bf16; returns uint16 bit patterns [numel].
 
-    "QLoRA, explained", The forward pass and gradients: first the 8-bit scales are restored with the
-    fp32 constants, then the NF4 indices with those scales, giving a bf16 weight. Rounding order (the
+    "QLoRA, explained", The forward pass and gradients: the block scales are recovered from their
+    8-bit codes and group constants first; those scales then turn the NF4 indices into a bf16 weight. Rounding order (the
     reading taken): c1' = fl32(e4m3 * c2), w32 = fl32(q[idx] * c1'), bf16 = RNE(w32).
     """
     idx = unpack_nibbles(packed, numel).reshape(-1, BLOCK)

@@ -17,7 +17,7 @@ def int4_codebook() -> np.ndarray:
 
 
 def fp4_codebook() -> np.ndarray:
-    """The toy's E2M1 FP4 format scaled to [-1, 1]: magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} / 6 with
+    """The toy's FP4 codebook, E2M1 rescaled into [-1, 1]: magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} / 6 with
     both signs (the two zeros coincide), 15 distinct values."""
     mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]) / 6.0
     vals = np.unique(np.concatenate([-mags, mags]))

@@ -194,6 +194,34 @@ def test_bwd_validation():
     assert call(M=0) == q.NF4_OK
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (64, 65536, 65536),      # N*K = 2^32: the backward's packed-weight record passes 2^31 bytes
+    (64, 1 << 21, 4096),     # N*K = 2^33
+    (64, 1 << 22, 64),       # N = 2^22: a 256-row activation tile of dY passes 2^31 bytes
+    (64, 16, 1 << 22),       # K = 2^22: the same for x
+    (1 << 31, 4096, 4096),   # M = 2^31
+    (1 << 30, 16, 1 << 21),  # 2^24 row tiles x 2^14 column tiles: 2^38 workgroups
+])
+def test_linear_sizes_past_32_bit_offsets_are_refused(M, N, K):
+    w = ctypes.byref(_w(N=N, K=K))
+    big = 1 << 50   # a workspace size that is never the reason for a refusal
+    assert q.qlora_workspace_bytes(M, N, K, 16) == 0
+    assert lib.qlora_linear_fwd(w, FAKE, M, FAKE, FAKE, 16, 2.0, FAKE, None, FAKE, big, None) == q.NF4_ERR_SHAPE
+    assert lib.qlora_linear_fwd_recompute(w, FAKE, M, FAKE, FAKE, 16, 2.0, FAKE, FAKE, FAKE, big, None) == \
+        q.NF4_ERR_SHAPE
+    assert lib.qlora_linear_bwd(w, FAKE, FAKE, M, FAKE, FAKE, 16, 2.0, FAKE, FAKE, FAKE, FAKE, 0, FAKE, big,
+                                None) == q.NF4_ERR_SHAPE
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 65536, 65472), (64, (1 << 22) - 16, 1024), (64, 1024, (1 << 22) - 64),
+                                   (1 << 20, 4096, 4096)])
+def test_linear_sizes_just_inside_the_limits_are_accepted(M, N, K):
+    assert q.qlora_workspace_bytes(M, N, K, 16) > 0
+    # every argument check passes: only the missing workspace is reported
+    w = ctypes.byref(_w(N=N, K=K))
+    assert lib.qlora_linear_fwd(w, FAKE, M, FAKE, FAKE, 16, 2.0, FAKE, None, None, 0, None) == q.NF4_ERR_WORKSPACE
+
+
 def _ptrs(*vals):
     return (ctypes.c_void_p * len(vals))(*vals)
 

@@ -71,6 +71,16 @@ def test_single_linear_workload():
     (4, 208, 16448, 16, 2.0),      #   257 blocks per row: groups of 256 blocks split steps
     (1800, 14336, 128, 16, 2.0),   # forward: 896 tiles of 256 rows, ragged last row block
     (1800, 128, 14336, 16, 2.0),   # the same for the dX GEMM (14336 output columns)
+    # ranks that are not a power of two: the adapter kernels, the fused GEMMs' partial adapter steps
+    # (r > 64: two steps, the second partial) and the few-token epilogue's u runs (256 / r rounds down)
+    (300, 400, 960, 48, 1.0),      #   GEMM with a split contraction
+    (300, 400, 960, 80, 0.5),
+    (300, 400, 960, 96, 0.5),
+    (300, 400, 960, 112, 0.25),
+    (3, 400, 960, 48, 1.0),        #   M <= 4 few-token kernel
+    (1, 1040, 1088, 112, 0.25),
+    (16, 416, 1024, 80, 0.5),      #   16-row few-token kernel
+    (16, 416, 1024, 112, 0.25),
 ])
 def test_ragged_shapes(M, N, K, r, s):
     check_full(*_inputs(M * 7 + r, M, N, K, r), s, "ragged")

@@ -48,7 +48,8 @@ def _inputs(seed, n, k, r):
 
 
 @pytest.mark.parametrize("n,k,r,s", [(400, 960, 16, 2.0), (256, 1024, 64, 0.25), (48, 64, 128, 0.5),
-                                     (4096, 4096, 16, 2.0)])
+                                     (4096, 4096, 16, 2.0), (400, 960, 48, 1.0), (256, 1024, 80, 0.5),
+                                     (208, 960, 96, 0.5), (400, 1088, 112, 0.25)])
 def test_merge_matches_oracle(n, k, r, s):
     log(f"[merge] N={n} K={k} r={r} s={s}")
     w, a, b = _inputs(n + k + r, n, k, r)

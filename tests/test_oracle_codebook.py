@@ -24,7 +24,7 @@ def test_invariants():
     assert np.all((q >= -1) & (q <= 1))
     zeros = np.flatnonzero(q == 0.0)
     assert list(zeros) == [oracle.NF4_ZERO_INDEX] == [7], "exactly one exact zero, at index 7"
-    # 8 levels on one side and 9 on the other, sharing zero
+    # 8 codes at or below zero and 9 at or above it: zero belongs to both halves
     assert (q <= 0).sum() == 8 and (q >= 0).sum() == 9
     # denser near zero: gaps grow outward on each side
     neg_gaps = np.diff(q[:8])[::-1]      # from zero outward

@@ -58,7 +58,7 @@ def test_worked_example():
     rec = q[idx[0]] * c64
     assert [round(v, 4) for v in rec] == ex["reconstructed"]
     assert [round(abs(a - b), 4) for a, b in zip(rec, w.astype(np.float64))] == ex["abs_error"]
-    # the largest value is reconstructed exactly (it defines the scale)
+    # the block's absmax element maps to code -1 or +1, so it comes back exactly
     assert rec[3] == float(w[3])
 
 
