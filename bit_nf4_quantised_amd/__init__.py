@@ -56,6 +56,7 @@ _SIGS = {
     "nf4_double_quant": (ctypes.c_int, [_p, _i64, _p, _p, _p]),
     "nf4_dequant": (ctypes.c_int, [_W, _p, _p]),
     "qlora_linear_fwd": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz, _p]),
+    "qlora_linear_fwd_noalloc": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p]),
     "qlora_linear_bwd": (ctypes.c_int, [_W, _p, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _p,
                                         ctypes.c_int, _p, _sz, _p]),
     "qlora_linear_fwd_recompute": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz,
@@ -176,6 +177,22 @@ def qlora_linear_fwd(weight: NF4Weight, x, A, B, scale: float, y, u_out=None, ws
     _check(lib.qlora_linear_fwd(ctypes.byref(cw), _ptr(x), M, _ptr(A), _ptr(B), r, scale, _ptr(y),
                                 _ptr(u_out), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "qlora_linear_fwd")
+
+
+def qlora_linear_fwd_noalloc(weight: NF4Weight, x, A, B, scale: float, y, u_out=None,
+                             stream=None) -> None:
+    """qlora_linear_fwd with the library's own per-GPU workspace (no allocation anywhere)."""
+    for t in (x, A, B, y):
+        _dtype(t, *_BF16)
+    _dtype(u_out, torch.float32)
+    M = x.shape[0]
+    r = A.shape[0]
+    if x.shape != (M, weight.K) or A.shape != (r, weight.K) or B.shape != (weight.N, r) \
+            or y.shape != (M, weight.N) or (u_out is not None and u_out.numel() != M * r):
+        raise ValueError("shape mismatch")
+    cw = weight.c_struct()
+    _check(lib.qlora_linear_fwd_noalloc(ctypes.byref(cw), _ptr(x), M, _ptr(A), _ptr(B), r, scale, _ptr(y),
+                                        _ptr(u_out), _stream(stream)), "qlora_linear_fwd_noalloc")
 
 
 def qlora_merge(weight: NF4Weight, A, B, scale: float, out, stream=None) -> None:
@@ -405,7 +422,8 @@ def quantize_weight(w: torch.Tensor, stream=None, absmax: torch.Tensor | None = 
 
 
 __all__ = ["lib", "LIB_PATH", "EXPORTED", "NF4Error", "NF4Weight", "CNF4Weight", "nf4_quantize",
-           "nf4_double_quant", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_fwd_recompute",
+           "nf4_double_quant", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_fwd_noalloc",
+           "qlora_linear_fwd_recompute",
            "qlora_linear_bwd", "qlora_merge", "AdamWConfig", "CAdamWConfig", "AdamWPlan",
            "Q4_CODEBOOKS", "q4_codebook_values", "q4_quantize", "q4_dequant",
            "qlora_workspace_bytes", "nf4_storage_bytes", "nf4_codebook", "workspace",

@@ -5,10 +5,18 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "common.h"
 #include "launch.h"
+
+// The forward's workspace for callers that cannot allocate: 32 MiB of device memory that each GPU
+// the library runs on holds until the process ends. Its name is only a host-side stand-in; host
+// code reaches it through the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -76,7 +84,61 @@ int check_ptr_list(int64_t count, T* const* ptrs, uintptr_t align_mask, bool ent
   return NF4_OK;
 }
 
+// ---- the forward's workspace for callers that cannot allocate (qlora_linear_fwd_noalloc): the
+// file-scope array `scratch` below. The device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and every use goes through it.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NF4_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NF4_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return NF4_OK;
+}
+
+// Argument checks of the forward, shared by qlora_linear_fwd and qlora_linear_fwd_noalloc.
+int check_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
+              int32_t r, const uint16_t* y, const float* u_out) {
+  int st = check_weight(W);
+  if (st) return st;
+  if (!linear_shape_ok(M, W->N, W->K)) return NF4_ERR_SHAPE;
+  if ((st = check_rank(r))) return st;
+  if (M == 0) return NF4_OK;
+  if (!x || !A || !B || !y) return NF4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) || (u_out && !aligned16(u_out)))
+    return NF4_ERR_ALIGN;
+  return NF4_OK;
+}
+
+// The forward's launches once the arguments are checked and ws holds fwd_ws(M, N, K, r) bytes.
+int run_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
+            int32_t r, float scale, uint16_t* y, float* u_out, void* ws, hipStream_t stream) {
+  const int64_t N = W->N, K = W->K;
+  float* u = u_out ? u_out : static_cast<float*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
+  if (nf4::skinny_eligible(M, N, K) && (!W->absmax || M <= 4)) {
+    return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, A, B, r,
+                                           scale, part, u, y, stream));
+  }
+  hipError_t e = nf4::launch_lora_u(x, M, K, A, r, part, u, stream);
+  if (e != hipSuccess) return NF4_ERR_HIP;
+  return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, u, B,
+                                       r, scale, y, part, stream));
+}
+
 }  // namespace
+
 
 // the opaque plan of the adapter update: device memory holding the chunk table and scratch
 struct qlora_adamw_plan {
@@ -159,28 +221,22 @@ size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
 int qlora_linear_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A,
                      const uint16_t* B, int32_t r, float scale, uint16_t* y, float* u_out, void* ws,
                      size_t ws_bytes, hipStream_t stream) {
-  int st = check_weight(W);
-  if (st) return st;
-  if (!linear_shape_ok(M, W->N, W->K)) return NF4_ERR_SHAPE;
-  if ((st = check_rank(r))) return st;
-  if (M == 0) return NF4_OK;
-  if (!x || !A || !B || !y) return NF4_ERR_NULL;
-  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) ||
-      (u_out && !aligned16(u_out)) || (ws && !aligned16(ws)))
-    return NF4_ERR_ALIGN;
-  const int64_t N = W->N, K = W->K;
-  const size_t need = fwd_ws(M, N, K, r);
-  if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;
-  float* u = u_out ? u_out : static_cast<float*>(ws);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
-  if (nf4::skinny_eligible(M, N, K) && (!W->absmax || M <= 4)) {
-    return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, A, B, r,
-                                           scale, part, u, y, stream));
-  }
-  hipError_t e = nf4::launch_lora_u(x, M, K, A, r, part, u, stream);
-  if (e != hipSuccess) return NF4_ERR_HIP;
-  return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, u, B,
-                                       r, scale, y, part, stream));
+  int st = check_fwd(W, x, M, A, B, r, y, u_out);
+  if (st || M == 0) return st;
+  if (ws && !aligned16(ws)) return NF4_ERR_ALIGN;
+  if (!ws || ws_bytes < fwd_ws(M, W->N, W->K, r)) return NF4_ERR_WORKSPACE;
+  return run_fwd(W, x, M, A, B, r, scale, y, u_out, ws, stream);
+}
+
+int qlora_linear_fwd_noalloc(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A,
+                             const uint16_t* B, int32_t r, float scale, uint16_t* y, float* u_out,
+                             hipStream_t stream) {
+  int st = check_fwd(W, x, M, A, B, r, y, u_out);
+  if (st || M == 0) return st;
+  if (fwd_ws(M, W->N, W->K, r) > kScratchBytes) return NF4_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws))) return st;
+  return run_fwd(W, x, M, A, B, r, scale, y, u_out, ws, stream);
 }
 
 int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A,
