@@ -13,7 +13,9 @@ The same run also measures, each in its own timed loop:
     drawn from a pool of 8 distinct matrices, the skinny forward of an 8192 x 28672 weight at
     1, 4 and 16 tokens with 4 rotating weight copies, and the adapter merge into that weight, in
     HBM GB/s against 8 TB/s;
-  * the CPU oracle on a bounded sample of the same workload (cpu_baseline).
+  * the CPU oracle on a bounded sample of the same workload (cpu_baseline);
+  * the other layer sets in `configs`: the single 4096x4096 linear at 16 tokens, and the 65B- and
+    70B-shaped sets at 4096 tokens, rank 64 (step and fused forward GEMM).
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -140,6 +142,100 @@ def library_dense_gemm(torch, dev, m, lins, iters):
     return sum(2 * m * l.n * l.k for l in lins) / (ms * 1e-3) / 1e12
 
 
+def prepare(wk, q, dev, torch):
+    """Every linear's inputs resident in HBM: the NF4 weight (quantised on the GPU), x, A, B, dY and
+    the outputs. The seeded host generators run in a thread pool (numpy fills arrays without the
+    interpreter lock), one linear per thread."""
+    from concurrent.futures import ThreadPoolExecutor
+    M, r = wk.m, wk.r
+    lin_state, ws_bytes, flops = [], 0, 0
+    t16 = lambda arr: torch.from_numpy(arr.view(np.int16)).to(dev)  # noqa: E731
+    with ThreadPoolExecutor(max_workers=min(8, len(wk.linears))) as ex:
+        futs = [ex.submit(wl.linear_inputs, wk, li, lin) for li, lin in enumerate(wk.linears)]
+        for lin, fut in zip(wk.linears, futs):
+            w, x, a, b, dy = fut.result()
+            wt = torch.from_numpy(w).to(dev)
+            del w
+            qw = q.quantize_weight(wt)
+            del wt
+            lin_state.append(dict(lin=lin, qw=qw, x=t16(x), a=t16(a), b=t16(b), dy=t16(dy),
+                                  y=torch.empty(M, lin.n, dtype=torch.int16, device=dev),
+                                  u=torch.empty(M, r, dtype=torch.float32, device=dev),
+                                  dx=torch.empty(M, lin.k, dtype=torch.int16, device=dev),
+                                  dA=torch.empty(r, lin.k, dtype=torch.float32, device=dev),
+                                  dB=torch.empty(lin.n, r, dtype=torch.float32, device=dev)))
+            ws_bytes = max(ws_bytes, q.qlora_workspace_bytes(M, lin.n, lin.k, r))
+            flops += flops_fwd_bwd(lin.n, lin.k, M, r)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    return lin_state, ws, flops
+
+
+def step_fn(q, lin_state, ws, s):
+    def step(_i=0):
+        for st in lin_state:
+            q.qlora_linear_fwd(st["qw"], st["x"], st["a"], st["b"], s, st["y"], st["u"], ws=ws)
+            q.qlora_linear_bwd(st["qw"], st["x"], st["dy"], st["a"], st["b"], s, st["u"], st["dx"],
+                               st["dA"], st["dB"], ws=ws)
+    return step
+
+
+def fwd_gemm_fn(q, lin_state, M, s):
+    """The forward GEMMs of the linears whose forward runs the 256-row tile instantiation, one
+    launch each through the forward-recompute entry; returns (fn, linears, flops per call)."""
+    r = lin_state[0]["a"].shape[0]
+    big = [st for st in lin_state if fwd_tile_rows(M, st["lin"].n) == 256]
+
+    def recompute(_i=0):
+        for st in big:
+            q.qlora_linear_fwd_recompute(st["qw"], st["x"], st["a"], st["b"], s, st["u"], st["y"])
+    return recompute, big, sum(2 * M * st["lin"].n * (st["lin"].k + r) for st in big)
+
+
+def other_configs(torch, q, dev, skip):
+    """The other layer sets at their own shapes, each timed in a short loop after one untimed step:
+    the 16-token single linear (latency-bound: microseconds per step), and the 65B- and 70B-shaped
+    sets at 4096 tokens and rank 64 (step TFLOP/s and the fused forward GEMM alone)."""
+    out = {}
+    for name in ("single", "llama65b", "llama70b"):
+        if name == skip:
+            continue
+        wk = wl.WORKLOADS[name]
+        log(f"[bench] config {name}: preparing {len(wk.linears)} linears, M={wk.m}, r={wk.r}")
+        lin_state, ws, flops = prepare(wk, q, dev, torch)
+        step = step_fn(q, lin_state, ws, wk.scale)
+        step()
+        iters = 50 if name == "single" else 3
+        ms = timed(step, iters, torch)
+        tf = flops / (ms * 1e-3) / 1e12
+        ent = {"linears": {l.name: [l.n, l.k] for l in wk.linears}, "tokens": wk.m, "rank": wk.r,
+               "alpha": wk.alpha, "weights": wk.weight_kind, "flops_per_step": flops,
+               "ms_per_step": round(ms, 4), "TFLOPs": round(tf, 2),
+               "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "steps": iters}
+        if name == "single":
+            nf4 = sum(nf4_bytes(l.n * l.k) for l in wk.linears)
+            ent.update({"us_per_step": round(ms * 1e3, 2),
+                        "nf4_GBps": round(2 * nf4 / (ms * 1e-3) / 1e9, 1),
+                        "nf4_bytes_per_step": 2 * nf4,
+                        "what": "forward (few-token kernel) + backward (dX GEMM, dA, dB) of one "
+                                "4096x4096 linear at 16 tokens; the weight is read twice per step"})
+            log(f"[bench] config single: {ms*1e3:.1f} us per fwd+bwd")
+        else:
+            fwd, big, gflops = fwd_gemm_fn(q, lin_state, wk.m, wk.scale)
+            fwd()
+            ms_f = timed(fwd, iters, torch)
+            ach = gflops / (ms_f * 1e-3) / 1e12
+            ent["fused_fwd_gemm"] = {"kernel": ROOFLINE_KERNEL, "achieved_TFLOPs": round(ach, 2),
+                                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                                     "avg_launch_us": round(ms_f * 1e3 / len(big), 2),
+                                     "linears": [st["lin"].name for st in big]}
+            log(f"[bench] config {name}: step {ms:.2f} ms, {tf:.1f} TFLOP/s; fused fwd GEMM {ach:.1f} TFLOP/s")
+        out[name] = ent
+        del lin_state, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +244,8 @@ def main():
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "llama65b", "llama70b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paths", action="store_true", help="skip the bandwidth-path loops")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other layer sets (single linear, 65B- and 70B-shaped)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the known-size copy kernel used to scale HBM counters")
     args = ap.parse_args()
@@ -170,32 +268,8 @@ def main():
 
     # ---------------------------------------------------------------- step inputs, resident in HBM
     log(f"[bench] preparing {args.workload}: {len(wk.linears)} linears, M={M}, r={r}")
-    lin_state = []
-    ws_bytes = 0
-    flops = 0
-    for li, lin in enumerate(wk.linears):
-        w, x, a, b, dy = wl.linear_inputs(wk, li, lin)
-        wt = torch.from_numpy(w).to(dev)
-        qw = q.quantize_weight(wt)
-        del wt
-        t16 = lambda arr: torch.from_numpy(arr.view(np.int16)).to(dev)
-        st = dict(lin=lin, qw=qw, x=t16(x), a=t16(a), b=t16(b), dy=t16(dy),
-                  y=torch.empty(M, lin.n, dtype=torch.int16, device=dev),
-                  u=torch.empty(M, r, dtype=torch.float32, device=dev),
-                  dx=torch.empty(M, lin.k, dtype=torch.int16, device=dev),
-                  dA=torch.empty(r, lin.k, dtype=torch.float32, device=dev),
-                  dB=torch.empty(lin.n, r, dtype=torch.float32, device=dev))
-        lin_state.append(st)
-        ws_bytes = max(ws_bytes, q.qlora_workspace_bytes(M, lin.n, lin.k, r))
-        flops += flops_fwd_bwd(lin.n, lin.k, M, r)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-
-    def step(_i=0):
-        for st in lin_state:
-            q.qlora_linear_fwd(st["qw"], st["x"], st["a"], st["b"], s, st["y"], st["u"], ws=ws)
-            q.qlora_linear_bwd(st["qw"], st["x"], st["dy"], st["a"], st["b"], s, st["u"], st["dx"],
-                               st["dA"], st["dB"], ws=ws)
+    lin_state, ws, flops = prepare(wk, q, dev, torch)
+    step = step_fn(q, lin_state, ws, s)
 
     for _ in range(args.warmup):
         step()
@@ -208,13 +282,7 @@ def main():
     # Timed over the linears whose forward runs the 256-row tile instantiation
     # qlora_gemm_kernel<false, 256, false>, so that the average launch matches that kernel's entry in a
     # rocprofv3 kernel-trace summary of this same command.
-    big = [st for st in lin_state if fwd_tile_rows(M, st["lin"].n) == 256]
-    gemm_flops = sum(2 * M * st["lin"].n * (st["lin"].k + r) for st in big)
-
-    def recompute(_i=0):
-        for st in big:
-            q.qlora_linear_fwd_recompute(st["qw"], st["x"], st["a"], st["b"], s, st["u"], st["y"])
-
+    recompute, big, gemm_flops = fwd_gemm_fn(q, lin_state, M, s)
     recompute()
     ms_recompute = timed(recompute, args.steps, torch)
     launches = len(big)
@@ -260,6 +328,9 @@ def main():
     dequant_gbps = None
     if not args.no_paths:
         paths, dequant_gbps = bandwidth_paths(torch, q, dev, args)
+    del lin_state, ws
+    torch.cuda.empty_cache()
+    configs = {} if args.no_configs else other_configs(torch, q, dev, args.workload)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wk)
 
@@ -280,6 +351,7 @@ def main():
         "cpu_baseline": cpu,
         "paths": paths,
         "fwd_gemm_fp32_scales": fwd_f32s,
+        "configs": configs,
     }
     print(json.dumps(out), flush=True)
 
@@ -313,16 +385,30 @@ def bandwidth_paths(torch, q, dev, args):
     torch.cuda.synchronize()
     total = count * numel
     ng = (nb + 255) // 256
-    for name, fn, per_weight_bytes in (
-            ("quantize", quant, 4 + 0.5 + 4 / 64),
-            ("double_quant", dq, (4 * nb + nb + 4 * ng) / numel),
-            ("dequant", deq, nf4_bytes(numel) / numel + 2)):
-        ms = timed(fn, count, torch)
-        gbps = total * per_weight_bytes / (ms * count * 1e-3) / 1e9
-        res[name] = {"weights": total, "ms_total": round(ms * count, 3),
+    # double quantisation of all 136 matrices' scales through one nf4_double_quant_many call
+    # (64 matrices per launch), as a model's weights are processed at load time
+    # every matrix with its own scales and outputs (copies of its pool matrix's scales), as a
+    # model's weights have: 0.5 GB of scales in, 0.13 GB of codes and constants out
+    dq_in = [absmax[i % wl.STREAM_POOL].clone() for i in range(count)]
+    dq_q = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(count)]
+    dq_c2 = [torch.empty(ng, dtype=torch.float32, device=dev) for _ in range(count)]
+    dq_many = q.DoubleQuantMany(dq_in, dq_q, dq_c2)
+    dq_many()
+    for name, fn, calls, reps, per_weight_bytes in (
+            ("quantize", quant, count, 1, 4 + 0.5 + 4 / 64),
+            ("double_quant", lambda _i: dq_many(), 1, 10, (4 * nb + nb + 4 * ng) / numel),
+            ("dequant", deq, count, 1, nf4_bytes(numel) / numel + 2)):
+        ms = timed(fn, calls * reps, torch) * calls   # ms for the whole stream
+        gbps = total * per_weight_bytes / (ms * 1e-3) / 1e9
+        res[name] = {"weights": total, "ms_total": round(ms, 3),
                      "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
                      "bytes_per_weight": round(per_weight_bytes, 4)}
         log(f"[bench] {name}: {gbps:.0f} GB/s")
+    # one nf4_double_quant call per matrix, for comparison (launch-bound)
+    ms = timed(dq, count, torch)
+    res["double_quant"]["one_call_per_matrix_GBps"] = round(
+        total * (4 * nb + nb + 4 * ng) / numel / (ms * count * 1e-3) / 1e9, 1)
+    del dq_many, dq_in, dq_q, dq_c2
     dequant_gbps = res["dequant"]["GBps"]
 
     # codebook and blocksize variants over the same pool: quantise, and dequantise with fp32 scales

@@ -54,6 +54,7 @@ _W = ctypes.POINTER(CNF4Weight)
 _SIGS = {
     "nf4_quantize": (ctypes.c_int, [_p, _i64, _p, _p, _p]),
     "nf4_double_quant": (ctypes.c_int, [_p, _i64, _p, _p, _p]),
+    "nf4_double_quant_many": (ctypes.c_int, [_i64, _p, _p, _p, _p, _p]),
     "nf4_dequant": (ctypes.c_int, [_W, _p, _p]),
     "qlora_linear_fwd": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz, _p]),
     "qlora_linear_fwd_noalloc": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p]),
@@ -151,6 +152,32 @@ def nf4_double_quant(absmax, scale_q, scale_c2, stream=None) -> None:
         raise ValueError("output sizes must be nblocks and ceil(nblocks/256)")
     _check(lib.nf4_double_quant(_ptr(absmax), nb, _ptr(scale_q), _ptr(scale_c2), _stream(stream)),
            "nf4_double_quant")
+
+
+class DoubleQuantMany:
+    """nf4_double_quant_many over fixed lists of tensors, with the argument arrays marshalled once
+    (a model's weights at load time); calling it enqueues the launches on the stream."""
+
+    def __init__(self, absmax: list, scale_q: list, scale_c2: list):
+        n = len(absmax)
+        if len(scale_q) != n or len(scale_c2) != n:
+            raise ValueError("one scale_q and scale_c2 per absmax")
+        for a, c, g in zip(absmax, scale_q, scale_c2):
+            _dtype(a, torch.float32); _dtype(c, torch.uint8); _dtype(g, torch.float32)
+            if c.numel() != a.numel() or g.numel() != (a.numel() + 255) // 256:
+                raise ValueError("output sizes must be nblocks and ceil(nblocks/256)")
+        P = ctypes.c_void_p * max(n, 1)
+        self._keep = (list(absmax), list(scale_q), list(scale_c2))   # the tensors stay alive
+        self._args = (n, P(*[_ptr(a) for a in absmax]), (ctypes.c_int64 * max(n, 1))(*[a.numel() for a in absmax]),
+                      P(*[_ptr(c) for c in scale_q]), P(*[_ptr(g) for g in scale_c2]))
+
+    def __call__(self, stream=None) -> None:
+        _check(lib.nf4_double_quant_many(*self._args, _stream(stream)), "nf4_double_quant_many")
+
+
+def nf4_double_quant_many(absmax: list, scale_q: list, scale_c2: list, stream=None) -> None:
+    """nf4_double_quant over several weights' scales (up to 64 per kernel launch)."""
+    DoubleQuantMany(absmax, scale_q, scale_c2)(stream)
 
 
 def nf4_dequant(weight: NF4Weight, out, stream=None) -> None:
@@ -422,7 +449,7 @@ def quantize_weight(w: torch.Tensor, stream=None, absmax: torch.Tensor | None = 
 
 
 __all__ = ["lib", "LIB_PATH", "EXPORTED", "NF4Error", "NF4Weight", "CNF4Weight", "nf4_quantize",
-           "nf4_double_quant", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_fwd_noalloc",
+           "nf4_double_quant", "nf4_double_quant_many", "DoubleQuantMany", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_fwd_noalloc",
            "qlora_linear_fwd_recompute",
            "qlora_linear_bwd", "qlora_merge", "AdamWConfig", "CAdamWConfig", "AdamWPlan",
            "Q4_CODEBOOKS", "q4_codebook_values", "q4_quantize", "q4_dequant",

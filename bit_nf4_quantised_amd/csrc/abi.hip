@@ -187,6 +187,39 @@ int nf4_double_quant(const float* absmax, int64_t nblocks, uint8_t* scale_q, flo
   return from_hip(nf4::launch_double_quant(absmax, nblocks, scale_q, scale_c2, stream));
 }
 
+int nf4_double_quant_many(int64_t count, const float* const* absmax, const int64_t* nblocks,
+                          uint8_t* const* scale_q, float* const* scale_c2, hipStream_t stream) {
+  if (count < 0 || count > (int64_t(1) << 31)) return NF4_ERR_SHAPE;
+  if (count == 0) return NF4_OK;
+  if (!absmax || !nblocks || !scale_q || !scale_c2) return NF4_ERR_NULL;
+  for (int64_t i = 0; i < count; ++i) {
+    if (nblocks[i] < 0 || nblocks[i] > (int64_t(1) << 40)) return NF4_ERR_SHAPE;
+    if (nblocks[i] == 0) continue;
+    if (!absmax[i] || !scale_q[i] || !scale_c2[i]) return NF4_ERR_NULL;
+    if (!aligned16(absmax[i]) || !aligned16(scale_q[i]) || !aligned16(scale_c2[i])) return NF4_ERR_ALIGN;
+  }
+  for (int64_t i0 = 0; i0 < count; i0 += nf4::kDqBatch) {
+    nf4::DqBatch b{};
+    int n = 0;
+    b.group_begin[0] = 0;
+    for (int64_t i = i0; i < count && i < i0 + nf4::kDqBatch; ++i) {
+      if (nblocks[i] == 0) continue;
+      b.absmax[n] = absmax[i];
+      b.scale_q[n] = scale_q[i];
+      b.scale_c2[n] = scale_c2[i];
+      b.nblocks[n] = nblocks[i];
+      b.group_begin[n + 1] = b.group_begin[n] + (nblocks[i] + nf4::kGroup - 1) / nf4::kGroup;
+      ++n;
+    }
+    b.count = n;
+    if (n == 0) continue;
+    if (b.group_begin[n] * 64 >= (int64_t(1) << 32)) return NF4_ERR_SHAPE;   // threads of one launch
+    const int st = from_hip(nf4::launch_double_quant_many(b, stream));
+    if (st) return st;
+  }
+  return NF4_OK;
+}
+
 int nf4_dequant(const nf4_weight* W, uint16_t* out, hipStream_t stream) {
   int st = check_weight(W);
   if (st) return st;

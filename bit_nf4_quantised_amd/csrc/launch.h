@@ -10,6 +10,17 @@ hipError_t launch_quantize(const float* w, int64_t numel, uint8_t* packed, float
                            hipStream_t stream);
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, uint8_t* scale_q,
                                float* scale_c2, hipStream_t stream);
+// up to kDqBatch weights' scales per launch, passed by value in the kernel arguments
+constexpr int kDqBatch = 64;
+struct DqBatch {
+  const float* absmax[kDqBatch];
+  uint8_t* scale_q[kDqBatch];
+  float* scale_c2[kDqBatch];
+  int64_t nblocks[kDqBatch];
+  int64_t group_begin[kDqBatch + 1];   // prefix sums of ceil(nblocks / 256)
+  int count;
+};
+hipError_t launch_double_quant_many(const DqBatch& b, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                           int64_t numel, uint16_t* out, hipStream_t stream);
 

@@ -110,14 +110,15 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restri
 // stride of the grid and has the next group's scales in flight while it encodes the current one.
 // c2 is the exact group maximum; the code is the E4M3 value in [0, 1] nearest to the exact ratio
 // c1 / c2, ties to the even code:
-//   x = fl32(c1 / c2) (correctly rounded) is within 2^-24 x of the ratio, far less than the gap
-//   between neighbouring E4M3 values, so truncating x to E4M3 gives the code just below the ratio
-//   or, when the ratio sits within that distance of an E4M3 value, that value's neighbour. Either
-//   way the nearest code is one of the truncation c and c + 1, and the exact test c1 > c2 * m
-//   against their midpoint m decides (exact in fp64: a 24-bit scale times a midpoint of at most 5
-//   significant bits), with equality going to the even code.
-__device__ __forceinline__ uint32_t e4m3_code_of_ratio(float c1, float c2) {
-  if (c2 == 0.f) return 0;
+//   x = c1 * rcp(c2) is within a few 2^-24 of the ratio (relative), far less than half the gap
+//   between neighbouring E4M3 values (at least 2^-5 relative), so truncating x to E4M3 gives the
+//   code just below the ratio or, when the ratio sits within that distance of an E4M3 value, that
+//   value's neighbour. Either way the nearest code is the truncation c or c + 1, and the sign of
+//   c1 - c2 * m, m their midpoint, decides: one fused multiply-add forms the exact difference and
+//   rounds it once, which keeps its sign and whether it is zero (a tie, to the even code) as long
+//   as nothing underflows. A group maximum below 2^-60 takes the correctly rounded quotient and an
+//   fp64 test instead (c2 * m is exact in fp64: 24 times at most 5 significant bits).
+__device__ __forceinline__ uint32_t e4m3_code_of_ratio_exact(float c1, float c2) {
   const float x = __fdiv_rn(c1, c2);   // in [0, 1]
   uint32_t c;
   if (x < 0x1p-6f) {
@@ -132,6 +133,44 @@ __device__ __forceinline__ uint32_t e4m3_code_of_ratio(float c1, float c2) {
   if (a > b) return c + 1;
   if (a == b) return (c & 1u) ? c + 1 : c;
   return c;
+}
+
+// The common case (group maximum c2 >= 2^-60), without branches. rc = rcp(c2), shared by the
+// group. Midpoint of codes c and c + 1: for c >= 8 the value of c with one more mantissa bit set
+// (bit 19), for c < 8 (subnormal codes) (2c + 1) * 2^-10; for c = 0x38 (1.0) the midpoint to
+// 0x39 is 1.0625, above every ratio, so the clamp to 0x38 needs no special case.
+__device__ __forceinline__ uint32_t e4m3_code_of_ratio_fast(float c1, float c2, float rc) {
+  const float x = __fmul_rn(c1, rc);
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t c_norm = ((((bits >> 23) & 0xFFu) - 120u) << 3) | ((bits >> 20) & 7u);
+  const uint32_t c_sub = (uint32_t)(x * 0x1p9f);
+  const uint32_t c = min(x < 0x1p-6f ? c_sub : c_norm, 0x38u);
+  const float m_norm = __uint_as_float(((((c >> 3) & 15u) + 120u) << 23) | ((c & 7u) << 20) | (1u << 19));
+  const float m_sub = (float)(2u * c + 1u) * 0x1p-10f;
+  const float m = c < 8u ? m_sub : m_norm;
+  const float d = __builtin_fmaf(-c2, m, c1);
+  return c + ((d > 0.f) | ((d == 0.f) & (c & 1u)));
+}
+
+__device__ __forceinline__ uint32_t e4m3_code_of_ratio(float c1, float c2) {
+  if (c2 == 0.f) return 0;
+  if (c2 < 0x1p-60f) return e4m3_code_of_ratio_exact(c1, c2);
+  return e4m3_code_of_ratio_fast(c1, c2, __builtin_amdgcn_rcpf(c2));
+}
+
+// the four codes of a lane's scales against its group's c2 (wave-uniform), one byte each
+__device__ __forceinline__ uint32_t e4m3_codes4(const float c[4], float c2) {
+  uint32_t word = 0;
+  if (c2 == 0.f) return 0;
+  if (c2 < 0x1p-60f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) word |= e4m3_code_of_ratio_exact(c[i], c2) << (8 * i);
+  } else {
+    const float rc = __builtin_amdgcn_rcpf(c2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) word |= e4m3_code_of_ratio_fast(c[i], c2, rc) << (8 * i);
+  }
+  return word;
 }
 
 __global__ __launch_bounds__(256) void nf4_double_quant_kernel(const float* __restrict__ absmax,
@@ -153,10 +192,8 @@ __global__ __launch_bounds__(256) void nf4_double_quant_kernel(const float* __re
     for (; g < full; g += nw) {
       const f32x4 nxt = load(min(g + nw, full - 1));
       const float c2 = wave_max(fmaxf(fmaxf(cur[0], cur[1]), fmaxf(cur[2], cur[3])));
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) word |= e4m3_code_of_ratio(cur[i], c2) << (8 * i);
-      *reinterpret_cast<uint32_t*>(scale_q + g * kGroup + lane * 4) = word;
+      const float cc[4] = {cur[0], cur[1], cur[2], cur[3]};
+      *reinterpret_cast<uint32_t*>(scale_q + g * kGroup + lane * 4) = e4m3_codes4(cc, c2);
       if (lane == 0) scale_c2[g] = c2;
       cur = nxt;
     }
@@ -171,6 +208,83 @@ __global__ __launch_bounds__(256) void nf4_double_quant_kernel(const float* __re
     for (int i = 0; i < 4; ++i)
       if (first + i < nblocks) scale_q[first + i] = (uint8_t)e4m3_code_of_ratio(c[i], c2);
     if (lane == 0) scale_c2[full] = c2;
+  }
+}
+
+// Double quantisation of several weights' scales in one launch. The tensors' groups are numbered
+// one after the other (group_begin[t] is tensor t's first); each wave encodes a contiguous run of
+// per_wave groups, exactly as nf4_double_quant_kernel encodes a group, with the scales of the
+// next two groups in flight. The wave finds its first group's tensor by bisection once and steps to the
+// next tensor when its run crosses into it (empty tensors are not in the batch).
+__global__ __launch_bounds__(256) void nf4_double_quant_many_kernel(const DqBatch b, int64_t per_wave) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wv = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t total = b.group_begin[b.count];
+  int64_t g = wv * per_wave;
+  const int64_t g_end = min(total, g + per_wave);
+  if (g >= g_end) return;
+  int t = 0, hi = b.count;   // group_begin[t] <= g < group_begin[t + 1]
+  while (hi - t > 1) {
+    const int mid = (t + hi) >> 1;
+    if (g >= b.group_begin[mid]) t = mid;
+    else hi = mid;
+  }
+  // A tensor's fields, read from the kernel arguments once per tensor the run touches.
+  struct Tensor {
+    const float* absmax;
+    uint8_t* scale_q;
+    float* scale_c2;
+    int64_t nblocks, gbegin, gend;
+  };
+  auto tensor = [&](int tt) {
+    return Tensor{b.absmax[tt], b.scale_q[tt], b.scale_c2[tt], b.nblocks[tt], b.group_begin[tt],
+                  b.group_begin[tt + 1]};
+  };
+  // scales of group gg of tensor T (zeros past the tensor's end)
+  auto load = [&](const Tensor& T, int64_t gg) {
+    const int64_t lg = gg - T.gbegin, first = lg * kGroup + lane * 4;
+    if ((lg + 1) * kGroup <= T.nblocks) return *reinterpret_cast<const f32x4*>(T.absmax + first);
+    f32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (first + i < T.nblocks) ? T.absmax[first + i] : 0.f;
+    return v;
+  };
+  // two groups ahead in flight: the group after next is loaded while the current one is encoded
+  Tensor cur_t = tensor(t);
+  Tensor t1 = cur_t;
+  f32x4 cur = load(cur_t, g), nx1 = cur;
+  int i1 = t;
+  if (g + 1 < g_end) {
+    if (g + 1 >= t1.gend) t1 = tensor(++i1);
+    nx1 = load(t1, g + 1);
+  }
+  for (;;) {
+    const int64_t g2 = g + 2;
+    Tensor t2 = t1;
+    int i2 = i1;
+    f32x4 nx2 = nx1;
+    if (g2 < g_end) {
+      if (g2 >= t2.gend) t2 = tensor(++i2);
+      nx2 = load(t2, g2);
+    }
+    const int64_t lg = g - cur_t.gbegin;
+    const int64_t first = lg * kGroup + lane * 4;
+    const float c2 = wave_max(fmaxf(fmaxf(cur[0], cur[1]), fmaxf(cur[2], cur[3])));
+    if ((lg + 1) * kGroup <= cur_t.nblocks) {
+      const float cc[4] = {cur[0], cur[1], cur[2], cur[3]};
+      *reinterpret_cast<uint32_t*>(cur_t.scale_q + first) = e4m3_codes4(cc, c2);
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (first + i < cur_t.nblocks) cur_t.scale_q[first + i] = (uint8_t)e4m3_code_of_ratio(cur[i], c2);
+    }
+    if (lane == 0) cur_t.scale_c2[lg] = c2;
+    if (g + 1 >= g_end) break;
+    cur = nx1;
+    nx1 = nx2;
+    cur_t = t1;
+    t1 = t2;
+    i1 = i2;
+    ++g;
   }
 }
 
@@ -254,6 +368,17 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, uint8_t* sc
   const int grid = grid_for(ngroups, 4, 256 * 8);   // 4 waves per workgroup, one group each
   hipLaunchKernelGGL(nf4_double_quant_kernel, dim3(grid), dim3(256), 0, stream, absmax, nblocks,
                      scale_q, scale_c2);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_quant_many(const DqBatch& b, hipStream_t stream) {
+  const int64_t groups = b.group_begin[b.count];
+  if (groups == 0) return hipSuccess;
+  // runs of groups for at most 32 waves per CU over 256 CUs
+  const int64_t per_wave = (groups + 8191) / 8192;
+  const int64_t waves = (groups + per_wave - 1) / per_wave;
+  hipLaunchKernelGGL(nf4_double_quant_many_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, b,
+                     per_wave);
   return hipGetLastError();
 }
 

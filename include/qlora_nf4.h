@@ -95,6 +95,18 @@ int nf4_quantize(const float *w, int64_t numel, uint8_t *packed, float *absmax, 
 int nf4_double_quant(const float *absmax, int64_t nblocks, uint8_t *scale_q, float *scale_c2,
                      hipStream_t stream);
 
+/* nf4_double_quant over several weights: tensor i's absmax[i] (nblocks[i] scales) is encoded into
+ * scale_q[i] and scale_c2[i] exactly as nf4_double_quant would, with up to 64 tensors per kernel
+ * launch (their pointers travel in the kernel arguments; nothing is allocated). For a model's many
+ * weights at load time, where a launch per weight would be bound by launch overhead.
+ *   count      number of tensors (>= 0); absmax, nblocks, scale_q, scale_c2 are HOST arrays of
+ *              `count` entries (device pointers and sizes); entries with nblocks[i] == 0 are skipped
+ *              and may hold NULL pointers. Outputs must not overlap another tensor's inputs.
+ * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (count or a size < 0), NF4_ERR_ALIGN, NF4_ERR_HIP; on an
+ * argument error nothing is enqueued. */
+int nf4_double_quant_many(int64_t count, const float *const *absmax, const int64_t *nblocks,
+                          uint8_t *const *scale_q, float *const *scale_c2, hipStream_t stream);
+
 /* Two-level dequantisation of W to bf16.
  *   out  [N*K] uint16 (bf16) output, row-major N x K; bit-exact with the formula in Data formats.
  * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (N % 16, K % 64, N < 16, K < 64), NF4_ERR_ALIGN. */

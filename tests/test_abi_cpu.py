@@ -295,3 +295,18 @@ def test_q4_validation():
     assert g(FAKE, 4096, 2, 16, MISALIGNED, None, None, FAKE, None) == q.NF4_ERR_ALIGN
     assert g(FAKE, 4096, 2, 24, FAKE, None, None, FAKE, None) == q.NF4_ERR_SHAPE
     assert g(None, 0, 1, 4096, None, None, None, None, None) == q.NF4_OK
+
+
+def test_double_quant_many_validation():
+    f = lib.nf4_double_quant_many
+    nb = (ctypes.c_int64 * 2)(256, 300)
+    ok = _ptrs(FAKE, FAKE)
+    assert f(-1, ok, nb, ok, ok, None) == q.NF4_ERR_SHAPE
+    assert f(0, None, None, None, None, None) == q.NF4_OK
+    assert f(2, None, nb, ok, ok, None) == q.NF4_ERR_NULL
+    assert f(2, ok, None, ok, ok, None) == q.NF4_ERR_NULL
+    assert f(2, ok, nb, _ptrs(FAKE, None), ok, None) == q.NF4_ERR_NULL
+    assert f(2, ok, nb, ok, _ptrs(MISALIGNED, FAKE), None) == q.NF4_ERR_ALIGN
+    assert f(2, ok, (ctypes.c_int64 * 2)(256, -64), ok, ok, None) == q.NF4_ERR_SHAPE
+    # empty tensors are skipped, whatever their pointers
+    assert f(2, _ptrs(None, None), (ctypes.c_int64 * 2)(0, 0), _ptrs(None, None), _ptrs(None, None), None) == q.NF4_OK
