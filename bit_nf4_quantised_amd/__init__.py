@@ -53,6 +53,7 @@ _p, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, cty
 _W = ctypes.POINTER(CNF4Weight)
 _SIGS = {
     "nf4_quantize": (ctypes.c_int, [_p, _i64, _p, _p, _p]),
+    "nf4_quantize_bf16": (ctypes.c_int, [_p, _i64, _p, _p, _p]),
     "nf4_double_quant": (ctypes.c_int, [_p, _i64, _p, _p, _p]),
     "nf4_double_quant_many": (ctypes.c_int, [_i64, _p, _p, _p, _p, _p]),
     "nf4_dequant": (ctypes.c_int, [_W, _p, _p]),
@@ -143,6 +144,16 @@ def nf4_quantize(w, packed, absmax, stream=None) -> None:
     if packed.numel() * 2 != n or absmax.numel() * 64 != n:
         raise ValueError("output sizes must be numel/2 and numel/64")
     _check(lib.nf4_quantize(_ptr(w), n, _ptr(packed), _ptr(absmax), _stream(stream)), "nf4_quantize")
+
+
+def nf4_quantize_bf16(w, packed, absmax, stream=None) -> None:
+    """nf4_quantize of a bf16 array (a merged weight quantised again)."""
+    _dtype(w, *_BF16); _dtype(packed, torch.uint8); _dtype(absmax, torch.float32)
+    n = w.numel()
+    if packed.numel() * 2 != n or absmax.numel() * 64 != n:
+        raise ValueError("output sizes must be numel/2 and numel/64")
+    _check(lib.nf4_quantize_bf16(_ptr(w), n, _ptr(packed), _ptr(absmax), _stream(stream)),
+           "nf4_quantize_bf16")
 
 
 def nf4_double_quant(absmax, scale_q, scale_c2, stream=None) -> None:
@@ -449,6 +460,7 @@ def quantize_weight(w: torch.Tensor, stream=None, absmax: torch.Tensor | None = 
 
 
 __all__ = ["lib", "LIB_PATH", "EXPORTED", "NF4Error", "NF4Weight", "CNF4Weight", "nf4_quantize",
+           "nf4_quantize_bf16",
            "nf4_double_quant", "nf4_double_quant_many", "DoubleQuantMany", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_fwd_noalloc",
            "qlora_linear_fwd_recompute",
            "qlora_linear_bwd", "qlora_merge", "AdamWConfig", "CAdamWConfig", "AdamWPlan",

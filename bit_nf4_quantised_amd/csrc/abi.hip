@@ -178,6 +178,14 @@ int nf4_quantize(const float* w, int64_t numel, uint8_t* packed, float* absmax, 
   return from_hip(nf4::launch_quantize(w, numel, packed, absmax, stream));
 }
 
+int nf4_quantize_bf16(const uint16_t* w, int64_t numel, uint8_t* packed, float* absmax, hipStream_t stream) {
+  if (numel < 0 || numel % 64) return NF4_ERR_SHAPE;
+  if (numel == 0) return NF4_OK;
+  if (!w || !packed || !absmax) return NF4_ERR_NULL;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(absmax)) return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_quantize_bf16(w, numel, packed, absmax, stream));
+}
+
 int nf4_double_quant(const float* absmax, int64_t nblocks, uint8_t* scale_q, float* scale_c2,
                      hipStream_t stream) {
   if (nblocks < 0) return NF4_ERR_SHAPE;

@@ -8,6 +8,8 @@ namespace nf4 {
 
 hipError_t launch_quantize(const float* w, int64_t numel, uint8_t* packed, float* absmax,
                            hipStream_t stream);
+hipError_t launch_quantize_bf16(const uint16_t* w, int64_t numel, uint8_t* packed, float* absmax,
+                                hipStream_t stream);
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, uint8_t* scale_q,
                                float* scale_c2, hipStream_t stream);
 // up to kDqBatch weights' scales per launch, passed by value in the kernel arguments

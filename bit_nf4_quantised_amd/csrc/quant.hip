@@ -32,7 +32,10 @@ __device__ __forceinline__ double mid64(int i) {
   return ((double)code_value(i) + (double)code_value(i + 1)) * 0.5;
 }
 
-__global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restrict__ w,
+// BF16IN: the input is bf16 (a merged weight being re-quantised); its values widen to fp32 exactly,
+// so the codes and scales are those of the same values given as fp32.
+template <bool BF16IN>
+__global__ __launch_bounds__(256) void nf4_quantize_kernel(const void* __restrict__ w,
                                                            int64_t nblocks,
                                                            uint32_t* __restrict__ packed,
                                                            float* __restrict__ absmax) {
@@ -58,8 +61,16 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restri
     const int64_t blk = it * 8 + (lane >> 3);
     const bool valid = blk < nblocks;
     float v[8];
-    if (valid) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(w + blk * kBlock + (lane & 7) * 8);
+    if (valid && BF16IN) {
+      const u32x4 h = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(w) + blk * kBlock + (lane & 7) * 8));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(h[e] << 16);
+        v[2 * e + 1] = __uint_as_float(h[e] & 0xFFFF0000u);
+      }
+    } else if (valid) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(w) + blk * kBlock + (lane & 7) * 8);
       f32x4 a = __builtin_nontemporal_load(src), b = __builtin_nontemporal_load(src + 1);
       v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
       v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
@@ -350,15 +361,29 @@ static int grid_for(int64_t work_items, int per_block, int max_blocks) {
   return (int)g;
 }
 
-hipError_t launch_quantize(const float* w, int64_t numel, uint8_t* packed, float* absmax,
-                           hipStream_t stream) {
+static hipError_t launch_quantize_any(const void* w, bool bf16_in, int64_t numel, uint8_t* packed,
+                                      float* absmax, hipStream_t stream) {
   const int64_t nblocks = numel / kBlock;
   if (nblocks == 0) return hipSuccess;
   const int64_t iters = (nblocks + 7) / 8;         // one wave iteration per 8 blocks
   const int grid = grid_for(iters, 4, 256 * 32);   // 4 waves per workgroup
-  hipLaunchKernelGGL(nf4_quantize_kernel, dim3(grid), dim3(256), 0, stream, w, nblocks,
-                     reinterpret_cast<uint32_t*>(packed), absmax);
+  if (bf16_in)
+    hipLaunchKernelGGL(nf4_quantize_kernel<true>, dim3(grid), dim3(256), 0, stream, w, nblocks,
+                       reinterpret_cast<uint32_t*>(packed), absmax);
+  else
+    hipLaunchKernelGGL(nf4_quantize_kernel<false>, dim3(grid), dim3(256), 0, stream, w, nblocks,
+                       reinterpret_cast<uint32_t*>(packed), absmax);
   return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float* w, int64_t numel, uint8_t* packed, float* absmax,
+                           hipStream_t stream) {
+  return launch_quantize_any(w, false, numel, packed, absmax, stream);
+}
+
+hipError_t launch_quantize_bf16(const uint16_t* w, int64_t numel, uint8_t* packed, float* absmax,
+                                hipStream_t stream) {
+  return launch_quantize_any(w, true, numel, packed, absmax, stream);
 }
 
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, uint8_t* scale_q,

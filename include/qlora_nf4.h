@@ -13,7 +13,8 @@
  *   qlora_linear_bwd  section "The forward pass and gradients": dX = dY (W~ + s B A),
  *                     dA = s B^T G, dB = s G A^T with G = dY^T X; W gets no gradient.
  *   qlora_merge       section "Quality loss at merge time": the adapter merged into the
- *                     dequantised base, W~ + s B A, served in bf16.
+ *                     dequantised base, W~ + s B A, served in bf16; nf4_quantize_bf16 quantises
+ *                     such a merged weight again.
  *   qlora_adamw_plan_*   sections "The algorithm, step by step" and "Minimal implementation":
  *                     global gradient-norm clipping, then AdamW over A and B.
  *   q4_*              sections "A toy run" and "Double quantisation": FP4 and INT4 codebooks,
@@ -86,6 +87,15 @@ typedef struct {
  * whose absmax is 0 stores index 7 everywhere.
  * Errors: NF4_ERR_NULL (w, packed or absmax NULL while numel > 0), NF4_ERR_SHAPE, NF4_ERR_ALIGN. */
 int nf4_quantize(const float *w, int64_t numel, uint8_t *packed, float *absmax, hipStream_t stream);
+
+/* nf4_quantize of a bf16 array (uint16 bit patterns), for re-quantising a merged weight: "QLoRA,
+ * explained", section "Quality loss at merge time", names merging into W~ and quantising the
+ * result again. Every bf16 value widens to float32 exactly, so packed and absmax are bit for bit
+ * those of nf4_quantize on the widened array; the call reads 2 bytes per value instead of 4.
+ *   w       [numel] bf16 input, 16-byte aligned; numel % 64 == 0.
+ *   packed, absmax: as nf4_quantize.
+ * Errors: as nf4_quantize. */
+int nf4_quantize_bf16(const uint16_t *w, int64_t numel, uint8_t *packed, float *absmax, hipStream_t stream);
 
 /* Double quantisation of block scales.
  *   absmax    [nblocks] float32 input (from nf4_quantize).
@@ -172,12 +182,15 @@ int qlora_linear_fwd_recompute(const nf4_weight *W, const uint16_t *x, int64_t M
                                void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Adapter merged into the dequantised base weight, in bf16:
- *   out = bf16_rne(fl32(W~ + fl32(s * (B A))))      [N x K] bf16 output (uint16 bit patterns),
- * W~ exactly as nf4_dequant produces it, B A accumulated in fp32 from the exact bf16 products.
+ *   out = bf16_rne(W~ + s (B A))      [N x K] bf16 output (uint16 bit patterns),
+ * the exact value rounded once (nearest, ties to even), W~ exactly as nf4_dequant produces it.
  * "QLoRA, explained", section "Quality loss at merge time": training saw W~, never the original
  * weight, so adding the adapter to W~ preserves the trained model; the result is served in bf16
- * (re-quantising it, with nf4_quantize, rounds the update a second time).
- *   A [r x K] bf16;  B [N x r] bf16;  scale = s.
+ * (re-quantising it, with nf4_quantize_bf16, rounds the update a second time).
+ *   A [r x K] bf16;  B [N x r] bf16;  scale = s (used as given, in float).
+ * The sum is formed in fp32 and tested against the rounding ties of bf16 with a rigorous bound of
+ * its error; values within the bound of a tie are recomputed with exact products and a float64
+ * sum, which is exact for factors whose products span less than 2^30 in magnitude.
  * Errors: NF4_ERR_NULL, NF4_ERR_SHAPE (also a weight with fp32 scales), NF4_ERR_ALIGN,
  * NF4_ERR_RANK, NF4_ERR_HIP. */
 int qlora_merge(const nf4_weight *W, const uint16_t *A, const uint16_t *B, int32_t r, float scale,

@@ -68,6 +68,15 @@ def test_quantize_validation():
     assert lib.nf4_quantize(None, 0, None, None, None) == q.NF4_OK      # empty input: nothing to do
 
 
+def test_quantize_bf16_validation():
+    assert lib.nf4_quantize_bf16(FAKE, 65, FAKE, FAKE, None) == q.NF4_ERR_SHAPE
+    assert lib.nf4_quantize_bf16(FAKE, -64, FAKE, FAKE, None) == q.NF4_ERR_SHAPE
+    assert lib.nf4_quantize_bf16(None, 64, FAKE, FAKE, None) == q.NF4_ERR_NULL
+    assert lib.nf4_quantize_bf16(FAKE, 64, FAKE, None, None) == q.NF4_ERR_NULL
+    assert lib.nf4_quantize_bf16(MISALIGNED, 64, FAKE, FAKE, None) == q.NF4_ERR_ALIGN
+    assert lib.nf4_quantize_bf16(None, 0, None, None, None) == q.NF4_OK   # empty input: nothing to do
+
+
 def test_double_quant_validation():
     assert lib.nf4_double_quant(FAKE, -1, FAKE, FAKE, None) == q.NF4_ERR_SHAPE
     assert lib.nf4_double_quant(FAKE, 10, None, FAKE, None) == q.NF4_ERR_NULL
