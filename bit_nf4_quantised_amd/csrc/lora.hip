@@ -271,9 +271,10 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
 
 // Ordered sums of partial results. A job: out[i] = scale * (sum over p < nparts, in order, of
 // part[p * count + i]) (+ out[i]); with `transpose`, part is [C][r] and out is [r][C]. One launch
-// serves two jobs (blocks [0, blocks0) take job 0). A thread takes one output and issues the loads
-// of 8 partials at a time before adding them in order; the sums are latency-bound chains, so
-// one output per thread gives the most chains in flight.
+// serves two jobs (blocks [0, blocks0) take job 0). A thread takes one element of the partials'
+// own order (so the loads of a wave are contiguous; a transposed job scatters only its one store)
+// and issues the loads of 8 partials at a time before adding them in order; the sums are
+// latency-bound chains, so one output per thread gives the most chains in flight.
 struct ReduceJob {
   const float* part;
   int nparts;
@@ -286,9 +287,10 @@ struct ReduceJob {
 __global__ __launch_bounds__(256) void lora_reduce_kernel(const ReduceJob j0, const ReduceJob j1, int blocks0) {
   const bool second = (int)blockIdx.x >= blocks0;
   const ReduceJob& jb = second ? j1 : j0;
-  const int64_t i = (int64_t)(second ? blockIdx.x - blocks0 : blockIdx.x) * 256 + threadIdx.x;
-  if (i >= jb.count) return;
-  const int64_t src = jb.transpose ? (i % jb.C) * jb.r + i / jb.C : i;
+  const int64_t src = (int64_t)(second ? blockIdx.x - blocks0 : blockIdx.x) * 256 + threadIdx.x;
+  if (src >= jb.count) return;
+  // part [C][r] -> out [r][C]: element (c, j) = src goes to j * C + c
+  const int64_t i = jb.transpose ? (src % jb.r) * jb.C + src / jb.r : src;
   float s = 0.f;
   for (int p0 = 0; p0 < jb.nparts; p0 += 8) {
     float v[8];
