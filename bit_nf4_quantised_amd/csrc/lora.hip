@@ -11,7 +11,7 @@
 //   down:  Dn[m][j] = sum_c Q[m][c] R(c, j)    R(c, j) = A[j][c] (A is r x C) or B[c][j] (B is C x r)
 //   grad:  Gr[c][j] = sum_m Q[m][c] P[m][j]    P = u or v, fp32, as a bf16 hi + lo pair
 // The backward's pass over dY does both at once (v and dB), so dY is read once for the adapter.
-// A workgroup takes 256 (or, above rank 32, 128) rows and a range of columns, streaming 64-column
+// A workgroup takes 256 (or, above rank 64, 128) rows and a range of columns, streaming 64-column
 // steps of Q through LDS with LDS-DMA loads; the down products accumulate over its columns, the
 // grad products of each step are complete for its rows. Partial results go to a workspace and
 // lora_reduce_kernel sums them in a fixed order, so results are bitwise reproducible.
@@ -61,12 +61,12 @@ struct LoraPassArgs {
   float* part_grad;         // [row blocks][C][r]
 };
 
-// R16: the rank is exactly 16 (the common case): the grad operand fragments stay in registers.
-template <int MB, bool DOWN, bool GRAD, bool RT, bool R16>
+// RMAX: the rank rounded up to 16, 32, 64 or 128 (the tiles are sized for it); QS: Q stages in
+// LDS (QS - 1 steps in flight). With RMAX = 16 the grad operand fragments stay in registers.
+template <int MB, int RMAX, int QS, bool DOWN, bool GRAD, bool RT>
 __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
-  constexpr int QS = MB == 256 ? 3 : 2;                 // Q stages in LDS
+  constexpr bool R16 = RMAX == 16;
   constexpr int NQ = MB / 32;                           // Q DMA loads per wave per step
-  constexpr int RMAX = MB == 256 ? 32 : 128;            // largest rank handled
   constexpr int RTILE = DOWN ? kStepC * RMAX : 8;       // R tile elements per stage
   constexpr int PP = (GRAD ? RMAX : 0) + 8;             // pitch of the P tiles
   __shared__ __attribute__((aligned(16))) uint16_t Qs[QS][MB * kStepC];
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
   const int nsteps = (int)((c_end - c_begin + kStepC - 1) / kStepC);
 
   // ---- DMA of one step: Q rows m0.., columns c0 .. c0+63 (swizzled), then the R tile
-  const int rdma = (r + 31) / 32;   // R loads per wave per step (waves past the tile repeat one)
+  constexpr int rdma = (RMAX + 31) / 32;   // R loads per wave per step (waves past the tile repeat one)
   auto issue = [&](int t) {
     const int64_t c0 = c_begin + (int64_t)t * kStepC;
     const int st = t % QS;
@@ -228,27 +228,21 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
   // ---- pipeline: QS-1 steps in flight. Step t: start the DMA of step t+QS-1, wait until step
   // t's loads have landed (later steps' loads may stay in flight: vector-memory loads complete in
   // issue order), barrier, compute, barrier (the stage is refilled next).
-  const int per_step = NQ + (DOWN ? rdma : 0);
+  constexpr int PER = NQ + (DOWN ? rdma : 0);          // loads per wave per step
+  static_assert((QS - 1) * PER <= 63, "vmcnt range");
   for (int t = 0; t < QS - 1 && t < nsteps; ++t) issue(t);
   for (int t = 0; t < nsteps; ++t) {
     if (t + QS - 1 < nsteps) {
       issue(t + QS - 1);
-      // allowance: the loads of steps t+1 .. t+QS-1
-      if (QS == 3) {
-        if (per_step == NQ) wait_vmcnt<2 * NQ>();
-        else if (per_step == NQ + 1) wait_vmcnt<2 * (NQ + 1)>();
-        else if (per_step == NQ + 2) wait_vmcnt<2 * (NQ + 2)>();
-        else wait_vmcnt<0>();
-      } else {
-        if (per_step == NQ) wait_vmcnt<NQ>();
-        else if (per_step == NQ + 1) wait_vmcnt<NQ + 1>();
-        else if (per_step == NQ + 2) wait_vmcnt<NQ + 2>();
-        else if (per_step == NQ + 3) wait_vmcnt<NQ + 3>();
-        else if (per_step == NQ + 4) wait_vmcnt<NQ + 4>();
-        else wait_vmcnt<0>();
-      }
+      wait_vmcnt<(QS - 1) * PER>();   // the loads of steps t+1 .. t+QS-1 may stay in flight
     } else {
-      wait_vmcnt<0>();
+      // no more issues: steps t+1 .. nsteps-1 may stay in flight
+      const int ahead = nsteps - 1 - t;
+      if (QS > 5 && ahead >= 4) wait_vmcnt<(QS > 5 ? 4 : 0) * PER>();
+      else if (QS > 4 && ahead >= 3) wait_vmcnt<(QS > 4 ? 3 : 0) * PER>();
+      else if (QS > 3 && ahead >= 2) wait_vmcnt<(QS > 3 ? 2 : 0) * PER>();
+      else if (QS > 2 && ahead >= 1) wait_vmcnt<(QS > 2 ? 1 : 0) * PER>();
+      else wait_vmcnt<0>();
     }
     lds_barrier();
     compute(t);
@@ -305,11 +299,15 @@ __global__ __launch_bounds__(256) void lora_reduce_kernel(const ReduceJob j0, co
 }
 
 // ------------------------------------------------------------------------------------------
-// Work split of a pass: row blocks of 256 (128 above rank 32) and column ranges of whole steps,
-// about 256 workgroups in all with at least 4 steps per workgroup where the matrix allows it.
+// Work split of a pass: row blocks of 256 rows (128 above rank 64) and column ranges of whole steps,
+// about 256 workgroups in all with at least 4 steps per workgroup where the matrix allows it. The
+// grad partial sums (one [C][r] array per row block) cost as many bytes as Q itself at M = 4096,
+// r = 64 with 128-row blocks; 256-row blocks halve them.
+static int pass_rmax(int r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
+
 LoraPassPlan lora_pass_plan(int64_t M, int64_t C, int r) {
   LoraPassPlan p;
-  p.mb = r > 32 ? 128 : 256;
+  p.mb = pass_rmax(r) == 128 ? 128 : 256;
   p.mblocks = (int)((M + p.mb - 1) / p.mb);
   const int64_t steps = (C + kStepC - 1) / kStepC;
   int64_t want = (256 + p.mblocks - 1) / p.mblocks;
@@ -326,15 +324,32 @@ size_t lora_pass_ws_floats(int64_t M, int64_t C, int r, bool down, bool grad) {
   return (down ? (size_t)p.cranges * M * r : 0) + (grad ? (size_t)p.mblocks * C * r : 0);
 }
 
+// Q stages that fit one workgroup's LDS (one workgroup per CU), at most 6: 3 at ranks up to 32, 2
+// above
+template <int MB, int RMAX, bool DOWN, bool GRAD>
+constexpr int pass_stages() {
+  constexpr int stage = MB * kStepC * 2 + (DOWN ? kStepC * RMAX * 2 : 16);
+  constexpr int pbytes = GRAD ? 2 * MB * (RMAX + 8) * 2 : 2 * 16;
+  constexpr int q = (163840 - pbytes - 512) / stage;
+  return q > 6 ? 6 : q;
+}
+
+template <int MB, int RMAX, bool DOWN, bool GRAD, bool RT>
+static void launch_pass_t(dim3 grid, const LoraPassArgs& a, hipStream_t stream) {
+  constexpr int QS = pass_stages<MB, RMAX, DOWN, GRAD>();
+  static_assert(QS >= 2, "two stages at least");
+  hipLaunchKernelGGL((lora_pass_kernel<MB, RMAX, QS, DOWN, GRAD, RT>), grid, dim3(256), 0, stream, a);
+}
+
 template <bool DOWN, bool GRAD, bool RT>
 static void launch_pass(const LoraPassPlan& p, const LoraPassArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)p.mblocks, (unsigned)p.cranges);
-  if (p.mb == 256 && a.r == 16)
-    hipLaunchKernelGGL((lora_pass_kernel<256, DOWN, GRAD, RT, true>), grid, dim3(256), 0, stream, a);
-  else if (p.mb == 256)
-    hipLaunchKernelGGL((lora_pass_kernel<256, DOWN, GRAD, RT, false>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((lora_pass_kernel<128, DOWN, GRAD, RT, false>), grid, dim3(256), 0, stream, a);
+  switch (pass_rmax(a.r)) {
+    case 16: launch_pass_t<256, 16, DOWN, GRAD, RT>(grid, a, stream); break;
+    case 32: launch_pass_t<256, 32, DOWN, GRAD, RT>(grid, a, stream); break;
+    case 64: launch_pass_t<256, 64, DOWN, GRAD, RT>(grid, a, stream); break;
+    default: launch_pass_t<128, 128, DOWN, GRAD, RT>(grid, a, stream); break;
+  }
 }
 
 static ReduceJob reduce_job(const float* part, int nparts, int64_t count, int64_t C, int r, bool transpose,
