@@ -54,12 +54,16 @@ int from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Workspace layout (bytes, each region 256-aligned):
-//   forward : [u (M*r fp32)] [partials: the skinny path's splits, or the GEMM's contraction ranges]
+//   forward : [u (M*r fp32)] [partials: the skinny path's splits, or (in turn) those of u above rank
+//             16 and the GEMM's contraction ranges]
 //   backward: [v (M*r fp32)] [partials of the pass over dY, then of the pass over X]
 size_t fwd_part_floats(int64_t M, int64_t N, int64_t K, int r) {
   if (nf4::skinny_eligible(M, N, K)) return nf4::skinny_workspace_floats(M, N, K, r);
+  // the split GEMM's partial sums, after the partial sums of u (the two launches run in turn)
   const int ks = nf4::fwd_gemm_splits(M, N, K);
-  return ks > 1 ? (size_t)ks * M * N : 0;
+  const size_t gemm = ks > 1 ? (size_t)ks * M * N : 0;
+  const size_t lu = nf4::lora_u_uses_pass(r) ? nf4::lora_pass_ws_floats(M, K, r, true, false) : 0;
+  return gemm > lu ? gemm : lu;
 }
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
   return align_up((size_t)M * r * 4) + align_up(fwd_part_floats(M, N, K, r) * 4);

@@ -48,7 +48,9 @@ struct LoraPassPlan {
 };
 LoraPassPlan lora_pass_plan(int64_t M, int64_t C, int r);
 size_t lora_pass_ws_floats(int64_t M, int64_t C, int r, bool down, bool grad);
-// u = X A^T
+// u = X A^T. Above rank 16 (lora_u_uses_pass) it takes lora_pass_ws_floats(M, K, r, true, false)
+// floats of ws for partial sums; at rank 16 ws is not used.
+bool lora_u_uses_pass(int r);
 hipError_t launch_lora_u(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int r,
                          float* ws, float* u, hipStream_t stream);
 // v = dY B and dB = scale * dY^T u (+ dB if accumulate), in one pass over dY

@@ -364,7 +364,7 @@ static void launch_reduce(const ReduceJob& j0, const ReduceJob* j1, hipStream_t 
 }
 
 // ------------------------------------------------------------------------------------------
-// u = X A^T in one launch, without partial sums in memory (its contraction runs over K only, so
+// u = X A^T at rank 16 in one launch, without partial sums in memory (its contraction runs over K only, so
 // a workgroup can own whole rows): a workgroup owns 16 rows of X and all of K. Its 8 waves take
 // interleaved 32-column chunks (wave w: chunks w, w + 8, ...), NB chunks at a time with every
 // load of a batch issued before its MFMAs; lane (row = lane % 16, g = lane / 16) holds columns
@@ -423,9 +423,19 @@ __global__ __launch_bounds__(kUWaves * 64) void lora_u_kernel(const uint16_t* __
   }
 }
 
+bool lora_u_uses_pass(int r) { return r > 16; }
+
 hipError_t launch_lora_u(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int r,
                          float* ws, float* u, hipStream_t stream) {
-  (void)ws;
+  if (lora_u_uses_pass(r)) {
+    // above rank 16 a workgroup of lora_u_kernel would read r x K of A for its 16 rows: the pass
+    // reads A once per row block of 256 and leaves partial sums over column ranges in ws
+    const LoraPassPlan p = lora_pass_plan(M, K, r);
+    const LoraPassArgs a{X, M, K, A, nullptr, r, p.crange, ws, nullptr};
+    launch_pass<true, false, false>(p, a, stream);
+    launch_reduce(reduce_job(ws, p.cranges, M * r, 0, r, false, 1.f, 0, u), nullptr, stream);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((M + 15) / 16)), block(kUWaves * 64);
   switch (r / 16) {
     case 1: hipLaunchKernelGGL(lora_u_kernel<1>, grid, block, 0, stream, X, M, K, A, u); break;
