@@ -39,7 +39,7 @@ class CNF4Weight(ctypes.Structure):
     """Mirror of ``nf4_weight`` in include/qlora_nf4.h."""
     _fields_ = [("packed", ctypes.c_void_p), ("scale_q", ctypes.c_void_p),
                 ("scale_c2", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("absmax", ctypes.c_void_p)]
+                ("absmax", ctypes.c_void_p), ("codebook", ctypes.c_int32)]
 
 
 class CAdamWConfig(ctypes.Structure):
@@ -124,17 +124,19 @@ _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 @dataclass
 class NF4Weight:
     """A quantised N x K weight in device tensors: double-quantised scales (scale_q, scale_c2) or,
-    without double quantisation, the fp32 absmax (scale_q and scale_c2 None)."""
+    without double quantisation, the fp32 absmax (scale_q and scale_c2 None). codebook: the values
+    the indices select (0 NF4, 1 FP4, 2 INT4; see Q4_CODEBOOKS)."""
     packed: torch.Tensor           # uint8 [N*K/2]
     scale_q: torch.Tensor | None   # uint8 [N*K/64]
     scale_c2: torch.Tensor | None  # float32 [ceil(N*K/16384)]
     N: int
     K: int
     absmax: torch.Tensor | None = None   # float32 [N*K/64]
+    codebook: int = 0
 
     def c_struct(self) -> CNF4Weight:
         return CNF4Weight(_ptr(self.packed), _ptr(self.scale_q), _ptr(self.scale_c2), self.N, self.K,
-                          _ptr(self.absmax))
+                          _ptr(self.absmax), _book(self.codebook))
 
 
 # ------------------------------------------------------------------------- the five calls
@@ -435,27 +437,34 @@ def workspace(M: int, N: int, K: int, r: int, device="cuda") -> torch.Tensor:
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def empty_weight(N: int, K: int, device="cuda") -> NF4Weight:
+def empty_weight(N: int, K: int, device="cuda", codebook=0) -> NF4Weight:
     nb = N * K // 64
     return NF4Weight(torch.empty(N * K // 2, dtype=torch.uint8, device=device),
                      torch.empty(nb, dtype=torch.uint8, device=device),
-                     torch.empty((nb + 255) // 256, dtype=torch.float32, device=device), N, K)
+                     torch.empty((nb + 255) // 256, dtype=torch.float32, device=device), N, K,
+                     codebook=_book(codebook))
 
 
 def quantize_weight(w: torch.Tensor, stream=None, absmax: torch.Tensor | None = None,
-                    double_quant: bool = True) -> NF4Weight:
-    """Quantise a float32 N x K device tensor: nf4_quantize followed by nf4_double_quant, or with
-    double_quant=False a weight that keeps the fp32 absmax as its scales."""
+                    double_quant: bool = True, codebook=0) -> NF4Weight:
+    """Quantise a float32 N x K device tensor: nf4_quantize (q4_quantize at blocksize 64 for the FP4
+    or INT4 codebook) followed by nf4_double_quant, or with double_quant=False a weight that keeps
+    the fp32 absmax as its scales."""
     N, K = w.shape
+    book = _book(codebook)
     if absmax is None:
         absmax = torch.empty(N * K // 64, dtype=torch.float32, device=w.device)
     if not double_quant:
-        qw = NF4Weight(torch.empty(N * K // 2, dtype=torch.uint8, device=w.device), None, None, N, K, absmax)
+        qw = NF4Weight(torch.empty(N * K // 2, dtype=torch.uint8, device=w.device), None, None, N, K, absmax,
+                       codebook=book)
+    else:
+        qw = empty_weight(N, K, w.device, book)
+    if book == 0:
         nf4_quantize(w, qw.packed, absmax, stream)
-        return qw
-    qw = empty_weight(N, K, w.device)
-    nf4_quantize(w, qw.packed, absmax, stream)
-    nf4_double_quant(absmax, qw.scale_q, qw.scale_c2, stream)
+    else:
+        q4_quantize(w, book, 64, qw.packed, absmax, stream)
+    if double_quant:
+        nf4_double_quant(absmax, qw.scale_q, qw.scale_c2, stream)
     return qw
 
 

@@ -30,6 +30,7 @@ int check_weight(const nf4_weight* W) {
   if (W->absmax ? (W->scale_q || W->scale_c2) : !(W->scale_q && W->scale_c2)) return NF4_ERR_NULL;
   if (W->N < 16 || W->K < 64 || W->N % 16 || W->K % 64) return NF4_ERR_SHAPE;
   if (W->N > (int64_t(1) << 31) || W->K > (int64_t(1) << 31)) return NF4_ERR_SHAPE;
+  if (W->codebook < Q4_CODEBOOK_NF4 || W->codebook > Q4_CODEBOOK_INT4) return NF4_ERR_SHAPE;
   if (!aligned16(W->packed) || !aligned16(W->scale_q) || !aligned16(W->scale_c2) || !aligned16(W->absmax))
     return NF4_ERR_ALIGN;
   return NF4_OK;
@@ -133,12 +134,12 @@ int run_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
   if (nf4::skinny_eligible(M, N, K) && (!W->absmax || M <= 4)) {
     return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, A, B, r,
-                                           scale, part, u, y, stream));
+                                           scale, part, u, y, W->codebook, stream));
   }
   hipError_t e = nf4::launch_lora_u(x, M, K, A, r, part, u, stream);
   if (e != hipSuccess) return NF4_ERR_HIP;
   return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, u, B,
-                                       r, scale, y, part, stream));
+                                       r, scale, y, part, W->codebook, stream));
 }
 
 }  // namespace
@@ -237,9 +238,9 @@ int nf4_dequant(const nf4_weight* W, uint16_t* out, hipStream_t stream) {
   if (st) return st;
   if (!out) return NF4_ERR_NULL;
   if (!aligned16(out)) return NF4_ERR_ALIGN;
-  if (W->absmax)
-    return from_hip(nf4::launch_q4_dequant(W->packed, W->absmax, nullptr, nullptr, W->N * W->K, 0, 64, out,
-                                           stream));
+  if (W->absmax || W->codebook != Q4_CODEBOOK_NF4)
+    return from_hip(nf4::launch_q4_dequant(W->packed, W->absmax, W->scale_q, W->scale_c2, W->N * W->K,
+                                           W->codebook, 64, out, stream));
   return from_hip(nf4::launch_dequant(W->packed, W->scale_q, W->scale_c2, W->N * W->K, out, stream));
 }
 
@@ -252,7 +253,7 @@ int qlora_merge(const nf4_weight* W, const uint16_t* A, const uint16_t* B, int32
   if (!A || !B || !out) return NF4_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(out)) return NF4_ERR_ALIGN;
   return from_hip(nf4::launch_merge(W->packed, W->scale_q, W->scale_c2, W->N, W->K, A, B, r, scale,
-                                    out, stream));
+                                    out, W->codebook, stream));
 }
 
 size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
@@ -304,7 +305,7 @@ int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M
     float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
     float* u_scratch = static_cast<float*>(ws);
     return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, A, B, r,
-                                           scale, part, u_scratch, y, stream));
+                                           scale, part, u_scratch, y, W->codebook, stream));
   }
   // with a workspace of the forward's size, the same launches as qlora_linear_fwd (and the same
   // output bit for bit); without one, the GEMM in one pass over the contraction
@@ -312,7 +313,7 @@ int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M
   if (ws && ws_bytes >= fwd_ws(M, N, K, r) && fwd_part_floats(M, N, K, r) > 0)
     gpart = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
   return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, u, B,
-                                       r, scale, y, gpart, stream));
+                                       r, scale, y, gpart, W->codebook, stream));
 }
 
 int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy, int64_t M,
@@ -337,7 +338,7 @@ int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy,
   if (e != hipSuccess) return NF4_ERR_HIP;
   if (dx) {
     e = nf4::launch_dx_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, dy, M, v, A, r, scale, dx,
-                            stream);
+                            W->codebook, stream);
     if (e != hipSuccess) return NF4_ERR_HIP;
   }
   return from_hip(nf4::launch_lora_dx(x, M, K, v, r, scale, accumulate, part, dA, stream));

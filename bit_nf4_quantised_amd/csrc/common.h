@@ -67,6 +67,25 @@ struct BlockLut {
   uint32_t lo[4], hi[4];
 };
 
+// The 16 values a 4-bit index selects (NF4, FP4 or INT4, ascending; a 15-value codebook repeats
+// its last value at index 15), passed to kernels by value in their arguments.
+struct Codes {
+  float v[16];
+};
+
+__device__ __forceinline__ BlockLut make_lut(float c1p, const float (&q)[16]) {
+  uint32_t p[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) p[k] = pack_bf16x2(__fmul_rn(q[2 * k], c1p), __fmul_rn(q[2 * k + 1], c1p));
+  BlockLut t;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    t.lo[k] = __builtin_amdgcn_perm(p[2 * k + 1], p[2 * k], 0x06040200u);
+    t.hi[k] = __builtin_amdgcn_perm(p[2 * k + 1], p[2 * k], 0x07050301u);
+  }
+  return t;
+}
+
 __device__ __forceinline__ BlockLut make_lut(float c1p) {
   uint32_t p[8];
 #pragma unroll

@@ -67,6 +67,7 @@ struct GemmArgs {
   uint16_t* out;            // y [M x N] (forward) or dX [M x K] (backward), bf16
   int ksplit;               // contraction ranges (1: none)
   float* part;              // ksplit x M x Nout fp32 partial sums when ksplit > 1
+  Codes codes;              // the values the 4-bit indices select
 };
 
 constexpr int kBN = 128;        // output columns per tile
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
     const uint32_t h = lane & 1;
     float qv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qv[i] = h ? code_value(8 + i) : code_value(i);
+    for (int i = 0; i < 8; ++i) qv[i] = h ? g.codes.v[8 + i] : g.codes.v[i];
     const uint32_t hx = h ? 0x88888888u : 0u, hx4 = hx >> 4;
     // block index of this thread's chunk at step t: b0 + t * b_step; where its code and constant
     // sit in the scale stages
@@ -610,17 +611,19 @@ static hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t stream) {
 hipError_t launch_fwd_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                            const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                            const float* u, const uint16_t* B, int r, float scale, uint16_t* y,
-                           float* part, hipStream_t stream) {
+                           float* part, int book, hipStream_t stream) {
   const int ks = part ? fwd_gemm_splits(M, N, K) : 1;
-  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, x, M, u, B, r, scale, y, ks, part};
+  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, x, M, u, B, r, scale, y, ks, part, {}};
+  if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
   return absmax ? launch_gemm_t<false, true>(g, stream) : launch_gemm_t<false, false>(g, stream);
 }
 
 hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                           const float* absmax, int64_t N, int64_t K, const uint16_t* dy, int64_t M,
                           const float* v, const uint16_t* A, int r, float scale, uint16_t* dx,
-                          hipStream_t stream) {
-  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, dy, M, v, A, r, scale, dx, 1, nullptr};
+                          int book, hipStream_t stream) {
+  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, dy, M, v, A, r, scale, dx, 1, nullptr, {}};
+  if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
   return absmax ? launch_gemm_t<true, true>(g, stream) : launch_gemm_t<true, false>(g, stream);
 }
 

@@ -6,6 +6,8 @@
 
 namespace nf4 {
 
+struct Codes;   // common.h
+
 hipError_t launch_quantize(const float* w, int64_t numel, uint8_t* packed, float* absmax,
                            hipStream_t stream);
 hipError_t launch_quantize_bf16(const uint16_t* w, int64_t numel, uint8_t* packed, float* absmax,
@@ -26,17 +28,21 @@ hipError_t launch_double_quant_many(const DqBatch& b, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                           int64_t numel, uint16_t* out, hipStream_t stream);
 
+// The values of codebook `book` (0 NF4, 1 FP4 E2M1, 2 INT4); false for an unknown codebook. The
+// linear, few-token and merge kernels take them by value.
+bool codes_of(int book, Codes& out);
+
 // absmax != null: fp32 scales per block instead of scale_q / scale_c2. part: room for
 // fwd_gemm_splits(M, N, K) x M x N fp32 partial sums, or null (then the launch does not split)
 int fwd_gemm_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fwd_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                            const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                            const float* u, const uint16_t* B, int r, float scale, uint16_t* y,
-                           float* part, hipStream_t stream);
+                           float* part, int book, hipStream_t stream);
 hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                           const float* absmax, int64_t N, int64_t K, const uint16_t* dy, int64_t M,
                           const float* v, const uint16_t* A, int r, float scale, uint16_t* dx,
-                          hipStream_t stream);
+                          int book, hipStream_t stream);
 
 // Adapter passes over one bf16 matrix (see lora.hip). Each writes partial results to `ws`
 // (lora_pass_ws_floats floats) and reduces them in a fixed order.
@@ -74,13 +80,12 @@ size_t skinny_workspace_floats(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                              const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                              const uint16_t* A, const uint16_t* B, int r, float scale, float* part,
-                             float* u_out,
-                             uint16_t* y, hipStream_t stream);
+                             float* u_out, uint16_t* y, int book, hipStream_t stream);
 
 // Adapter merged into the dequantised base: out = bf16(W~ + s B A), [N x K].
 hipError_t launch_merge(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2, int64_t N,
                         int64_t K, const uint16_t* A, const uint16_t* B, int r, float scale, uint16_t* out,
-                        hipStream_t stream);
+                        int book, hipStream_t stream);
 
 // Adapter update over a plan: a device table of 4096-value chunk descriptors of every tensor.
 int64_t opt_chunk_count(int64_t count, const int64_t* numel);

@@ -68,6 +68,7 @@ struct MergeArgs {
   float tie_floor;      // smallest radius (covers products an accumulator might flush to zero)
   int row_chunks;       // workgroups per strip
   uint16_t* out;        // [N x K] bf16
+  Codes codes;          // the values the 4-bit indices select
 };
 
 __device__ __forceinline__ float bf16_val(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -247,7 +248,7 @@ void qlora_merge_kernel(const MergeArgs g) {
     // ---- dequantise, add, test, round
     const uint32_t b = (uint32_t)(n0 * kb) + (uint32_t)lane_b;   // low bits of the block index
     const uint32_t code = in.cw >> ((b & 3u) * 8u);              // e4m3_decode reads bits 0 .. 6
-    const BlockLut lut = make_lut(__fmul_rn(e4m3_decode(code), in.c2));
+    const BlockLut lut = make_lut(__fmul_rn(e4m3_decode(code), in.c2), g.codes.v);
     const float* u = urow + rl * kMgPitch + (col - k0);
     // near-tie radius 2 |s| E for this row and these columns (rounded up by tie_coef's margin)
     const float radius = fmaxf(g.tie_coef * (__fsqrt_rn(urow[rl * kMgPitch + kMgCols]) * amax), g.tie_floor);
@@ -341,7 +342,7 @@ void qlora_merge_kernel(const MergeArgs g) {
 
 hipError_t launch_merge(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2, int64_t N,
                         int64_t K, const uint16_t* A, const uint16_t* B, int r, float scale, uint16_t* out,
-                        hipStream_t stream) {
+                        int book, hipStream_t stream) {
   const int64_t strips = (K + kMgCols - 1) / kMgCols;
   const int64_t tiles = (N + kMgRows - 1) / kMgRows;
   int64_t chunks = (2048 + strips - 1) / strips;   // about 2048 workgroups in all
@@ -351,7 +352,8 @@ hipError_t launch_merge(const uint8_t* packed, const uint8_t* scale_q, const flo
   // norms' sums of at most 128 squares, their square roots and the products)
   const float coef = (float)(4.0 * fabs((double)scale) * (r + 1) * 0x1p-24 * (1.0 + 0x1p-14));
   const float floor_ = (float)((fabs((double)scale) + 1.0) * 0x1p-90);
-  MergeArgs g{packed, scale_q, scale_c2, N, K, A, B, r, scale, coef, floor_, (int)chunks, out};
+  MergeArgs g{packed, scale_q, scale_c2, N, K, A, B, r, scale, coef, floor_, (int)chunks, out, {}};
+  if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(strips * chunks)), block(256);
   switch (r / 16) {
     case 1: hipLaunchKernelGGL((qlora_merge_kernel<1, true>), grid, block, 0, stream, g); break;

@@ -55,6 +55,7 @@ struct SkinnyArgs {
   float* part;         // [w_splits][M][N]
   float* upart;        // [u parts][M][r]
   const float* absmax; // fp32 block scales instead of scale_q / scale_c2 (M <= 4 kernel only)
+  Codes codes;         // the values the 4-bit indices select
 };
 
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
@@ -72,8 +73,6 @@ struct SkinnyS {
   u32x4 a;         // adapter fragment: 8 bf16 of A
 };
 
-__constant__ uint32_t kSkinnyCodes[16] = {NF4_CODE_BITS};
-
 __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyArgs g) {
   __shared__ __attribute__((aligned(16))) f32x2 tab[256 * 32];
   // activation stages: 16 tokens x 64 chunks of 8 bf16
@@ -88,8 +87,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
   // pair table: thread t fills copies 8 (t & 3) .. +7 of byte value t / 4
   {
     const int byte = tid >> 2;
-    const float hi = __uint_as_float(kSkinnyCodes[byte >> 4]);
-    const float lo = __uint_as_float(kSkinnyCodes[byte & 15]);
+    const float hi = g.codes.v[byte >> 4];
+    const float lo = g.codes.v[byte & 15];
     const u32x4 v = u32x4{__float_as_uint(hi), __float_as_uint(lo), __float_as_uint(hi), __float_as_uint(lo)};
     u32x4* dst = reinterpret_cast<u32x4*>(&tab[byte * 32 + (tid & 3) * 8]);
 #pragma unroll
@@ -313,8 +312,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
 
   {
     const int byte = tid >> 2;
-    const float hi = __uint_as_float(kSkinnyCodes[byte >> 4]);
-    const float lo = __uint_as_float(kSkinnyCodes[byte & 15]);
+    const float hi = g.codes.v[byte >> 4];
+    const float lo = g.codes.v[byte & 15];
     const u32x4 v = u32x4{__float_as_uint(hi), __float_as_uint(lo), __float_as_uint(hi), __float_as_uint(lo)};
     u32x4* dst = reinterpret_cast<u32x4*>(&tab[byte * 32 + (tid & 3) * 8]);
 #pragma unroll
@@ -514,6 +513,20 @@ __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __res
   __shared__ float us[128];
   const int64_t mm = blockIdx.y;
   const int tid = threadIdx.x;
+  const int64_t n = (int64_t)blockIdx.x * 256 + tid;
+  const bool live = n < N;
+  // the split partials and the row of B do not depend on u: their loads go out first, so that
+  // they travel together with the u partials' loads
+  float ysum = 0.f;
+  u32x4 bv[8];
+  if (live) {
+#pragma unroll 8
+    for (int sp = 0; sp < splits; ++sp) ysum += part[((int64_t)sp * M + mm) * N + n];
+    const u32x4* brow = reinterpret_cast<const u32x4*>(B + n * r);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c < r / 8) bv[c] = brow[c];
+  }
   // nruns * r <= 256 and nruns * per_run >= u_parts: threads past nruns * r (r = 48, 80, 96, 112)
   // form a run past the last partial, which sums nothing and is never read
   const int nruns = 256 / r;
@@ -534,22 +547,21 @@ __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __res
     if (blockIdx.x == 0) u_out[mm * r + tid] = s;
   }
   __syncthreads();
-  const int64_t n = (int64_t)blockIdx.x * 256 + tid;
-  if (n >= N) return;
-  float s = 0.f;
-#pragma unroll 8
-  for (int sp = 0; sp < splits; ++sp) s += part[((int64_t)sp * M + mm) * N + n];
+  if (!live) return;
   float l = 0.f;
   const u32x4* brow = reinterpret_cast<const u32x4*>(B + n * r);
-  for (int c = 0; c < r / 8; ++c) {
-    const u32x4 v = brow[c];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      l = fmaf(us[8 * c + 2 * q], __uint_as_float(v[q] << 16), l);
-      l = fmaf(us[8 * c + 2 * q + 1], __uint_as_float(v[q] & 0xFFFF0000u), l);
+  for (int c = 0; c < 16; ++c) {
+    if (c < r / 8) {
+      const u32x4 v = c < 8 ? bv[c] : brow[c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        l = fmaf(us[8 * c + 2 * q], __uint_as_float(v[q] << 16), l);
+        l = fmaf(us[8 * c + 2 * q + 1], __uint_as_float(v[q] & 0xFFFF0000u), l);
+      }
     }
   }
-  y[mm * N + n] = (uint16_t)(pack_bf16x2(s + scale * l, 0.f) & 0xFFFFu);
+  y[mm * N + n] = (uint16_t)(pack_bf16x2(ysum + scale * l, 0.f) & 0xFFFFu);
 }
 
 // Scale codes and second-level constants are addressed with 32-bit buffer offsets.
@@ -589,11 +601,12 @@ size_t skinny_workspace_floats(int64_t M, int64_t N, int64_t K, int r) {
 hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                              const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                              const uint16_t* A, const uint16_t* B, int r, float scale, float* part,
-                             float* u_out, uint16_t* y, hipStream_t stream) {
+                             float* u_out, uint16_t* y, int book, hipStream_t stream) {
   const SkinnyPlan p = skinny_plan(M, N, K, r);
   if (absmax && !p.narrow) return hipErrorInvalidValue;   // fp32 scales: the M <= 4 kernel only
   float* upart = part + skinny_wpart_floats(p, M, N);
-  SkinnyArgs g{packed, scale_q, scale_c2, N, K, x, M, A, r, p, part, upart, absmax};
+  SkinnyArgs g{packed, scale_q, scale_c2, N, K, x, M, A, r, p, part, upart, absmax, {}};
+  if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
   const int items = p.w_blocks * p.w_splits;
   if (p.narrow && absmax)
     hipLaunchKernelGGL(skinny4_fwd_kernel<true>, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);

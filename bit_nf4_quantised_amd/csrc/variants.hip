@@ -138,19 +138,6 @@ __global__ __launch_bounds__(256) void q4_quantize_kernel(const f32x4* __restric
 // instruction writes 1 KB of contiguous output.
 constexpr int kQdWaves = 4;
 
-__device__ __forceinline__ BlockLut make_lut_book(const Q4Book& cb, float s) {
-  uint32_t p[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) p[k] = pack_bf16x2(__fmul_rn(cb.q[2 * k], s), __fmul_rn(cb.q[2 * k + 1], s));
-  BlockLut t;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    t.lo[k] = __builtin_amdgcn_perm(p[2 * k + 1], p[2 * k], 0x06040200u);
-    t.hi[k] = __builtin_amdgcn_perm(p[2 * k + 1], p[2 * k], 0x07050301u);
-  }
-  return t;
-}
-
 template <int L, bool kDQ>
 __global__ __launch_bounds__(kQdWaves * 64) void q4_dequant_kernel(const uint8_t* __restrict__ packed,
                                                                    const float* __restrict__ absmax,
@@ -176,7 +163,7 @@ __global__ __launch_bounds__(kQdWaves * 64) void q4_dequant_kernel(const uint8_t
     const int64_t b = L == 1 ? (u >> unit_shift) : u * L + l;
     const float s = kDQ ? __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)scale_q[b], 0), scale_c2[b / kGroup])
                         : absmax[b];
-    t[l] = make_lut_book(cb, s);
+    t[l] = make_lut(s, cb.q);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -232,6 +219,13 @@ static bool make_book(int id, Q4Book& b) {
     const double m0 = ((double)b.q[i] + b.q[i + 1]) * 0.5, m1 = ((double)b.q[i + 1] + b.q[i + 2]) * 0.5;
     if (m1 - m0 <= 1.0 / 128.0) return false;
   }
+  return true;
+}
+
+bool codes_of(int book, Codes& out) {
+  Q4Book b;
+  if (!make_book(book, b)) return false;
+  for (int i = 0; i < 16; ++i) out.v[i] = b.q[i];
   return true;
 }
 

@@ -28,15 +28,16 @@
  *            to the exact ratio, ties to the even code.
  *   scale_c2 float[ceil(N*K/64/256)]: c2[g] = max of the 256 block absmax values of group g.
  *   bf16     stored as uint16 bit patterns. Dequantised value: bf16_rne(fl32(q[idx] * c1')) with
- *            c1' = fl32(e4m3(scale_q) * c2).
+ *            c1' = fl32(e4m3(scale_q) * c2); q is the NF4 codebook unless the weight names another.
  *   LoRA     A: bf16 r x K, B: bf16 N x r, scale s = lora_alpha / r; 16 <= r <= 128, r % 16 == 0.
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers to caller-owned memory (except nf4_codebook's output, a host
  *     array), each 16-byte aligned. Apart from qlora_adamw_plan_create (which allocates the plan's
  *     device memory and blocks until its table is uploaded) and qlora_adamw_plan_destroy (which
- *     frees it), the library never allocates or frees device memory and never synchronises; it
- *     keeps no mutable global state and its calls are thread-safe.
+ *     frees it), the library never allocates or frees device memory and never synchronises. Its
+ *     only mutable global state is qlora_linear_fwd_noalloc's workspace (see there); every other
+ *     call is thread-safe.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the default stream).
  *     The return value reports argument validation and launch status; faults inside kernels
  *     surface at the caller's next synchronisation.
@@ -65,18 +66,31 @@ typedef enum {
   NF4_ERR_HIP = 6         /* the HIP runtime rejected a kernel launch */
 } nf4_status;
 
+/* The 4-bit codebooks ("QLoRA, explained", A toy run, which sets NF4 beside an INT4 grid of 15
+ * levels k/7 and E2M1 FP4 rescaled to [-1, 1]). */
+enum {
+  Q4_CODEBOOK_NF4 = 0,    /* the 16 NF4 codes (nf4_codebook) */
+  Q4_CODEBOOK_FP4 = 1,    /* E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} / 6, both signs: 15 codes */
+  Q4_CODEBOOK_INT4 = 2    /* k / 7 for k = -7..7: 15 codes */
+};
+
 /* A quantised weight W (N x K), device memory. Its block scales are either double quantised
  * (scale_q and scale_c2 set, absmax NULL: 4.127 bits per weight) or the fp32 absmax itself
  * (absmax set, scale_q and scale_c2 NULL: the 4.5-bit baseline without double quantisation,
  * "QLoRA, explained", Double quantisation). nf4_dequant and the linear calls take either; with
  * fp32 scales the few-token forward path serves M <= 4 only (the fused GEMM above) and
- * qlora_merge is not available (NF4_ERR_SHAPE). */
+ * qlora_merge is not available (NF4_ERR_SHAPE).
+ * codebook names the values the indices select: Q4_CODEBOOK_NF4 (0, what nf4_quantize writes),
+ * or Q4_CODEBOOK_FP4 / Q4_CODEBOOK_INT4 for indices written by q4_quantize at blocksize 64 (their
+ * indices must be below 15). Every call that takes an nf4_weight dequantises with it; any other
+ * value is NF4_ERR_SHAPE. */
 typedef struct {
   const uint8_t *packed;    /* [N*K/2]                 */
   const uint8_t *scale_q;   /* [N*K/64]                */
   const float *scale_c2;    /* [ceil(N*K/64/256)]      */
   int64_t N, K;
   const float *absmax;      /* [N*K/64] or NULL        */
+  int32_t codebook;         /* Q4_CODEBOOK_*           */
 } nf4_weight;
 
 /* Blockwise absmax NF4 quantisation of a float32 array (any shape, flattened row-major).
@@ -197,17 +211,12 @@ int qlora_merge(const nf4_weight *W, const uint16_t *A, const uint16_t *B, int32
                 uint16_t *out, hipStream_t stream);
 
 /* ---- Codebook and blocksize variants, and scales without double quantisation ("QLoRA, explained",
- * A toy run, which sets NF4 beside an INT4 grid of 15 levels k/7 and E2M1 FP4 rescaled to [-1, 1],
- * and discusses blocksizes from 16 to 4096; Double quantisation, whose baseline keeps one fp32
- * absmax per block). The same storage layout as above with another codebook and blocksize:
- * packed[j] holds the indices of elements 2j (high nibble) and 2j+1 (low nibble); one fp32 absmax
- * per block of `blocksize` consecutive values. Double quantisation of those scales is
- * nf4_double_quant on the absmax array (any length; groups of 256 blocks). */
-enum {
-  Q4_CODEBOOK_NF4 = 0,    /* the 16 NF4 codes above */
-  Q4_CODEBOOK_FP4 = 1,    /* E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} / 6, both signs: 15 codes */
-  Q4_CODEBOOK_INT4 = 2    /* k / 7 for k = -7..7: 15 codes */
-};
+ * A toy run, with the codebooks above and blocksizes from 16 to 4096; Double quantisation, whose
+ * baseline keeps one fp32 absmax per block). The same storage layout as above with another
+ * codebook and blocksize: packed[j] holds the indices of elements 2j (high nibble) and 2j+1 (low
+ * nibble); one fp32 absmax per block of `blocksize` consecutive values. Double quantisation of
+ * those scales is nf4_double_quant on the absmax array (any length; groups of 256 blocks). At
+ * blocksize 64 the result is an nf4_weight with that codebook. */
 
 /* Writes the codebook's values, ascending, as fp32 (out[15] repeats the last code when there are
  * 15) and returns how many there are (15 or 16); a negative status for an unknown codebook. */

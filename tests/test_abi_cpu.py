@@ -110,6 +110,28 @@ def test_weight_scale_kinds():
     assert lib.qlora_merge(ctypes.byref(f32s), FAKE, FAKE, 16, 2.0, FAKE, None) == q.NF4_ERR_SHAPE
 
 
+def test_weight_codebook_validation():
+    # the codebook field of the weight: 0 NF4, 1 FP4, 2 INT4; anything else is a shape error in
+    # every call that takes a weight, before any HIP call
+    for bad in (-1, 3, 1 << 20):
+        w = ctypes.byref(q.CNF4Weight(FAKE, FAKE, FAKE, 4096, 4096, None, bad))
+        assert lib.nf4_dequant(w, FAKE, None) == q.NF4_ERR_SHAPE
+        assert lib.qlora_merge(w, FAKE, FAKE, 16, 2.0, FAKE, None) == q.NF4_ERR_SHAPE
+        assert lib.qlora_linear_fwd(w, FAKE, 64, FAKE, FAKE, 16, 2.0, FAKE, None, FAKE, 1 << 30,
+                                    None) == q.NF4_ERR_SHAPE
+        assert lib.qlora_linear_fwd_noalloc(w, FAKE, 64, FAKE, FAKE, 16, 2.0, FAKE, None,
+                                            None) == q.NF4_ERR_SHAPE
+        assert lib.qlora_linear_fwd_recompute(w, FAKE, 64, FAKE, FAKE, 16, 2.0, FAKE, FAKE, FAKE,
+                                              1 << 30, None) == q.NF4_ERR_SHAPE
+        assert lib.qlora_linear_bwd(w, FAKE, FAKE, 64, FAKE, FAKE, 16, 2.0, FAKE, FAKE, FAKE, FAKE,
+                                    0, FAKE, 1 << 30, None) == q.NF4_ERR_SHAPE
+    # the binding names the codebooks and passes the field through
+    assert q.NF4Weight(None, None, None, 64, 64, codebook="fp4").c_struct().codebook == 1
+    assert q.NF4Weight(None, None, None, 64, 64, codebook=2).c_struct().codebook == 2
+    assert q.NF4Weight(None, None, None, 64, 64).c_struct().codebook == 0
+    assert q.CNF4Weight(FAKE, FAKE, FAKE, 64, 64).codebook == 0
+
+
 def test_merge_validation():
     w = ctypes.byref(_w())
     assert lib.qlora_merge(None, FAKE, FAKE, 16, 2.0, FAKE, None) == q.NF4_ERR_NULL
