@@ -25,10 +25,11 @@
 //     v_perm forms the address (byte * 256 + copy * 8), then two fp32 products with the block
 //     scale and one bf16 pair conversion, giving bit for bit bf16(fl32(q[idx] * c1')). Four waves
 //     per SIMD keep enough of these lookups in flight;
-//   * the r rows of A (bf16) ride along: in the items of row block b < r / 16, wave w also
-//     multiplies one 32-column slice (i = w / 4, d = w % 4) of each step of A's tile b (one more
-//     MFMA per step), so u = x A^T is formed as 16 partial sums per split without separate work
-//     items;
+//   * u = x A^T is shared out evenly: every item forms the partial sums of u over its own slice of
+//     the contraction (its split's columns cut into one run per row block), each (token, row of A)
+//     pair summed by one thread in column order while the item's first weight loads are in flight.
+//     (With the rows of A riding along in the items of the first row blocks instead, those items
+//     read twice the bytes of the others and finished 4-8 us after them);
 //   * every wave writes the fp32 partial sums of its own rows; skinny_epilogue_kernel sums the
 //     split partials in split order, forms u from its partials, adds s * u B^T in fp32 and rounds
 //     y to bf16.
@@ -70,8 +71,43 @@ struct SkinnyW {
 struct SkinnyS {
   u32x4 cw;        // 16 bytes from the aligned word holding the step's first scale code
   u32x2 c2;        // second-level constants of the step's first group and the next one
-  u32x4 a;         // adapter fragment: 8 bf16 of A
 };
+
+// This item's partial sums of u = x A^T: the 8-column chunks [ch0, ch1) of the contraction, for
+// every token m < M and row j < r. Thread t sums the pairs p = (m, j) = (p / r, p % r), p = t, t +
+// 1024, ..., over its chunks in column order, so each partial is formed in one fixed order; the
+// sums go to dst[m r + j].
+__device__ __forceinline__ void u_share(const SkinnyArgs& g, int64_t ch0, int64_t ch1, int tid,
+                                        float* __restrict__ dst) {
+  const int pairs = (int)g.M * g.r;
+  for (int p = tid; p < pairs; p += kSkWaves * 64) {
+    const int m = p / g.r, j = p % g.r;
+    const uint16_t* xr = g.x + (int64_t)m * g.K;
+    const uint16_t* ar = g.A + (int64_t)j * g.K;
+    float sum = 0.f;
+#pragma unroll 8
+    for (int64_t ch = ch0; ch < ch1; ++ch) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + 8 * ch);
+      const u32x4 av = *reinterpret_cast<const u32x4*>(ar + 8 * ch);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sum = __builtin_fmaf(__uint_as_float(xv[q] << 16), __uint_as_float(av[q] << 16), sum);
+        sum = __builtin_fmaf(__uint_as_float(xv[q] & 0xFFFF0000u), __uint_as_float(av[q] & 0xFFFF0000u), sum);
+      }
+    }
+    dst[p] = sum;
+  }
+}
+
+// The chunk range of item (rb, split) for u_share: the split's columns [step s_begin, step s_end)
+// (clipped at K) in 8-column chunks, cut into w_blocks runs of near-equal length.
+__device__ __forceinline__ void u_chunks(const SkinnyArgs& g, int64_t step, int s_begin, int s_end, int rb,
+                                         int64_t& ch0, int64_t& ch1) {
+  const int64_t lo = (int64_t)s_begin * step / 8, hi = min((int64_t)s_end * step, g.K) / 8;
+  const int64_t n = hi > lo ? hi - lo : 0;
+  ch0 = lo + n * rb / g.p.w_blocks;
+  ch1 = lo + n * (rb + 1) / g.p.w_blocks;
+}
 
 __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyArgs g) {
   __shared__ __attribute__((aligned(16))) f32x2 tab[256 * 32];
@@ -105,16 +141,11 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
       (void*)g.scale_q, (short)0, (int)((nblocks + 3) & ~int64_t(3)), kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rs_c2 = __builtin_amdgcn_make_buffer_rsrc(
       (void*)g.scale_c2, (short)0, (int)(((nblocks + kGroup - 1) / kGroup) * 4), kRsrcFlags);
-  // adapter slice of this wave: tile rb of A, 32-column slice (ai, ad) = (w / 4, w % 4) of each step
-  const bool a_live = rb * 16 < g.r;
-  const int64_t arow = min((int64_t)rb * 16 + m, (int64_t)g.r - 1);
-  const int ai = wave >> 2, ad = wave & 3;
   // per-lane bases, so that the step loop works with 32-bit offsets (the block count of W is
   // below 2^31, so block indices fit)
   const int kb = (int)(g.K / kBlock);                         // blocks per row
   const uint32_t rowb = (uint32_t)(rowc * kb);                // first block of this lane's row
   const uint8_t* prow = g.packed + (int64_t)rowb * 32 + 16 * (grp & 1);
-  const uint16_t* arp = g.A + arow * g.K;
   // block of instruction i of this lane in step s, within the row (clamped: blocks past K re-read
   // the row's last block, whose activations are zeros)
   auto blk_of = [&](int s, int i) { return min(s * 8 + 2 * i + (grp >> 1), kb - 1); };
@@ -131,10 +162,6 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
     ss.cw = __builtin_amdgcn_raw_buffer_load_b128(rs_q, b0 & ~3u, 0, 0);
     ss.c2 = __builtin_amdgcn_raw_buffer_load_b64(rs_c2, (b0 >> 8) * 4u, 0, 0);
   };
-  auto load_a = [&](int s, SkinnyS& ss) {
-    const uint32_t ak = (uint32_t)min((int64_t)s * kStep + 128 * ai + 32 * grp + 8 * ad, g.K - 8);
-    ss.a = *reinterpret_cast<const u32x4*>(arp + ak);
-  };
 
   // activation copy: thread t moves token t / 64, slot t % 64 (source chunk slot ^ token)
   const int xt = tid >> 6, xslot = tid & 63, xchunk = xslot ^ xt;
@@ -149,7 +176,6 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
   };
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 accu = f32x4{0.f, 0.f, 0.f, 0.f};
   const char* tab_bytes = reinterpret_cast<const char*>(tab);
 
   // process step s; with `more`, the small operands of step s + 1 are loaded as soon as those of
@@ -195,11 +221,6 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (a_live) {
-      const bf16x8 bx = __builtin_bit_cast(bf16x8, xsv[m * 64 + ((16 * ai + 4 * grp + ad) ^ m)]);
-      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ss.a), bx, accu, 0, 0, 0);
-    }
-    if (more) load_a(s + 1, ss);
   };
 
   // Phase of step s (parity p = (s - s_begin) % 2): the activations and packed weight of s + 1 are
@@ -215,7 +236,9 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
     const u32x4 x0 = load_x(s_begin);
     load_w(s_begin, w[0]);
     load_scales(s_begin, ss);
-    load_a(s_begin, ss);
+    int64_t ch0, ch1;
+    u_chunks(g, kStep, s_begin, s_end, rb, ch0, ch1);
+    u_share(g, ch0, ch1, tid, g.upart + (int64_t)blockIdx.x * g.M * g.r);
     store_x(s_begin, xs[0], x0);
   }
   __syncthreads();   // the pair table and the first activation stage are in place
@@ -248,11 +271,6 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
       const int64_t r_out = (int64_t)rb * kSkRows + wave * 16 + 4 * grp + i;
       if (r_out < g.N) g.part[((int64_t)split * g.M + m) * g.N + r_out] = acc[i];
     }
-    if (a_live) {
-      float* dst = g.upart + ((int64_t)split * kSkWaves + wave) * g.M * g.r + (int64_t)m * g.r;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[rb * 16 + 4 * grp + i] = accu[i];
-    }
   }
 }
 
@@ -279,10 +297,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
 //   * the lane's four blocks of a step (one per window) lie 4 apart in one 16-byte window of scale
 //     codes (whose start is shifted per lane by a whole dword so that it covers them); blocks past
 //     the row's end get a zero scale (their activation columns are zeros as well);
-//   * activations (4 tokens x 2048 columns, 16 KB) go through LDS one step ahead, as in the 16-row
-//     kernel; the r rows of A ride along in the items of row block b < r / 16: wave w multiplies
-//     the A rows 16 b + 4 (w / 4) .. + 3 against the activation fragment (q, d = w % 4) of every
-//     window, with the same diagonal layout;
+//   * activations (4 tokens x 2048 columns, 16 KB) go through LDS one step ahead, and every item
+//     forms its share of u, as in the 16-row kernel;
 //   * with fp32 block scales (no double quantisation) the lane loads its four blocks' scales
 //     directly (F32S);
 //   * the split partials go to the 16-row kernel's epilogue.
@@ -295,7 +311,6 @@ struct Skinny4W {
 struct Skinny4S {
   u32x4 cw;        // 16 scale codes: the lane's block of window q is byte p + 4 q
   u32x2 c2;        // second-level constants of the step's first group and the next one
-  u32x4 a[4];      // adapter fragments of the four windows
 };
 
 template <bool F32S>
@@ -342,11 +357,6 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
   const uint32_t e0 = (rowb & 3u) + (uint32_t)(2 * kb2 + (c >> 1));   // 0..6
   const uint32_t wsh = (e0 >> 2) * 4u, pbyte = e0 & 3u;
   const uint32_t gsel = pbyte | ((pbyte + 4u) << 8);                  // bytes p of two dwords
-  // adapter rows of this wave (items of row block rb < r / 16)
-  const bool a_live = rb * 16 < g.r;
-  const int64_t arow = min((int64_t)rb * 16 + 4 * (wave >> 2) + rho, (int64_t)g.r - 1);
-  const int dA = wave & 3;
-  const uint16_t* arp = g.A + arow * g.K;
 
   auto load_w = [&](int s, Skinny4W& st) {
 #pragma unroll
@@ -365,12 +375,6 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
       ss.c2 = __builtin_amdgcn_raw_buffer_load_b64(rs_c2, ((rowb + (uint32_t)(32 * s)) >> 8) * 4u, 0, 0);
     }
   };
-  auto a_col = [&](int s, int q) {
-    return (uint32_t)min((int64_t)s * kS4Step + 256 * (q + 4 * hh) + 128 * kb2 + 32 * c + 8 * dA, g.K - 8);
-  };
-  auto load_a = [&](int s, int q, Skinny4S& ss) {
-    ss.a[q] = *reinterpret_cast<const u32x4*>(arp + a_col(s, q));
-  };
 
   // activation copy: thread t moves token t / 256, chunk t % 256 (slot chunk ^ token)
   const int xt = tid >> 8, xch = tid & 255;
@@ -387,7 +391,6 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
   const int xbase = rho * 256 + 128 * hh + 16 * kb2 + 4 * c;
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 accu = f32x4{0.f, 0.f, 0.f, 0.f};
   const char* tab_bytes = reinterpret_cast<const char*>(tab);
 
   auto process = [&](int s, const Skinny4W& st, Skinny4W& nx, Skinny4S& ss, const u32x4* xsv, bool more) {
@@ -438,11 +441,6 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, (u32x4{a[0], a[1], a[2], a[3]})),
                                                       bx, acc, 0, 0, 0);
       }
-      if (a_live) {
-        const bf16x8 bx = __builtin_bit_cast(bf16x8, xsv[xbase + 32 * q + (dA ^ rho)]);
-        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ss.a[q]), bx, accu, 0, 0, 0);
-        if (more) load_a(s + 1, q, ss);
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -453,10 +451,9 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
     const u32x4 x0 = load_x(s_begin);
     load_w(s_begin, w[0]);
     load_scales(s_begin, ss);
-    if (a_live) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) load_a(s_begin, q, ss);
-    }
+    int64_t ch0, ch1;
+    u_chunks(g, kS4Step, s_begin, s_end, rb, ch0, ch1);
+    u_share(g, ch0, ch1, tid, g.upart + (int64_t)blockIdx.x * g.M * g.r);
     store_x(s_begin, xs[0], x0);
   }
   __syncthreads();   // the pair table and the first activation stage are in place
@@ -488,14 +485,9 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
     return d;
   };
   const float yv = diag_sum(acc);
-  const float uv = diag_sum(accu);
   if (c == 0 && rho < g.M) {
     const int64_t r_out = (int64_t)rb * kS4Rows + wave * 4 + kg;
     if (r_out < g.N) g.part[((int64_t)split * g.M + rho) * g.N + r_out] = yv;
-    if (a_live) {
-      const int ar = rb * 16 + 4 * (wave >> 2) + kg;
-      g.upart[(((int64_t)split * 4 + dA) * g.M + rho) * g.r + ar] = uv;
-    }
   }
 }
 
@@ -575,8 +567,7 @@ SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r) {
   const int rows = p.narrow ? kS4Rows : kSkRows;
   const int64_t step = p.narrow ? kS4Step : kStep;
   const int64_t nsteps = (K + step - 1) / step;
-  // every 16-row tile of A needs a row block to ride along with
-  p.w_blocks = (int)max((N + rows - 1) / rows, (int64_t)(r / 16));
+  p.w_blocks = (int)((N + rows - 1) / rows);
   int64_t want = kSkSlots / p.w_blocks;
   if (want > nsteps) want = nsteps;
   if (want < 1) want = 1;
@@ -585,8 +576,8 @@ SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r) {
   return p;
 }
 
-// u partial sums per split: one per wave (16-row kernel) or one per activation dword (M <= 4)
-static int skinny_u_parts(const SkinnyPlan& p) { return p.w_splits * (p.narrow ? 4 : kSkWaves); }
+// u partial sums: one per item
+static int skinny_u_parts(const SkinnyPlan& p) { return p.w_splits * p.w_blocks; }
 
 static size_t skinny_wpart_floats(const SkinnyPlan& p, int64_t M, int64_t N) {
   // the u partials start on a 16-byte boundary
