@@ -164,16 +164,16 @@ def test_fwd_validation():
 
 def _skinny_fwd_bytes(M, N, K, r):
     """Forward workspace of the few-token path, from its documented plan: M <= 4 takes 64-row
-    blocks and 2048-column steps with one u partial per activation dword (4 per split), larger M
-    256-row blocks and 512-column steps with one u partial per wave (16 per split); the row blocks
-    times the k splits fill 256 workgroups at most, and u plus the partials come first."""
-    rows, step, uper = (64, 2048, 4) if M <= 4 else (256, 512, 16)
+    blocks and 2048-column steps, larger M 256-row blocks and 512-column steps; the row blocks
+    times the k splits (the items) fill 256 workgroups at most, every item leaves one partial sum
+    of u, and u plus the partials come first."""
+    rows, step = (64, 2048) if M <= 4 else (256, 512)
     nsteps = -(-K // step)
-    blocks = max(-(-N // rows), r // 16)
+    blocks = -(-N // rows)
     want = min(max(256 // blocks, 1), nsteps)
     sub = -(-nsteps // want)
     splits = -(-nsteps // sub)
-    part = ((splits * M * N + 3) // 4) * 4 + splits * uper * M * r
+    part = ((splits * M * N + 3) // 4) * 4 + splits * blocks * M * r
     up = lambda v: (v + 255) // 256 * 256  # noqa: E731
     return up(M * r * 4) + up(part * 4)
 
