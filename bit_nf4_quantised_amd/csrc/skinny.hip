@@ -74,19 +74,22 @@ struct SkinnyS {
 };
 
 // This item's partial sums of u = x A^T: the 8-column chunks [ch0, ch1) of the contraction, for
-// every token m < M and row j < r. Thread t sums the pairs p = (m, j) = (p / r, p % r), p = t, t +
-// 1024, ..., over its chunks in column order, so each partial is formed in one fixed order; the
-// sums go to dst[m r + j].
+// every token m < M and row j < r (pair p = m r + j). With P = M r pairs below 1024, the chunks are
+// cut into S = min(1024 / P, ch1 - ch0) runs, thread t sums run t / P of pair t % P in column order
+// into stage[t] (LDS), and after the workgroup barrier u_share_finish adds the S runs of a pair in
+// run order; with more pairs, each thread sums whole pairs (t, t + 1024, ...) straight into dst.
+// Either way each partial has one fixed order. The loads go out right after the item's first
+// weight loads, one chunk per thread at the sizes that matter, so they add no round trip of their own.
 __device__ __forceinline__ void u_share(const SkinnyArgs& g, int64_t ch0, int64_t ch1, int tid,
-                                        float* __restrict__ dst) {
+                                        float* __restrict__ stage, float* __restrict__ dst) {
   const int pairs = (int)g.M * g.r;
-  for (int p = tid; p < pairs; p += kSkWaves * 64) {
+  auto sum_run = [&](int p, int64_t c0, int64_t c1) {
     const int m = p / g.r, j = p % g.r;
     const uint16_t* xr = g.x + (int64_t)m * g.K;
     const uint16_t* ar = g.A + (int64_t)j * g.K;
     float sum = 0.f;
-#pragma unroll 8
-    for (int64_t ch = ch0; ch < ch1; ++ch) {
+#pragma unroll 4
+    for (int64_t ch = c0; ch < c1; ++ch) {
       const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + 8 * ch);
       const u32x4 av = *reinterpret_cast<const u32x4*>(ar + 8 * ch);
 #pragma unroll
@@ -95,8 +98,27 @@ __device__ __forceinline__ void u_share(const SkinnyArgs& g, int64_t ch0, int64_
         sum = __builtin_fmaf(__uint_as_float(xv[q] & 0xFFFF0000u), __uint_as_float(av[q] & 0xFFFF0000u), sum);
       }
     }
-    dst[p] = sum;
+    return sum;
+  };
+  if (pairs >= kSkWaves * 64) {
+    for (int p = tid; p < pairs; p += kSkWaves * 64) dst[p] = sum_run(p, ch0, ch1);
+    return;
   }
+  const int64_t n = ch1 - ch0;
+  const int runs = (int)max((int64_t)1, min((int64_t)(kSkWaves * 64 / pairs), n));
+  const int run = tid / pairs;
+  if (run < runs) stage[tid] = sum_run(tid % pairs, ch0 + n * run / runs, ch0 + n * (run + 1) / runs);
+}
+
+// After the barrier that follows u_share: the runs of each pair added in run order.
+__device__ __forceinline__ void u_share_finish(const SkinnyArgs& g, int64_t ch0, int64_t ch1, int tid,
+                                               const float* __restrict__ stage, float* __restrict__ dst) {
+  const int pairs = (int)g.M * g.r;
+  if (pairs >= kSkWaves * 64 || tid >= pairs) return;
+  const int runs = (int)max((int64_t)1, min((int64_t)(kSkWaves * 64 / pairs), ch1 - ch0));
+  float sum = 0.f;
+  for (int run = 0; run < runs; ++run) sum += stage[run * pairs + tid];
+  dst[tid] = sum;
 }
 
 // The chunk range of item (rb, split) for u_share: the split's columns [step s_begin, step s_end)
@@ -113,6 +135,7 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
   __shared__ __attribute__((aligned(16))) f32x2 tab[256 * 32];
   // activation stages: 16 tokens x 64 chunks of 8 bf16
   __shared__ __attribute__((aligned(16))) u32x4 xs[2][16 * 64];
+  __shared__ float ustage[kSkWaves * 64];   // runs of the u partial sums
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4;
@@ -232,16 +255,17 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
   // whose value is never used would make the compiler wait for it before reusing its registers).
   SkinnyW w[2];
   SkinnyS ss;
+  int64_t uch0, uch1;
   {
     const u32x4 x0 = load_x(s_begin);
     load_w(s_begin, w[0]);
     load_scales(s_begin, ss);
-    int64_t ch0, ch1;
-    u_chunks(g, kStep, s_begin, s_end, rb, ch0, ch1);
-    u_share(g, ch0, ch1, tid, g.upart + (int64_t)blockIdx.x * g.M * g.r);
+    u_chunks(g, kStep, s_begin, s_end, rb, uch0, uch1);
+    u_share(g, uch0, uch1, tid, ustage, g.upart + (int64_t)blockIdx.x * g.M * g.r);
     store_x(s_begin, xs[0], x0);
   }
-  __syncthreads();   // the pair table and the first activation stage are in place
+  __syncthreads();   // the pair table, the first activation stage and the u runs are in place
+  u_share_finish(g, uch0, uch1, tid, ustage, g.upart + (int64_t)blockIdx.x * g.M * g.r);
   auto phase = [&](int sp, int p, bool more) {
     u32x4 xn = u32x4{0u, 0u, 0u, 0u};
     if (more) {
@@ -318,6 +342,7 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
   __shared__ __attribute__((aligned(16))) f32x2 tab[256 * 32];
   // activation stages: 4 tokens x 256 chunks of 8 bf16; chunk k of token t sits at slot k ^ t
   __shared__ __attribute__((aligned(16))) u32x4 xs[2][4 * 256];
+  __shared__ float ustage[kSkWaves * 64];   // runs of the u partial sums
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, hh = kg >> 1, kb2 = kg & 1;
@@ -447,16 +472,17 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny4_fwd_kernel(const Skinny
 
   Skinny4W w[2];
   Skinny4S ss;
+  int64_t uch0, uch1;
   {
     const u32x4 x0 = load_x(s_begin);
     load_w(s_begin, w[0]);
     load_scales(s_begin, ss);
-    int64_t ch0, ch1;
-    u_chunks(g, kS4Step, s_begin, s_end, rb, ch0, ch1);
-    u_share(g, ch0, ch1, tid, g.upart + (int64_t)blockIdx.x * g.M * g.r);
+    u_chunks(g, kS4Step, s_begin, s_end, rb, uch0, uch1);
+    u_share(g, uch0, uch1, tid, ustage, g.upart + (int64_t)blockIdx.x * g.M * g.r);
     store_x(s_begin, xs[0], x0);
   }
-  __syncthreads();   // the pair table and the first activation stage are in place
+  __syncthreads();   // the pair table, the first activation stage and the u runs are in place
+  u_share_finish(g, uch0, uch1, tid, ustage, g.upart + (int64_t)blockIdx.x * g.M * g.r);
   auto phase = [&](int sp, int p, bool more) {
     u32x4 xn = u32x4{0u, 0u, 0u, 0u};
     if (more) xn = load_x(sp + 1);
@@ -527,7 +553,7 @@ __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __res
     const int j = tid % r, run = tid / r;
     const int p0 = run * per_run, p1 = min(u_parts, p0 + per_run);
     float s = 0.f;
-#pragma unroll 8
+#pragma unroll 16
     for (int p = p0; p < p1; ++p) s += upart[((int64_t)p * M + mm) * r + j];
     runs[tid] = s;
   }
