@@ -12,10 +12,10 @@
 #include "common.h"
 #include "launch.h"
 
-// The forward's workspace for callers that cannot allocate: 32 MiB of device memory that each GPU
+// The forward's workspace for callers that cannot allocate: 64 MiB of device memory that each GPU
 // the library runs on holds until the process ends. Its name is only a host-side stand-in; host
 // code reaches it through the address hipGetSymbolAddress returns for the current device.
-constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr size_t kScratchBytes = size_t(64) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {

@@ -575,35 +575,48 @@ __global__ __launch_bounds__(256) void gemm_ksum_kernel(const f32x4* __restrict_
   out[i] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
 }
 
-// Contraction ranges of a forward launch: two when the 128-row tiles would number at most 128
-// (at most half of MI355X's 256 CUs busy) and there are at least 8 steps to share; else one. The
-// rule depends on the shapes only, so the workspace size and the launch always agree.
-int fwd_gemm_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t gx = (N + kBN - 1) / kBN;
-  if ((M > 128 && gx * ((M + 255) / 256) >= 192) || M <= 64) return 1;
+// Tile height and contraction ranges of a forward launch (they depend on the shapes only, so the
+// workspace size and the launch always agree):
+//   * 256-row tiles when there are at least 192 of them;
+//   * else, above 128 tokens, 256-row tiles with the contraction cut into ks = 2..4 ranges (at
+//     least 8 steps each) when that makes at least 192 workgroups: a dequantised W tile then
+//     feeds 256 token rows instead of 128, which halves the dequantisation per flop (the k and v
+//     projections of a layer: 1024 output columns);
+//   * else 128-row tiles (64 at most 64 tokens), with two ranges when the 128-row tiles would
+//     number at most 128 (at most half of MI355X's 256 CUs busy) and there are at least 8 steps.
+struct FwdPlan {
+  int bm, ks;
+};
+static FwdPlan fwd_gemm_plan(int64_t M, int64_t N, int64_t K) {
+  const int64_t gx = (N + kBN - 1) / kBN, steps = (K + kBK - 1) / kBK;
+  const int64_t t256 = gx * ((M + 255) / 256);
+  if (M > 128 && t256 >= 192) return {256, 1};
+  if (M > 128) {
+    int64_t ks = min((int64_t)4, min(steps / 8, (256 + t256 - 1) / t256));
+    if (ks > 1 && t256 * ks >= 192) return {256, (int)ks};
+  }
+  if (M <= 64) return {64, 1};
   const int64_t tiles = gx * ((M + 127) / 128);
-  return (tiles <= 128 && (K + kBK - 1) / kBK >= 8) ? 2 : 1;
+  return {128, (tiles <= 128 && steps >= 8) ? 2 : 1};
 }
 
+int fwd_gemm_splits(int64_t M, int64_t N, int64_t K) { return fwd_gemm_plan(M, N, K).ks; }
+
+// bm: tile height (256, 128 or 64); g.ksplit contraction ranges, their partial sums added by
+// gemm_ksum_kernel in range order
 template <bool DX, bool F32S>
-static hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t stream) {
+static hipError_t launch_gemm_t(const GemmArgs& g, int bm, hipStream_t stream) {
   const int64_t Nout = DX ? g.K : g.N;
   const int gx = (int)((Nout + kBN - 1) / kBN);
-  const int64_t tiles256 = (int64_t)gx * ((g.M + 255) / 256);
-  if (g.M > 128 && tiles256 >= 192) {
-    const int gy = (int)((g.M + 255) / 256);
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 256, F32S>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
-  } else if (g.M > 64) {
-    const int gy = (int)((g.M + 127) / 128);
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 128, F32S>), dim3(gx, gy * g.ksplit), dim3(kThreads), 0, stream, g);
-    if (g.ksplit > 1) {
-      const int64_t n4 = g.M * Nout / 4;
-      hipLaunchKernelGGL(gemm_ksum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                         (const f32x4*)g.part, n4, g.ksplit, reinterpret_cast<u32x2*>(g.out));
-    }
-  } else {
-    const int gy = (int)((g.M + 63) / 64);
-    hipLaunchKernelGGL((qlora_gemm_kernel<DX, 64, F32S>), dim3(gx, gy), dim3(kThreads), 0, stream, g);
+  const int gy = (int)((g.M + bm - 1) / bm);
+  const dim3 grid(gx, gy * g.ksplit);
+  if (bm == 256) hipLaunchKernelGGL((qlora_gemm_kernel<DX, 256, F32S>), grid, dim3(kThreads), 0, stream, g);
+  else if (bm == 128) hipLaunchKernelGGL((qlora_gemm_kernel<DX, 128, F32S>), grid, dim3(kThreads), 0, stream, g);
+  else hipLaunchKernelGGL((qlora_gemm_kernel<DX, 64, F32S>), grid, dim3(kThreads), 0, stream, g);
+  if (g.ksplit > 1) {
+    const int64_t n4 = g.M * Nout / 4;
+    hipLaunchKernelGGL(gemm_ksum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                       (const f32x4*)g.part, n4, g.ksplit, reinterpret_cast<u32x2*>(g.out));
   }
   return hipGetLastError();
 }
@@ -612,10 +625,15 @@ hipError_t launch_fwd_gemm(const uint8_t* packed, const uint8_t* scale_q, const 
                            const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                            const float* u, const uint16_t* B, int r, float scale, uint16_t* y,
                            float* part, int book, hipStream_t stream) {
-  const int ks = part ? fwd_gemm_splits(M, N, K) : 1;
-  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, x, M, u, B, r, scale, y, ks, part, {}};
+  FwdPlan p = fwd_gemm_plan(M, N, K);
+  if (!part) {   // no room for partial sums: one contraction range, at the tile height the plan
+    p.ks = 1;    // takes without splitting
+    const int64_t gx = (N + kBN - 1) / kBN;
+    p.bm = (M > 128 && gx * ((M + 255) / 256) >= 192) ? 256 : M > 64 ? 128 : 64;
+  }
+  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, x, M, u, B, r, scale, y, p.ks, part, {}};
   if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
-  return absmax ? launch_gemm_t<false, true>(g, stream) : launch_gemm_t<false, false>(g, stream);
+  return absmax ? launch_gemm_t<false, true>(g, p.bm, stream) : launch_gemm_t<false, false>(g, p.bm, stream);
 }
 
 hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
@@ -624,7 +642,9 @@ hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const f
                           int book, hipStream_t stream) {
   GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, dy, M, v, A, r, scale, dx, 1, nullptr, {}};
   if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
-  return absmax ? launch_gemm_t<true, true>(g, stream) : launch_gemm_t<true, false>(g, stream);
+  const int64_t gx = (K + kBN - 1) / kBN;
+  const int bm = (M > 128 && gx * ((M + 255) / 256) >= 192) ? 256 : M > 64 ? 128 : 64;
+  return absmax ? launch_gemm_t<true, true>(g, bm, stream) : launch_gemm_t<true, false>(g, bm, stream);
 }
 
 }  // namespace nf4

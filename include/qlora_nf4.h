@@ -155,14 +155,14 @@ int qlora_linear_fwd(const nf4_weight *W, const uint16_t *x, int64_t M, const ui
 
 /* qlora_linear_fwd for callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the same launches and the same outputs,
- * bit for bit, with the workspace taken from a 32 MiB array inside the library instead of `ws`.
+ * bit for bit, with the workspace taken from a 64 MiB array inside the library instead of `ws`.
  * Each GPU the library runs on holds its own copy of that array until the process ends; its
  * device address is looked up (hipGetSymbolAddress) on the first call on that device. The call
  * allocates nothing, and nothing in the array needs clearing: every launch overwrites what it
  * reads. All calls on one GPU share its array, so calls that overlap on one GPU (other streams or
  * threads without ordering between them) race.
  * Errors as qlora_linear_fwd; NF4_ERR_WORKSPACE when the forward's workspace for these sizes
- * (with u kept in it when u_out is NULL) exceeds 32 MiB; NF4_ERR_HIP when the array's address
+ * (with u kept in it when u_out is NULL) exceeds 64 MiB; NF4_ERR_HIP when the array's address
  * cannot be obtained. */
 int qlora_linear_fwd_noalloc(const nf4_weight *W, const uint16_t *x, int64_t M, const uint16_t *A,
                              const uint16_t *B, int32_t r, float scale, uint16_t *y, float *u_out,

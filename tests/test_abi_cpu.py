@@ -190,6 +190,38 @@ def test_skinny_workspace_follows_the_plan(M, N, K, r):
         q.NF4_ERR_WORKSPACE
 
 
+def _gemm_fwd_bytes(M, N, K, r):
+    """Forward workspace of the fused-GEMM path (M > 16), from its documented plan: 256-row tiles
+    when there are at least 192 of them; else, above 128 tokens, 256-row tiles with ks = 2..4
+    contraction ranges of at least 8 steps when that makes at least 192 workgroups; else 128-row
+    tiles (64 at most 64 tokens) with two ranges when they number at most 128 and there are 8
+    steps. Each range beyond one leaves M x N fp32 partial sums; u comes first. (At rank 16 the
+    adapter's u needs no partial sums of its own.)"""
+    gx, steps = -(-N // 128), -(-K // 64)
+    t256 = gx * -(-M // 256)
+    ks = 1
+    if M > 128 and t256 >= 192:
+        ks = 1
+    elif M > 128 and min(4, steps // 8, -(-256 // t256)) > 1 and t256 * min(4, steps // 8, -(-256 // t256)) >= 192:
+        ks = min(4, steps // 8, -(-256 // t256))
+    elif M > 64:
+        ks = 2 if gx * -(-M // 128) <= 128 and steps >= 8 else 1
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    return up(M * r * 4) + (up(ks * M * N * 4) if ks > 1 else 0), ks
+
+
+@pytest.mark.parametrize("M,N,K,ks", [(2048, 1024, 4096, 4), (4096, 1024, 8192, 2), (1500, 1040, 2112, 4),
+                                      (2048, 4096, 4096, 1), (300, 400, 960, 2), (1800, 128, 14336, 2)])
+def test_gemm_workspace_follows_the_plan(M, N, K, ks):
+    need, plan_ks = _gemm_fwd_bytes(M, N, K, 16)
+    assert plan_ks == ks
+    assert q.qlora_workspace_bytes(M, N, K, 16) >= need
+    if ks > 1:   # one byte less than u plus the partial sums is refused before any launch
+        w = ctypes.byref(_w(N=N, K=K))
+        assert lib.qlora_linear_fwd(w, FAKE, M, FAKE, FAKE, 16, 2.0, FAKE, None, FAKE, need - 1, None) == \
+            q.NF4_ERR_WORKSPACE
+
+
 def test_recompute_validation():
     w = ctypes.byref(_w())
     f = lib.qlora_linear_fwd_recompute

@@ -71,6 +71,8 @@ def test_single_linear_workload():
     (4, 208, 16448, 16, 2.0),      #   257 blocks per row: groups of 256 blocks split steps
     (1800, 14336, 128, 16, 2.0),   # forward: 896 tiles of 256 rows, ragged last row block
     (1800, 128, 14336, 16, 2.0),   # the same for the dX GEMM (14336 output columns)
+    (1500, 1040, 2112, 16, 2.0),   # 256-row tiles with the contraction in 4 ranges (54 tiles, the
+    (1536, 1024, 2048, 64, 0.5),   #   last range shorter), ragged rows and columns; then exact fit
     # ranks that are not a power of two: the adapter kernels, the fused GEMMs' partial adapter steps
     # (r > 64: two steps, the second partial) and the few-token epilogue's u runs (256 / r rounds down)
     (300, 400, 960, 48, 1.0),      #   GEMM with a split contraction
@@ -183,6 +185,7 @@ def _f32s_weight(w):
     (4, 96, 4160, 32, 1.0),        #   65 blocks per row, a 64-column last step
     (3, 1040, 1088, 128, 0.5),     #   rank 128, ragged rows
     (2048, 4096, 4096, 16, 2.0),   # the q/o shape of the 8B layer set
+    (1500, 1040, 2112, 16, 2.0),   # 256-row tiles, contraction in 4 ranges
 ])
 def test_fp32_scale_weight_matches_oracle(M, N, K, r, s):
     from gpu_helpers import gpu_dequant

@@ -58,7 +58,7 @@ def test_noalloc_forward_equals_the_workspace_forward_on_consecutive_calls():
 
 def test_noalloc_forward_refuses_a_workspace_past_the_array():
     import bit_nf4_quantised_amd as q
-    # 16 tokens of a 2^21 x 64 weight: 128 MiB of split partials, past the 32 MiB array
+    # 16 tokens of a 2^21 x 64 weight: 128 MiB of split partials, past the 64 MiB array
     cw = q.CNF4Weight(0x100000, 0x100000, 0x100000, 1 << 21, 64)
     st = q.lib.qlora_linear_fwd_noalloc(ctypes.byref(cw), 0x100000, 16, 0x100000, 0x100000, 16, 1.0, 0x100000,
                                         None, None)
