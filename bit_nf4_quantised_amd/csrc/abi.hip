@@ -57,12 +57,12 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 // Workspace layout (bytes, each region 256-aligned):
 //   forward : [u (M*r fp32)] [partials: the skinny path's splits, or (in turn) those of u above rank
 //             16 and the GEMM's contraction ranges]
-//   backward: [v (M*r fp32)] [partials of the pass over dY, then of the pass over X]
+//   backward: [v (M*r fp32)] [partials of the pass over dY, then of the dX GEMM's tail, then of the
+//             pass over X (each launch's partials are consumed before the next one writes)]
 size_t fwd_part_floats(int64_t M, int64_t N, int64_t K, int r) {
   if (nf4::skinny_eligible(M, N, K)) return nf4::skinny_workspace_floats(M, N, K, r);
   // the split GEMM's partial sums, after the partial sums of u (the two launches run in turn)
-  const int ks = nf4::fwd_gemm_splits(M, N, K);
-  const size_t gemm = ks > 1 ? (size_t)ks * M * N : 0;
+  const size_t gemm = nf4::fwd_gemm_part_floats(M, N, K);
   const size_t lu = nf4::lora_u_uses_pass(r) ? nf4::lora_pass_ws_floats(M, K, r, true, false) : 0;
   return gemm > lu ? gemm : lu;
 }
@@ -72,7 +72,9 @@ size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
 size_t bwd_ws(int64_t M, int64_t N, int64_t K, int r) {
   size_t part = nf4::lora_pass_ws_floats(M, N, r, true, true);
   const size_t ga = nf4::lora_pass_ws_floats(M, K, r, false, true);
+  const size_t gx = nf4::dx_gemm_part_floats(M, N, K);
   if (ga > part) part = ga;
+  if (gx > part) part = gx;
   return align_up((size_t)M * r * 4) + align_up(part * 4);
 }
 
@@ -338,7 +340,7 @@ int qlora_linear_bwd(const nf4_weight* W, const uint16_t* x, const uint16_t* dy,
   if (e != hipSuccess) return NF4_ERR_HIP;
   if (dx) {
     e = nf4::launch_dx_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, dy, M, v, A, r, scale, dx,
-                            W->codebook, stream);
+                            part, W->codebook, stream);
     if (e != hipSuccess) return NF4_ERR_HIP;
   }
   return from_hip(nf4::launch_lora_dx(x, M, K, v, r, scale, accumulate, part, dA, stream));

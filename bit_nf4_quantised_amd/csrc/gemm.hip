@@ -40,7 +40,8 @@
 // A tile's time is set by its number of steps (a step costs the dequantisers' work on one W tile,
 // whatever the tile's height), so halving the steps per workgroup halves it. Each range writes
 // fp32 partial sums; gemm_ksum_kernel adds them in range order and rounds to bf16. The adapter
-// steps ride with the last range.
+// steps ride with the last range. The same cut applied to the last, partial round of tiles only
+// (tail mode, forward and dX) keeps that round from leaving most CUs idle; see GemmPlan.
 //
 // With F32S the weight keeps one fp32 absmax per block instead of double-quantised scales (the
 // baseline of "QLoRA, explained", Double quantisation): the loaders bring that scale where they
@@ -65,8 +66,12 @@ struct GemmArgs {
   int r;
   float scale;
   uint16_t* out;            // y [M x N] (forward) or dX [M x K] (backward), bf16
-  int ksplit;               // contraction ranges (1: none)
-  float* part;              // ksplit x M x Nout fp32 partial sums when ksplit > 1
+  int ksplit;               // contraction ranges of every tile (1: none)
+  float* part;              // ksplit x M x Nout fp32 partial sums when ksplit > 1; the tail's
+                            // pieces otherwise (tail_split x tail_tiles x BM x kBN, tile-major)
+  int whole_tiles;          // tail mode (tail_tiles > 0): tiles 0 .. whole_tiles - 1 whole,
+  int tail_tiles;           //   the last tail_tiles tiles cut into tail_split contraction ranges
+  int tail_split;
   Codes codes;              // the values the 4-bit indices select
 };
 
@@ -135,25 +140,47 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // Tile coordinates; workgroups are dealt round-robin over the 8 XCDs, so give each XCD a
-  // contiguous run of tiles that share an activation row block.
-  // The contraction range is the slowest index, so the ranges of a tile go to different XCDs.
-  const int gx = gridDim.x, total = gridDim.x * gridDim.y;
-  int lin = blockIdx.x + gx * blockIdx.y;
-  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
-  const int tiles = total / g.ksplit;
-  const int split = lin / tiles;
-  lin %= tiles;
-  const int64_t col0 = (int64_t)(lin % gx) * kBN;
-  const int64_t m0 = (int64_t)(lin / gx) * BM;
-
   const int64_t Lc = DX ? g.N : g.K;       // contraction length
   const int64_t Nout = DX ? g.K : g.N;     // output columns
+  const int gx = (int)((Nout + kBN - 1) / kBN);   // column tiles
+
+  // Tile coordinates. Workgroups are dealt round-robin over the 8 XCDs (workgroup i to XCD i % 8,
+  // in order of i), so each XCD gets a contiguous run of tiles that share an activation row block.
+  // Uniform split: the contraction range is the slowest index, so the ranges of a tile go to
+  // different XCDs. Tail mode (the tiles past the last whole round of the CUs cut into ranges, so
+  // that the last round is full): each XCD first takes its share of the whole tiles, then its
+  // share of the tail's pieces.
+  const int total = gridDim.x * gridDim.y;
+  const int bid = blockIdx.x + gridDim.x * blockIdx.y;
+  int tile, split = 0, nsplit = g.ksplit, tail_r = 0;
+  if (g.tail_tiles > 0) {
+    const int xcd = bid & 7, k = bid >> 3;
+    const int wx = g.whole_tiles >> 3, px = (g.tail_tiles * g.tail_split) >> 3;
+    if (k < wx) {
+      tile = xcd * wx + k;
+      nsplit = 1;
+    } else {
+      const int piece = xcd * px + (k - wx);
+      tail_r = piece / g.tail_split;
+      split = piece % g.tail_split;
+      tile = g.whole_tiles + tail_r;
+      nsplit = g.tail_split;
+    }
+  } else {
+    int lin = bid;
+    if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+    const int tiles = total / g.ksplit;
+    split = lin / tiles;
+    tile = lin % tiles;
+  }
+  const int64_t col0 = (int64_t)(tile % gx) * kBN;
+  const int64_t m0 = (int64_t)(tile / gx) * BM;
+
   const int main_total = (int)((Lc + kBK - 1) / kBK);
-  const int per_split = (main_total + g.ksplit - 1) / g.ksplit;
+  const int per_split = (main_total + nsplit - 1) / nsplit;
   const int T0 = split * per_split;        // first contraction step of this range
   const int main_steps = min(per_split, main_total - T0);
-  const int lora_steps = split == g.ksplit - 1 ? (g.r + kBK - 1) / kBK : 0;
+  const int lora_steps = split == nsplit - 1 ? (g.r + kBK - 1) / kBK : 0;
   const int steps = main_steps + lora_steps;
   const uint32_t kb = (uint32_t)(g.K / kBlock);   // blocks per row of W
 
@@ -513,10 +540,15 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
   if (s + 4 < steps) { compute(c1, c0); lds_barrier(); }
 
   // ---------------------------------------------------------------- epilogue
-  if (g.ksplit > 1) {
+  if (nsplit > 1) {
     // fp32 partial sums of this contraction range, straight from the accumulators (lane: one row,
-    // four consecutive columns per group of four registers)
-    float* pp = g.part + (int64_t)split * g.M * Nout;
+    // four consecutive columns per group of four registers): [range][M][Nout] for a uniform split,
+    // [range][tail tile][BM][kBN] for a tail piece
+    const bool tail = g.tail_tiles > 0;
+    float* pp = tail ? g.part + ((int64_t)split * g.tail_tiles + tail_r) * (BM * kBN)
+                     : g.part + (int64_t)split * g.M * Nout;
+    const int64_t pitch = tail ? kBN : Nout;
+    const int64_t r0 = tail ? m0 : 0, c0 = tail ? col0 : 0;
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
@@ -527,7 +559,8 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
         for (int rq = 0; rq < 4; ++rq) {
           const int64_t n = col0 + wn0 + tn * 32 + 8 * rq + 4 * (lane >> 5);
           if (m < g.M && n < Nout)
-            *reinterpret_cast<f32x4*>(pp + m * Nout + n) = f32x4{a[4 * rq], a[4 * rq + 1], a[4 * rq + 2], a[4 * rq + 3]};
+            *reinterpret_cast<f32x4*>(pp + (m - r0) * pitch + (n - c0)) =
+                f32x4{a[4 * rq], a[4 * rq + 1], a[4 * rq + 2], a[4 * rq + 3]};
         }
       }
     return;
@@ -575,76 +608,169 @@ __global__ __launch_bounds__(256) void gemm_ksum_kernel(const f32x4* __restrict_
   out[i] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
 }
 
-// Tile height and contraction ranges of a forward launch (they depend on the shapes only, so the
-// workspace size and the launch always agree):
-//   * 256-row tiles when there are at least 192 of them;
+// Sum of the tail pieces' partial sums (tile-major: [range][tail tile][bm][kBN]), in range order,
+// rounded to bf16. Workgroup w takes 32 rows of tail tile w / (bm / 32) (tile first + that); a
+// thread 4 groups of 4 values, all loads of all ranges in flight together. Rows past M and columns
+// past Nout were never written and are skipped.
+constexpr int kKsumRows = 32;
+template <int NS>
+__global__ __launch_bounds__(256) void gemm_ksum_tail_kernel(const f32x4* __restrict__ part, int tail, int first,
+                                                             int gx, int bm, int64_t M, int64_t Nout,
+                                                             u32x2* __restrict__ out) {
+  const int per_tile = bm / kKsumRows;
+  const int tr = blockIdx.x / per_tile, rs = blockIdx.x % per_tile, tile = first + tr;
+  const int64_t m0 = (int64_t)(tile / gx) * bm + rs * kKsumRows, c0 = (int64_t)(tile % gx) * kBN;
+  const int per = bm * kBN / 4;   // 4-value groups per tile
+  const f32x4* src = part + (int64_t)tr * per + rs * kKsumRows * (kBN / 4);
+  f32x4 v[NS][4];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[s][i] = src[(int64_t)s * tail * per + threadIdx.x + 256 * i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    const int64_t m = m0 + e / (kBN / 4), n = c0 + 4 * (e % (kBN / 4));
+    f32x4 a = v[0][i];
+#pragma unroll
+    for (int s = 1; s < NS; ++s) a = f32x4{a[0] + v[s][i][0], a[1] + v[s][i][1], a[2] + v[s][i][2], a[3] + v[s][i][3]};
+    if (m < M && n < Nout) out[(m * Nout + n) / 4] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+  }
+}
+
+// A launch plan of the fused GEMM (it depends on the shapes only, so the workspace size and the
+// launch always agree): the tile height, contraction ranges of every tile (uniform split), and the
+// tail. With one workgroup per CU, T tiles take ceil(T / 256) rounds of the 256 CUs; past the last
+// whole round the other R = T mod 256 tiles would leave 256 - R CUs idle for a whole tile's time.
+// Tail mode cuts each of those R tiles into s = 2..4 contraction ranges (at least 8 steps each),
+// so the last round holds R s shorter pieces; gemm_ksum_tail_kernel then adds them. The forward:
+//   * 256-row tiles when there are at least 192 of them (then the tail, when R <= 128);
 //   * else, above 128 tokens, 256-row tiles with the contraction cut into ks = 2..4 ranges (at
 //     least 8 steps each) when that makes at least 192 workgroups: a dequantised W tile then
 //     feeds 256 token rows instead of 128, which halves the dequantisation per flop (the k and v
 //     projections of a layer: 1024 output columns);
 //   * else 128-row tiles (64 at most 64 tokens), with two ranges when the 128-row tiles would
 //     number at most 128 (at most half of MI355X's 256 CUs busy) and there are at least 8 steps.
-struct FwdPlan {
+// The dX GEMM takes 256-row tiles when there are at least 192 of them (with the tail), else 128 or
+// 64, never a uniform split.
+struct GemmPlan {
   int bm, ks;
+  int whole, tail, tsplit;   // tail mode when tail > 0
 };
-static FwdPlan fwd_gemm_plan(int64_t M, int64_t N, int64_t K) {
-  const int64_t gx = (N + kBN - 1) / kBN, steps = (K + kBK - 1) / kBK;
-  const int64_t t256 = gx * ((M + 255) / 256);
-  if (M > 128 && t256 >= 192) return {256, 1};
-  if (M > 128) {
-    int64_t ks = min((int64_t)4, min(steps / 8, (256 + t256 - 1) / t256));
-    if (ks > 1 && t256 * ks >= 192) return {256, (int)ks};
-  }
-  if (M <= 64) return {64, 1};
-  const int64_t tiles = gx * ((M + 127) / 128);
-  return {128, (tiles <= 128 && steps >= 8) ? 2 : 1};
+
+static void plan_tail(GemmPlan& p, int64_t tiles, int64_t steps) {
+  const int64_t R = tiles % 256;
+  if (tiles <= 256 || R == 0) return;
+  const int64_t s = min((int64_t)4, min(256 / R, steps / 8));
+  if (s < 2 || (tiles - R) % 8 || (R * s) % 8) return;   // each XCD takes an equal share of both
+  p.whole = (int)(tiles - R);
+  p.tail = (int)R;
+  p.tsplit = (int)s;
 }
 
-int fwd_gemm_splits(int64_t M, int64_t N, int64_t K) { return fwd_gemm_plan(M, N, K).ks; }
+static GemmPlan fwd_gemm_plan(int64_t M, int64_t N, int64_t K) {
+  GemmPlan p{0, 1, 0, 0, 0};
+  const int64_t gx = (N + kBN - 1) / kBN, steps = (K + kBK - 1) / kBK;
+  const int64_t t256 = gx * ((M + 255) / 256);
+  if (M > 128 && t256 >= 192) {
+    p.bm = 256;
+    plan_tail(p, t256, steps);
+    return p;
+  }
+  if (M > 128) {
+    const int64_t ks = min((int64_t)4, min(steps / 8, (256 + t256 - 1) / t256));
+    if (ks > 1 && t256 * ks >= 192) {
+      p.bm = 256;
+      p.ks = (int)ks;
+      return p;
+    }
+  }
+  if (M <= 64) {
+    p.bm = 64;
+    return p;
+  }
+  const int64_t tiles = gx * ((M + 127) / 128);
+  p.bm = 128;
+  p.ks = (tiles <= 128 && steps >= 8) ? 2 : 1;
+  return p;
+}
 
-// bm: tile height (256, 128 or 64); g.ksplit contraction ranges, their partial sums added by
-// gemm_ksum_kernel in range order
+static GemmPlan dx_gemm_plan(int64_t M, int64_t N, int64_t K) {
+  GemmPlan p{0, 1, 0, 0, 0};
+  const int64_t gx = (K + kBN - 1) / kBN, steps = (N + kBK - 1) / kBK;
+  const int64_t t256 = gx * ((M + 255) / 256);
+  p.bm = (M > 128 && t256 >= 192) ? 256 : M > 64 ? 128 : 64;
+  if (p.bm == 256) plan_tail(p, t256, steps);
+  return p;
+}
+
+static size_t plan_part_floats(const GemmPlan& p, int64_t M, int64_t Nout) {
+  if (p.ks > 1) return (size_t)p.ks * (size_t)M * (size_t)Nout;
+  if (p.tail > 0) return (size_t)p.tsplit * (size_t)p.tail * (size_t)p.bm * kBN;
+  return 0;
+}
+
+size_t fwd_gemm_part_floats(int64_t M, int64_t N, int64_t K) { return plan_part_floats(fwd_gemm_plan(M, N, K), M, N); }
+size_t dx_gemm_part_floats(int64_t M, int64_t N, int64_t K) { return plan_part_floats(dx_gemm_plan(M, N, K), M, K); }
+
 template <bool DX, bool F32S>
-static hipError_t launch_gemm_t(const GemmArgs& g, int bm, hipStream_t stream) {
+static hipError_t launch_gemm_t(GemmArgs g, const GemmPlan& p, hipStream_t stream) {
   const int64_t Nout = DX ? g.K : g.N;
   const int gx = (int)((Nout + kBN - 1) / kBN);
-  const int gy = (int)((g.M + bm - 1) / bm);
-  const dim3 grid(gx, gy * g.ksplit);
-  if (bm == 256) hipLaunchKernelGGL((qlora_gemm_kernel<DX, 256, F32S>), grid, dim3(kThreads), 0, stream, g);
-  else if (bm == 128) hipLaunchKernelGGL((qlora_gemm_kernel<DX, 128, F32S>), grid, dim3(kThreads), 0, stream, g);
+  const int gy = (int)((g.M + p.bm - 1) / p.bm);
+  g.ksplit = p.ks;
+  g.whole_tiles = p.whole;
+  g.tail_tiles = p.tail;
+  g.tail_split = p.tsplit;
+  const dim3 grid = p.tail > 0 ? dim3((unsigned)(p.whole + p.tail * p.tsplit)) : dim3(gx, gy * p.ks);
+  if (p.bm == 256) hipLaunchKernelGGL((qlora_gemm_kernel<DX, 256, F32S>), grid, dim3(kThreads), 0, stream, g);
+  else if (p.bm == 128) hipLaunchKernelGGL((qlora_gemm_kernel<DX, 128, F32S>), grid, dim3(kThreads), 0, stream, g);
   else hipLaunchKernelGGL((qlora_gemm_kernel<DX, 64, F32S>), grid, dim3(kThreads), 0, stream, g);
-  if (g.ksplit > 1) {
+  if (p.ks > 1) {
     const int64_t n4 = g.M * Nout / 4;
     hipLaunchKernelGGL(gemm_ksum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                       (const f32x4*)g.part, n4, g.ksplit, reinterpret_cast<u32x2*>(g.out));
+                       (const f32x4*)g.part, n4, p.ks, reinterpret_cast<u32x2*>(g.out));
+  } else if (p.tail > 0) {
+    const dim3 kg((unsigned)(p.tail * (p.bm / kKsumRows)));
+    const f32x4* src = (const f32x4*)g.part;
+    u32x2* dst = reinterpret_cast<u32x2*>(g.out);
+    if (p.tsplit == 2) hipLaunchKernelGGL((gemm_ksum_tail_kernel<2>), kg, dim3(256), 0, stream, src, p.tail, p.whole, gx, p.bm, g.M, Nout, dst);
+    else if (p.tsplit == 3) hipLaunchKernelGGL((gemm_ksum_tail_kernel<3>), kg, dim3(256), 0, stream, src, p.tail, p.whole, gx, p.bm, g.M, Nout, dst);
+    else hipLaunchKernelGGL((gemm_ksum_tail_kernel<4>), kg, dim3(256), 0, stream, src, p.tail, p.whole, gx, p.bm, g.M, Nout, dst);
   }
   return hipGetLastError();
+}
+
+// Without room for partial sums (part null): one contraction range for every tile.
+static void plan_without_part(GemmPlan& p) {
+  p.ks = 1;
+  p.whole = p.tail = p.tsplit = 0;
 }
 
 hipError_t launch_fwd_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                            const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                            const float* u, const uint16_t* B, int r, float scale, uint16_t* y,
                            float* part, int book, hipStream_t stream) {
-  FwdPlan p = fwd_gemm_plan(M, N, K);
-  if (!part) {   // no room for partial sums: one contraction range, at the tile height the plan
-    p.ks = 1;    // takes without splitting
+  GemmPlan p = fwd_gemm_plan(M, N, K);
+  if (!part) {   // at the tile height the plan takes without splitting
+    plan_without_part(p);
     const int64_t gx = (N + kBN - 1) / kBN;
     p.bm = (M > 128 && gx * ((M + 255) / 256) >= 192) ? 256 : M > 64 ? 128 : 64;
   }
-  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, x, M, u, B, r, scale, y, p.ks, part, {}};
+  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, x, M, u, B, r, scale, y, 1, part, 0, 0, 0, {}};
   if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
-  return absmax ? launch_gemm_t<false, true>(g, p.bm, stream) : launch_gemm_t<false, false>(g, p.bm, stream);
+  return absmax ? launch_gemm_t<false, true>(g, p, stream) : launch_gemm_t<false, false>(g, p, stream);
 }
 
 hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                           const float* absmax, int64_t N, int64_t K, const uint16_t* dy, int64_t M,
                           const float* v, const uint16_t* A, int r, float scale, uint16_t* dx,
-                          int book, hipStream_t stream) {
-  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, dy, M, v, A, r, scale, dx, 1, nullptr, {}};
+                          float* part, int book, hipStream_t stream) {
+  GemmPlan p = dx_gemm_plan(M, N, K);
+  if (!part) plan_without_part(p);
+  GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, dy, M, v, A, r, scale, dx, 1, part, 0, 0, 0, {}};
   if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
-  const int64_t gx = (K + kBN - 1) / kBN;
-  const int bm = (M > 128 && gx * ((M + 255) / 256) >= 192) ? 256 : M > 64 ? 128 : 64;
-  return absmax ? launch_gemm_t<true, true>(g, bm, stream) : launch_gemm_t<true, false>(g, bm, stream);
+  return absmax ? launch_gemm_t<true, true>(g, p, stream) : launch_gemm_t<true, false>(g, p, stream);
 }
 
 }  // namespace nf4

@@ -33,8 +33,10 @@ hipError_t launch_dequant(const uint8_t* packed, const uint8_t* scale_q, const f
 bool codes_of(int book, Codes& out);
 
 // absmax != null: fp32 scales per block instead of scale_q / scale_c2. part: room for
-// fwd_gemm_splits(M, N, K) x M x N fp32 partial sums, or null (then the launch does not split)
-int fwd_gemm_splits(int64_t M, int64_t N, int64_t K);
+// fwd_gemm_part_floats(M, N, K) (forward) or dx_gemm_part_floats(M, N, K) (dX) fp32 partial sums,
+// or null (then no tile's contraction is split)
+size_t fwd_gemm_part_floats(int64_t M, int64_t N, int64_t K);
+size_t dx_gemm_part_floats(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fwd_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                            const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                            const float* u, const uint16_t* B, int r, float scale, uint16_t* y,
@@ -42,7 +44,7 @@ hipError_t launch_fwd_gemm(const uint8_t* packed, const uint8_t* scale_q, const 
 hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                           const float* absmax, int64_t N, int64_t K, const uint16_t* dy, int64_t M,
                           const float* v, const uint16_t* A, int r, float scale, uint16_t* dx,
-                          int book, hipStream_t stream);
+                          float* part, int book, hipStream_t stream);
 
 // Adapter passes over one bf16 matrix (see lora.hip). Each writes partial results to `ws`
 // (lora_pass_ws_floats floats) and reduces them in a fixed order.

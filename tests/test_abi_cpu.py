@@ -192,26 +192,34 @@ def test_skinny_workspace_follows_the_plan(M, N, K, r):
 
 def _gemm_fwd_bytes(M, N, K, r):
     """Forward workspace of the fused-GEMM path (M > 16), from its documented plan: 256-row tiles
-    when there are at least 192 of them; else, above 128 tokens, 256-row tiles with ks = 2..4
-    contraction ranges of at least 8 steps when that makes at least 192 workgroups; else 128-row
-    tiles (64 at most 64 tokens) with two ranges when they number at most 128 and there are 8
-    steps. Each range beyond one leaves M x N fp32 partial sums; u comes first. (At rank 16 the
-    adapter's u needs no partial sums of its own.)"""
+    when there are at least 192 of them, with the tiles past the last whole round of 256 CUs cut
+    into 2..4 contraction ranges (tile-major partial sums of 256 x 128 per piece); else, above 128
+    tokens, 256-row tiles with ks = 2..4 contraction ranges of at least 8 steps when that makes at
+    least 192 workgroups; else 128-row tiles (64 at most 64 tokens) with two ranges when they
+    number at most 128 and there are 8 steps. A uniform split leaves ks x M x N fp32 partial sums;
+    u comes first. (At rank 16 the adapter's u needs no partial sums of its own.)"""
     gx, steps = -(-N // 128), -(-K // 64)
     t256 = gx * -(-M // 256)
-    ks = 1
+    ks, part = 1, 0
     if M > 128 and t256 >= 192:
-        ks = 1
+        # the tail: the tiles past the last whole round of 256 CUs, cut into 2..4 ranges
+        rem = t256 % 256
+        s = min(4, 256 // rem, steps // 8) if rem else 0
+        if t256 > 256 and rem and s >= 2 and (t256 - rem) % 8 == 0 and (rem * s) % 8 == 0:
+            ks, part = s, s * rem * 256 * 128
     elif M > 128 and min(4, steps // 8, -(-256 // t256)) > 1 and t256 * min(4, steps // 8, -(-256 // t256)) >= 192:
         ks = min(4, steps // 8, -(-256 // t256))
+        part = ks * M * N
     elif M > 64:
         ks = 2 if gx * -(-M // 128) <= 128 and steps >= 8 else 1
+        part = ks * M * N if ks > 1 else 0
     up = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    return up(M * r * 4) + (up(ks * M * N * 4) if ks > 1 else 0), ks
+    return up(M * r * 4) + (up(part * 4) if part else 0), ks
 
 
 @pytest.mark.parametrize("M,N,K,ks", [(2048, 1024, 4096, 4), (4096, 1024, 8192, 2), (1500, 1040, 2112, 4),
-                                      (2048, 4096, 4096, 1), (300, 400, 960, 2), (1800, 128, 14336, 2)])
+                                      (2048, 4096, 4096, 1), (300, 400, 960, 2), (1800, 128, 14336, 2),
+                                      (2048, 14336, 4096, 2), (300, 16512, 2048, 4), (4096, 28672, 8192, 1)])
 def test_gemm_workspace_follows_the_plan(M, N, K, ks):
     need, plan_ks = _gemm_fwd_bytes(M, N, K, 16)
     assert plan_ks == ks

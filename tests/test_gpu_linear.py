@@ -73,6 +73,9 @@ def test_single_linear_workload():
     (1800, 128, 14336, 16, 2.0),   # the same for the dX GEMM (14336 output columns)
     (1500, 1040, 2112, 16, 2.0),   # 256-row tiles with the contraction in 4 ranges (54 tiles, the
     (1536, 1024, 2048, 64, 0.5),   #   last range shorter), ragged rows and columns; then exact fit
+    (300, 16512, 2048, 16, 2.0),   # forward: 258 tiles of 256 rows, the 2 past the first round of 256
+                                   #   CUs in 4 contraction ranges each (the tail), ragged rows
+    (300, 2048, 16512, 16, 2.0),   # the same for the dX GEMM (16512 output columns)
     # ranks that are not a power of two: the adapter kernels, the fused GEMMs' partial adapter steps
     # (r > 64: two steps, the second partial) and the few-token epilogue's u runs (256 / r rounds down)
     (300, 400, 960, 48, 1.0),      #   GEMM with a split contraction
