@@ -27,6 +27,7 @@ import json
 import os
 import sys
 import time
+from types import SimpleNamespace
 
 import numpy as np
 
@@ -52,6 +53,11 @@ def nf4_bytes(numel: int) -> int:
 
 
 ROOFLINE_KERNEL = "qlora_gemm_kernel<false, 256, false>"
+
+
+# Linears that share their input run their forward as one grouped launch (qlora_linear_fwd_group):
+# a layer's query, key and value projections, and its gate and up projections.
+GROUPS = (("q", "k", "v"), ("gate", "up"))
 
 
 def fwd_tile_rows(m: int, n: int) -> int:
@@ -166,30 +172,84 @@ def prepare(wk, q, dev, torch):
                                   dB=torch.empty(lin.n, r, dtype=torch.float32, device=dev)))
             ws_bytes = max(ws_bytes, q.qlora_workspace_bytes(M, lin.n, lin.k, r))
             flops += flops_fwd_bwd(lin.n, lin.k, M, r)
+    # units of the step: the groups (members share the first member's x, as the projections of one
+    # layer input do), then every other linear on its own, in the order of their first linear
+    by_name = {st["lin"].name: st for st in lin_state}
+    grouped = set()
+    units = []
+    for st in lin_state:
+        name = st["lin"].name
+        if name in grouped:
+            continue
+        unit = [st]
+        for grp in GROUPS:
+            if name == grp[0] and all(n in by_name for n in grp) and \
+                    len({by_name[n]["lin"].k for n in grp}) == 1:
+                unit = [by_name[n] for n in grp]
+                for other in unit[1:]:
+                    other["x"] = st["x"]
+                grouped.update(grp)
+                ws_bytes = max(ws_bytes, q.qlora_workspace_bytes_group(M, [u["lin"].n for u in unit], st["lin"].k, r))
+        units.append(unit)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    return lin_state, ws, flops
+    return units, ws, flops
 
 
-def step_fn(q, lin_state, ws, s):
+def fwd_unit(q, unit, s, ws):
+    """The forward of one unit: a grouped launch, or one linear."""
+    if len(unit) > 1:
+        q.qlora_linear_fwd_group([st["qw"] for st in unit], unit[0]["x"], [st["a"] for st in unit],
+                                 [st["b"] for st in unit], s, [st["y"] for st in unit], [st["u"] for st in unit],
+                                 ws=ws)
+    else:
+        st = unit[0]
+        q.qlora_linear_fwd(st["qw"], st["x"], st["a"], st["b"], s, st["y"], st["u"], ws=ws)
+
+
+def step_fn(q, units, ws, s):
     def step(_i=0):
-        for st in lin_state:
-            q.qlora_linear_fwd(st["qw"], st["x"], st["a"], st["b"], s, st["y"], st["u"], ws=ws)
-            q.qlora_linear_bwd(st["qw"], st["x"], st["dy"], st["a"], st["b"], s, st["u"], st["dx"],
-                               st["dA"], st["dB"], ws=ws)
+        for unit in units:
+            fwd_unit(q, unit, s, ws)
+            for st in unit:
+                q.qlora_linear_bwd(st["qw"], st["x"], st["dy"], st["a"], st["b"], s, st["u"], st["dx"],
+                                   st["dA"], st["dB"], ws=ws)
     return step
 
 
-def fwd_gemm_fn(q, lin_state, M, s):
-    """The forward GEMMs of the linears whose forward runs the 256-row tile instantiation, one
-    launch each through the forward-recompute entry; returns (fn, linears, flops per call)."""
-    r = lin_state[0]["a"].shape[0]
-    big = [st for st in lin_state if fwd_tile_rows(M, st["lin"].n) == 256]
+def unit_name(unit):
+    return "+".join(st["lin"].name for st in unit)
+
+
+def unit_tile_rows(M, unit):
+    """Token rows per tile of a unit's forward GEMM: a group of linears takes 256-row tiles when
+    their tiles together number at least 192 (above 128 tokens), as the grouped launcher decides."""
+    if len(unit) > 1:
+        tiles = sum(-(-st["lin"].n // 128) for st in unit) * -(-M // 256)
+        return 256 if M > 128 and tiles >= 192 else 0
+    return fwd_tile_rows(M, unit[0]["lin"].n)
+
+
+def fwd_gemm_fn(q, units, M, s, weights=None):
+    """The forward GEMMs of the units whose forward runs the 256-row tile instantiation, as the step
+    launches them (a group as one launch), through the forward-recompute entries; returns (fn,
+    units, flops per call). `weights` maps linear names to other quantised weights of the same
+    shapes (default: each linear's own)."""
+    r = units[0][0]["a"].shape[0]
+    big = [u for u in units if unit_tile_rows(M, u) == 256]
+    w = (lambda st: weights[st["lin"].name]) if weights else (lambda st: st["qw"])  # noqa: E731
 
     def recompute(_i=0):
-        for st in big:
-            q.qlora_linear_fwd_recompute(st["qw"], st["x"], st["a"], st["b"], s, st["u"], st["y"])
-    return recompute, big, sum(2 * M * st["lin"].n * (st["lin"].k + r) for st in big)
+        for unit in big:
+            if len(unit) > 1:
+                q.qlora_linear_fwd_recompute_group([w(st) for st in unit], unit[0]["x"], [st["a"] for st in unit],
+                                                   [st["b"] for st in unit], s, [st["u"] for st in unit],
+                                                   [st["y"] for st in unit])
+            else:
+                st = unit[0]
+                q.qlora_linear_fwd_recompute(w(st), st["x"], st["a"], st["b"], s, st["u"], st["y"])
+    flops = sum(2 * M * st["lin"].n * (st["lin"].k + r) for u in big for st in u)
+    return recompute, big, flops
 
 
 def other_configs(torch, q, dev, skip):
@@ -202,8 +262,8 @@ def other_configs(torch, q, dev, skip):
             continue
         wk = wl.WORKLOADS[name]
         log(f"[bench] config {name}: preparing {len(wk.linears)} linears, M={wk.m}, r={wk.r}")
-        lin_state, ws, flops = prepare(wk, q, dev, torch)
-        step = step_fn(q, lin_state, ws, wk.scale)
+        units, ws, flops = prepare(wk, q, dev, torch)
+        step = step_fn(q, units, ws, wk.scale)
         step()
         iters = 50 if name == "single" else 3
         ms = timed(step, iters, torch)
@@ -221,17 +281,17 @@ def other_configs(torch, q, dev, skip):
                                 "4096x4096 linear at 16 tokens; the weight is read twice per step"})
             log(f"[bench] config single: {ms*1e3:.1f} us per fwd+bwd")
         else:
-            fwd, big, gflops = fwd_gemm_fn(q, lin_state, wk.m, wk.scale)
+            fwd, big, gflops = fwd_gemm_fn(q, units, wk.m, wk.scale)
             fwd()
             ms_f = timed(fwd, iters, torch)
             ach = gflops / (ms_f * 1e-3) / 1e12
             ent["fused_fwd_gemm"] = {"kernel": ROOFLINE_KERNEL, "achieved_TFLOPs": round(ach, 2),
                                      "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                                      "avg_launch_us": round(ms_f * 1e3 / len(big), 2),
-                                     "linears": [st["lin"].name for st in big]}
+                                     "launches": [unit_name(u) for u in big]}
             log(f"[bench] config {name}: step {ms:.2f} ms, {tf:.1f} TFLOP/s; fused fwd GEMM {ach:.1f} TFLOP/s")
         out[name] = ent
-        del lin_state, ws
+        del units, ws
         torch.cuda.empty_cache()
     return out
 
@@ -268,8 +328,9 @@ def main():
 
     # ---------------------------------------------------------------- step inputs, resident in HBM
     log(f"[bench] preparing {args.workload}: {len(wk.linears)} linears, M={M}, r={r}")
-    lin_state, ws, flops = prepare(wk, q, dev, torch)
-    step = step_fn(q, lin_state, ws, s)
+    units, ws, flops = prepare(wk, q, dev, torch)
+    lin_state = [st for u in units for st in u]
+    step = step_fn(q, units, ws, s)
 
     for _ in range(args.warmup):
         step()
@@ -279,10 +340,10 @@ def main():
     log(f"[bench] step {ms_per_step:.3f} ms, {tflops:.1f} TFLOP/s")
 
     # ------------------------------------------------ dominant kernel: fused forward GEMM, alone
-    # Timed over the linears whose forward runs the 256-row tile instantiation
-    # qlora_gemm_kernel<false, 256, false>, so that the average launch matches that kernel's entry in a
-    # rocprofv3 kernel-trace summary of this same command.
-    recompute, big, gemm_flops = fwd_gemm_fn(q, lin_state, M, s)
+    # Timed over the forward launches of the 256-row tile instantiation qlora_gemm_kernel<false,
+    # 256, false>, as the step issues them (a group as one launch), so that the average launch
+    # matches that kernel's entry in a rocprofv3 kernel-trace summary of this same command.
+    recompute, big, gemm_flops = fwd_gemm_fn(q, units, M, s)
     recompute()
     ms_recompute = timed(recompute, args.steps, torch)
     launches = len(big)
@@ -294,20 +355,17 @@ def main():
                 "unit": "TFLOP/s", "frac": round(gemm_achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                 "flops_per_launch": gemm_flops // launches,
-                "linears": [st["lin"].name for st in big]}
+                "launches": [unit_name(u) for u in big]}
     log(f"[bench] fused fwd GEMM {gemm_achieved:.1f} TFLOP/s, {avg_launch_ms*1e3:.1f} us/launch")
     # the same forward GEMMs on weights that keep fp32 scales (no double quantisation)
     f32s = {}
-    for st in big:
-        li = wk.linears.index(st["lin"])
-        wt = torch.from_numpy(wl.linear_inputs(wk, li, st["lin"], m=1)[0]).to(dev)
-        f32s[st["lin"].name] = q.quantize_weight(wt, double_quant=False)
-        del wt
-
-    def recompute_f32s(_i=0):
-        for st in big:
-            q.qlora_linear_fwd_recompute(f32s[st["lin"].name], st["x"], st["a"], st["b"], s, st["u"], st["y"])
-
+    for unit in big:
+        for st in unit:
+            li = wk.linears.index(st["lin"])
+            wt = torch.from_numpy(wl.linear_inputs(wk, li, st["lin"], m=1)[0]).to(dev)
+            f32s[st["lin"].name] = q.quantize_weight(wt, double_quant=False)
+            del wt
+    recompute_f32s, _, _ = fwd_gemm_fn(q, units, M, s, weights=f32s)
     recompute_f32s()
     ms_f32s = timed(recompute_f32s, args.steps, torch)
     fwd_f32s = {"TFLOPs": round(gemm_flops / (ms_f32s * 1e-3) / 1e12, 2),
@@ -316,7 +374,9 @@ def main():
                         "double-quantised ones (4.5 instead of 4.127 bits per weight)"}
     log(f"[bench] fused fwd GEMM, fp32 scales: {fwd_f32s['TFLOPs']:.1f} TFLOP/s")
     del f32s
-    dense = library_dense_gemm(torch, dev, M, [st["lin"] for st in big], args.steps)
+    # a group as one GEMM of its stacked weights
+    shapes = [SimpleNamespace(n=sum(st["lin"].n for st in u), k=u[0]["lin"].k) for u in big]
+    dense = library_dense_gemm(torch, dev, M, shapes, args.steps)
     log(f"[bench] library dense bf16 GEMM, same shapes: {dense:.1f} TFLOP/s")
     context = {"library_dense_bf16_gemm_TFLOPs": round(dense, 2),
                "fused_vs_library_dense": round(gemm_achieved / dense, 4),
@@ -328,7 +388,8 @@ def main():
     dequant_gbps = None
     if not args.no_paths:
         paths, dequant_gbps = bandwidth_paths(torch, q, dev, args)
-    del lin_state, ws
+    group_names = [unit_name(u) for u in units if len(u) > 1]
+    del lin_state, units, ws
     torch.cuda.empty_cache()
     configs = {} if args.no_configs else other_configs(torch, q, dev, args.workload)
 
@@ -338,11 +399,12 @@ def main():
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded; weights N(0,0.02^2), x and dY N(0,1), A and B N(0,0.01^2))",
+        "data": "synthetic (seeded; weights N(0,0.02^2), x and dY N(0,1) with one x per layer input (q/k/v share one, gate/up another), A and B N(0,0.01^2))",
         "config": {"workload": f"{args.workload} layer set, all 7 linears NF4 + double quant, "
                                f"fwd + bwd (dX, dA, dB)",
                    "tokens": M, "rank": r, "alpha": wk.alpha,
                    "linears": {l.name: [l.n, l.k] for l in wk.linears},
+                   "grouped_forwards": group_names,
                    "flops_per_step": flops},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "dequant_GBps": dequant_gbps,

@@ -59,6 +59,9 @@ _SIGS = {
     "nf4_dequant": (ctypes.c_int, [_W, _p, _p]),
     "qlora_linear_fwd": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz, _p]),
     "qlora_linear_fwd_noalloc": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p]),
+    "qlora_linear_fwd_group": (ctypes.c_int, [_i32, _p, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz, _p]),
+    "qlora_linear_fwd_recompute_group": (ctypes.c_int, [_i32, _p, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz,
+                                                        _p]),
     "qlora_linear_bwd": (ctypes.c_int, [_W, _p, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _p,
                                         ctypes.c_int, _p, _sz, _p]),
     "qlora_linear_fwd_recompute": (ctypes.c_int, [_W, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _sz,
@@ -72,6 +75,7 @@ _SIGS = {
     "qlora_adamw_plan_step": (ctypes.c_int, [_p, ctypes.POINTER(CAdamWConfig), _i64, _p, _p]),
     "qlora_adamw_plan_destroy": (ctypes.c_int, [_p]),
     "qlora_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "qlora_workspace_bytes_group": (_sz, [_i32, _p, _i64, _i64, _i32]),
     "nf4_storage_bytes": (_i64, [_i64]),
     "nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
     "nf4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -217,6 +221,79 @@ def qlora_linear_fwd(weight: NF4Weight, x, A, B, scale: float, y, u_out=None, ws
     _check(lib.qlora_linear_fwd(ctypes.byref(cw), _ptr(x), M, _ptr(A), _ptr(B), r, scale, _ptr(y),
                                 _ptr(u_out), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "qlora_linear_fwd")
+
+
+def qlora_workspace_bytes_group(M: int, N: list, K: int, r: int) -> int:
+    n = (ctypes.c_int64 * max(len(N), 1))(*[int(v) for v in N])
+    return int(lib.qlora_workspace_bytes_group(len(N), n, M, K, r))
+
+
+def workspace_group(M: int, N: list, K: int, r: int, device="cuda") -> torch.Tensor:
+    """A device workspace large enough for qlora_linear_fwd_group over weights of N rows."""
+    nbytes = max(qlora_workspace_bytes_group(M, N, K, r), 256)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def qlora_linear_fwd_group(weights: list, x, As: list, Bs: list, scale: float, ys: list, us=None, ws=None,
+                           stream=None) -> None:
+    """Forward of several linears that share x (e.g. q/k/v or gate/up): ys[i] = x W~_i^T +
+    s (x A_i^T) B_i^T, as one fused launch where the shapes allow (see qlora_linear_fwd_group in
+    include/qlora_nf4.h); us[i] (optional) receives u_i = x A_i^T."""
+    n = len(weights)
+    if not (len(As) == len(Bs) == len(ys) == n) or (us is not None and len(us) != n):
+        raise ValueError("one A, B and y (and u) per weight")
+    _dtype(x, *_BF16)
+    M = x.shape[0]
+    r = As[0].shape[0]
+    for w, A, B, y in zip(weights, As, Bs, ys):
+        for t in (A, B, y):
+            _dtype(t, *_BF16)
+        if x.shape != (M, w.K) or A.shape != (r, w.K) or B.shape != (w.N, r) or y.shape != (M, w.N):
+            raise ValueError("shape mismatch")
+    if us is not None:
+        for u in us:
+            _dtype(u, torch.float32)
+            if u is not None and u.numel() != M * r:
+                raise ValueError("shape mismatch")
+    if ws is None:
+        ws = workspace_group(M, [w.N for w in weights], weights[0].K, r, x.device)
+    cws = [w.c_struct() for w in weights]
+    P = ctypes.c_void_p
+    wp = (P * n)(*[ctypes.addressof(c) for c in cws])
+    ap = (P * n)(*[_ptr(A) for A in As])
+    bp = (P * n)(*[_ptr(B) for B in Bs])
+    yp = (P * n)(*[_ptr(y) for y in ys])
+    up = (P * n)(*[_ptr(u) for u in us]) if us is not None else None
+    _check(lib.qlora_linear_fwd_group(n, wp, _ptr(x), M, ap, bp, r, scale, yp, up, _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)), "qlora_linear_fwd_group")
+
+
+def qlora_linear_fwd_recompute_group(weights: list, x, As: list, Bs: list, scale: float, us: list, ys: list,
+                                     ws=None, stream=None) -> None:
+    """qlora_linear_fwd_group with every u_i = x A_i^T known: the fused GEMMs only."""
+    n = len(weights)
+    if not (len(As) == len(Bs) == len(ys) == len(us) == n):
+        raise ValueError("one A, B, u and y per weight")
+    _dtype(x, *_BF16)
+    M = x.shape[0]
+    r = As[0].shape[0]
+    for w, A, B, y, u in zip(weights, As, Bs, ys, us):
+        for t in (A, B, y):
+            _dtype(t, *_BF16)
+        _dtype(u, torch.float32)
+        if x.shape != (M, w.K) or A.shape != (r, w.K) or B.shape != (w.N, r) or y.shape != (M, w.N) \
+                or u.numel() != M * r:
+            raise ValueError("shape mismatch")
+    if ws is None:
+        ws = workspace_group(M, [w.N for w in weights], weights[0].K, r, x.device)
+    cws = [w.c_struct() for w in weights]
+    P = ctypes.c_void_p
+    wp = (P * n)(*[ctypes.addressof(c) for c in cws])
+    _check(lib.qlora_linear_fwd_recompute_group(n, wp, _ptr(x), M, (P * n)(*[_ptr(A) for A in As]),
+                                                (P * n)(*[_ptr(B) for B in Bs]), r, scale,
+                                                (P * n)(*[_ptr(u) for u in us]), (P * n)(*[_ptr(y) for y in ys]),
+                                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qlora_linear_fwd_recompute_group")
 
 
 def qlora_linear_fwd_noalloc(weight: NF4Weight, x, A, B, scale: float, y, u_out=None,
@@ -471,7 +548,9 @@ def quantize_weight(w: torch.Tensor, stream=None, absmax: torch.Tensor | None = 
 __all__ = ["lib", "LIB_PATH", "EXPORTED", "NF4Error", "NF4Weight", "CNF4Weight", "nf4_quantize",
            "nf4_quantize_bf16",
            "nf4_double_quant", "nf4_double_quant_many", "DoubleQuantMany", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_fwd_noalloc",
-           "qlora_linear_fwd_recompute",
+           "qlora_linear_fwd_recompute", "qlora_linear_fwd_group", "qlora_linear_fwd_recompute_group",
+           "qlora_workspace_bytes_group",
+           "workspace_group",
            "qlora_linear_bwd", "qlora_merge", "AdamWConfig", "CAdamWConfig", "AdamWPlan",
            "Q4_CODEBOOKS", "q4_codebook_values", "q4_quantize", "q4_dequant",
            "qlora_workspace_bytes", "nf4_storage_bytes", "nf4_codebook", "workspace",

@@ -128,12 +128,10 @@ int check_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t*
   return NF4_OK;
 }
 
-// The forward's launches once the arguments are checked and ws holds fwd_ws(M, N, K, r) bytes.
-int run_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
-            int32_t r, float scale, uint16_t* y, float* u_out, void* ws, hipStream_t stream) {
+// The forward's launches with u and the partial sums (fwd_part_floats(M, N, K, r)) placed.
+int run_fwd_at(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
+               int32_t r, float scale, uint16_t* y, float* u, float* part, hipStream_t stream) {
   const int64_t N = W->N, K = W->K;
-  float* u = u_out ? u_out : static_cast<float*>(ws);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
   if (nf4::skinny_eligible(M, N, K) && (!W->absmax || M <= 4)) {
     return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, A, B, r,
                                            scale, part, u, y, W->codebook, stream));
@@ -142,6 +140,26 @@ int run_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A
   if (e != hipSuccess) return NF4_ERR_HIP;
   return from_hip(nf4::launch_fwd_gemm(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, u, B,
                                        r, scale, y, part, W->codebook, stream));
+}
+
+// The forward's launches once the arguments are checked and ws holds fwd_ws(M, N, K, r) bytes.
+int run_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
+            int32_t r, float scale, uint16_t* y, float* u_out, void* ws, hipStream_t stream) {
+  float* u = u_out ? u_out : static_cast<float*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * r * 4));
+  return run_fwd_at(W, x, M, A, B, r, scale, y, u, part, stream);
+}
+
+// Workspace of a grouped forward: [u of each linear (M*r fp32 each)] [partial sums: the largest of
+// the group launch's tail and of each linear's own forward (u's partial sums above rank 16, the
+// few-token path, or the linear alone when the group is not eligible)].
+size_t fwd_group_ws(int count, const int64_t* N, int64_t M, int64_t K, int r) {
+  size_t part = nf4::fwd_group_part_floats(count, N, M, K);
+  for (int i = 0; i < count; ++i) {
+    const size_t f = fwd_part_floats(M, N[i], K, r);
+    if (f > part) part = f;
+  }
+  return (size_t)count * align_up((size_t)M * r * 4) + align_up(part * 4);
 }
 
 }  // namespace
@@ -274,6 +292,79 @@ int qlora_linear_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const ui
   if (ws && !aligned16(ws)) return NF4_ERR_ALIGN;
   if (!ws || ws_bytes < fwd_ws(M, W->N, W->K, r)) return NF4_ERR_WORKSPACE;
   return run_fwd(W, x, M, A, B, r, scale, y, u_out, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The grouped forward; with `recompute`, u_i is given (u_in) and only the GEMMs run, as in
+// qlora_linear_fwd_recompute.
+int run_fwd_group(int32_t count, const nf4_weight* const* W, const uint16_t* x, int64_t M, const uint16_t* const* A,
+                  const uint16_t* const* B, int32_t r, float scale, uint16_t* const* y, float* const* u_io,
+                  bool recompute, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (count < 1 || count > 4) return NF4_ERR_SHAPE;
+  if (!W || !A || !B || !y || (recompute && !u_io)) return NF4_ERR_NULL;
+  int64_t N[4];
+  for (int i = 0; i < count; ++i) {
+    const int st = check_fwd(W[i], x, M, A[i], B[i], r, y[i], u_io ? u_io[i] : nullptr);
+    if (st) return st;
+    if (W[i]->K != W[0]->K || W[i]->codebook != W[0]->codebook || (W[i]->absmax == nullptr) != (W[0]->absmax == nullptr))
+      return NF4_ERR_SHAPE;
+    if (recompute && M > 0 && !u_io[i]) return NF4_ERR_NULL;
+    N[i] = W[i]->N;
+  }
+  if (M == 0) return NF4_OK;
+  const int64_t K = W[0]->K;
+  if (ws && !aligned16(ws)) return NF4_ERR_ALIGN;
+  if (!ws || ws_bytes < fwd_group_ws(count, N, M, K, r)) return NF4_ERR_WORKSPACE;
+  const size_t uslot = align_up((size_t)M * r * 4);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + count * uslot);
+  float* u[4];
+  for (int i = 0; i < count; ++i)
+    u[i] = u_io && u_io[i] ? u_io[i] : reinterpret_cast<float*>(static_cast<char*>(ws) + i * uslot);
+  if (!nf4::fwd_group_eligible(count, N, M, K)) {
+    for (int i = 0; i < count; ++i) {
+      // linear by linear, as qlora_linear_fwd (or its recompute) would run each; the workspace
+      // holds one linear's [u][partial sums] at its start
+      const int st = recompute
+          ? qlora_linear_fwd_recompute(W[i], x, M, A[i], B[i], r, scale, u[i], y[i], ws, ws_bytes, stream)
+          : run_fwd_at(W[i], x, M, A[i], B[i], r, scale, y[i], u[i], part, stream);
+      if (st) return st;
+    }
+    return NF4_OK;
+  }
+  nf4::FwdGroupItem it[4];
+  for (int i = 0; i < count; ++i) {
+    if (!recompute && nf4::launch_lora_u(x, M, K, A[i], r, part, u[i], stream) != hipSuccess) return NF4_ERR_HIP;
+    it[i] = nf4::FwdGroupItem{W[i]->packed, W[i]->scale_q, W[i]->scale_c2, W[i]->absmax, N[i], u[i], B[i], y[i]};
+  }
+  return from_hip(nf4::launch_fwd_gemm_group(count, it, K, x, M, r, scale, part, W[0]->codebook, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_linear_fwd_group(int32_t count, const nf4_weight* const* W, const uint16_t* x, int64_t M,
+                           const uint16_t* const* A, const uint16_t* const* B, int32_t r, float scale,
+                           uint16_t* const* y, float* const* u_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_fwd_group(count, W, x, M, A, B, r, scale, y, u_out, false, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_recompute_group(int32_t count, const nf4_weight* const* W, const uint16_t* x, int64_t M,
+                                     const uint16_t* const* A, const uint16_t* const* B, int32_t r, float scale,
+                                     float* const* u, uint16_t* const* y, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  return run_fwd_group(count, W, x, M, A, B, r, scale, y, u, true, ws, ws_bytes, stream);
+}
+
+size_t qlora_workspace_bytes_group(int32_t count, const int64_t* N, int64_t M, int64_t K, int32_t r) {
+  if (count < 1 || count > 4 || !N || M < 0 || K < 64 || K % 64 || check_rank(r)) return 0;
+  for (int i = 0; i < count; ++i)
+    if (N[i] < 16 || N[i] % 16 || !linear_shape_ok(M, N[i], K)) return 0;
+  if (M == 0) return 0;
+  return fwd_group_ws(count, N, M, K, r);
 }
 
 int qlora_linear_fwd_noalloc(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A,

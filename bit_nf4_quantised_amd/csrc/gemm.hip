@@ -53,6 +53,22 @@
 
 namespace nf4 {
 
+// One weight of a grouped forward: several adapted linears that share their input x (a layer's
+// query, key and value projections, or its gate and up projections) as one launch whose column
+// tiles run over the weights in turn.
+struct GemmWeight {
+  const uint8_t* packed;
+  const uint8_t* scale_q;
+  const float* scale_c2;
+  const float* absmax;
+  int64_t N;
+  const float* lora_act;    // u of this linear [M x r]
+  const uint16_t* lora_w;   // B of this linear [N x r]
+  uint16_t* out;            // y of this linear [M x N]
+  int tile0;                // its first column tile in the group
+};
+constexpr int kMaxGroup = 4;
+
 struct GemmArgs {
   const uint8_t* packed;
   const uint8_t* scale_q;
@@ -73,6 +89,9 @@ struct GemmArgs {
   int tail_tiles;           //   the last tail_tiles tiles cut into tail_split contraction ranges
   int tail_split;
   Codes codes;              // the values the 4-bit indices select
+  int nw;                   // grouped forward: weights in w (1: the fields above are the weight)
+  int gx_total;             //   column tiles of all of them
+  GemmWeight w[kMaxGroup];
 };
 
 constexpr int kBN = 128;        // output columns per tile
@@ -80,6 +99,29 @@ constexpr int kBK = 64;         // contraction per step
 constexpr int kXStages = 3;     // activation stages in LDS
 constexpr int kPStages = 4;     // packed weight stages in LDS
 constexpr int kThreads = 1024;  // 8 consumer + 4 dequantiser + 4 loader waves
+
+// The weight of a grouped forward that owns global column tile gcol (uniform per workgroup; a
+// select per field keeps the kernel arguments out of private memory).
+__device__ __forceinline__ void select_weight(GemmArgs& g, const GemmArgs& ga, int gcol, int64_t& col0) {
+  int wi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < ga.nw && gcol >= ga.w[i].tile0) wi = i;
+#pragma unroll
+  for (int i = 0; i < kMaxGroup; ++i) {
+    if (i == wi) {
+      g.packed = ga.w[i].packed;
+      g.scale_q = ga.w[i].scale_q;
+      g.scale_c2 = ga.w[i].scale_c2;
+      g.absmax = ga.w[i].absmax;
+      g.N = ga.w[i].N;
+      g.lora_act = ga.w[i].lora_act;
+      g.lora_w = ga.w[i].lora_w;
+      g.out = ga.w[i].out;
+      col0 = (int64_t)(gcol - ga.w[i].tile0) * kBN;
+    }
+  }
+}
 
 template <bool DX>
 struct WTile {
@@ -122,7 +164,7 @@ __device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
 }
 
 template <bool DX, int BM, bool F32S>
-__global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) {
+__global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs ga) {
   using WT = WTile<DX>;
   using CW = Waves<BM>;
   constexpr int TM = CW::TM, TN = CW::TN;
@@ -140,9 +182,9 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+  GemmArgs g = ga;                          // a grouped forward's workgroup swaps in its weight
   const int64_t Lc = DX ? g.N : g.K;       // contraction length
-  const int64_t Nout = DX ? g.K : g.N;     // output columns
-  const int gx = (int)((Nout + kBN - 1) / kBN);   // column tiles
+  const int gx = ga.nw > 1 ? ga.gx_total : (int)(((DX ? g.K : g.N) + kBN - 1) / kBN);   // column tiles
 
   // Tile coordinates. Workgroups are dealt round-robin over the 8 XCDs (workgroup i to XCD i % 8,
   // in order of i), so each XCD gets a contiguous run of tiles that share an activation row block.
@@ -173,8 +215,10 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs g) 
     split = lin / tiles;
     tile = lin % tiles;
   }
-  const int64_t col0 = (int64_t)(tile % gx) * kBN;
+  int64_t col0 = (int64_t)(tile % gx) * kBN;
   const int64_t m0 = (int64_t)(tile / gx) * BM;
+  if (!DX && ga.nw > 1) select_weight(g, ga, tile % gx, col0);
+  const int64_t Nout = DX ? g.K : g.N;     // output columns
 
   const int main_total = (int)((Lc + kBK - 1) / kBK);
   const int per_split = (main_total + nsplit - 1) / nsplit;
@@ -613,13 +657,17 @@ __global__ __launch_bounds__(256) void gemm_ksum_kernel(const f32x4* __restrict_
 // thread 4 groups of 4 values, all loads of all ranges in flight together. Rows past M and columns
 // past Nout were never written and are skipped.
 constexpr int kKsumRows = 32;
-template <int NS>
-__global__ __launch_bounds__(256) void gemm_ksum_tail_kernel(const f32x4* __restrict__ part, int tail, int first,
-                                                             int gx, int bm, int64_t M, int64_t Nout,
-                                                             u32x2* __restrict__ out) {
+template <int NS, bool DX>
+__global__ __launch_bounds__(256) void gemm_ksum_tail_kernel(const f32x4* __restrict__ part, const GemmArgs ga,
+                                                             int tail, int first, int gx, int bm) {
   const int per_tile = bm / kKsumRows;
   const int tr = blockIdx.x / per_tile, rs = blockIdx.x % per_tile, tile = first + tr;
-  const int64_t m0 = (int64_t)(tile / gx) * bm + rs * kKsumRows, c0 = (int64_t)(tile % gx) * kBN;
+  const int64_t m0 = (int64_t)(tile / gx) * bm + rs * kKsumRows;
+  int64_t c0 = (int64_t)(tile % gx) * kBN;
+  GemmArgs g = ga;
+  if (!DX && ga.nw > 1) select_weight(g, ga, tile % gx, c0);
+  const int64_t M = g.M, Nout = DX ? g.K : g.N;
+  u32x2* __restrict__ out = reinterpret_cast<u32x2*>(g.out);
   const int per = bm * kBN / 4;   // 4-value groups per tile
   const f32x4* src = part + (int64_t)tr * per + rs * kKsumRows * (kBN / 4);
   f32x4 v[NS][4];
@@ -716,7 +764,7 @@ size_t dx_gemm_part_floats(int64_t M, int64_t N, int64_t K) { return plan_part_f
 template <bool DX, bool F32S>
 static hipError_t launch_gemm_t(GemmArgs g, const GemmPlan& p, hipStream_t stream) {
   const int64_t Nout = DX ? g.K : g.N;
-  const int gx = (int)((Nout + kBN - 1) / kBN);
+  const int gx = g.nw > 1 ? g.gx_total : (int)((Nout + kBN - 1) / kBN);
   const int gy = (int)((g.M + p.bm - 1) / p.bm);
   g.ksplit = p.ks;
   g.whole_tiles = p.whole;
@@ -733,10 +781,9 @@ static hipError_t launch_gemm_t(GemmArgs g, const GemmPlan& p, hipStream_t strea
   } else if (p.tail > 0) {
     const dim3 kg((unsigned)(p.tail * (p.bm / kKsumRows)));
     const f32x4* src = (const f32x4*)g.part;
-    u32x2* dst = reinterpret_cast<u32x2*>(g.out);
-    if (p.tsplit == 2) hipLaunchKernelGGL((gemm_ksum_tail_kernel<2>), kg, dim3(256), 0, stream, src, p.tail, p.whole, gx, p.bm, g.M, Nout, dst);
-    else if (p.tsplit == 3) hipLaunchKernelGGL((gemm_ksum_tail_kernel<3>), kg, dim3(256), 0, stream, src, p.tail, p.whole, gx, p.bm, g.M, Nout, dst);
-    else hipLaunchKernelGGL((gemm_ksum_tail_kernel<4>), kg, dim3(256), 0, stream, src, p.tail, p.whole, gx, p.bm, g.M, Nout, dst);
+    if (p.tsplit == 2) hipLaunchKernelGGL((gemm_ksum_tail_kernel<2, DX>), kg, dim3(256), 0, stream, src, g, p.tail, p.whole, gx, p.bm);
+    else if (p.tsplit == 3) hipLaunchKernelGGL((gemm_ksum_tail_kernel<3, DX>), kg, dim3(256), 0, stream, src, g, p.tail, p.whole, gx, p.bm);
+    else hipLaunchKernelGGL((gemm_ksum_tail_kernel<4, DX>), kg, dim3(256), 0, stream, src, g, p.tail, p.whole, gx, p.bm);
   }
   return hipGetLastError();
 }
@@ -771,6 +818,54 @@ hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const f
   GemmArgs g{packed, scale_q, scale_c2, absmax, N, K, dy, M, v, A, r, scale, dx, 1, part, 0, 0, 0, {}};
   if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
   return absmax ? launch_gemm_t<true, true>(g, p, stream) : launch_gemm_t<true, false>(g, p, stream);
+}
+
+// The grouped forward (forward only, 256-row tiles): its column tiles run over the weights in
+// turn, and the tail is planned over all of them. Not eligible (false) when the group's tiles would
+// not take 256-row tiles by themselves; the caller then launches the linears one by one.
+static bool fwd_group_plan(int count, const int64_t* N, int64_t M, int64_t K, GemmPlan& p, int& gx_total) {
+  gx_total = 0;
+  for (int i = 0; i < count; ++i) gx_total += (int)((N[i] + kBN - 1) / kBN);
+  const int64_t t256 = (int64_t)gx_total * ((M + 255) / 256), steps = (K + kBK - 1) / kBK;
+  p = GemmPlan{256, 1, 0, 0, 0};
+  if (count < 2 || count > kMaxGroup || M <= 128 || t256 < 192) return false;
+  plan_tail(p, t256, steps);
+  return true;
+}
+
+bool fwd_group_eligible(int count, const int64_t* N, int64_t M, int64_t K) {
+  GemmPlan p;
+  int gx;
+  return fwd_group_plan(count, N, M, K, p, gx);
+}
+
+size_t fwd_group_part_floats(int count, const int64_t* N, int64_t M, int64_t K) {
+  GemmPlan p;
+  int gx;
+  if (!fwd_group_plan(count, N, M, K, p, gx)) return 0;
+  return plan_part_floats(p, M, 0);
+}
+
+hipError_t launch_fwd_gemm_group(int count, const FwdGroupItem* it, int64_t K, const uint16_t* x, int64_t M,
+                                 int r, float scale, float* part, int book, hipStream_t stream) {
+  int64_t N[kMaxGroup];
+  for (int i = 0; i < count && i < kMaxGroup; ++i) N[i] = it[i].N;
+  GemmPlan p;
+  int gx_total;
+  if (!fwd_group_plan(count, N, M, K, p, gx_total)) return hipErrorInvalidValue;
+  if (!part) plan_without_part(p);
+  const bool f32s = it[0].absmax != nullptr;
+  GemmArgs g{it[0].packed, it[0].scale_q, it[0].scale_c2, it[0].absmax, it[0].N, K, x, M, it[0].u, it[0].B, r, scale,
+             it[0].y, 1, part, 0, 0, 0, {}, count, gx_total, {}};
+  if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
+  int tile0 = 0;
+  for (int i = 0; i < count; ++i) {
+    if ((it[i].absmax != nullptr) != f32s) return hipErrorInvalidValue;
+    g.w[i] = GemmWeight{it[i].packed, it[i].scale_q, it[i].scale_c2, it[i].absmax, it[i].N, it[i].u, it[i].B, it[i].y,
+                        tile0};
+    tile0 += (int)((it[i].N + kBN - 1) / kBN);
+  }
+  return f32s ? launch_gemm_t<false, true>(g, p, stream) : launch_gemm_t<false, false>(g, p, stream);
 }
 
 }  // namespace nf4

@@ -41,6 +41,22 @@ hipError_t launch_fwd_gemm(const uint8_t* packed, const uint8_t* scale_q, const 
                            const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                            const float* u, const uint16_t* B, int r, float scale, uint16_t* y,
                            float* part, int book, hipStream_t stream);
+// A grouped forward: several linears that share x (and K, r, scale, codebook and kind of scales),
+// as one launch. Eligible when M > 128 and their 256-row tiles number at least 192.
+struct FwdGroupItem {
+  const uint8_t* packed;
+  const uint8_t* scale_q;
+  const float* scale_c2;
+  const float* absmax;
+  int64_t N;
+  const float* u;        // u = x A^T of this linear [M x r]
+  const uint16_t* B;     // [N x r]
+  uint16_t* y;           // [M x N]
+};
+bool fwd_group_eligible(int count, const int64_t* N, int64_t M, int64_t K);
+size_t fwd_group_part_floats(int count, const int64_t* N, int64_t M, int64_t K);
+hipError_t launch_fwd_gemm_group(int count, const FwdGroupItem* items, int64_t K, const uint16_t* x, int64_t M,
+                                 int r, float scale, float* part, int book, hipStream_t stream);
 hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                           const float* absmax, int64_t N, int64_t K, const uint16_t* dy, int64_t M,
                           const float* v, const uint16_t* A, int r, float scale, uint16_t* dx,

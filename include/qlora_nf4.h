@@ -9,7 +9,8 @@
  *                     in groups of 256 with one fp32 constant per group.
  *   nf4_dequant       section "The forward pass and gradients": first the 8-bit scales are restored
  *                     with the fp32 constants, then the indices with those scales, giving bf16.
- *   qlora_linear_fwd  section "The algorithm, step by step": y = x W~^T + s x A^T B^T.
+ *   qlora_linear_fwd  section "The algorithm, step by step": y = x W~^T + s x A^T B^T
+ *                     (qlora_linear_fwd_group: several linears that share x, as one launch).
  *   qlora_linear_bwd  section "The forward pass and gradients": dX = dY (W~ + s B A),
  *                     dA = s B^T G, dB = s G A^T with G = dY^T X; W gets no gradient.
  *   qlora_merge       section "Quality loss at merge time": the adapter merged into the
@@ -152,6 +153,37 @@ int nf4_dequant(const nf4_weight *W, uint16_t *out, hipStream_t stream);
 int qlora_linear_fwd(const nf4_weight *W, const uint16_t *x, int64_t M, const uint16_t *A,
                      const uint16_t *B, int32_t r, float scale, uint16_t *y, float *u_out, void *ws,
                      size_t ws_bytes, hipStream_t stream);
+
+/* Forward of several adapted linears that share their input x, such as a layer's query, key and
+ * value projections or its gate and up projections: y_i = x W~_i^T + s (x A_i^T) B_i^T for
+ * i < count (1..4), each as in qlora_linear_fwd ("QLoRA, explained", The algorithm, step by step,
+ * applied to every linear). All weights share K, the rank r, the scale, the codebook and the kind
+ * of scales. Above 128 tokens, when the weights' 256-row tiles number at least 192 together, the
+ * fused GEMMs run as one launch whose column tiles run over the weights in turn (fewer launches,
+ * and small linears such as the key and value projections share the large one's efficiency);
+ * otherwise each linear runs as qlora_linear_fwd runs it. The results are those of qlora_linear_fwd
+ * up to the order in which the contraction is summed (within the forward's tolerance).
+ *   W, A, B, y: HOST arrays of count entries, each as in qlora_linear_fwd.
+ *   u_out: NULL, or a HOST array of count entries of which any may be NULL; u_i = x A_i^T goes there
+ *          (for qlora_linear_bwd) or into the workspace.
+ *   ws: at least qlora_workspace_bytes_group(count, N, M, K, r) bytes (N the weights' row counts).
+ * Errors: as qlora_linear_fwd; NF4_ERR_SHAPE also for count outside 1..4 and for weights that
+ * differ in K, codebook or kind of scales. */
+int qlora_linear_fwd_group(int32_t count, const nf4_weight *const *W, const uint16_t *x, int64_t M,
+                           const uint16_t *const *A, const uint16_t *const *B, int32_t r, float scale,
+                           uint16_t *const *y, float *const *u_out, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+/* qlora_linear_fwd_group with every u_i = x A_i^T already known (u: HOST array of count device
+ * pointers, all set), as qlora_linear_fwd_recompute is to qlora_linear_fwd: the GEMMs only, the
+ * same launches as qlora_linear_fwd_group after its u (so y_i equal its output bit for bit).
+ * Errors as qlora_linear_fwd_group. */
+int qlora_linear_fwd_recompute_group(int32_t count, const nf4_weight *const *W, const uint16_t *x, int64_t M,
+                                     const uint16_t *const *A, const uint16_t *const *B, int32_t r,
+                                     float scale, float *const *u, uint16_t *const *y, void *ws,
+                                     size_t ws_bytes, hipStream_t stream);
+/* Workspace bytes of qlora_linear_fwd_group (and of its recompute) for weights of N[0..count-1]
+ * rows; 0 for sizes it refuses. N is a HOST array. */
+size_t qlora_workspace_bytes_group(int32_t count, const int64_t *N, int64_t M, int64_t K, int32_t r);
 
 /* qlora_linear_fwd for callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the same launches and the same outputs,

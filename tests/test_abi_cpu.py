@@ -230,6 +230,43 @@ def test_gemm_workspace_follows_the_plan(M, N, K, ks):
             q.NF4_ERR_WORKSPACE
 
 
+def test_group_validation():
+    f = lib.qlora_linear_fwd_group
+    P = ctypes.c_void_p
+    a, b, c = q.CNF4Weight(FAKE, FAKE, FAKE, 4096, 4096), q.CNF4Weight(FAKE, FAKE, FAKE, 1024, 4096), \
+        q.CNF4Weight(FAKE, FAKE, FAKE, 1024, 2048)
+    ptrs = lambda *ws: (P * len(ws))(*[ctypes.addressof(w) for w in ws])  # noqa: E731
+    fake = lambda n: (P * n)(*([FAKE] * n))  # noqa: E731
+    n2 = (ctypes.c_int64 * 2)(4096, 1024)
+    need = q.lib.qlora_workspace_bytes_group(2, n2, 2048, 4096, 16)
+    assert need > 0
+    # (no call with valid arguments: it would launch kernels on the fake pointers)
+    assert f(0, ptrs(a, b), FAKE, 2048, fake(2), fake(2), 16, 2.0, fake(2), None, FAKE, need, None) == q.NF4_ERR_SHAPE
+    assert f(5, ptrs(a, b, a, b, a), FAKE, 2048, fake(5), fake(5), 16, 2.0, fake(5), None, FAKE, need, None) == \
+        q.NF4_ERR_SHAPE
+    assert f(2, None, FAKE, 2048, fake(2), fake(2), 16, 2.0, fake(2), None, FAKE, need, None) == q.NF4_ERR_NULL
+    assert f(2, ptrs(a, b), FAKE, 2048, None, fake(2), 16, 2.0, fake(2), None, FAKE, need, None) == q.NF4_ERR_NULL
+    # weights that differ in K, or in the kind of scales
+    assert f(2, ptrs(a, c), FAKE, 2048, fake(2), fake(2), 16, 2.0, fake(2), None, FAKE, need, None) == \
+        q.NF4_ERR_SHAPE
+    d = q.CNF4Weight(FAKE, None, None, 1024, 4096, FAKE)
+    assert f(2, ptrs(a, d), FAKE, 2048, fake(2), fake(2), 16, 2.0, fake(2), None, FAKE, need, None) == \
+        q.NF4_ERR_SHAPE
+    e = q.CNF4Weight(FAKE, FAKE, FAKE, 1024, 4096, None, 1)
+    assert f(2, ptrs(a, e), FAKE, 2048, fake(2), fake(2), 16, 2.0, fake(2), None, FAKE, need, None) == \
+        q.NF4_ERR_SHAPE
+    # the workspace: one byte short is refused, and sizes past the limits give 0
+    assert f(2, ptrs(a, b), FAKE, 2048, fake(2), fake(2), 16, 2.0, fake(2), None, FAKE, need - 1, None) == \
+        q.NF4_ERR_WORKSPACE
+    assert f(2, ptrs(a, b), FAKE, 2048, fake(2), fake(2), 24, 2.0, fake(2), None, FAKE, need, None) == q.NF4_ERR_RANK
+    assert q.lib.qlora_workspace_bytes_group(2, (ctypes.c_int64 * 2)(4096, 1000), 2048, 4096, 16) == 0
+    assert q.lib.qlora_workspace_bytes_group(0, n2, 2048, 4096, 16) == 0
+    # the u of every linear plus at least the group launch's tail: 3 x 1024 tiles... of (4096, 1024, 1024)
+    # at 2048 tokens: 48 column tiles x 8 row blocks = 384 tiles, 128 past the first round in 2 ranges
+    n3 = (ctypes.c_int64 * 3)(4096, 1024, 1024)
+    assert q.lib.qlora_workspace_bytes_group(3, n3, 2048, 4096, 16) >= 3 * 2048 * 16 * 4 + 2 * 128 * 256 * 128 * 4
+
+
 def test_recompute_validation():
     w = ctypes.byref(_w())
     f = lib.qlora_linear_fwd_recompute
