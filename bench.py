@@ -207,13 +207,24 @@ def fwd_unit(q, unit, s, ws):
         q.qlora_linear_fwd(st["qw"], st["x"], st["a"], st["b"], s, st["y"], st["u"], ws=ws)
 
 
+def bwd_unit(q, unit, s, ws):
+    """The backward of one unit: a grouped backward (one dX launch for the group), or one linear."""
+    if len(unit) > 1:
+        q.qlora_linear_bwd_group([st["qw"] for st in unit], unit[0]["x"], [st["dy"] for st in unit],
+                                 [st["a"] for st in unit], [st["b"] for st in unit], s, [st["u"] for st in unit],
+                                 [st["dx"] for st in unit], [st["dA"] for st in unit], [st["dB"] for st in unit],
+                                 ws=ws)
+    else:
+        st = unit[0]
+        q.qlora_linear_bwd(st["qw"], st["x"], st["dy"], st["a"], st["b"], s, st["u"], st["dx"],
+                           st["dA"], st["dB"], ws=ws)
+
+
 def step_fn(q, units, ws, s):
     def step(_i=0):
         for unit in units:
             fwd_unit(q, unit, s, ws)
-            for st in unit:
-                q.qlora_linear_bwd(st["qw"], st["x"], st["dy"], st["a"], st["b"], s, st["u"], st["dx"],
-                                   st["dA"], st["dB"], ws=ws)
+            bwd_unit(q, unit, s, ws)
     return step
 
 
@@ -404,7 +415,7 @@ def main():
                                f"fwd + bwd (dX, dA, dB)",
                    "tokens": M, "rank": r, "alpha": wk.alpha,
                    "linears": {l.name: [l.n, l.k] for l in wk.linears},
-                   "grouped_forwards": group_names,
+                   "grouped": group_names,
                    "flops_per_step": flops},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "dequant_GBps": dequant_gbps,

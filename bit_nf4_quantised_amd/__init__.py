@@ -76,6 +76,8 @@ _SIGS = {
     "qlora_adamw_plan_destroy": (ctypes.c_int, [_p]),
     "qlora_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "qlora_workspace_bytes_group": (_sz, [_i32, _p, _i64, _i64, _i32]),
+    "qlora_linear_bwd_group": (ctypes.c_int, [_i32, _p, _p, _p, _i64, _p, _p, _i32, _f32, _p, _p, _p, _p,
+                                              ctypes.c_int, _p, _sz, _p]),
     "nf4_storage_bytes": (_i64, [_i64]),
     "nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
     "nf4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -294,6 +296,37 @@ def qlora_linear_fwd_recompute_group(weights: list, x, As: list, Bs: list, scale
                                                 (P * n)(*[_ptr(u) for u in us]), (P * n)(*[_ptr(y) for y in ys]),
                                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "qlora_linear_fwd_recompute_group")
+
+
+def qlora_linear_bwd_group(weights: list, x, dys: list, As: list, Bs: list, scale: float, us: list, dxs,
+                           dAs: list, dBs: list, accumulate: bool = False, ws=None, stream=None) -> None:
+    """Backward of several linears that share x: for each i as qlora_linear_bwd (dxs[i], dAs[i],
+    dBs[i]), the dX GEMMs as one launch where the shapes allow; dxs None skips the input gradients."""
+    n = len(weights)
+    if not (len(dys) == len(As) == len(Bs) == len(us) == len(dAs) == len(dBs) == n) or \
+            (dxs is not None and len(dxs) != n):
+        raise ValueError("one dY, A, B, u, dA and dB (and dX) per weight")
+    _dtype(x, *_BF16)
+    M = x.shape[0]
+    r = As[0].shape[0]
+    for i, w in enumerate(weights):
+        for t in (dys[i], As[i], Bs[i]) + ((dxs[i],) if dxs is not None else ()):
+            _dtype(t, *_BF16)
+        for t in (us[i], dAs[i], dBs[i]):
+            _dtype(t, torch.float32)
+        if x.shape != (M, w.K) or dys[i].shape != (M, w.N) or As[i].shape != (r, w.K) or Bs[i].shape != (w.N, r) \
+                or us[i].numel() != M * r or dAs[i].shape != (r, w.K) or dBs[i].shape != (w.N, r) \
+                or (dxs is not None and dxs[i].shape != (M, w.K)):
+            raise ValueError("shape mismatch")
+    if ws is None:
+        ws = workspace_group(M, [w.N for w in weights], weights[0].K, r, x.device)
+    cws = [w.c_struct() for w in weights]
+    P = ctypes.c_void_p
+    arr = lambda ts: (P * n)(*[_ptr(t) for t in ts])  # noqa: E731
+    _check(lib.qlora_linear_bwd_group(n, (P * n)(*[ctypes.addressof(c) for c in cws]), _ptr(x), arr(dys), M,
+                                      arr(As), arr(Bs), r, scale, arr(us), arr(dxs) if dxs is not None else None,
+                                      arr(dAs), arr(dBs), int(bool(accumulate)), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)), "qlora_linear_bwd_group")
 
 
 def qlora_linear_fwd_noalloc(weight: NF4Weight, x, A, B, scale: float, y, u_out=None,
@@ -549,7 +582,7 @@ __all__ = ["lib", "LIB_PATH", "EXPORTED", "NF4Error", "NF4Weight", "CNF4Weight",
            "nf4_quantize_bf16",
            "nf4_double_quant", "nf4_double_quant_many", "DoubleQuantMany", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_fwd_noalloc",
            "qlora_linear_fwd_recompute", "qlora_linear_fwd_group", "qlora_linear_fwd_recompute_group",
-           "qlora_workspace_bytes_group",
+           "qlora_workspace_bytes_group", "qlora_linear_bwd_group",
            "workspace_group",
            "qlora_linear_bwd", "qlora_merge", "AdamWConfig", "CAdamWConfig", "AdamWPlan",
            "Q4_CODEBOOKS", "q4_codebook_values", "q4_quantize", "q4_dequant",

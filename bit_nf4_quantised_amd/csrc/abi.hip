@@ -162,6 +162,18 @@ size_t fwd_group_ws(int count, const int64_t* N, int64_t M, int64_t K, int r) {
   return (size_t)count * align_up((size_t)M * r * 4) + align_up(part * 4);
 }
 
+// Workspace of a grouped backward: [v of each linear (M*r fp32 each)] [partial sums: the largest of
+// each linear's passes and of its dX launch when it runs alone].
+size_t bwd_group_ws(int count, const int64_t* N, int64_t M, int64_t K, int r) {
+  size_t part = nf4::lora_pass_ws_floats(M, K, r, false, true);
+  for (int i = 0; i < count; ++i) {
+    const size_t d = nf4::lora_pass_ws_floats(M, N[i], r, true, true), x = nf4::dx_gemm_part_floats(M, N[i], K);
+    if (d > part) part = d;
+    if (x > part) part = x;
+  }
+  return (size_t)count * align_up((size_t)M * r * 4) + align_up(part * 4);
+}
+
 }  // namespace
 
 
@@ -364,7 +376,72 @@ size_t qlora_workspace_bytes_group(int32_t count, const int64_t* N, int64_t M, i
   for (int i = 0; i < count; ++i)
     if (N[i] < 16 || N[i] % 16 || !linear_shape_ok(M, N[i], K)) return 0;
   if (M == 0) return 0;
-  return fwd_group_ws(count, N, M, K, r);
+  const size_t f = fwd_group_ws(count, N, M, K, r), b = bwd_group_ws(count, N, M, K, r);
+  return f > b ? f : b;
+}
+
+int qlora_linear_bwd_group(int32_t count, const nf4_weight* const* W, const uint16_t* x, const uint16_t* const* dy,
+                           int64_t M, const uint16_t* const* A, const uint16_t* const* B, int32_t r, float scale,
+                           const float* const* u, uint16_t* const* dx, float* const* dA, float* const* dB,
+                           int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (count < 1 || count > 4) return NF4_ERR_SHAPE;
+  if (!W || !dy || !A || !B || !u || !dA || !dB) return NF4_ERR_NULL;
+  int64_t N[4];
+  int st;
+  for (int i = 0; i < count; ++i) {
+    if ((st = check_weight(W[i]))) return st;
+    if (!linear_shape_ok(M, W[i]->N, W[i]->K)) return NF4_ERR_SHAPE;
+    if (W[i]->K != W[0]->K || W[i]->codebook != W[0]->codebook || (W[i]->absmax == nullptr) != (W[0]->absmax == nullptr))
+      return NF4_ERR_SHAPE;
+    N[i] = W[i]->N;
+  }
+  if ((st = check_rank(r))) return st;
+  if (M == 0) return NF4_OK;
+  if (!x || !aligned16(x) || (ws && !aligned16(ws))) return !x ? NF4_ERR_NULL : NF4_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!dy[i] || !A[i] || !B[i] || !u[i] || !dA[i] || !dB[i] || (dx && !dx[i])) return NF4_ERR_NULL;
+    if (!aligned16(dy[i]) || !aligned16(A[i]) || !aligned16(B[i]) || !aligned16(u[i]) || !aligned16(dA[i]) ||
+        !aligned16(dB[i]) || (dx && !aligned16(dx[i])))
+      return NF4_ERR_ALIGN;
+  }
+  const int64_t K = W[0]->K;
+  if (!ws || ws_bytes < bwd_group_ws(count, N, M, K, r)) return NF4_ERR_WORKSPACE;
+  const size_t vslot = align_up((size_t)M * r * 4);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + count * vslot);
+  float* v[4];
+  for (int i = 0; i < count; ++i) {
+    v[i] = reinterpret_cast<float*>(static_cast<char*>(ws) + i * vslot);
+    if (nf4::launch_lora_dy(dy[i], M, N[i], B[i], u[i], r, scale, accumulate, part, v[i], dB[i], stream) != hipSuccess)
+      return NF4_ERR_HIP;
+  }
+  if (dx) {
+    if (nf4::dx_group_eligible(count, M, K)) {
+      // the longest contraction first, so that every XCD gets its share of each weight's tiles in
+      // that order and ends with the short ones
+      int order[4] = {0, 1, 2, 3};
+      for (int a = 0; a < count; ++a)
+        for (int b = a + 1; b < count; ++b)
+          if (N[order[b]] > N[order[a]]) {
+            const int t = order[a];
+            order[a] = order[b];
+            order[b] = t;
+          }
+      nf4::DxGroupItem it[4];
+      for (int k = 0; k < count; ++k) {
+        const int i = order[k];
+        it[k] = nf4::DxGroupItem{W[i]->packed, W[i]->scale_q, W[i]->scale_c2, W[i]->absmax, N[i], dy[i], v[i], A[i], dx[i]};
+      }
+      if (nf4::launch_dx_gemm_group(count, it, K, M, r, scale, W[0]->codebook, stream) != hipSuccess) return NF4_ERR_HIP;
+    } else {
+      for (int i = 0; i < count; ++i)
+        if (nf4::launch_dx_gemm(W[i]->packed, W[i]->scale_q, W[i]->scale_c2, W[i]->absmax, N[i], K, dy[i], M, v[i], A[i],
+                                r, scale, dx[i], part, W[i]->codebook, stream) != hipSuccess)
+          return NF4_ERR_HIP;
+    }
+  }
+  for (int i = 0; i < count; ++i)
+    if (nf4::launch_lora_dx(x, M, K, v[i], r, scale, accumulate, part, dA[i], stream) != hipSuccess) return NF4_ERR_HIP;
+  return NF4_OK;
 }
 
 int qlora_linear_fwd_noalloc(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A,

@@ -53,19 +53,21 @@
 
 namespace nf4 {
 
-// One weight of a grouped forward: several adapted linears that share their input x (a layer's
-// query, key and value projections, or its gate and up projections) as one launch whose column
-// tiles run over the weights in turn.
+// One weight of a grouped launch over several adapted linears that share their input x (a layer's
+// query, key and value projections, or its gate and up projections). Forward: the column tiles run
+// over the weights in turn (y_i = x W~_i^T + ...). dX: each weight's tiles in turn, every linear
+// with its own dY_i and dX_i (dX_i = dY_i W~_i + ...).
 struct GemmWeight {
   const uint8_t* packed;
   const uint8_t* scale_q;
   const float* scale_c2;
   const float* absmax;
   int64_t N;
-  const float* lora_act;    // u of this linear [M x r]
-  const uint16_t* lora_w;   // B of this linear [N x r]
-  uint16_t* out;            // y of this linear [M x N]
-  int tile0;                // its first column tile in the group
+  const uint16_t* act;      // dY of this linear [M x N] (dX only)
+  const float* lora_act;    // u [M x r] (forward) or v [M x r] (dX) of this linear
+  const uint16_t* lora_w;   // B [N x r] (forward) or A [r x K] (dX) of this linear
+  uint16_t* out;            // y [M x N] or dX [M x K] of this linear
+  int tile0;                // forward: its first column tile in the group
 };
 constexpr int kMaxGroup = 4;
 
@@ -100,13 +102,10 @@ constexpr int kXStages = 3;     // activation stages in LDS
 constexpr int kPStages = 4;     // packed weight stages in LDS
 constexpr int kThreads = 1024;  // 8 consumer + 4 dequantiser + 4 loader waves
 
-// The weight of a grouped forward that owns global column tile gcol (uniform per workgroup; a
-// select per field keeps the kernel arguments out of private memory).
-__device__ __forceinline__ void select_weight(GemmArgs& g, const GemmArgs& ga, int gcol, int64_t& col0) {
-  int wi = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxGroup; ++i)
-    if (i < ga.nw && gcol >= ga.w[i].tile0) wi = i;
+// Weight wi of a grouped launch into g (uniform per workgroup; a select per field keeps the kernel
+// arguments out of private memory).
+template <bool DX>
+__device__ __forceinline__ void use_weight(GemmArgs& g, const GemmArgs& ga, int wi) {
 #pragma unroll
   for (int i = 0; i < kMaxGroup; ++i) {
     if (i == wi) {
@@ -115,12 +114,25 @@ __device__ __forceinline__ void select_weight(GemmArgs& g, const GemmArgs& ga, i
       g.scale_c2 = ga.w[i].scale_c2;
       g.absmax = ga.w[i].absmax;
       g.N = ga.w[i].N;
+      if (DX) g.act = ga.w[i].act;
       g.lora_act = ga.w[i].lora_act;
       g.lora_w = ga.w[i].lora_w;
       g.out = ga.w[i].out;
-      col0 = (int64_t)(gcol - ga.w[i].tile0) * kBN;
     }
   }
+}
+
+// The weight of a grouped forward that owns global column tile gcol, and the tile's first column
+// within it.
+__device__ __forceinline__ void select_weight(GemmArgs& g, const GemmArgs& ga, int gcol, int64_t& col0) {
+  int wi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < ga.nw && gcol >= ga.w[i].tile0) wi = i;
+  use_weight<false>(g, ga, wi);
+#pragma unroll
+  for (int i = 0; i < kMaxGroup; ++i)
+    if (i == wi) col0 = (int64_t)(gcol - ga.w[i].tile0) * kBN;
 }
 
 template <bool DX>
@@ -182,9 +194,9 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs ga)
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  GemmArgs g = ga;                          // a grouped forward's workgroup swaps in its weight
-  const int64_t Lc = DX ? g.N : g.K;       // contraction length
-  const int gx = ga.nw > 1 ? ga.gx_total : (int)(((DX ? g.K : g.N) + kBN - 1) / kBN);   // column tiles
+  GemmArgs g = ga;                          // a grouped launch's workgroup swaps in its weight
+  // column tiles (of the whole group in a grouped forward; of each weight's dX, all of width K)
+  const int gx = (!DX && ga.nw > 1) ? ga.gx_total : (int)(((DX ? g.K : g.N) + kBN - 1) / kBN);
 
   // Tile coordinates. Workgroups are dealt round-robin over the 8 XCDs (workgroup i to XCD i % 8,
   // in order of i), so each XCD gets a contiguous run of tiles that share an activation row block.
@@ -208,6 +220,20 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs ga)
       tile = g.whole_tiles + tail_r;
       nsplit = g.tail_split;
     }
+  } else if (DX && ga.nw > 1) {
+    // grouped dX: T tiles per weight; each XCD takes a contiguous run of every weight's tiles in
+    // turn (the longest contraction first, as the caller orders them), so the XCDs get equal work
+    const int T = total / ga.nw;
+    int wi;
+    if ((T & 7) == 0) {
+      const int xcd = bid & 7, k = bid >> 3, t8 = T >> 3;
+      wi = k / t8;
+      tile = xcd * t8 + k % t8;
+    } else {
+      wi = bid / T;
+      tile = bid % T;
+    }
+    use_weight<true>(g, ga, wi);
   } else {
     int lin = bid;
     if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
@@ -218,6 +244,7 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs ga)
   int64_t col0 = (int64_t)(tile % gx) * kBN;
   const int64_t m0 = (int64_t)(tile / gx) * BM;
   if (!DX && ga.nw > 1) select_weight(g, ga, tile % gx, col0);
+  const int64_t Lc = DX ? g.N : g.K;       // contraction length
   const int64_t Nout = DX ? g.K : g.N;     // output columns
 
   const int main_total = (int)((Lc + kBK - 1) / kBK);
@@ -861,11 +888,37 @@ hipError_t launch_fwd_gemm_group(int count, const FwdGroupItem* it, int64_t K, c
   int tile0 = 0;
   for (int i = 0; i < count; ++i) {
     if ((it[i].absmax != nullptr) != f32s) return hipErrorInvalidValue;
-    g.w[i] = GemmWeight{it[i].packed, it[i].scale_q, it[i].scale_c2, it[i].absmax, it[i].N, it[i].u, it[i].B, it[i].y,
-                        tile0};
+    g.w[i] = GemmWeight{it[i].packed, it[i].scale_q, it[i].scale_c2, it[i].absmax, it[i].N, nullptr, it[i].u, it[i].B,
+                        it[i].y, tile0};
     tile0 += (int)((it[i].N + kBN - 1) / kBN);
   }
   return f32s ? launch_gemm_t<false, true>(g, p, stream) : launch_gemm_t<false, false>(g, p, stream);
+}
+
+// The grouped dX (256-row tiles, no split): every weight's M x K tiles in turn, each linear with its
+// own dY, v, A and dX. Eligible when M > 128 and the tiles of all weights number at least 192.
+bool dx_group_eligible(int count, int64_t M, int64_t K) {
+  const int64_t t = ((K + kBN - 1) / kBN) * ((M + 255) / 256);
+  return count >= 2 && count <= kMaxGroup && M > 128 && t * count >= 192;
+}
+
+hipError_t launch_dx_gemm_group(int count, const DxGroupItem* it, int64_t K, int64_t M, int r, float scale,
+                                int book, hipStream_t stream) {
+  if (!dx_group_eligible(count, M, K)) return hipErrorInvalidValue;
+  const bool f32s = it[0].absmax != nullptr;
+  GemmArgs g{it[0].packed, it[0].scale_q, it[0].scale_c2, it[0].absmax, it[0].N, K, it[0].dy, M, it[0].v, it[0].A, r,
+             scale, it[0].dx, 1, nullptr, 0, 0, 0, {}, count, 0, {}};
+  if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
+  for (int i = 0; i < count; ++i) {
+    if ((it[i].absmax != nullptr) != f32s) return hipErrorInvalidValue;
+    g.w[i] = GemmWeight{it[i].packed, it[i].scale_q, it[i].scale_c2, it[i].absmax, it[i].N, it[i].dy, it[i].v, it[i].A,
+                        it[i].dx, 0};
+  }
+  const int gx = (int)((K + kBN - 1) / kBN), gy = (int)((M + 255) / 256);
+  const dim3 grid((unsigned)(gx * gy * count));
+  if (f32s) hipLaunchKernelGGL((qlora_gemm_kernel<true, 256, true>), grid, dim3(kThreads), 0, stream, g);
+  else hipLaunchKernelGGL((qlora_gemm_kernel<true, 256, false>), grid, dim3(kThreads), 0, stream, g);
+  return hipGetLastError();
 }
 
 }  // namespace nf4

@@ -57,6 +57,23 @@ bool fwd_group_eligible(int count, const int64_t* N, int64_t M, int64_t K);
 size_t fwd_group_part_floats(int count, const int64_t* N, int64_t M, int64_t K);
 hipError_t launch_fwd_gemm_group(int count, const FwdGroupItem* items, int64_t K, const uint16_t* x, int64_t M,
                                  int r, float scale, float* part, int book, hipStream_t stream);
+// A grouped dX: several linears that share x, each dX_i = dY_i W~_i + s v_i A_i into its own dx_i,
+// as one launch (the same per-tile arithmetic as launch_dx_gemm without partial sums). Eligible when
+// M > 128 and their 256-row tiles number at least 192.
+struct DxGroupItem {
+  const uint8_t* packed;
+  const uint8_t* scale_q;
+  const float* scale_c2;
+  const float* absmax;
+  int64_t N;
+  const uint16_t* dy;    // [M x N]
+  const float* v;        // v = dY B [M x r]
+  const uint16_t* A;     // [r x K]
+  uint16_t* dx;          // [M x K]
+};
+bool dx_group_eligible(int count, int64_t M, int64_t K);
+hipError_t launch_dx_gemm_group(int count, const DxGroupItem* items, int64_t K, int64_t M, int r, float scale,
+                                int book, hipStream_t stream);
 hipError_t launch_dx_gemm(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                           const float* absmax, int64_t N, int64_t K, const uint16_t* dy, int64_t M,
                           const float* v, const uint16_t* A, int r, float scale, uint16_t* dx,

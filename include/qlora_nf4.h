@@ -181,8 +181,24 @@ int qlora_linear_fwd_recompute_group(int32_t count, const nf4_weight *const *W, 
                                      const uint16_t *const *A, const uint16_t *const *B, int32_t r,
                                      float scale, float *const *u, uint16_t *const *y, void *ws,
                                      size_t ws_bytes, hipStream_t stream);
-/* Workspace bytes of qlora_linear_fwd_group (and of its recompute) for weights of N[0..count-1]
- * rows; 0 for sizes it refuses. N is a HOST array. */
+/* Backward of several adapted linears that share their input x (the group of
+ * qlora_linear_fwd_group): for every i < count, as qlora_linear_bwd on linear i (dX_i, dA_i, dB_i
+ * into its own outputs). Above 128 tokens, when the linears' 256-row dX tiles number at least 192
+ * together, their dX GEMMs run as one launch (each dX_i is then computed exactly as a dX launch
+ * without a split contraction computes it); the adapter passes run per linear.
+ *   W, dy, A, B, u, dA, dB: HOST arrays of count entries, each as in qlora_linear_bwd.
+ *   dx: NULL (no input gradient) or a HOST array of count device pointers, all set. A layer's
+ *       gradient with respect to the shared x is the sum of the dX_i.
+ *   ws: at least qlora_workspace_bytes_group(count, N, M, K, r) bytes.
+ * Errors: as qlora_linear_bwd; NF4_ERR_SHAPE also for count outside 1..4 and for weights that
+ * differ in K, codebook or kind of scales. */
+int qlora_linear_bwd_group(int32_t count, const nf4_weight *const *W, const uint16_t *x,
+                           const uint16_t *const *dy, int64_t M, const uint16_t *const *A,
+                           const uint16_t *const *B, int32_t r, float scale, const float *const *u,
+                           uint16_t *const *dx, float *const *dA, float *const *dB, int accumulate,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+/* Workspace bytes of qlora_linear_fwd_group, its recompute and qlora_linear_bwd_group for weights
+ * of N[0..count-1] rows; 0 for sizes they refuse. N is a HOST array. */
 size_t qlora_workspace_bytes_group(int32_t count, const int64_t *N, int64_t M, int64_t K, int32_t r);
 
 /* qlora_linear_fwd for callers that cannot allocate device memory (code under HIP graph capture,

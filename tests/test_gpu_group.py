@@ -132,3 +132,80 @@ def test_group_recompute_equals_the_forward(M, Ns, K):
     torch.cuda.synchronize()
     for i in range(len(qws)):
         assert np.array_equal(bits_from_dev(y2[i]), ys[i]), i
+
+
+def _run_bwd_group(qws, x, dys, As, Bs, s, us, accumulate=False, dA0=None, dB0=None):
+    import torch
+    import bit_nf4_quantised_amd as q
+    M, K = x.shape
+    r = As[0].shape[0]
+    dxs = [torch.empty(M, K, dtype=torch.int16, device=dev()) for _ in qws]
+    dAs = [to_dev(a) if dA0 is not None else torch.empty(r, K, dtype=torch.float32, device=dev())
+           for a in (dA0 if dA0 is not None else qws)]
+    dBs = [to_dev(b) if dB0 is not None else torch.empty(w.N, r, dtype=torch.float32, device=dev())
+           for w, b in zip(qws, dB0 if dB0 is not None else qws)]
+    q.qlora_linear_bwd_group(qws, bf16_to_dev(x), [bf16_to_dev(d) for d in dys], [bf16_to_dev(a) for a in As],
+                             [bf16_to_dev(b) for b in Bs], s, [to_dev(u) for u in us], dxs, dAs, dBs,
+                             accumulate=accumulate)
+    torch.cuda.synchronize()
+    return [bits_from_dev(d) for d in dxs], [d.cpu().numpy() for d in dAs], [d.cpu().numpy() for d in dBs]
+
+
+@pytest.mark.parametrize("M,Ns,K,r,s", [
+    (300, (2048, 512, 512), 12288, 16, 2.0),   # one dX launch: 3 x 192 tiles (each linear alone: 256-row
+                                               #   tiles, no split, so dX bit-equal to the single calls)
+    (600, (2064, 1040), 4096, 32, 0.5),        # one dX launch, ragged contractions, 3 row blocks
+    (100, (400, 128), 960, 16, 2.0),           # at most 128 tokens: linear by linear
+])
+def test_bwd_group_matches_oracle_and_single_calls(M, Ns, K, r, s):
+    import torch
+    import bit_nf4_quantised_amd as q
+    x, ws, As, Bs = _group(17 + M, M, Ns, K, r)
+    g = wl.rng_for("single", 900 + M, "dy")
+    dys = [wl.to_bf16_bits(g.standard_normal((M, N), dtype=np.float32)) for N in Ns]
+    log(f"[group] bwd M={M} N={Ns} K={K} r={r}")
+    qw_wt = [_quantize(w) for w in ws]
+    qws = [qw for qw, _ in qw_wt]
+    _, us = _run_group(qws, x, As, Bs, s)
+    dxs, dAs, dBs = _run_bwd_group(qws, x, dys, As, Bs, s, us)
+    for i, ((qw, wt), a, b, dy) in enumerate(zip(qw_wt, As, Bs, dys)):
+        dxr, dar, dbr = oracle.linear_bwd(x, dy, wt, a, b, s)
+        assert_close(f"dx{i}", f64_from_bits(dxs[i]), dxr)
+        assert_close(f"dA{i}", dAs[i], dar)
+        assert_close(f"dB{i}", dBs[i], dbr)
+        # the single backward of the same linear: dA, dB bit for bit (same launches); dX bit for bit
+        # where its own launch takes the same tiles without a split, else within the tolerance
+        dx1 = torch.empty(M, K, dtype=torch.int16, device=dev())
+        dA1 = torch.empty(r, K, dtype=torch.float32, device=dev())
+        dB1 = torch.empty(qw.N, r, dtype=torch.float32, device=dev())
+        q.qlora_linear_bwd(qw, bf16_to_dev(x), bf16_to_dev(dy), bf16_to_dev(a), bf16_to_dev(b), s, to_dev(us[i]), dx1,
+                           dA1, dB1)
+        torch.cuda.synchronize()
+        assert np.array_equal(dA1.cpu().numpy(), dAs[i]), i
+        assert np.array_equal(dB1.cpu().numpy(), dBs[i]), i
+        if M == 300:
+            assert np.array_equal(bits_from_dev(dx1), dxs[i]), i
+        else:
+            assert_close(f"dx{i} single", f64_from_bits(dxs[i]), f64_from_bits(bits_from_dev(dx1)))
+
+
+def test_bwd_group_one_hot_rows_are_exact():
+    # B = 0: row i of dY_j one-hot at row n_i of W_j gives dX_j[i] = row n_i of W~_j, for every
+    # linear j of a one-launch group (which pins the weight, activation and output of every tile)
+    M, Ns, K, r = 300, (2048, 512, 512), 12288, 16
+    x, ws, As, Bs = _group(21, M, Ns, K, r)
+    qw_wt = [_quantize(w) for w in ws]
+    qws = [qw for qw, _ in qw_wt]
+    dys = []
+    rows = []
+    for N in Ns:
+        d = np.zeros((M, N), np.uint16)
+        rr = [(5 * i + 1) % N for i in range(M)]
+        for i, n in enumerate(rr):
+            d[i, n] = 0x3F80
+        dys.append(d)
+        rows.append(rr)
+    us = [np.zeros((M, r), np.float32) for _ in Ns]
+    dxs, _, _ = _run_bwd_group(qws, x, dys, As, [np.zeros_like(b) for b in Bs], 2.0, us)
+    for j, (_, wt) in enumerate(qw_wt):
+        assert np.array_equal(dxs[j], wt[rows[j]]), j
