@@ -347,8 +347,13 @@ int run_fwd_group(int32_t count, const nf4_weight* const* W, const uint16_t* x, 
     return NF4_OK;
   }
   nf4::FwdGroupItem it[4];
+  if (!recompute && !nf4::lora_u_uses_pass(r)) {
+    // rank 16: every u_i in one pass over x
+    if (nf4::launch_lora_u_group(x, M, K, count, A, u, stream) != hipSuccess) return NF4_ERR_HIP;
+  }
   for (int i = 0; i < count; ++i) {
-    if (!recompute && nf4::launch_lora_u(x, M, K, A[i], r, part, u[i], stream) != hipSuccess) return NF4_ERR_HIP;
+    if (!recompute && nf4::lora_u_uses_pass(r) && nf4::launch_lora_u(x, M, K, A[i], r, part, u[i], stream) != hipSuccess)
+      return NF4_ERR_HIP;
     it[i] = nf4::FwdGroupItem{W[i]->packed, W[i]->scale_q, W[i]->scale_c2, W[i]->absmax, N[i], u[i], B[i], y[i]};
   }
   return from_hip(nf4::launch_fwd_gemm_group(count, it, K, x, M, r, scale, part, W[0]->codebook, stream));

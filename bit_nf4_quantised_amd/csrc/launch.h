@@ -94,6 +94,10 @@ size_t lora_pass_ws_floats(int64_t M, int64_t C, int r, bool down, bool grad);
 bool lora_u_uses_pass(int r);
 hipError_t launch_lora_u(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int r,
                          float* ws, float* u, hipStream_t stream);
+// u_i = X A_i^T for `count` (<= 8) linears of rank 16 that share X, in one launch (each u_i as
+// launch_lora_u forms it, bit for bit)
+hipError_t launch_lora_u_group(const uint16_t* X, int64_t M, int64_t K, int count, const uint16_t* const* A,
+                               float* const* u, hipStream_t stream);
 // v = dY B and dB = scale * dY^T u (+ dB if accumulate), in one pass over dY
 hipError_t launch_lora_dy(const uint16_t* dY, int64_t M, int64_t N, const uint16_t* B, const float* u,
                           int r, float scale, int accumulate, float* ws, float* v, float* dB,

@@ -373,10 +373,18 @@ static void launch_reduce(const ReduceJob& j0, const ReduceJob* j1, hipStream_t 
 // the 8 waves in LDS in wave order.
 constexpr int kUWaves = 8;
 
-template <int NT>   // r / 16
+// The 16-row tiles of A that one launch multiplies x by, and where each tile's 16 columns of u go:
+// tile t reads rows A[t] .. +15 (row pitch K) and writes u[t][m * ustride + 0..15]. One linear of
+// rank r has r / 16 consecutive tiles; the linears of a group at rank 16 have one tile each.
+struct UTiles {
+  const uint16_t* A[8];
+  float* u[8];
+  int ustride;
+};
+
+template <int NT>   // tiles
 __global__ __launch_bounds__(kUWaves * 64) void lora_u_kernel(const uint16_t* __restrict__ X, int64_t M,
-                                                            int64_t K, const uint16_t* __restrict__ A,
-                                                            float* __restrict__ u) {
+                                                            int64_t K, const UTiles ut) {
   constexpr int NB = NT >= 8 ? 1 : 8 / NT;   // chunks per batch
   constexpr int r = 16 * NT;
   __shared__ f32x4 red[kUWaves][NT][64];
@@ -385,7 +393,7 @@ __global__ __launch_bounds__(kUWaves * 64) void lora_u_kernel(const uint16_t* __
   const int g = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
   const uint16_t* xrow = X + min(m0 + (lane & 15), M - 1) * K + 8 * g;
-  const uint16_t* arow = A + (int64_t)(lane & 15) * K + 8 * g;
+  const int64_t aoff = (int64_t)(lane & 15) * K + 8 * g;
   const int64_t nchunks = K / 32;
 
   f32x4 acc[NT];
@@ -399,7 +407,7 @@ __global__ __launch_bounds__(kUWaves * 64) void lora_u_kernel(const uint16_t* __
       const int64_t col = min(c0 + (int64_t)kUWaves * b, nchunks - 1) * 32;
       xv[b] = *reinterpret_cast<const bf16x8*>(xrow + col);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) av[b][t] = *reinterpret_cast<const bf16x8*>(arow + (int64_t)t * 16 * K + col);
+      for (int t = 0; t < NT; ++t) av[b][t] = *reinterpret_cast<const bf16x8*>(ut.A[t] + aoff + col);
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -419,11 +427,42 @@ __global__ __launch_bounds__(kUWaves * 64) void lora_u_kernel(const uint16_t* __
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kUWaves; ++w) v += red[w][t][ln][i];
-    if (m0 + row < M) u[(m0 + row) * r + j] = v;
+    if (m0 + row < M) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+        if (tt == t) ut.u[tt][(m0 + row) * ut.ustride + (j & 15)] = v;
+    }
   }
 }
 
 bool lora_u_uses_pass(int r) { return r > 16; }
+
+static void launch_u_tiles(const uint16_t* X, int64_t M, int64_t K, int nt, const UTiles& ut, hipStream_t stream) {
+  const dim3 grid((unsigned)((M + 15) / 16)), block(kUWaves * 64);
+  switch (nt) {
+    case 1: hipLaunchKernelGGL(lora_u_kernel<1>, grid, block, 0, stream, X, M, K, ut); break;
+    case 2: hipLaunchKernelGGL(lora_u_kernel<2>, grid, block, 0, stream, X, M, K, ut); break;
+    case 3: hipLaunchKernelGGL(lora_u_kernel<3>, grid, block, 0, stream, X, M, K, ut); break;
+    case 4: hipLaunchKernelGGL(lora_u_kernel<4>, grid, block, 0, stream, X, M, K, ut); break;
+    case 5: hipLaunchKernelGGL(lora_u_kernel<5>, grid, block, 0, stream, X, M, K, ut); break;
+    case 6: hipLaunchKernelGGL(lora_u_kernel<6>, grid, block, 0, stream, X, M, K, ut); break;
+    case 7: hipLaunchKernelGGL(lora_u_kernel<7>, grid, block, 0, stream, X, M, K, ut); break;
+    default: hipLaunchKernelGGL(lora_u_kernel<8>, grid, block, 0, stream, X, M, K, ut); break;
+  }
+}
+
+hipError_t launch_lora_u_group(const uint16_t* X, int64_t M, int64_t K, int count, const uint16_t* const* A,
+                               float* const* u, hipStream_t stream) {
+  if (count < 1 || count > 8) return hipErrorInvalidValue;
+  UTiles ut{};
+  for (int i = 0; i < count; ++i) {
+    ut.A[i] = A[i];
+    ut.u[i] = u[i];
+  }
+  ut.ustride = 16;
+  launch_u_tiles(X, M, K, count, ut, stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_lora_u(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int r,
                          float* ws, float* u, hipStream_t stream) {
@@ -436,17 +475,13 @@ hipError_t launch_lora_u(const uint16_t* X, int64_t M, int64_t K, const uint16_t
     launch_reduce(reduce_job(ws, p.cranges, M * r, 0, r, false, 1.f, 0, u), nullptr, stream);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((M + 15) / 16)), block(kUWaves * 64);
-  switch (r / 16) {
-    case 1: hipLaunchKernelGGL(lora_u_kernel<1>, grid, block, 0, stream, X, M, K, A, u); break;
-    case 2: hipLaunchKernelGGL(lora_u_kernel<2>, grid, block, 0, stream, X, M, K, A, u); break;
-    case 3: hipLaunchKernelGGL(lora_u_kernel<3>, grid, block, 0, stream, X, M, K, A, u); break;
-    case 4: hipLaunchKernelGGL(lora_u_kernel<4>, grid, block, 0, stream, X, M, K, A, u); break;
-    case 5: hipLaunchKernelGGL(lora_u_kernel<5>, grid, block, 0, stream, X, M, K, A, u); break;
-    case 6: hipLaunchKernelGGL(lora_u_kernel<6>, grid, block, 0, stream, X, M, K, A, u); break;
-    case 7: hipLaunchKernelGGL(lora_u_kernel<7>, grid, block, 0, stream, X, M, K, A, u); break;
-    default: hipLaunchKernelGGL(lora_u_kernel<8>, grid, block, 0, stream, X, M, K, A, u); break;
+  UTiles ut{};
+  for (int t = 0; t < r / 16; ++t) {
+    ut.A[t] = A + (int64_t)t * 16 * K;
+    ut.u[t] = u + 16 * t;
   }
+  ut.ustride = r;
+  launch_u_tiles(X, M, K, r / 16, ut, stream);
   return hipGetLastError();
 }
 
