@@ -163,12 +163,13 @@ size_t fwd_group_ws(int count, const int64_t* N, int64_t M, int64_t K, int r) {
 }
 
 // Workspace of a grouped backward: [v of each linear (M*r fp32 each)] [partial sums: the largest of
-// each linear's passes and of its dX launch when it runs alone].
+// the passes over every dY, of a dX launch of one linear and of the passes over X].
 size_t bwd_group_ws(int count, const int64_t* N, int64_t M, int64_t K, int r) {
-  size_t part = nf4::lora_pass_ws_floats(M, K, r, false, true);
+  size_t part = nf4::lora_dy_group_ws_floats(count, N, M, r);
+  const size_t ga = nf4::lora_dx_group_ws_floats(count, M, K, r);
+  if (ga > part) part = ga;
   for (int i = 0; i < count; ++i) {
-    const size_t d = nf4::lora_pass_ws_floats(M, N[i], r, true, true), x = nf4::dx_gemm_part_floats(M, N[i], K);
-    if (d > part) part = d;
+    const size_t x = nf4::dx_gemm_part_floats(M, N[i], K);
     if (x > part) part = x;
   }
   return (size_t)count * align_up((size_t)M * r * 4) + align_up(part * 4);
@@ -414,11 +415,12 @@ int qlora_linear_bwd_group(int32_t count, const nf4_weight* const* W, const uint
   const size_t vslot = align_up((size_t)M * r * 4);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + count * vslot);
   float* v[4];
+  nf4::LoraDyItem dyi[4];
   for (int i = 0; i < count; ++i) {
     v[i] = reinterpret_cast<float*>(static_cast<char*>(ws) + i * vslot);
-    if (nf4::launch_lora_dy(dy[i], M, N[i], B[i], u[i], r, scale, accumulate, part, v[i], dB[i], stream) != hipSuccess)
-      return NF4_ERR_HIP;
+    dyi[i] = nf4::LoraDyItem{dy[i], N[i], B[i], u[i], v[i], dB[i]};
   }
+  if (nf4::launch_lora_dy_group(count, dyi, M, r, scale, accumulate, part, stream) != hipSuccess) return NF4_ERR_HIP;
   if (dx) {
     if (nf4::dx_group_eligible(count, M, K)) {
       // the longest contraction first, so that every XCD gets its share of each weight's tiles in
@@ -444,9 +446,9 @@ int qlora_linear_bwd_group(int32_t count, const nf4_weight* const* W, const uint
           return NF4_ERR_HIP;
     }
   }
-  for (int i = 0; i < count; ++i)
-    if (nf4::launch_lora_dx(x, M, K, v[i], r, scale, accumulate, part, dA[i], stream) != hipSuccess) return NF4_ERR_HIP;
-  return NF4_OK;
+  return nf4::launch_lora_dx_group(count, x, M, K, v, r, scale, accumulate, part, dA, stream) == hipSuccess
+             ? NF4_OK
+             : NF4_ERR_HIP;
 }
 
 int qlora_linear_fwd_noalloc(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A,

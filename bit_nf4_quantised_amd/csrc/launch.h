@@ -105,6 +105,24 @@ hipError_t launch_lora_dy(const uint16_t* dY, int64_t M, int64_t N, const uint16
 // dA = scale * v^T X (+ dA if accumulate)
 hipError_t launch_lora_dx(const uint16_t* X, int64_t M, int64_t K, const float* v, int r, float scale,
                           int accumulate, float* ws, float* dA, hipStream_t stream);
+// The same for `count` linears at once, each result bit for bit as the one-linear call gives it.
+// dY side (count <= 4): every linear's pass, then one launch of the ordered sums of all of them; ws
+// holds lora_dy_group_ws_floats floats (each linear's partial sums in turn).
+struct LoraDyItem {
+  const uint16_t* dY;
+  int64_t N;
+  const uint16_t* B;
+  const float* u;
+  float* v;
+  float* dB;
+};
+size_t lora_dy_group_ws_floats(int count, const int64_t* N, int64_t M, int r);
+hipError_t launch_lora_dy_group(int count, const LoraDyItem* it, int64_t M, int r, float scale, int accumulate,
+                                float* ws, hipStream_t stream);
+// X side (count <= 4 linears sharing X): dA_i = scale * v_i^T X; ws holds lora_dx_group_ws_floats floats
+size_t lora_dx_group_ws_floats(int count, int64_t M, int64_t K, int r);
+hipError_t launch_lora_dx_group(int count, const uint16_t* X, int64_t M, int64_t K, const float* const* v, int r,
+                                float scale, int accumulate, float* ws, float* const* dA, hipStream_t stream);
 
 // Skinny forward (M <= 16): split-K dequant-GEMV on MFMA with a deterministic reduction.
 // `part` holds skinny_workspace_floats(M, N, K, r) floats; u_out receives u = x A^T [M x r].

@@ -54,11 +54,14 @@ struct LoraPassArgs {
   const uint16_t* Q;        // [M x C] bf16
   int64_t M, C;
   const uint16_t* R;        // down operand: A [r x C] (RT = false) or B [C x r] (RT = true)
-  const float* P;           // grad operand [M x r] fp32
+  // grad operand [M x r] fp32: the r / rl operands P[i], each [M x rl], side by side (linears of rank rl
+  // that share Q; one operand, rl = r, otherwise)
+  const float* P[4];
+  int rl;
   int r;
   int64_t crange;           // columns per workgroup column range (a multiple of kStepC)
   float* part_down;         // [column ranges][M][r]
-  float* part_grad;         // [row blocks][C][r]
+  float* part_grad;         // [r / rl][row blocks][C][rl]: each operand's partial sums on their own
 };
 
 // RMAX: the rank rounded up to 16, 32, 64 or 128 (the tiles are sized for it); QS: Q stages in
@@ -131,8 +134,13 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
     const int cols4 = r / 4;
     for (int q = tid; q < MB * cols4; q += 256) {
       const int row = q / cols4, c4 = (q % cols4) * 4;
+      const int li = c4 / a.rl;
+      const float* src = a.P[0];
+      if (li == 1) src = a.P[1];
+      if (li == 2) src = a.P[2];
+      if (li == 3) src = a.P[3];
       f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (row < rows_valid) v = *reinterpret_cast<const f32x4*>(a.P + (m0 + row) * r + c4);
+      if (row < rows_valid) v = *reinterpret_cast<const f32x4*>(src + (m0 + row) * a.rl + c4 - li * a.rl);
       const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
       const uint32_t l01 = pack_bf16x2(v[0] - __uint_as_float(h01 << 16), v[1] - __uint_as_float(h01 & 0xFFFF0000u));
       const uint32_t l23 = pack_bf16x2(v[2] - __uint_as_float(h23 << 16), v[3] - __uint_as_float(h23 & 0xFFFF0000u));
@@ -154,6 +162,14 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
 
   // ---- accumulators. down: wave owns rows wave * MB/4 ..; grad: wave owns columns 16 wave .. of
   // each step.
+  // where the 16 grad columns of tile jt go: operand jt * 16 / rl, its columns from jt * 16 % rl
+  float* gdst[RMAX / 16];
+#pragma unroll
+  for (int jt = 0; jt < RMAX / 16; ++jt) {
+    const int li = GRAD && jt < RT16 ? jt * 16 / a.rl : 0;
+    gdst[jt] = a.part_grad + ((int64_t)li * gridDim.x + blockIdx.x) * a.C * a.rl + jt * 16 - li * a.rl;
+  }
+
   constexpr int MT = MB / 64;   // 16-row tiles of a wave (down)
   f32x4 dacc[DOWN ? MT : 1][RMAX / 16];
   f32x4 gacc[RMAX / 16];
@@ -217,10 +233,9 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
       }
       const int64_t c = c0 + wave * 16 + (lane & 15);
       if (c < a.C) {
-        float* dst = a.part_grad + ((int64_t)blockIdx.x * a.C + c) * r + 4 * (lane >> 4);
 #pragma unroll
         for (int jt = 0; jt < RMAX / 16; ++jt)
-          if (jt < RT16) *reinterpret_cast<f32x4*>(dst + jt * 16) = gacc[jt];
+          if (jt < RT16) *reinterpret_cast<f32x4*>(gdst[jt] + c * a.rl + 4 * (lane >> 4)) = gacc[jt];
       }
     }
   };
@@ -265,10 +280,10 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
 
 // Ordered sums of partial results. A job: out[i] = scale * (sum over p < nparts, in order, of
 // part[p * count + i]) (+ out[i]); with `transpose`, part is [C][r] and out is [r][C]. One launch
-// serves two jobs (blocks [0, blocks0) take job 0). A thread takes one element of the partials'
-// own order (so the loads of a wave are contiguous; a transposed job scatters only its one store)
-// and issues the loads of 8 partials at a time before adding them in order; the sums are
-// latency-bound chains, so one output per thread gives the most chains in flight.
+// serves up to kMaxReduceJobs jobs (blocks [first[k], first[k + 1]) take job k). A thread takes one
+// element of the partials' own order (so the loads of a wave are contiguous; a transposed job
+// scatters only its one store) and issues the loads of 8 partials at a time before adding them in
+// order; the sums are latency-bound chains, so one output per thread gives the most chains in flight.
 struct ReduceJob {
   const float* part;
   int nparts;
@@ -277,11 +292,24 @@ struct ReduceJob {
   float scale;
   float* out;
 };
+constexpr int kMaxReduceJobs = 8;
+struct ReduceJobs {
+  ReduceJob j[kMaxReduceJobs];
+  int first[kMaxReduceJobs];
+  int n;
+};
 
-__global__ __launch_bounds__(256) void lora_reduce_kernel(const ReduceJob j0, const ReduceJob j1, int blocks0) {
-  const bool second = (int)blockIdx.x >= blocks0;
-  const ReduceJob& jb = second ? j1 : j0;
-  const int64_t src = (int64_t)(second ? blockIdx.x - blocks0 : blockIdx.x) * 256 + threadIdx.x;
+__global__ __launch_bounds__(256) void lora_reduce_kernel(const ReduceJobs js) {
+  // the job of this workgroup, chosen by scalar selects (no indexing of the argument block)
+  ReduceJob jb = js.j[0];
+  int b0 = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxReduceJobs; ++k)
+    if (k < js.n && (int)blockIdx.x >= js.first[k]) {
+      jb = js.j[k];
+      b0 = js.first[k];
+    }
+  const int64_t src = (int64_t)((int)blockIdx.x - b0) * 256 + threadIdx.x;
   if (src >= jb.count) return;
   // part [C][r] -> out [r][C]: element (c, j) = src goes to j * C + c
   const int64_t i = jb.transpose ? (src % jb.r) * jb.C + src / jb.r : src;
@@ -357,10 +385,16 @@ static ReduceJob reduce_job(const float* part, int nparts, int64_t count, int64_
   return ReduceJob{part, nparts, count, C, r, transpose ? 1 : 0, accumulate, scale, out};
 }
 
-static void launch_reduce(const ReduceJob& j0, const ReduceJob* j1, hipStream_t stream) {
-  const int b0 = (int)((j0.count + 255) / 256);
-  const int b1 = j1 ? (int)((j1->count + 255) / 256) : 0;
-  hipLaunchKernelGGL(lora_reduce_kernel, dim3((unsigned)(b0 + b1)), dim3(256), 0, stream, j0, j1 ? *j1 : j0, b0);
+static void launch_reduce(const ReduceJob* jobs, int n, hipStream_t stream) {
+  ReduceJobs js{};
+  int blocks = 0;
+  for (int k = 0; k < n; ++k) {
+    js.j[k] = jobs[k];
+    js.first[k] = blocks;
+    blocks += (int)((jobs[k].count + 255) / 256);
+  }
+  js.n = n;
+  hipLaunchKernelGGL(lora_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, js);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -470,9 +504,10 @@ hipError_t launch_lora_u(const uint16_t* X, int64_t M, int64_t K, const uint16_t
     // above rank 16 a workgroup of lora_u_kernel would read r x K of A for its 16 rows: the pass
     // reads A once per row block of 256 and leaves partial sums over column ranges in ws
     const LoraPassPlan p = lora_pass_plan(M, K, r);
-    const LoraPassArgs a{X, M, K, A, nullptr, r, p.crange, ws, nullptr};
+    const LoraPassArgs a{X, M, K, A, {}, r, r, p.crange, ws, nullptr};
     launch_pass<true, false, false>(p, a, stream);
-    launch_reduce(reduce_job(ws, p.cranges, M * r, 0, r, false, 1.f, 0, u), nullptr, stream);
+    const ReduceJob j = reduce_job(ws, p.cranges, M * r, 0, r, false, 1.f, 0, u);
+    launch_reduce(&j, 1, stream);
     return hipGetLastError();
   }
   UTiles ut{};
@@ -485,27 +520,74 @@ hipError_t launch_lora_u(const uint16_t* X, int64_t M, int64_t K, const uint16_t
   return hipGetLastError();
 }
 
+size_t lora_dy_group_ws_floats(int count, const int64_t* N, int64_t M, int r) {
+  size_t f = 0;
+  for (int i = 0; i < count; ++i) f += lora_pass_ws_floats(M, N[i], r, true, true);
+  return f;
+}
+
+hipError_t launch_lora_dy_group(int count, const LoraDyItem* it, int64_t M, int r, float scale, int accumulate,
+                                float* ws, hipStream_t stream) {
+  if (count < 1 || count > kMaxReduceJobs / 2) return hipErrorInvalidValue;
+  ReduceJob jobs[kMaxReduceJobs];
+  for (int i = 0; i < count; ++i) {
+    const LoraPassPlan p = lora_pass_plan(M, it[i].N, r);
+    float* part_down = ws;
+    float* part_grad = ws + (size_t)p.cranges * M * r;
+    ws = part_grad + (size_t)p.mblocks * it[i].N * r;
+    const LoraPassArgs a{it[i].dY, M, it[i].N, it[i].B, {it[i].u}, r, r, p.crange, part_down, part_grad};
+    launch_pass<true, true, true>(p, a, stream);
+    jobs[2 * i] = reduce_job(part_down, p.cranges, M * r, 0, r, false, 1.f, 0, it[i].v);
+    jobs[2 * i + 1] = reduce_job(part_grad, p.mblocks, it[i].N * r, 0, r, false, scale, accumulate, it[i].dB);
+  }
+  launch_reduce(jobs, 2 * count, stream);
+  return hipGetLastError();
+}
+
 hipError_t launch_lora_dy(const uint16_t* dY, int64_t M, int64_t N, const uint16_t* B, const float* u,
                           int r, float scale, int accumulate, float* ws, float* v, float* dB,
                           hipStream_t stream) {
-  const LoraPassPlan p = lora_pass_plan(M, N, r);
-  float* part_down = ws;
-  float* part_grad = ws + (size_t)p.cranges * M * r;
-  LoraPassArgs a{dY, M, N, B, u, r, p.crange, part_down, part_grad};
-  launch_pass<true, true, true>(p, a, stream);
-  const ReduceJob jv = reduce_job(part_down, p.cranges, M * r, 0, r, false, 1.f, 0, v);
-  const ReduceJob jb = reduce_job(part_grad, p.mblocks, N * r, 0, r, false, scale, accumulate, dB);
-  launch_reduce(jv, &jb, stream);
+  const LoraDyItem it{dY, N, B, u, v, dB};
+  return launch_lora_dy_group(1, &it, M, r, scale, accumulate, ws, stream);
+}
+
+// The passes over X of linears that share it take one launch while their ranks add up to 64 or less:
+// the grad operands then sit side by side in the pass's tiles and the row blocks stay 256 rows, so
+// each dA comes out as its own pass would give it, bit for bit.
+static bool dx_pass_grouped(int count, int r) { return count > 1 && count * r <= 64; }
+
+size_t lora_dx_group_ws_floats(int count, int64_t M, int64_t K, int r) {
+  return dx_pass_grouped(count, r) ? lora_pass_ws_floats(M, K, count * r, false, true)
+                                   : (size_t)count * lora_pass_ws_floats(M, K, r, false, true);
+}
+
+hipError_t launch_lora_dx_group(int count, const uint16_t* X, int64_t M, int64_t K, const float* const* v, int r,
+                                float scale, int accumulate, float* ws, float* const* dA, hipStream_t stream) {
+  if (count < 1 || count > 4) return hipErrorInvalidValue;
+  ReduceJob jobs[4];
+  if (dx_pass_grouped(count, r)) {
+    const LoraPassPlan p = lora_pass_plan(M, K, count * r);
+    LoraPassArgs a{X, M, K, nullptr, {}, r, count * r, p.crange, nullptr, ws};
+    for (int i = 0; i < count; ++i) a.P[i] = v[i];
+    launch_pass<false, true, false>(p, a, stream);
+    for (int i = 0; i < count; ++i)
+      jobs[i] = reduce_job(ws + (size_t)i * p.mblocks * K * r, p.mblocks, K * r, K, r, true, scale, accumulate, dA[i]);
+  } else {
+    for (int i = 0; i < count; ++i) {
+      const LoraPassPlan p = lora_pass_plan(M, K, r);
+      const LoraPassArgs a{X, M, K, nullptr, {v[i]}, r, r, p.crange, nullptr, ws};
+      launch_pass<false, true, false>(p, a, stream);
+      jobs[i] = reduce_job(ws, p.mblocks, K * r, K, r, true, scale, accumulate, dA[i]);
+      ws += (size_t)p.mblocks * K * r;
+    }
+  }
+  launch_reduce(jobs, count, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_lora_dx(const uint16_t* X, int64_t M, int64_t K, const float* v, int r, float scale,
                           int accumulate, float* ws, float* dA, hipStream_t stream) {
-  const LoraPassPlan p = lora_pass_plan(M, K, r);
-  LoraPassArgs a{X, M, K, nullptr, v, r, p.crange, nullptr, ws};
-  launch_pass<false, true, false>(p, a, stream);
-  launch_reduce(reduce_job(ws, p.mblocks, K * r, K, r, true, scale, accumulate, dA), nullptr, stream);
-  return hipGetLastError();
+  return launch_lora_dx_group(1, X, M, K, &v, r, scale, accumulate, ws, &dA, stream);
 }
 
 }  // namespace nf4

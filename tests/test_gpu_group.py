@@ -156,6 +156,9 @@ def _run_bwd_group(qws, x, dys, As, Bs, s, us, accumulate=False, dA0=None, dB0=N
                                                #   tiles, no split, so dX bit-equal to the single calls)
     (600, (2064, 1040), 4096, 32, 0.5),        # one dX launch, ragged contractions, 3 row blocks
     (100, (400, 128), 960, 16, 2.0),           # at most 128 tokens: linear by linear
+    (200, (512, 256, 384, 128), 1024, 32, 1.0),  # four linears: ranks add up past 64, so one pass over X
+                                                 #   per linear, and eight sums in one reduction launch
+    (130, (256, 256, 256, 256), 2048, 16, 2.0),  # four linears at rank 16: one pass over X for all
 ])
 def test_bwd_group_matches_oracle_and_single_calls(M, Ns, K, r, s):
     import torch
@@ -209,3 +212,33 @@ def test_bwd_group_one_hot_rows_are_exact():
     dxs, _, _ = _run_bwd_group(qws, x, dys, As, [np.zeros_like(b) for b in Bs], 2.0, us)
     for j, (_, wt) in enumerate(qw_wt):
         assert np.array_equal(dxs[j], wt[rows[j]]), j
+
+
+@pytest.mark.parametrize("Ns,r", [((512, 256, 256), 16), ((256, 384, 128, 256), 32)])
+def test_bwd_group_accumulates_like_single_calls(Ns, r):
+    # accumulate = 1 adds into dA, dB as the single backward does, bit for bit, in both forms of the
+    # passes over X (one launch for the group, one per linear)
+    import torch
+    import bit_nf4_quantised_amd as q
+    M, K, s = 260, 1088, 0.5
+    x, ws, As, Bs = _group(29 + r, M, Ns, K, r)
+    g = wl.rng_for("single", 950 + r, "dy")
+    dys = [wl.to_bf16_bits(g.standard_normal((M, N), dtype=np.float32)) for N in Ns]
+    dA0 = [g.standard_normal((r, K), dtype=np.float32) for _ in Ns]
+    dB0 = [g.standard_normal((N, r), dtype=np.float32) for N in Ns]
+    log(f"[group] bwd accumulate N={Ns} r={r}")
+    qw_wt = [_quantize(w) for w in ws]
+    qws = [qw for qw, _ in qw_wt]
+    _, us = _run_group(qws, x, As, Bs, s)
+    _, dAs, dBs = _run_bwd_group(qws, x, dys, As, Bs, s, us, accumulate=True, dA0=dA0, dB0=dB0)
+    for i, ((qw, wt), a, b, dy) in enumerate(zip(qw_wt, As, Bs, dys)):
+        _, dar, dbr = oracle.linear_bwd(x, dy, wt, a, b, s)
+        assert_close(f"dA{i}", dAs[i] - dA0[i].astype(np.float64), dar)
+        assert_close(f"dB{i}", dBs[i] - dB0[i].astype(np.float64), dbr)
+        dx1 = torch.empty(M, K, dtype=torch.int16, device=dev())
+        dA1, dB1 = to_dev(dA0[i]), to_dev(dB0[i])
+        q.qlora_linear_bwd(qw, bf16_to_dev(x), bf16_to_dev(dy), bf16_to_dev(a), bf16_to_dev(b), s, to_dev(us[i]), dx1,
+                           dA1, dB1, accumulate=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(dA1.cpu().numpy(), dAs[i]), i
+        assert np.array_equal(dB1.cpu().numpy(), dBs[i]), i
