@@ -399,13 +399,19 @@ static void launch_reduce(const ReduceJob* jobs, int n, hipStream_t stream) {
 
 // ------------------------------------------------------------------------------------------
 // u = X A^T at rank 16 in one launch, without partial sums in memory (its contraction runs over K only, so
-// a workgroup can own whole rows): a workgroup owns 16 rows of X and all of K. Its 8 waves take
-// interleaved 32-column chunks (wave w: chunks w, w + 8, ...), NB chunks at a time with every
-// load of a batch issued before its MFMAs; lane (row = lane % 16, g = lane / 16) holds columns
-// 8 g .. 8 g + 7 of the chunk of its row of X and of row 16 t + lane % 16 of A for each 16-row
-// tile t of A, and v_mfma_f32_16x16x32_bf16 accumulates u[row][16 t + j]. The workgroup then sums
-// the 8 waves in LDS in wave order.
-constexpr int kUWaves = 8;
+// a workgroup can own whole rows): a workgroup owns 16 rows of X and all of K. Its 16 waves take
+// groups of 8 adjacent 32-column chunks in turn (wave w: chunks 8 w .. 8 w + 7, then those 128
+// chunks on), in batches of NB chunks (NB divides 8). A wave adds its chunks in the same order
+// whatever NB is, so u comes out bit for bit the same for any number of tiles in the launch.
+// The MFMA operand layout (lane (row = lane % 16, g = lane / 16): columns 8 g .. 8 g + 7 of the
+// chunk in its row) would have each load instruction touch 16 rows at 64 bytes each; instead a wave
+// loads each batch of X and of every tile of A row by row, 64 NB contiguous bytes a row (whole
+// 128-byte lines from NB = 2 on) with consecutive lanes on consecutive 16-byte pieces, stores it to
+// its own LDS slice (pieces XOR-swizzled by row against bank conflicts) and reads it back in the
+// operand layout; v_mfma_f32_16x16x32_bf16 then accumulates u[row][16 t + j]. The workgroup sums
+// the 16 waves in LDS in wave order at the end.
+constexpr int kUWaves = 16;
+constexpr int kUGroup = 8;   // adjacent chunks per wave before the next wave's
 
 // The 16-row tiles of A that one launch multiplies x by, and where each tile's 16 columns of u go:
 // tile t reads rows A[t] .. +15 (row pitch K) and writes u[t][m * ustride + 0..15]. One linear of
@@ -416,43 +422,81 @@ struct UTiles {
   int ustride;
 };
 
+// chunks per batch: the wave's LDS slice, (1 + NT) NB KB, stays at 9 KB or less
+template <int NT>
+constexpr int u_batch() { return NT == 1 ? 4 : NT <= 3 ? 2 : 1; }
+
 template <int NT>   // tiles
 __global__ __launch_bounds__(kUWaves * 64) void lora_u_kernel(const uint16_t* __restrict__ X, int64_t M,
                                                             int64_t K, const UTiles ut) {
-  constexpr int NB = NT >= 8 ? 1 : 8 / NT;   // chunks per batch
+  constexpr int NB = u_batch<NT>();
+  constexpr int P = 4 * NB;            // 16-byte pieces of a row in a batch
+  constexpr int RI = 64 / P;           // rows per load instruction
+  constexpr int SLICE = (1 + NT) * 16 * P;   // pieces in a wave's slice
   constexpr int r = 16 * NT;
-  __shared__ f32x4 red[kUWaves][NT][64];
+  constexpr int STAGE = kUWaves * SLICE, RED = kUWaves * NT * 64;
+  __shared__ u32x4 lds[STAGE > RED ? STAGE : RED];
+  static_assert(kUGroup % NB == 0, "a batch stays inside one group of chunks");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const uint16_t* xrow = X + min(m0 + (lane & 15), M - 1) * K + 8 * g;
-  const int64_t aoff = (int64_t)(lane & 15) * K + 8 * g;
   const int64_t nchunks = K / 32;
+  u32x4* slice = lds + wave * SLICE;
+  // slot of piece p of row m of matrix q (0: X, 1 + t: tile t of A) in the slice
+  auto slot = [&](int q, int m, int p) {
+    const int sw = P >= 8 ? (m & 7) : ((m >> 1) & 3);
+    return (q * 16 + m) * P + (p ^ sw);
+  };
+  // the loads: instruction i of a matrix covers rows RI i + lane / P, piece lane % P
+  const int lp = lane % P;
+  const uint16_t* xsrc[16 / RI];
+#pragma unroll
+  for (int i = 0; i < 16 / RI; ++i) xsrc[i] = X + min(m0 + RI * i + lane / P, M - 1) * K + 8 * (lp & 3);
+  const int64_t aoff = (int64_t)(lane / P) * K + 8 * (lp & 3);
 
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t c0 = wave; c0 < nchunks; c0 += (int64_t)kUWaves * NB) {
-    bf16x8 xv[NB], av[NB][NT];
+  for (int64_t k0 = 0;; k0 += NB) {
+    const int64_t c0 = ((k0 / kUGroup) * kUWaves + wave) * kUGroup + k0 % kUGroup;
+    if (c0 >= nchunks) break;
+    // the lane's chunk; chunks past the end re-read the last one and are not accumulated
+    const int64_t col = min(c0 + lp / 4, nchunks - 1) * 32;
+    u32x4 xv[16 / RI], av[NT][16 / RI];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      // chunks past the end re-read the last one and are not accumulated
-      const int64_t col = min(c0 + (int64_t)kUWaves * b, nchunks - 1) * 32;
-      xv[b] = *reinterpret_cast<const bf16x8*>(xrow + col);
+    for (int i = 0; i < 16 / RI; ++i) xv[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + col);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) av[b][t] = *reinterpret_cast<const bf16x8*>(ut.A[t] + aoff + col);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16 / RI; ++i)
+        av[t][i] = *reinterpret_cast<const u32x4*>(ut.A[t] + (int64_t)RI * i * K + aoff + col);
+    __builtin_amdgcn_wave_barrier();   // the previous batch's slice reads come first
+#pragma unroll
+    for (int i = 0; i < 16 / RI; ++i) {
+      slice[slot(0, RI * i + lane / P, lp)] = xv[i];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) slice[slot(1 + t, RI * i + lane / P, lp)] = av[t][i];
     }
+    __builtin_amdgcn_wave_barrier();   // the slice is written before it is read
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      if (c0 + (int64_t)kUWaves * b < nchunks) {
+      const int m = lane & 15, p = 4 * b + (lane >> 4);
+      const u32x4 xo = slice[slot(0, m, p)];
+      u32x4 ao[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[b], av[b][t], acc[t], 0, 0, 0);
+      for (int t = 0; t < NT; ++t) ao[t] = slice[slot(1 + t, m, p)];
+      if (c0 + b < nchunks) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xo), __builtin_bit_cast(bf16x8, ao[t]),
+                                                           acc[t], 0, 0, 0);
       }
     }
   }
+  __syncthreads();   // every wave is done with its slice; the space now holds the waves' sums
+  f32x4* red = reinterpret_cast<f32x4*>(lds);   // [wave][t][lane]
 #pragma unroll
-  for (int t = 0; t < NT; ++t) red[wave][t][lane] = acc[t];
+  for (int t = 0; t < NT; ++t) red[(wave * NT + t) * 64 + lane] = acc[t];
   __syncthreads();
   // output o = (row, j): acc[t][i] of lane (row / 4) * 16 + j % 16 holds row 4 (lane / 16) + i
   for (int o = tid; o < 16 * r; o += kUWaves * 64) {
@@ -460,7 +504,7 @@ __global__ __launch_bounds__(kUWaves * 64) void lora_u_kernel(const uint16_t* __
     const int t = j >> 4, ln = (row >> 2) * 16 + (j & 15), i = row & 3;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kUWaves; ++w) v += red[w][t][ln][i];
+    for (int w = 0; w < kUWaves; ++w) v += red[(w * NT + t) * 64 + ln][i];
     if (m0 + row < M) {
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
