@@ -62,12 +62,32 @@ struct LoraPassArgs {
   int64_t crange;           // columns per workgroup column range (a multiple of kStepC)
   float* part_down;         // [column ranges][M][r]
   float* part_grad;         // [r / rl][row blocks][C][rl]: each operand's partial sums on their own
+  int mblocks;              // row blocks (workgroup b of the pass: row block b % mblocks, range b / mblocks)
+};
+
+// Passes of one kind and rank over different matrices, as one launch: workgroups [first[k],
+// first[k + 1]) run pass k. Each pass computes what it computes alone.
+constexpr int kMaxPassGroup = 4;
+struct LoraPassGroup {
+  LoraPassArgs a[kMaxPassGroup];
+  int first[kMaxPassGroup];
+  int n;
 };
 
 // RMAX: the rank rounded up to 16, 32, 64 or 128 (the tiles are sized for it); QS: Q stages in
 // LDS (QS - 1 steps in flight). With RMAX = 16 the grad operand fragments stay in registers.
 template <int MB, int RMAX, int QS, bool DOWN, bool GRAD, bool RT>
-__global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
+__global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassGroup pg) {
+  // this workgroup's pass, chosen by scalar selects (no indexing of the argument block)
+  LoraPassArgs a = pg.a[0];
+  int b0 = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxPassGroup; ++k)
+    if (k < pg.n && (int)blockIdx.x >= pg.first[k]) {
+      a = pg.a[k];
+      b0 = pg.first[k];
+    }
+  const int mbi = ((int)blockIdx.x - b0) % a.mblocks, cri = ((int)blockIdx.x - b0) / a.mblocks;
   constexpr bool R16 = RMAX == 16;
   constexpr int NQ = MB / 32;                           // Q DMA loads per wave per step
   constexpr int RTILE = DOWN ? kStepC * RMAX : 8;       // R tile elements per stage
@@ -80,9 +100,9 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = R16 ? 16 : a.r, RT16 = r / 16;
-  const int64_t m0 = (int64_t)blockIdx.x * MB;
+  const int64_t m0 = (int64_t)mbi * MB;
   const int64_t rows_valid = min(a.M - m0, (int64_t)MB);
-  const int64_t c_begin = (int64_t)blockIdx.y * a.crange;
+  const int64_t c_begin = (int64_t)cri * a.crange;
   const int64_t c_end = min(a.C, c_begin + a.crange);
   const int nsteps = (int)((c_end - c_begin + kStepC - 1) / kStepC);
 
@@ -167,7 +187,7 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
 #pragma unroll
   for (int jt = 0; jt < RMAX / 16; ++jt) {
     const int li = GRAD && jt < RT16 ? jt * 16 / a.rl : 0;
-    gdst[jt] = a.part_grad + ((int64_t)li * gridDim.x + blockIdx.x) * a.C * a.rl + jt * 16 - li * a.rl;
+    gdst[jt] = a.part_grad + ((int64_t)li * a.mblocks + mbi) * a.C * a.rl + jt * 16 - li * a.rl;
   }
 
   constexpr int MT = MB / 64;   // 16-row tiles of a wave (down)
@@ -265,7 +285,7 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(const LoraPassArgs a) {
   }
 
   if (DOWN) {
-    float* dst = a.part_down + (int64_t)blockIdx.y * a.M * r;
+    float* dst = a.part_down + (int64_t)cri * a.M * r;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int64_t m = m0 + wave * (MB / 4) + mt * 16 + (lane & 15);
@@ -363,21 +383,35 @@ constexpr int pass_stages() {
 }
 
 template <int MB, int RMAX, bool DOWN, bool GRAD, bool RT>
-static void launch_pass_t(dim3 grid, const LoraPassArgs& a, hipStream_t stream) {
+static void launch_pass_t(unsigned blocks, const LoraPassGroup& pg, hipStream_t stream) {
   constexpr int QS = pass_stages<MB, RMAX, DOWN, GRAD>();
   static_assert(QS >= 2, "two stages at least");
-  hipLaunchKernelGGL((lora_pass_kernel<MB, RMAX, QS, DOWN, GRAD, RT>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((lora_pass_kernel<MB, RMAX, QS, DOWN, GRAD, RT>), dim3(blocks), dim3(256), 0, stream, pg);
+}
+
+// n passes of one rank (each with its plan p[k]) as one launch
+template <bool DOWN, bool GRAD, bool RT>
+static void launch_passes(int n, const LoraPassPlan* p, const LoraPassArgs* a, hipStream_t stream) {
+  LoraPassGroup pg{};
+  unsigned blocks = 0;
+  for (int k = 0; k < n; ++k) {
+    pg.a[k] = a[k];
+    pg.a[k].mblocks = p[k].mblocks;
+    pg.first[k] = (int)blocks;
+    blocks += (unsigned)p[k].mblocks * (unsigned)p[k].cranges;
+  }
+  pg.n = n;
+  switch (pass_rmax(a[0].r)) {
+    case 16: launch_pass_t<256, 16, DOWN, GRAD, RT>(blocks, pg, stream); break;
+    case 32: launch_pass_t<256, 32, DOWN, GRAD, RT>(blocks, pg, stream); break;
+    case 64: launch_pass_t<256, 64, DOWN, GRAD, RT>(blocks, pg, stream); break;
+    default: launch_pass_t<128, 128, DOWN, GRAD, RT>(blocks, pg, stream); break;
+  }
 }
 
 template <bool DOWN, bool GRAD, bool RT>
 static void launch_pass(const LoraPassPlan& p, const LoraPassArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)p.mblocks, (unsigned)p.cranges);
-  switch (pass_rmax(a.r)) {
-    case 16: launch_pass_t<256, 16, DOWN, GRAD, RT>(grid, a, stream); break;
-    case 32: launch_pass_t<256, 32, DOWN, GRAD, RT>(grid, a, stream); break;
-    case 64: launch_pass_t<256, 64, DOWN, GRAD, RT>(grid, a, stream); break;
-    default: launch_pass_t<128, 128, DOWN, GRAD, RT>(grid, a, stream); break;
-  }
+  launch_passes<DOWN, GRAD, RT>(1, &p, &a, stream);
 }
 
 static ReduceJob reduce_job(const float* part, int nparts, int64_t count, int64_t C, int r, bool transpose,
@@ -548,7 +582,7 @@ hipError_t launch_lora_u(const uint16_t* X, int64_t M, int64_t K, const uint16_t
     // above rank 16 a workgroup of lora_u_kernel would read r x K of A for its 16 rows: the pass
     // reads A once per row block of 256 and leaves partial sums over column ranges in ws
     const LoraPassPlan p = lora_pass_plan(M, K, r);
-    const LoraPassArgs a{X, M, K, A, {}, r, r, p.crange, ws, nullptr};
+    const LoraPassArgs a{X, M, K, A, {}, r, r, p.crange, ws, nullptr, 0};
     launch_pass<true, false, false>(p, a, stream);
     const ReduceJob j = reduce_job(ws, p.cranges, M * r, 0, r, false, 1.f, 0, u);
     launch_reduce(&j, 1, stream);
@@ -572,18 +606,20 @@ size_t lora_dy_group_ws_floats(int count, const int64_t* N, int64_t M, int r) {
 
 hipError_t launch_lora_dy_group(int count, const LoraDyItem* it, int64_t M, int r, float scale, int accumulate,
                                 float* ws, hipStream_t stream) {
-  if (count < 1 || count > kMaxReduceJobs / 2) return hipErrorInvalidValue;
+  if (count < 1 || count > kMaxPassGroup || 2 * count > kMaxReduceJobs) return hipErrorInvalidValue;
   ReduceJob jobs[kMaxReduceJobs];
+  LoraPassPlan p[kMaxPassGroup];
+  LoraPassArgs a[kMaxPassGroup];
   for (int i = 0; i < count; ++i) {
-    const LoraPassPlan p = lora_pass_plan(M, it[i].N, r);
+    p[i] = lora_pass_plan(M, it[i].N, r);
     float* part_down = ws;
-    float* part_grad = ws + (size_t)p.cranges * M * r;
-    ws = part_grad + (size_t)p.mblocks * it[i].N * r;
-    const LoraPassArgs a{it[i].dY, M, it[i].N, it[i].B, {it[i].u}, r, r, p.crange, part_down, part_grad};
-    launch_pass<true, true, true>(p, a, stream);
-    jobs[2 * i] = reduce_job(part_down, p.cranges, M * r, 0, r, false, 1.f, 0, it[i].v);
-    jobs[2 * i + 1] = reduce_job(part_grad, p.mblocks, it[i].N * r, 0, r, false, scale, accumulate, it[i].dB);
+    float* part_grad = ws + (size_t)p[i].cranges * M * r;
+    ws = part_grad + (size_t)p[i].mblocks * it[i].N * r;
+    a[i] = LoraPassArgs{it[i].dY, M, it[i].N, it[i].B, {it[i].u}, r, r, p[i].crange, part_down, part_grad, 0};
+    jobs[2 * i] = reduce_job(part_down, p[i].cranges, M * r, 0, r, false, 1.f, 0, it[i].v);
+    jobs[2 * i + 1] = reduce_job(part_grad, p[i].mblocks, it[i].N * r, 0, r, false, scale, accumulate, it[i].dB);
   }
+  launch_passes<true, true, true>(count, p, a, stream);
   launch_reduce(jobs, 2 * count, stream);
   return hipGetLastError();
 }
@@ -611,19 +647,22 @@ hipError_t launch_lora_dx_group(int count, const uint16_t* X, int64_t M, int64_t
   ReduceJob jobs[4];
   if (dx_pass_grouped(count, r)) {
     const LoraPassPlan p = lora_pass_plan(M, K, count * r);
-    LoraPassArgs a{X, M, K, nullptr, {}, r, count * r, p.crange, nullptr, ws};
+    LoraPassArgs a{X, M, K, nullptr, {}, r, count * r, p.crange, nullptr, ws, 0};
     for (int i = 0; i < count; ++i) a.P[i] = v[i];
     launch_pass<false, true, false>(p, a, stream);
     for (int i = 0; i < count; ++i)
       jobs[i] = reduce_job(ws + (size_t)i * p.mblocks * K * r, p.mblocks, K * r, K, r, true, scale, accumulate, dA[i]);
   } else {
+    // one pass per linear, all in one launch
+    LoraPassPlan p[kMaxPassGroup];
+    LoraPassArgs a[kMaxPassGroup];
     for (int i = 0; i < count; ++i) {
-      const LoraPassPlan p = lora_pass_plan(M, K, r);
-      const LoraPassArgs a{X, M, K, nullptr, {v[i]}, r, r, p.crange, nullptr, ws};
-      launch_pass<false, true, false>(p, a, stream);
-      jobs[i] = reduce_job(ws, p.mblocks, K * r, K, r, true, scale, accumulate, dA[i]);
-      ws += (size_t)p.mblocks * K * r;
+      p[i] = lora_pass_plan(M, K, r);
+      a[i] = LoraPassArgs{X, M, K, nullptr, {v[i]}, r, r, p[i].crange, nullptr, ws, 0};
+      jobs[i] = reduce_job(ws, p[i].mblocks, K * r, K, r, true, scale, accumulate, dA[i]);
+      ws += (size_t)p[i].mblocks * K * r;
     }
+    launch_passes<false, true, false>(count, p, a, stream);
   }
   launch_reduce(jobs, count, stream);
   return hipGetLastError();
