@@ -79,6 +79,7 @@ def test_single_linear_workload():
     # ranks that are not a power of two: the adapter kernels, the fused GEMMs' partial adapter steps
     # (r > 64: two steps, the second partial) and the few-token epilogue's u runs (256 / r rounds down)
     (300, 400, 960, 48, 1.0),      #   GEMM with a split contraction
+    (700, 1040, 4160, 48, 0.5),    #   rank-48 adapter passes: three row blocks, ragged column ranges
     (300, 400, 960, 80, 0.5),
     (300, 400, 960, 96, 0.5),
     (300, 400, 960, 112, 0.25),
