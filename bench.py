@@ -322,7 +322,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (the data-"
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 (the data-"
                                    "parallel sharding across GPUs is described, not built)"}))
         sys.exit(2)
 

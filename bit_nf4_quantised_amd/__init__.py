@@ -448,8 +448,9 @@ def q4_dequant(packed, numel: int, codebook, blocksize: int, out, absmax=None, s
 # ------------------------------------------------------------------------- the adapter update
 @dataclass(frozen=True)
 class AdamWConfig:
-    """Hyper-parameters of the adapter update; lr and the clipping threshold are the paper's,
-    the rest torch's AdamW defaults."""
+    """Hyper-parameters of the adapter update; lr and the clipping threshold are the ones "QLoRA,
+    explained" gives (The algorithm, step by step; Minimal implementation), the rest torch's AdamW
+    defaults."""
     lr: float = 2e-4
     beta1: float = 0.9
     beta2: float = 0.999

@@ -1,7 +1,7 @@
 // The adapter update of a training step (gfx950): global gradient-norm clipping, then AdamW.
 //
 // "QLoRA, explained", The algorithm, step by step / Minimal implementation: after the backward the
-// adapter gradients are clipped by their global norm (0.3 in the paper) and AdamW (32-bit state)
+// adapter gradients are clipped by their global norm (0.3 in the original runs) and AdamW (32-bit state)
 // updates A and B only. AdamW with decoupled weight decay, for clipped gradient g at step t:
 //   p <- p (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;
 //   p <- p - (lr / (1 - b1^t)) m / (sqrt(v) / sqrt(1 - b2^t) + eps)

@@ -287,7 +287,7 @@ int q4_dequant(const uint8_t *packed, int64_t numel, int32_t codebook, int32_t b
 
 /* ---- The adapter update of a training step ("QLoRA, explained", The algorithm, step by step, and
  * Minimal implementation): the adapter gradients are clipped by their global L2 norm (0.3 in the
- * paper), then AdamW with 32-bit state updates A and B only. AdamW as torch documents it
+ * original runs), then AdamW with 32-bit state updates A and B only. AdamW as torch documents it
  * (decoupled weight decay); for clipped gradient g = c * grad at step t = 1, 2, ...:
  *   p <- p * (1 - lr*weight_decay);  m <- beta1*m + (1-beta1)*g;  v <- beta2*v + (1-beta2)*g^2;
  *   p <- p - (lr / (1 - beta1^t)) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps),

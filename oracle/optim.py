@@ -1,7 +1,7 @@
 """The adapter update of a training step: gradient-norm clipping, then AdamW. TEST INFRASTRUCTURE ONLY.
 
 "QLoRA, explained", The algorithm, step by step: once the backward pass has produced them, the
-gradients of A and B are clipped by their global norm (0.3 in the paper's runs) and an AdamW optimiser (32-bit state, or 8-bit,
+gradients of A and B are clipped by their global norm (0.3 in the original runs) and an AdamW optimiser (32-bit state, or 8-bit,
 optionally paged) updates A and B only; "Minimal implementation" shows torch's AdamW with lr 2e-4
 and clip_grad_norm_(..., 0.3). The pages fix no other constants, so the reading taken is the
 plainest one: the AdamW of Loshchilov and Hutter with decoupled weight decay, in the form torch

@@ -70,7 +70,7 @@ def test_quantiles_against_high_precision():
 
 def test_delta_is_pinned_by_printed_codes():
     """Neighbouring readings of the tail probability fail to reproduce the printed codes, so the
-    printed values do pin the construction (the survey of readings: 1-1/32, 1-1/30, 16/17)."""
+    printed values do pin the construction (the readings tried: 1-1/32, 1-1/30, 16/17)."""
     ex = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
 
     def book(delta):
