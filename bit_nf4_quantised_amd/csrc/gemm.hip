@@ -517,18 +517,22 @@ __global__ __launch_bounds__(kThreads) void qlora_gemm_kernel(const GemmArgs ga)
       }
     };
 
-    lds_barrier();
-    StepWords cur = fetch(0);
-    for (int q = 0; q <= steps; ++q) {
+    // one phase: expand step q's words (read a phase ago) while reading step q + 1's into `nxt`;
+    // the loop below alternates two sets of words, so none is copied from one phase to the next
+    auto phase = [&](int q, const StepWords& cur, StepWords& nxt) {
       if (q < main_steps) {
-        StepWords nxt = cur;
         if (q + 1 < main_steps) nxt = fetch(q + 1);
         dequant(q, cur);
-        cur = nxt;
       } else if (q < steps) {
         store_lora(q);
       }
       lds_barrier();
+    };
+    lds_barrier();
+    StepWords wa = fetch(0), wb = wa;
+    for (int q = 0; q <= steps; q += 2) {   // steps + 1 phases, one barrier each
+      phase(q, wa, wb);
+      if (q + 1 <= steps) phase(q + 1, wb, wa);
     }
     return;
   }
