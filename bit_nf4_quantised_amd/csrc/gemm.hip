@@ -731,7 +731,8 @@ __global__ __launch_bounds__(256) void gemm_ksum_tail_kernel(const f32x4* __rest
 //   * else 128-row tiles (64 at most 64 tokens), with two ranges when the 128-row tiles would
 //     number at most 128 (at most half of MI355X's 256 CUs busy) and there are at least 8 steps.
 // The dX GEMM takes 256-row tiles when there are at least 192 of them (with the tail), else 128 or
-// 64, never a uniform split.
+// 64 with the contraction cut into up to 4 or 8 ranges (at least 8 steps each) when the tiles are
+// few: at 16 tokens a 4096x4096 weight makes 32 tiles, and a tile's time follows its steps.
 struct GemmPlan {
   int bm, ks;
   int whole, tail, tsplit;   // tail mode when tail > 0
@@ -779,7 +780,15 @@ static GemmPlan dx_gemm_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t gx = (K + kBN - 1) / kBN, steps = (N + kBK - 1) / kBK;
   const int64_t t256 = gx * ((M + 255) / 256);
   p.bm = (M > 128 && t256 >= 192) ? 256 : M > 64 ? 128 : 64;
-  if (p.bm == 256) plan_tail(p, t256, steps);
+  if (p.bm == 256) {
+    plan_tail(p, t256, steps);
+    return p;
+  }
+  // few tokens: each tile's contraction in up to 8 (64-row tiles) or 4 (128-row tiles) ranges of at
+  // least 8 steps, so that about 256 workgroups share the weight's steps
+  const int64_t tiles = gx * ((M + p.bm - 1) / p.bm);
+  const int64_t ks = min((int64_t)(p.bm == 64 ? 8 : 4), min(steps / 8, (256 + tiles - 1) / tiles));
+  if (ks > 1) p.ks = (int)ks;
   return p;
 }
 

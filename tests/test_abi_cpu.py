@@ -230,6 +230,36 @@ def test_gemm_workspace_follows_the_plan(M, N, K, ks):
             q.NF4_ERR_WORKSPACE
 
 
+def _dx_plan_ks(M, N, K):
+    """Contraction ranges of the dX GEMM, from its documented plan: 256-row tiles when there are at
+    least 192 of them (their tail aside, never a uniform split); else 128-row tiles (64 at most 64
+    tokens) with the contraction cut into up to 4 (8 for 64-row tiles) ranges of at least 8 steps,
+    as many as bring the workgroups to about 256."""
+    gx, steps = -(-K // 128), -(-N // 64)
+    if M > 128 and gx * -(-M // 256) >= 192:
+        return 1
+    bm = 128 if M > 64 else 64
+    tiles = gx * -(-M // bm)
+    ks = min(8 if bm == 64 else 4, steps // 8, -(-256 // tiles))
+    return ks if ks > 1 else 1
+
+
+@pytest.mark.parametrize("M,N,K,ks", [(16, 4096, 28672, 2), (16, 4096, 4096, 8), (100, 2048, 1024, 4),
+                                      (40, 1040, 2112, 2), (16, 416, 1024, 1), (2048, 4096, 4096, 1)])
+def test_dx_workspace_follows_the_plan(M, N, K, ks):
+    assert _dx_plan_ks(M, N, K) == ks
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    part = ks * M * K * 4 if ks > 1 else 0
+    assert q.qlora_workspace_bytes(M, N, K, 16) >= up(M * 16 * 4) + (up(part) if part else 0)
+    if (M, N, K) == (16, 4096, 28672):
+        # the dX partial sums are the backward's largest partials here, so its workspace is v plus
+        # them exactly: one byte less is refused before any launch
+        need = up(M * 16 * 4) + up(part)
+        w = ctypes.byref(_w(N=N, K=K))
+        assert lib.qlora_linear_bwd(w, FAKE, FAKE, M, FAKE, FAKE, 16, 2.0, FAKE, FAKE, FAKE, FAKE, 0, FAKE,
+                                    need - 1, None) == q.NF4_ERR_WORKSPACE
+
+
 def test_group_validation():
     f = lib.qlora_linear_fwd_group
     P = ctypes.c_void_p
