@@ -728,11 +728,11 @@ __global__ __launch_bounds__(256) void gemm_ksum_tail_kernel(const f32x4* __rest
 //     least 8 steps each) when that makes at least 192 workgroups: a dequantised W tile then
 //     feeds 256 token rows instead of 128, which halves the dequantisation per flop (the k and v
 //     projections of a layer: 1024 output columns);
-//   * else 128-row tiles (64 at most 64 tokens), with two ranges when the 128-row tiles would
-//     number at most 128 (at most half of MI355X's 256 CUs busy) and there are at least 8 steps.
+//   * else 128-row tiles (64 at most 64 tokens), with the contraction cut into up to 4 (8 for
+//     64-row tiles) ranges, as many as keep the workgroups within one round (few_tile_ranges).
 // The dX GEMM takes 256-row tiles when there are at least 192 of them (with the tail), else 128 or
-// 64 with the contraction cut into up to 4 or 8 ranges (at least 8 steps each) when the tiles are
-// few: at 16 tokens a 4096x4096 weight makes 32 tiles, and a tile's time follows its steps.
+// 64 with the contraction cut the same way: at 16 tokens a 4096x4096 weight makes 32 tiles, and a
+// tile's time follows its steps.
 struct GemmPlan {
   int bm, ks;
   int whole, tail, tsplit;   // tail mode when tail > 0
@@ -746,6 +746,17 @@ static void plan_tail(GemmPlan& p, int64_t tiles, int64_t steps) {
   p.whole = (int)(tiles - R);
   p.tail = (int)R;
   p.tsplit = (int)s;
+}
+
+// Contraction ranges of 128- and 64-row tiles: as many as keep the workgroups within one round of
+// the 256 CUs, at most 4 (8 for 64-row tiles), each of at least 8 steps (two ranges from 8 steps
+// on). The last range then always keeps a step: ks <= 8 and ks <= steps / 8 give (ks - 1) *
+// ceil(steps / ks) < steps.
+static int few_tile_ranges(int64_t tiles, int64_t steps, int bm) {
+  if (steps < 8) return 1;
+  const int64_t by_steps = steps / 8 > 2 ? steps / 8 : 2;
+  const int64_t ks = min((int64_t)(bm == 64 ? 8 : 4), min(by_steps, 256 / tiles));
+  return ks > 1 ? (int)ks : 1;
 }
 
 static GemmPlan fwd_gemm_plan(int64_t M, int64_t N, int64_t K) {
@@ -765,13 +776,8 @@ static GemmPlan fwd_gemm_plan(int64_t M, int64_t N, int64_t K) {
       return p;
     }
   }
-  if (M <= 64) {
-    p.bm = 64;
-    return p;
-  }
-  const int64_t tiles = gx * ((M + 127) / 128);
-  p.bm = 128;
-  p.ks = (tiles <= 128 && steps >= 8) ? 2 : 1;
+  p.bm = M <= 64 ? 64 : 128;
+  p.ks = few_tile_ranges(gx * ((M + p.bm - 1) / p.bm), steps, p.bm);
   return p;
 }
 
@@ -784,11 +790,7 @@ static GemmPlan dx_gemm_plan(int64_t M, int64_t N, int64_t K) {
     plan_tail(p, t256, steps);
     return p;
   }
-  // few tokens: each tile's contraction in up to 8 (64-row tiles) or 4 (128-row tiles) ranges of at
-  // least 8 steps, so that about 256 workgroups share the weight's steps
-  const int64_t tiles = gx * ((M + p.bm - 1) / p.bm);
-  const int64_t ks = min((int64_t)(p.bm == 64 ? 8 : 4), min(steps / 8, (256 + tiles - 1) / tiles));
-  if (ks > 1) p.ks = (int)ks;
+  p.ks = few_tile_ranges(gx * ((M + p.bm - 1) / p.bm), steps, p.bm);
   return p;
 }
 

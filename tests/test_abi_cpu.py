@@ -190,14 +190,23 @@ def test_skinny_workspace_follows_the_plan(M, N, K, r):
         q.NF4_ERR_WORKSPACE
 
 
+def _few_tile_ranges(tiles, steps, bm):
+    """Contraction ranges of 128- and 64-row tiles: none below 8 steps; else as many as keep the
+    workgroups within one round of 256 CUs, at most 4 (8 for 64-row tiles), and at most
+    max(2, steps // 8)."""
+    if steps < 8:
+        return 1
+    return max(1, min(8 if bm == 64 else 4, max(2, steps // 8), 256 // tiles))
+
+
 def _gemm_fwd_bytes(M, N, K, r):
     """Forward workspace of the fused-GEMM path (M > 16), from its documented plan: 256-row tiles
     when there are at least 192 of them, with the tiles past the last whole round of 256 CUs cut
     into 2..4 contraction ranges (tile-major partial sums of 256 x 128 per piece); else, above 128
     tokens, 256-row tiles with ks = 2..4 contraction ranges of at least 8 steps when that makes at
-    least 192 workgroups; else 128-row tiles (64 at most 64 tokens) with two ranges when they
-    number at most 128 and there are 8 steps. A uniform split leaves ks x M x N fp32 partial sums;
-    u comes first. (At rank 16 the adapter's u needs no partial sums of its own.)"""
+    least 192 workgroups; else 128-row tiles (64 at most 64 tokens) with _few_tile_ranges ranges.
+    A uniform split leaves ks x M x N fp32 partial sums; u comes first. (At rank 16 the adapter's u
+    needs no partial sums of its own.)"""
     gx, steps = -(-N // 128), -(-K // 64)
     t256 = gx * -(-M // 256)
     ks, part = 1, 0
@@ -210,16 +219,19 @@ def _gemm_fwd_bytes(M, N, K, r):
     elif M > 128 and min(4, steps // 8, -(-256 // t256)) > 1 and t256 * min(4, steps // 8, -(-256 // t256)) >= 192:
         ks = min(4, steps // 8, -(-256 // t256))
         part = ks * M * N
-    elif M > 64:
-        ks = 2 if gx * -(-M // 128) <= 128 and steps >= 8 else 1
+    else:
+        bm = 64 if M <= 64 else 128
+        ks = _few_tile_ranges(gx * -(-M // bm), steps, bm)
         part = ks * M * N if ks > 1 else 0
     up = lambda v: (v + 255) // 256 * 256  # noqa: E731
     return up(M * r * 4) + (up(part * 4) if part else 0), ks
 
 
 @pytest.mark.parametrize("M,N,K,ks", [(2048, 1024, 4096, 4), (4096, 1024, 8192, 2), (1500, 1040, 2112, 4),
-                                      (2048, 4096, 4096, 1), (300, 400, 960, 2), (1800, 128, 14336, 2),
-                                      (2048, 14336, 4096, 2), (300, 16512, 2048, 4), (4096, 28672, 8192, 1)])
+                                      (2048, 4096, 4096, 1), (300, 400, 960, 2), (1800, 128, 14336, 4),
+                                      (2048, 14336, 4096, 2), (300, 16512, 2048, 4), (4096, 28672, 8192, 1),
+                                      (40, 4096, 2048, 4), (64, 4096, 4096, 8), (100, 256, 1024, 2),
+                                      (40, 256, 512, 2), (300, 19200, 960, 1)])
 def test_gemm_workspace_follows_the_plan(M, N, K, ks):
     need, plan_ks = _gemm_fwd_bytes(M, N, K, 16)
     assert plan_ks == ks
@@ -233,25 +245,22 @@ def test_gemm_workspace_follows_the_plan(M, N, K, ks):
 def _dx_plan_ks(M, N, K):
     """Contraction ranges of the dX GEMM, from its documented plan: 256-row tiles when there are at
     least 192 of them (their tail aside, never a uniform split); else 128-row tiles (64 at most 64
-    tokens) with the contraction cut into up to 4 (8 for 64-row tiles) ranges of at least 8 steps,
-    as many as bring the workgroups to about 256."""
+    tokens) with _few_tile_ranges ranges."""
     gx, steps = -(-K // 128), -(-N // 64)
     if M > 128 and gx * -(-M // 256) >= 192:
         return 1
     bm = 128 if M > 64 else 64
-    tiles = gx * -(-M // bm)
-    ks = min(8 if bm == 64 else 4, steps // 8, -(-256 // tiles))
-    return ks if ks > 1 else 1
+    return _few_tile_ranges(gx * -(-M // bm), steps, bm)
 
 
-@pytest.mark.parametrize("M,N,K,ks", [(16, 4096, 28672, 2), (16, 4096, 4096, 8), (100, 2048, 1024, 4),
+@pytest.mark.parametrize("M,N,K,ks", [(16, 4096, 28672, 1), (16, 4096, 4096, 8), (100, 2048, 1024, 4),
                                       (40, 1040, 2112, 2), (16, 416, 1024, 1), (2048, 4096, 4096, 1)])
 def test_dx_workspace_follows_the_plan(M, N, K, ks):
     assert _dx_plan_ks(M, N, K) == ks
     up = lambda v: (v + 255) // 256 * 256  # noqa: E731
     part = ks * M * K * 4 if ks > 1 else 0
     assert q.qlora_workspace_bytes(M, N, K, 16) >= up(M * 16 * 4) + (up(part) if part else 0)
-    if (M, N, K) == (16, 4096, 28672):
+    if (M, N, K) == (16, 4096, 4096):
         # the dX partial sums are the backward's largest partials here, so its workspace is v plus
         # them exactly: one byte less is refused before any launch
         need = up(M * 16 * 4) + up(part)

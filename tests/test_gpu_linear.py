@@ -61,6 +61,8 @@ def test_single_linear_workload():
     (16, 4096, 4096, 16, 2.0),     # 16 tokens on a 4096x4096 weight: dX in 8 contraction ranges
     (40, 1040, 2112, 16, 0.5),     #   two ranges, the second ending in a partial step
     (100, 2048, 1024, 32, 1.0),    #   128-row dX tiles in 4 ranges
+    (40, 4096, 2048, 16, 2.0),     # 17..64 tokens: the forward in 4 contraction ranges, dX in 8
+    (64, 2064, 4160, 16, 0.5),     #   forward in 8 ranges, the last of 2 steps; dX in 2, ragged
     (513, 128, 128, 16, 2.0),      # three row tiles, the last with one row
     (1, 400, 960, 16, 2.0),        # skinny forward
     (4, 400, 960, 64, 0.25),
