@@ -185,7 +185,10 @@ int qlora_linear_fwd_recompute_group(int32_t count, const nf4_weight *const *W, 
  * qlora_linear_fwd_group): for every i < count, as qlora_linear_bwd on linear i (dX_i, dA_i, dB_i
  * into its own outputs). Above 128 tokens, when the linears' 256-row dX tiles number at least 192
  * together, their dX GEMMs run as one launch (each dX_i is then computed exactly as a dX launch
- * without a split contraction computes it); the adapter passes run per linear.
+ * without a split contraction computes it). The adapter work is batched the same way: the passes
+ * over every dY_i as one launch, the passes over the shared x as one (a single pass for all dA_i
+ * when the ranks add up to 64 or less), and their ordered sums in one launch each; every dA_i and
+ * dB_i equals what qlora_linear_bwd returns for linear i, bit for bit.
  *   W, dy, A, B, u, dA, dB: HOST arrays of count entries, each as in qlora_linear_bwd.
  *   dx: NULL (no input gradient) or a HOST array of count device pointers, all set. A layer's
  *       gradient with respect to the shared x is the sum of the dX_i.
