@@ -60,11 +60,15 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 //   backward: [v (M*r fp32)] [partials of the pass over dY, then of the dX GEMM's tail, then of the
 //             pass over X (each launch's partials are consumed before the next one writes)]
 size_t fwd_part_floats(int64_t M, int64_t N, int64_t K, int r) {
-  if (nf4::skinny_eligible(M, N, K)) return nf4::skinny_workspace_floats(M, N, K, r);
   // the split GEMM's partial sums, after the partial sums of u (the two launches run in turn)
   const size_t gemm = nf4::fwd_gemm_part_floats(M, N, K);
   const size_t lu = nf4::lora_u_uses_pass(r) ? nf4::lora_pass_ws_floats(M, K, r, true, false) : 0;
-  return gemm > lu ? gemm : lu;
+  const size_t fused = gemm > lu ? gemm : lu;
+  if (!nf4::skinny_eligible(M, N, K)) return fused;
+  // few tokens: the skinny path's splits; from 5 tokens on a weight with fp32 scales takes the
+  // fused path instead, and the size does not depend on the weight, so it covers both
+  const size_t sk = nf4::skinny_workspace_floats(M, N, K, r);
+  return M <= 4 || sk >= fused ? sk : fused;
 }
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
   return align_up((size_t)M * r * 4) + align_up(fwd_part_floats(M, N, K, r) * 4);

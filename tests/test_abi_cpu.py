@@ -269,6 +269,22 @@ def test_dx_workspace_follows_the_plan(M, N, K, ks):
                                     need - 1, None) == q.NF4_ERR_WORKSPACE
 
 
+@pytest.mark.parametrize("M", [5, 16])
+def test_few_token_workspace_covers_the_fused_path(M):
+    # from 5 tokens on, a weight with fp32 scales takes the fused GEMM instead of the few-token
+    # kernel, and the workspace size does not depend on the weight: at K = 512 the GEMM cuts its
+    # contraction into 2 ranges (2 x M x N partial floats) where the few-token plan has one split
+    N, K, r = 4096, 512, 16
+    assert _few_tile_ranges(-(-N // 128), K // 64, 64) == 2
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    need = up(M * r * 4) + up(2 * M * N * 4)
+    assert q.qlora_workspace_bytes(M, N, K, r) >= need
+    w = q.CNF4Weight(FAKE, None, None, N, K)
+    w.absmax = FAKE
+    assert lib.qlora_linear_fwd(ctypes.byref(w), FAKE, M, FAKE, FAKE, r, 2.0, FAKE, None, FAKE, need - 1, None) == \
+        q.NF4_ERR_WORKSPACE
+
+
 def test_group_validation():
     f = lib.qlora_linear_fwd_group
     P = ctypes.c_void_p

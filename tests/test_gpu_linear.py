@@ -190,6 +190,8 @@ def _f32s_weight(w):
     (513, 128, 128, 64, 0.25),     # three row tiles, the last with one row
     (77, 1040, 1088, 128, 0.5),
     (8, 400, 960, 16, 2.0),        # few tokens: the fused GEMM, not the skinny path
+    (16, 4096, 512, 16, 2.0),      #   its contraction in 2 ranges, more partial sums than the
+                                   #   skinny path's single split: the workspace holds either
     (1, 400, 960, 16, 2.0),        # M <= 4: the few-token kernel with fp32 scales
     (4, 96, 4160, 32, 1.0),        #   65 blocks per row, a 64-column last step
     (3, 1040, 1088, 128, 0.5),     #   rank 128, ragged rows
