@@ -223,79 +223,64 @@ __global__ __launch_bounds__(256) void nf4_double_quant_kernel(const float* __re
 }
 
 // Double quantisation of several weights' scales in one launch. The tensors' groups are numbered
-// one after the other (group_begin[t] is tensor t's first); each wave encodes a contiguous run of
-// per_wave groups, exactly as nf4_double_quant_kernel encodes a group, with the scales of the
-// next two groups in flight. The wave finds its first group's tensor by bisection once and steps to the
-// next tensor when its run crosses into it (empty tensors are not in the batch).
-__global__ __launch_bounds__(256) void nf4_double_quant_many_kernel(const DqBatch b, int64_t per_wave) {
+// one after the other (group_begin[t] is tensor t's first); each wave encodes kDqRun consecutive
+// groups, exactly as nf4_double_quant_kernel encodes a group. It issues the loads of all of them
+// before it encodes any, so every wave keeps kDqRun KB in flight and a launch holds many short
+// waves instead of few long ones (a wave that walked 28 groups with two in flight spent most of
+// its time on the round trip of each). The wave finds its first group's tensor by bisection and
+// steps to the next tensor when its run crosses into it (empty tensors are not in the batch).
+constexpr int kDqRun = 4;
+__global__ __launch_bounds__(256) void nf4_double_quant_many_kernel(const DqBatch b) {
   const int lane = threadIdx.x & 63;
   const int64_t wv = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t total = b.group_begin[b.count];
-  int64_t g = wv * per_wave;
-  const int64_t g_end = min(total, g + per_wave);
-  if (g >= g_end) return;
-  int t = 0, hi = b.count;   // group_begin[t] <= g < group_begin[t + 1]
+  const int64_t g0 = wv * kDqRun;
+  if (g0 >= total) return;
+  int t = 0, hi = b.count;   // group_begin[t] <= g0 < group_begin[t + 1]
   while (hi - t > 1) {
     const int mid = (t + hi) >> 1;
-    if (g >= b.group_begin[mid]) t = mid;
+    if (g0 >= b.group_begin[mid]) t = mid;
     else hi = mid;
   }
-  // A tensor's fields, read from the kernel arguments once per tensor the run touches.
-  struct Tensor {
-    const float* absmax;
-    uint8_t* scale_q;
-    float* scale_c2;
-    int64_t nblocks, gbegin, gend;
-  };
-  auto tensor = [&](int tt) {
-    return Tensor{b.absmax[tt], b.scale_q[tt], b.scale_c2[tt], b.nblocks[tt], b.group_begin[tt],
-                  b.group_begin[tt + 1]};
-  };
-  // scales of group gg of tensor T (zeros past the tensor's end)
-  auto load = [&](const Tensor& T, int64_t gg) {
-    const int64_t lg = gg - T.gbegin, first = lg * kGroup + lane * 4;
-    if ((lg + 1) * kGroup <= T.nblocks) return *reinterpret_cast<const f32x4*>(T.absmax + first);
+  // scales of group gg of tensor tt (zeros past the tensor's end)
+  auto load = [&](int tt, int64_t gg) {
+    const float* absmax = b.absmax[tt];
+    const int64_t nblocks = b.nblocks[tt];
+    const int64_t lg = gg - b.group_begin[tt], first = lg * kGroup + lane * 4;
+    if ((lg + 1) * kGroup <= nblocks) return *reinterpret_cast<const f32x4*>(absmax + first);
     f32x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (first + i < T.nblocks) ? T.absmax[first + i] : 0.f;
+    for (int i = 0; i < 4; ++i) v[i] = (first + i < nblocks) ? absmax[first + i] : 0.f;
     return v;
   };
-  // two groups ahead in flight: the group after next is loaded while the current one is encoded
-  Tensor cur_t = tensor(t);
-  Tensor t1 = cur_t;
-  f32x4 cur = load(cur_t, g), nx1 = cur;
-  int i1 = t;
-  if (g + 1 < g_end) {
-    if (g + 1 >= t1.gend) t1 = tensor(++i1);
-    nx1 = load(t1, g + 1);
+  int tt[kDqRun];
+  f32x4 v[kDqRun];
+#pragma unroll
+  for (int i = 0; i < kDqRun; ++i) {
+    const int64_t g = g0 + i;
+    if (g < total) {
+      while (g >= b.group_begin[t + 1]) ++t;
+      tt[i] = t;
+      v[i] = load(t, g);
+    }
   }
-  for (;;) {
-    const int64_t g2 = g + 2;
-    Tensor t2 = t1;
-    int i2 = i1;
-    f32x4 nx2 = nx1;
-    if (g2 < g_end) {
-      if (g2 >= t2.gend) t2 = tensor(++i2);
-      nx2 = load(t2, g2);
-    }
-    const int64_t lg = g - cur_t.gbegin;
-    const int64_t first = lg * kGroup + lane * 4;
+#pragma unroll
+  for (int i = 0; i < kDqRun; ++i) {
+    const int64_t g = g0 + i;
+    if (g >= total) break;
+    uint8_t* scale_q = b.scale_q[tt[i]];
+    const int64_t nblocks = b.nblocks[tt[i]];
+    const int64_t lg = g - b.group_begin[tt[i]], first = lg * kGroup + lane * 4;
+    const f32x4 cur = v[i];
     const float c2 = wave_max(fmaxf(fmaxf(cur[0], cur[1]), fmaxf(cur[2], cur[3])));
-    if ((lg + 1) * kGroup <= cur_t.nblocks) {
+    if ((lg + 1) * kGroup <= nblocks) {
       const float cc[4] = {cur[0], cur[1], cur[2], cur[3]};
-      *reinterpret_cast<uint32_t*>(cur_t.scale_q + first) = e4m3_codes4(cc, c2);
+      *reinterpret_cast<uint32_t*>(scale_q + first) = e4m3_codes4(cc, c2);
     } else {
-      for (int i = 0; i < 4; ++i)
-        if (first + i < cur_t.nblocks) cur_t.scale_q[first + i] = (uint8_t)e4m3_code_of_ratio(cur[i], c2);
+      for (int k = 0; k < 4; ++k)
+        if (first + k < nblocks) scale_q[first + k] = (uint8_t)e4m3_code_of_ratio(cur[k], c2);
     }
-    if (lane == 0) cur_t.scale_c2[lg] = c2;
-    if (g + 1 >= g_end) break;
-    cur = nx1;
-    nx1 = nx2;
-    cur_t = t1;
-    t1 = t2;
-    i1 = i2;
-    ++g;
+    if (lane == 0) b.scale_c2[tt[i]][lg] = c2;
   }
 }
 
@@ -399,11 +384,8 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, uint8_t* sc
 hipError_t launch_double_quant_many(const DqBatch& b, hipStream_t stream) {
   const int64_t groups = b.group_begin[b.count];
   if (groups == 0) return hipSuccess;
-  // runs of groups for at most 32 waves per CU over 256 CUs
-  const int64_t per_wave = (groups + 8191) / 8192;
-  const int64_t waves = (groups + per_wave - 1) / per_wave;
-  hipLaunchKernelGGL(nf4_double_quant_many_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, b,
-                     per_wave);
+  const int64_t waves = (groups + kDqRun - 1) / kDqRun;
+  hipLaunchKernelGGL(nf4_double_quant_many_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, b);
   return hipGetLastError();
 }
 
