@@ -546,7 +546,7 @@ def bandwidth_paths(torch, q, dev, args):
         skinny[f"M={m}"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
                             "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "bytes": nbytes}
         log(f"[bench] skinny M={m}: {ms*1e3:.1f} us, {gbps:.0f} GB/s")
-        if m == 1:
+        if m in (1, 16):
             # the same forward with fp32 block scales (no double quantisation), 4 rotating copies
             fcopies = [base_f32] + [q.NF4Weight(base_f32.packed.clone(), None, None, base_f32.N, base_f32.K,
                                                 absmax=base_f32.absmax.clone()) for _ in range(3)]
@@ -557,10 +557,10 @@ def bandwidth_paths(torch, q, dev, args):
             fcall(0)
             fms = timed(fcall, 200, torch)
             fbytes = nbytes - nf4_bytes(lin.n * lin.k) + lin.n * lin.k // 2 + 4 * (lin.n * lin.k // 64)
-            skinny["M=1 fp32 scales"] = {"us": round(fms * 1e3, 2), "GBps": round(fbytes / (fms * 1e-3) / 1e9, 1),
-                                         "frac_hbm": round(fbytes / (fms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                                         "bytes": fbytes}
-            log(f"[bench] skinny M=1, fp32 scales: {fms*1e3:.1f} us")
+            skinny[f"M={m} fp32 scales"] = {"us": round(fms * 1e3, 2), "GBps": round(fbytes / (fms * 1e-3) / 1e9, 1),
+                                            "frac_hbm": round(fbytes / (fms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                                            "bytes": fbytes}
+            log(f"[bench] skinny M={m}, fp32 scales: {fms*1e3:.1f} us")
             del fcopies
     res["skinny_fwd_8192x28672"] = skinny
     del base_f32

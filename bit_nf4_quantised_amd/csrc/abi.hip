@@ -63,12 +63,9 @@ size_t fwd_part_floats(int64_t M, int64_t N, int64_t K, int r) {
   // the split GEMM's partial sums, after the partial sums of u (the two launches run in turn)
   const size_t gemm = nf4::fwd_gemm_part_floats(M, N, K);
   const size_t lu = nf4::lora_u_uses_pass(r) ? nf4::lora_pass_ws_floats(M, K, r, true, false) : 0;
-  const size_t fused = gemm > lu ? gemm : lu;
-  if (!nf4::skinny_eligible(M, N, K)) return fused;
-  // few tokens: the skinny path's splits; from 5 tokens on a weight with fp32 scales takes the
-  // fused path instead, and the size does not depend on the weight, so it covers both
-  const size_t sk = nf4::skinny_workspace_floats(M, N, K, r);
-  return M <= 4 || sk >= fused ? sk : fused;
+  // few tokens (either kind of scales): the skinny path's splits
+  if (nf4::skinny_eligible(M, N, K)) return nf4::skinny_workspace_floats(M, N, K, r);
+  return gemm > lu ? gemm : lu;
 }
 size_t fwd_ws(int64_t M, int64_t N, int64_t K, int r) {
   return align_up((size_t)M * r * 4) + align_up(fwd_part_floats(M, N, K, r) * 4);
@@ -136,7 +133,7 @@ int check_fwd(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t*
 int run_fwd_at(const nf4_weight* W, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
                int32_t r, float scale, uint16_t* y, float* u, float* part, hipStream_t stream) {
   const int64_t N = W->N, K = W->K;
-  if (nf4::skinny_eligible(M, N, K) && (!W->absmax || M <= 4)) {
+  if (nf4::skinny_eligible(M, N, K)) {
     return from_hip(nf4::launch_skinny_fwd(W->packed, W->scale_q, W->scale_c2, W->absmax, N, K, x, M, A, B, r,
                                            scale, part, u, y, W->codebook, stream));
   }
@@ -479,7 +476,7 @@ int qlora_linear_fwd_recompute(const nf4_weight* W, const uint16_t* x, int64_t M
       (ws && !aligned16(ws)))
     return NF4_ERR_ALIGN;
   const int64_t N = W->N, K = W->K;
-  if (nf4::skinny_eligible(M, N, K) && (!W->absmax || M <= 4)) {
+  if (nf4::skinny_eligible(M, N, K)) {
     // the skinny path forms u itself from the adapter rows; it needs the workspace
     const size_t need = fwd_ws(M, N, K, r);
     if (!ws || ws_bytes < need) return NF4_ERR_WORKSPACE;

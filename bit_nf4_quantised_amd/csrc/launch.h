@@ -133,7 +133,7 @@ struct SkinnyPlan {
 };
 SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r);
 size_t skinny_workspace_floats(int64_t M, int64_t N, int64_t K, int r);
-// absmax (fp32 block scales, scale_q / scale_c2 unused) is taken at M <= 4 only
+// absmax != null: fp32 block scales (scale_q / scale_c2 unused)
 hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, const float* scale_c2,
                              const float* absmax, int64_t N, int64_t K, const uint16_t* x, int64_t M,
                              const uint16_t* A, const uint16_t* B, int r, float scale, float* part,

@@ -55,7 +55,7 @@ struct SkinnyArgs {
   SkinnyPlan p;
   float* part;         // [w_splits][M][N]
   float* upart;        // [u parts][M][r]
-  const float* absmax; // fp32 block scales instead of scale_q / scale_c2 (M <= 4 kernel only)
+  const float* absmax; // fp32 block scales instead of scale_q / scale_c2
   Codes codes;         // the values the 4-bit indices select
 };
 
@@ -71,6 +71,7 @@ struct SkinnyW {
 struct SkinnyS {
   u32x4 cw;        // 16 bytes from the aligned word holding the step's first scale code
   u32x2 c2;        // second-level constants of the step's first group and the next one
+  u32x4 f0, f1;    // fp32 block scales (F32S): the step's eight blocks of the row
 };
 
 // This item's partial sums of u = x A^T: the 8-column chunks [ch0, ch1) of the contraction, for
@@ -131,6 +132,7 @@ __device__ __forceinline__ void u_chunks(const SkinnyArgs& g, int64_t step, int 
   ch1 = lo + n * (rb + 1) / g.p.w_blocks;
 }
 
+template <bool F32S>
 __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyArgs g) {
   __shared__ __attribute__((aligned(16))) f32x2 tab[256 * 32];
   // activation stages: 16 tokens x 64 chunks of 8 bf16
@@ -160,8 +162,9 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
   const int64_t row = (int64_t)rb * kSkRows + wave * 16 + m;   // this lane's row of W
   const int64_t rowc = min(row, g.N - 1);
   const int64_t nblocks = g.N * (g.K / kBlock);
-  const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.scale_q, (short)0, (int)((nblocks + 3) & ~int64_t(3)), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rs_q = F32S
+      ? __builtin_amdgcn_make_buffer_rsrc((void*)g.absmax, (short)0, (int)(nblocks * 4), kRsrcFlags)
+      : __builtin_amdgcn_make_buffer_rsrc((void*)g.scale_q, (short)0, (int)((nblocks + 3) & ~int64_t(3)), kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rs_c2 = __builtin_amdgcn_make_buffer_rsrc(
       (void*)g.scale_c2, (short)0, (int)(((nblocks + kGroup - 1) / kGroup) * 4), kRsrcFlags);
   // per-lane bases, so that the step loop works with 32-bit offsets (the block count of W is
@@ -182,8 +185,15 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
   };
   auto load_scales = [&](int s, SkinnyS& ss) {
     const uint32_t b0 = rowb + (uint32_t)min(s * 8, kb - 1);
-    ss.cw = __builtin_amdgcn_raw_buffer_load_b128(rs_q, b0 & ~3u, 0, 0);
-    ss.c2 = __builtin_amdgcn_raw_buffer_load_b64(rs_c2, (b0 >> 8) * 4u, 0, 0);
+    if constexpr (F32S) {
+      // the step's eight blocks (blocks past the row's end read another row's scale, or zero past
+      // the array: they only meet zero activations)
+      ss.f0 = __builtin_amdgcn_raw_buffer_load_b128(rs_q, b0 * 4u, 0, 0);
+      ss.f1 = __builtin_amdgcn_raw_buffer_load_b128(rs_q, b0 * 4u + 16u, 0, 0);
+    } else {
+      ss.cw = __builtin_amdgcn_raw_buffer_load_b128(rs_q, b0 & ~3u, 0, 0);
+      ss.c2 = __builtin_amdgcn_raw_buffer_load_b64(rs_c2, (b0 >> 8) * 4u, 0, 0);
+    }
   };
 
   // activation copy: thread t moves token t / 64, slot t % 64 (source chunk slot ^ token)
@@ -211,14 +221,23 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
     const uint32_t b0 = rowb + (uint32_t)min(s * 8, kb - 1);
     const uint32_t base = b0 & 3u;   // byte of the step's first code in the 16 loaded bytes
     float c1p[4];
+    if constexpr (F32S) {
+      // block 2 i + grp / 2 of the step's eight
+      const bool odd = (grp >> 1) != 0;
+      c1p[0] = __uint_as_float(odd ? ss.f0[1] : ss.f0[0]);
+      c1p[1] = __uint_as_float(odd ? ss.f0[3] : ss.f0[2]);
+      c1p[2] = __uint_as_float(odd ? ss.f1[1] : ss.f1[0]);
+      c1p[3] = __uint_as_float(odd ? ss.f1[3] : ss.f1[2]);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t b = rowb + (uint32_t)blk_of(s, i);
-      const uint32_t byte = base + (b - b0);   // < 16
-      const uint32_t word = byte < 4 ? ss.cw[0] : byte < 8 ? ss.cw[1] : byte < 12 ? ss.cw[2] : ss.cw[3];
-      const uint32_t code = word >> ((byte & 3u) * 8u);
-      const float c2 = (b >> 8) == (b0 >> 8) ? __uint_as_float(ss.c2[0]) : __uint_as_float(ss.c2[1]);
-      c1p[i] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)code, 0), c2);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t b = rowb + (uint32_t)blk_of(s, i);
+        const uint32_t byte = base + (b - b0);   // < 16
+        const uint32_t word = byte < 4 ? ss.cw[0] : byte < 8 ? ss.cw[1] : byte < 12 ? ss.cw[2] : ss.cw[3];
+        const uint32_t code = word >> ((byte & 3u) * 8u);
+        const float c2 = (b >> 8) == (b0 >> 8) ? __uint_as_float(ss.c2[0]) : __uint_as_float(ss.c2[1]);
+        c1p[i] = __fmul_rn(__builtin_amdgcn_cvt_f32_fp8((int)code, 0), c2);
+      }
     }
     if (more) load_scales(s + 1, ss);
     __builtin_amdgcn_sched_barrier(0);
@@ -620,7 +639,6 @@ hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, cons
                              const uint16_t* A, const uint16_t* B, int r, float scale, float* part,
                              float* u_out, uint16_t* y, int book, hipStream_t stream) {
   const SkinnyPlan p = skinny_plan(M, N, K, r);
-  if (absmax && !p.narrow) return hipErrorInvalidValue;   // fp32 scales: the M <= 4 kernel only
   float* upart = part + skinny_wpart_floats(p, M, N);
   SkinnyArgs g{packed, scale_q, scale_c2, N, K, x, M, A, r, p, part, upart, absmax, {}};
   if (!codes_of(book, g.codes)) return hipErrorInvalidValue;
@@ -629,8 +647,10 @@ hipError_t launch_skinny_fwd(const uint8_t* packed, const uint8_t* scale_q, cons
     hipLaunchKernelGGL(skinny4_fwd_kernel<true>, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
   else if (p.narrow)
     hipLaunchKernelGGL(skinny4_fwd_kernel<false>, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
+  else if (absmax)
+    hipLaunchKernelGGL(skinny_fwd_kernel<true>, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
   else
-    hipLaunchKernelGGL(skinny_fwd_kernel, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
+    hipLaunchKernelGGL(skinny_fwd_kernel<false>, dim3((unsigned)items), dim3(kSkWaves * 64), 0, stream, g);
   hipLaunchKernelGGL(skinny_epilogue_kernel, dim3((unsigned)((N + 255) / 256), (unsigned)M), dim3(256), 0,
                      stream, part, p.w_splits, upart, skinny_u_parts(p), M, N, r, B, scale, u_out, y);
   return hipGetLastError();

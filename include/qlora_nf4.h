@@ -78,9 +78,8 @@ enum {
 /* A quantised weight W (N x K), device memory. Its block scales are either double quantised
  * (scale_q and scale_c2 set, absmax NULL: 4.127 bits per weight) or the fp32 absmax itself
  * (absmax set, scale_q and scale_c2 NULL: the 4.5-bit baseline without double quantisation,
- * "QLoRA, explained", Double quantisation). nf4_dequant and the linear calls take either; with
- * fp32 scales the few-token forward path serves M <= 4 only (the fused GEMM above) and
- * qlora_merge is not available (NF4_ERR_SHAPE).
+ * "QLoRA, explained", Double quantisation). nf4_dequant, the linear calls (the few-token forward
+ * path included) take either; with fp32 scales qlora_merge is not available (NF4_ERR_SHAPE).
  * codebook names the values the indices select: Q4_CODEBOOK_NF4 (0, what nf4_quantize writes),
  * or Q4_CODEBOOK_FP4 / Q4_CODEBOOK_INT4 for indices written by q4_quantize at blocksize 64 (their
  * indices must be below 15). Every call that takes an nf4_weight dequantises with it; any other
@@ -237,8 +236,7 @@ int qlora_linear_bwd(const nf4_weight *W, const uint16_t *x, const uint16_t *dy,
  * dequantise + MFMA GEMM alone: one launch, or, when the output has too few tiles to fill the GPU
  * and ws holds qlora_workspace_bytes(M, N, K, r) bytes, the GEMM split over two contraction ranges
  * plus a launch that adds the two halves, exactly as qlora_linear_fwd does (so y equals its output
- * bit for bit). For M <= 16 it runs the skinny path (which forms u again from A) and needs ws,
- * unless the weight has fp32 scales and M > 4, where the fused GEMM serves.
+ * bit for bit). For M <= 16 it runs the skinny path (which forms u again from A) and needs ws.
  *   u   [M x r] float32 input.  y [M x N] bf16 output.  ws as qlora_linear_fwd (may be NULL if M > 16:
  *   then the GEMM is never split, same tolerance).
  * Errors as qlora_linear_fwd. */

@@ -269,15 +269,12 @@ def test_dx_workspace_follows_the_plan(M, N, K, ks):
                                     need - 1, None) == q.NF4_ERR_WORKSPACE
 
 
-@pytest.mark.parametrize("M", [5, 16])
-def test_few_token_workspace_covers_the_fused_path(M):
-    # from 5 tokens on, a weight with fp32 scales takes the fused GEMM instead of the few-token
-    # kernel, and the workspace size does not depend on the weight: at K = 512 the GEMM cuts its
-    # contraction into 2 ranges (2 x M x N partial floats) where the few-token plan has one split
-    N, K, r = 4096, 512, 16
-    assert _few_tile_ranges(-(-N // 128), K // 64, 64) == 2
-    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    need = up(M * r * 4) + up(2 * M * N * 4)
+@pytest.mark.parametrize("M,N,K", [(1, 8192, 28672), (5, 4096, 512), (16, 4096, 512), (16, 8192, 28672)])
+def test_fp32_scale_few_token_workspace_follows_the_plan(M, N, K):
+    # a weight with fp32 scales takes the few-token path at 1..16 tokens like a double-quantised
+    # one, with the same plan: one byte less than its partial sums is refused before any launch
+    r = 16
+    need = _skinny_fwd_bytes(M, N, K, r)
     assert q.qlora_workspace_bytes(M, N, K, r) >= need
     w = q.CNF4Weight(FAKE, None, None, N, K)
     w.absmax = FAKE

@@ -189,9 +189,10 @@ def _f32s_weight(w):
     (300, 400, 960, 16, 2.0),      # ragged in every tile dimension, K % 128 == 64
     (513, 128, 128, 64, 0.25),     # three row tiles, the last with one row
     (77, 1040, 1088, 128, 0.5),
-    (8, 400, 960, 16, 2.0),        # few tokens: the fused GEMM, not the skinny path
-    (16, 4096, 512, 16, 2.0),      #   its contraction in 2 ranges, more partial sums than the
-                                   #   skinny path's single split: the workspace holds either
+    (8, 400, 960, 16, 2.0),        # 5..16 tokens: the 16-row few-token kernel with fp32 scales
+    (16, 4096, 512, 16, 2.0),      #   one 512-column step per row block
+    (5, 1040, 4160, 128, 0.5),     #   65 blocks per row (a 64-column last step), ragged rows
+    (13, 528, 2112, 48, 1.0),      #   rank 48, a row block of 16 rows past its last whole tile
     (1, 400, 960, 16, 2.0),        # M <= 4: the few-token kernel with fp32 scales
     (4, 96, 4160, 32, 1.0),        #   65 blocks per row, a 64-column last step
     (3, 1040, 1088, 128, 0.5),     #   rank 128, ragged rows
@@ -213,11 +214,11 @@ def test_fp32_scale_weight_matches_oracle(M, N, K, r, s):
     assert_close("dB", dB, dbr)
 
 
-@pytest.mark.parametrize("M", [3, 200])
+@pytest.mark.parametrize("M", [3, 9, 200])
 def test_fp32_scale_weight_one_hot_and_recompute(M):
     # with B = 0, one-hot rows of x give y rows equal to columns of W~ bit for bit, one-hot rows of
     # dY give dX rows equal to rows of W~; the recompute forward equals the forward (M = 3: the
-    # few-token kernel, M = 200: the fused GEMM)
+    # four-row few-token kernel, M = 9: the 16-row one, M = 200: the fused GEMM)
     import torch
     import bit_nf4_quantised_amd as q
     from gpu_helpers import bf16_to_dev, bits_from_dev, dev

@@ -141,3 +141,28 @@ def test_skinny_forward(M):
     yr, ur = oracle.linear_fwd(x, wt, a, b, wk.scale)
     assert_close("y", f64_from_bits(bits_from_dev(y)), yr)
     assert_close("u", u.cpu().numpy(), ur)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_skinny_forward_fp32_scales(M):
+    # the few-token forward on the same full-size weight keeping its fp32 absmax (no double
+    # quantisation): the four-row kernel at M = 1, the 16-row kernel at M = 16
+    wk = wl.SKINNY
+    lin = wk.linears[0]
+    log(f"[workload] skinny fp32 scales M={M} N={lin.n} K={lin.k}")
+    w, x, a, b, dy = wl.linear_inputs(wk, 0, lin, m=M)
+    import torch
+    import bit_nf4_quantised_amd as q
+    from gpu_helpers import bf16_to_dev, bits_from_dev, dev, to_dev
+    qw = q.quantize_weight(to_dev(w.astype(np.float32)), double_quant=False)
+    y = torch.empty(M, lin.n, dtype=torch.int16, device=dev())
+    u = torch.empty(M, wk.r, dtype=torch.float32, device=dev())
+    q.qlora_linear_fwd(qw, bf16_to_dev(x), bf16_to_dev(a), bf16_to_dev(b), wk.scale, y, u)
+    torch.cuda.synchronize()
+    p_ref, c1_ref = oracle.quantize(w)
+    assert np.array_equal(qw.packed.cpu().numpy(), p_ref)
+    assert np.array_equal(qw.absmax.cpu().numpy(), c1_ref.astype(np.float32))
+    wt = oracle.dequant_blocks(p_ref, c1_ref, oracle.codebook(), 64, w.size).reshape(lin.n, lin.k)
+    yr, ur = oracle.linear_fwd(x, wt, a, b, wk.scale)
+    assert_close("y", f64_from_bits(bits_from_dev(y)), yr)
+    assert_close("u", u.cpu().numpy(), ur)
