@@ -186,8 +186,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
   auto load_scales = [&](int s, SkinnyS& ss) {
     const uint32_t b0 = rowb + (uint32_t)min(s * 8, kb - 1);
     if constexpr (F32S) {
-      // the step's eight blocks (blocks past the row's end read another row's scale, or zero past
-      // the array: they only meet zero activations)
+      // the step's eight blocks (past the row's end these are other rows' scales, or zeros past
+      // the array; process() replaces them with zero)
       ss.f0 = __builtin_amdgcn_raw_buffer_load_b128(rs_q, b0 * 4u, 0, 0);
       ss.f1 = __builtin_amdgcn_raw_buffer_load_b128(rs_q, b0 * 4u + 16u, 0, 0);
     } else {
@@ -228,6 +228,11 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_fwd_kernel(const SkinnyA
       c1p[1] = __uint_as_float(odd ? ss.f0[3] : ss.f0[2]);
       c1p[2] = __uint_as_float(odd ? ss.f1[1] : ss.f1[0]);
       c1p[3] = __uint_as_float(odd ? ss.f1[3] : ss.f1[2]);
+      if (s * 8 + 8 > kb) {   // the step runs past the row's end (wave-uniform)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (s * 8 + 2 * i + (grp >> 1) >= kb) c1p[i] = 0.f;
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
