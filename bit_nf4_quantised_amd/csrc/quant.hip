@@ -15,9 +15,11 @@ namespace nf4 {
 // ------------------------------------------------------------------------------------------
 // Quantise. One wave handles 8 blocks per iteration: lane l covers 8 consecutive values of block
 // (l / 8). The nearest-code decision must be exact (as if w / c were computed without rounding):
-//   fast path: x = w * (1/c) is within 2^-22.9 of w / c. The 15 decision midpoints of the
-//     codebook, binned on a grid of width 1/16 over [-1, 1], fall one per bin at most and at least
-//     1.6e-3 from any bin edge, so the bin of x gives the count of midpoints below it up to the
+//   fast path: x = w * rcp(c) (rcp to 1 ulp, one rounding in the product) is within
+//     1.5 * 2^-23 of w / c, so |x| <= 1 + 2^-22 and the bin index fma(x, 16, 16) truncated to an
+//     unsigned integer (negative and NaN values convert to 0) lies in 0 .. 32. The 15 decision
+//     midpoints of the codebook, binned on a grid of width 1/16 over [-1, 1], fall one per bin at
+//     most and at least 1.6e-3 from any bin edge, so the bin of x gives the count of midpoints below it up to the
 //     one midpoint inside the bin, which is compared directly. If x lies within 2^-20 of that
 //     midpoint, or the block scale is below 2^-100 (1/c could overflow), the value takes the
 //     slow path;
@@ -82,13 +84,13 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const void* __restric
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
     amax = max8(amax);
-    const float inv = 1.0f / amax;
+    const float inv = __builtin_amdgcn_rcpf(amax);
     const bool tiny = amax < 0x1p-100f;
     uint32_t word = 0, slow = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = v[e] * inv;
-      const uint32_t bin = min(__float2uint_rz(fmaf(x, 16.f, 16.f)), 32u);
+      const uint32_t bin = __float2uint_rz(fmaf(x, 16.f, 16.f));
       const BinEntry be = tab[bin];
       const uint32_t idx = be.base + (x > be.mid ? 1u : 0u);
       if (fabsf(x - be.mid) <= 0x1p-20f || tiny) slow |= 1u << e;
