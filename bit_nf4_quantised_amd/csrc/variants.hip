@@ -10,9 +10,9 @@
 //   q4_dequant_kernel<L, DQ>    bf16(fl32(q[idx] * s)), s = the fp32 absmax itself, or
 //                               fl32(e4m3 * c2) when the scales are double quantised.
 //
-// Exact nearest code for any such codebook: x = w * fl32(1 / c) is within 2^-23 of w / c. A table
-// of 256 bins of width 1/128 over [-1, 1], built once on the host from the codebook and copied
-// into LDS by each workgroup, holds per bin the number of decision midpoints below it and the
+// Exact nearest code for any such codebook: x = w * rcp(c) (rcp to 1 ulp) is within 1.5 * 2^-23 of
+// w / c. A table of 256 bins of width 1/128 over [-1, 1], built once on the host from the codebook
+// and copied into LDS by each workgroup, holds per bin the number of decision midpoints below it and the
 // midpoint inside it (at most one: the codebooks' midpoints are at least 0.04 apart). Then idx = base + (x > mid) is the
 // exact count of midpoints below x, and it equals the count below w / c unless x lies within 2^-20
 // of the bin's midpoint or of one of its edges (or the scale is below 2^-100): such values count
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void q4_quantize_kernel(const f32x4* __restric
   if (valid && (threadIdx.x & (B / 16 - 1)) == 0) absmax[e0 / B] = c;
 
   const bool tiny = c < 0x1p-100f;                  // includes an all-zero block
-  const float inv = tiny ? 0.f : __fdiv_rn(1.0f, c);
+  const float inv = tiny ? 0.f : __builtin_amdgcn_rcpf(c);
   uint32_t idx[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
