@@ -133,6 +133,54 @@ def test_double_quant_ties_and_sizes(nblocks):
     assert np.array_equal(codes.cpu().numpy(), codes_ref)
 
 
+def _e4m3_boundary_scales(c2: float, width: int = 8) -> np.ndarray:
+    """Scales of groups whose maximum is c2: the float32 values within `width` ulps of c2 times every
+    E4M3 value in [0, 1] and of c2 times every midpoint between neighbouring values, capped at c2;
+    each group of 256 starts with c2 itself."""
+    unit = oracle.e4m3_unit_values()
+    pts = np.concatenate([unit, (unit[:-1] + unit[1:]) / 2])
+    base = (pts * c2).astype(np.float32).view(np.uint32).astype(np.int64)
+    cand = (base[:, None] + np.arange(-width, width + 1)[None, :]).reshape(-1)
+    cand = cand[(cand >= 0) & (cand < 0x7F800000)].astype(np.uint32).view(np.float32)
+    cand = np.unique(cand[cand <= np.float32(c2)])
+    per = 255
+    groups = -(-cand.size // per)
+    out = np.zeros(groups * 256, np.float32)
+    for g in range(groups):
+        chunk = cand[g * per:(g + 1) * per]
+        out[g * 256] = np.float32(c2)
+        out[g * 256 + 1:g * 256 + 1 + chunk.size] = chunk
+    return out
+
+
+@pytest.mark.parametrize("c2", [1.0, 0.0213, 3.7e-5, 117.3, 2.0 ** -59, 1e-20])
+def test_double_quant_at_every_code_boundary(c2):
+    # scales within a few ulps of c2 times every E4M3 value and every midpoint between neighbours:
+    # where the truncation to E4M3 and the one-fma midpoint decision are closest to going wrong
+    # (c2 = 1e-20 takes the exact path for group maxima below 2^-60)
+    import bit_nf4_quantised_amd as q
+    c1 = _e4m3_boundary_scales(c2)
+    log(f"[dq] boundary sweep c2={c2} scales={c1.size}")
+    codes = torch.empty(c1.size, dtype=torch.uint8, device=dev())
+    c2d = torch.empty(c1.size // 256, dtype=torch.float32, device=dev())
+    q.nf4_double_quant(to_dev(c1), codes, c2d)
+    torch.cuda.synchronize()
+    codes_ref, c2_ref = oracle.double_quant(c1)
+    assert np.array_equal(c2d.cpu().numpy().view(np.uint32), c2_ref.view(np.uint32))
+    assert np.array_equal(codes.cpu().numpy(), codes_ref)
+    # the batched kernel on the same scales, cut into three weights (the middle one ragged)
+    cuts = [0, 768, 768 + 700, c1.size]
+    parts = [to_dev(c1[a:b]) for a, b in zip(cuts, cuts[1:])]
+    mcodes = [torch.empty(p.numel(), dtype=torch.uint8, device=dev()) for p in parts]
+    mc2 = [torch.empty((p.numel() + 255) // 256, dtype=torch.float32, device=dev()) for p in parts]
+    q.nf4_double_quant_many(parts, mcodes, mc2)
+    torch.cuda.synchronize()
+    for (a, b), mc, m2 in zip(zip(cuts, cuts[1:]), mcodes, mc2):
+        cr, c2r = oracle.double_quant(c1[a:b])
+        assert np.array_equal(mc.cpu().numpy(), cr)
+        assert np.array_equal(m2.cpu().numpy().view(np.uint32), c2r.view(np.uint32))
+
+
 def test_empty_input_is_a_noop():
     import bit_nf4_quantised_amd as q
     e = torch.empty(0, dtype=torch.float32, device=dev())
