@@ -291,6 +291,19 @@ def other_configs(torch, q, dev, skip):
                         "what": "forward (few-token kernel) + backward (dX GEMM, dA, dB) of one "
                                 "4096x4096 linear at 16 tokens; the weight is read twice per step"})
             log(f"[bench] config single: {ms*1e3:.1f} us per fwd+bwd")
+            # the same step captured in a HIP graph (every call is a plain sequence of kernel
+            # launches): ten steps per graph, replayed, so that the host's launch work per kernel
+            # leaves the measured time; the eager figure above is the primary one
+            reps = 10
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(reps):
+                    step(i)
+            graph.replay()
+            ms_g = timed(lambda _i: graph.replay(), 5, torch) / reps
+            ent["us_per_step_hip_graph"] = round(ms_g * 1e3, 2)
+            log(f"[bench] config single, replayed from a HIP graph: {ms_g*1e3:.1f} us per fwd+bwd")
+            del graph
         else:
             fwd, big, gflops = fwd_gemm_fn(q, units, wk.m, wk.scale)
             fwd()

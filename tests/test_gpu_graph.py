@@ -1,8 +1,8 @@
 """A training step captured in a HIP graph and replayed: every per-step call of the library is a
 plain sequence of kernel launches (no allocation, copy, memset or synchronisation), so a caller can
-capture it. One step: forward and backward of two adapted linears, then the clipped AdamW update of
-their adapters through a plan, whose bf16 copies are the A and B the next forward reads. The graph
-is replayed three times, with eager work and a synchronisation between replays, and every replay
+capture it. One step (at 384 tokens, and at 16: the few-token path): forward and backward of two
+adapted linears, then the clipped AdamW update of their adapters through a plan, whose bf16 copies
+are the A and B the next forward reads. The graph is replayed three times, with eager work and a synchronisation between replays, and every replay
 must equal the same step run eagerly, bit for bit (all kernels are deterministic).
 """
 import numpy as np
@@ -14,10 +14,10 @@ from gpu_helpers import dev, log
 pytestmark = pytest.mark.gpu
 
 
-def _setup():
+def _setup(M):
     import torch
     import bit_nf4_quantised_amd as q
-    M, r, s = 384, 16, 2.0
+    r, s = 16, 2.0
     shapes = [(1024, 512), (768, 1024)]
     lins = []
     for i, (N, K) in enumerate(shapes):
@@ -56,9 +56,13 @@ def _setup():
     return step, state
 
 
-def test_training_step_replays_from_a_graph():
+@pytest.mark.parametrize("M", [384, 16])
+def test_training_step_replays_from_a_graph(M):
+    # 384 tokens: the fused GEMMs; 16 tokens: the few-token forward and its epilogue, and the dX
+    # GEMM with its contraction split into ranges and their ordered sum
     import torch
-    step, state = _setup()
+    log(f"[graph] M={M}")
+    step, state = _setup(M)
     torch.cuda.synchronize()
     start = [t.clone() for t in state]
     eager = []
