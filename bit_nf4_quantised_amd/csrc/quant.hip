@@ -15,14 +15,16 @@ namespace nf4 {
 // ------------------------------------------------------------------------------------------
 // Quantise. One wave handles 8 blocks per iteration: lane l covers 8 consecutive values of block
 // (l / 8). The nearest-code decision must be exact (as if w / c were computed without rounding):
-//   fast path: x = w * rcp(c) (rcp to 1 ulp, one rounding in the product) is within
-//     1.5 * 2^-23 of w / c, so |x| <= 1 + 2^-22 and the bin index fma(x, 16, 16) truncated to an
-//     unsigned integer (negative and NaN values convert to 0) lies in 0 .. 32. The 15 decision
-//     midpoints of the codebook, binned on a grid of width 1/16 over [-1, 1], fall one per bin at
-//     most and at least 1.6e-3 from any bin edge, so the bin of x gives the count of midpoints below it up to the
-//     one midpoint inside the bin, which is compared directly. If x lies within 2^-20 of that
-//     midpoint, or the block scale is below 2^-100 (1/c could overflow), the value takes the
-//     slow path;
+//   fast path, in bin units: y = fma(w, 16 rcp(c), 16) (rcp to 1 ulp; 16 rcp(c) is exact; one
+//     rounding) is within 2^-18 of 16 w / c + 16, so y <= 32 + 2^-17 and its truncation to an
+//     unsigned integer (negative and NaN values convert to 0) is a bin index in 0 .. 32. The 15
+//     decision midpoints m of the codebook, binned on a grid of width 1/16 over [-1, 1], fall one
+//     per bin at most and at least 1.6e-3 (0.0256 bin units) from any bin edge, so the bin gives
+//     the count of midpoints below up to the one midpoint inside the bin, stored as
+//     fl32(16 m + 16) (within 2^-19 of the exact value) and compared with y directly: that
+//     decides as w / c against m whenever the two differ by more than 2^-18 + 2^-19 bin units. If
+//     y lies within 2^-16 bin units (2^-20 of w / c) of the midpoint, or the block scale is below
+//     2^-100 (rcp(c) could overflow), the value takes the slow path;
 //   slow path: count the midpoints m_i with w > c * m_i in fp64, where the product of a 24-bit
 //     scale and a <= 26-bit midpoint is exact.
 struct BinEntry {
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const void* __restric
     for (int i = 0; i < 15; ++i) {
       double m = mid64(i);
       if (m < lo) ++base;
-      else if (m < hi) mid = (float)m;
+      else if (m < hi) mid = (float)(16.0 * m + 16.0);   // in bin units
     }
     tab[threadIdx.x] = BinEntry{mid, base};
   }
@@ -84,24 +86,26 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const void* __restric
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
     amax = max8(amax);
-    const float inv = __builtin_amdgcn_rcpf(amax);
+    const float inv16 = 16.f * __builtin_amdgcn_rcpf(amax);
     const bool tiny = amax < 0x1p-100f;
-    uint32_t word = 0, slow = 0;
+    uint32_t word = 0;
+    float dmin = __builtin_inff();   // closest approach of y to a bin's midpoint, over the 8 values
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x = v[e] * inv;
-      const uint32_t bin = __float2uint_rz(fmaf(x, 16.f, 16.f));
-      const BinEntry be = tab[bin];
-      const uint32_t idx = be.base + (x > be.mid ? 1u : 0u);
-      if (fabsf(x - be.mid) <= 0x1p-20f || tiny) slow |= 1u << e;
+      const float y = fmaf(v[e], inv16, 16.f);
+      const BinEntry be = tab[__float2uint_rz(y)];
+      const uint32_t idx = be.base + (y > be.mid ? 1u : 0u);
+      dmin = fminf(dmin, fabsf(y - be.mid));
       word |= idx << (8 * (e >> 1) + ((e & 1) ? 0 : 4));
     }
-    if (__builtin_expect(__any(slow != 0), 0)) {
-      if (slow) {
+    const bool any_slow = tiny || dmin <= 0x1p-16f;
+    if (__builtin_expect(__any(any_slow), 0)) {
+      if (any_slow) {
         const double c = (double)amax;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          if (slow & (1u << e)) {
+          const float y = fmaf(v[e], inv16, 16.f);
+          if (tiny || fabsf(y - tab[__float2uint_rz(y)].mid) <= 0x1p-16f) {
             uint32_t idx = 0;
             for (int i = 0; i < 15; ++i) idx += ((double)v[e] > c * mid64(i)) ? 1u : 0u;
             const int sh = 8 * (e >> 1) + ((e & 1) ? 0 : 4);
